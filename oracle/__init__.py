@@ -1,0 +1,20 @@
+"""CPU oracle for large-beam Gated DeltaNet decoding.
+
+TEST INFRASTRUCTURE, not part of the product.  Only tests/,
+__graft_entry__.smoke() and bench.py's cpu_baseline leg may import, call or
+execute anything here.  The HIP path never routes through it.
+
+A plain, slow FullState implementation in float64: every beam materialises
+its d_v x d_k state by eq. (4) of the OneLA reading note, states are copied
+when beams are re-parented, and scoring, selection and ancestry are done by
+brute force (full sort).  It imports nothing from the GPU package; both sides
+share only the seeded input generators in synth/.
+
+Parity status: every function here is pinned by tests/test_oracle_*.py
+(exact-arithmetic identities, closed forms, brute force, library routines);
+no function is "parity unpinned".
+"""
+from .gdn import gdn_token, prefill, rank1_transition  # noqa: F401
+from .beam import (FullStateDecoder, ancestry_update, capacity_elements,  # noqa: F401
+                   log_softmax_rows, step_scores, top_w)
+from .run import decode_request, prefill_request  # noqa: F401
