@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Throughput of large-beam GDN decoding on one MI355X.
+
+One bench step = one whole decode of a synthetic batch: gdn_beam_init, then for
+every SID step t: gdn_beam_step (fused projection + replay + update + record
+append) and gdn_beam_select (scoring, exact global top-W, ancestry remap).
+value = beam transitions (sum over steps of R*H*W_t) per second of wall time.
+
+The step kernel is also timed on its own stream with HIP events around each
+launch; its achieved algorithmic bandwidth is reported against the 8 TB/s HBM
+peak.  The CPU oracle (float64 FullState) is timed on a bounded sample of the
+same workload.
+
+    python bench.py [--workload batch|stress|growing|single|tiny] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN beam-transitions/sec (R×H×W per SID step) at 1 MI355X; % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_beam_amd", "csrc", "gdn_beam_kernels.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="batch")
+    p.add_argument("--mode", choices=["select", "forced"], default="select")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU oracle time")
+    p.add_argument("--quiet", action="store_true")
+    return p.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def step_bytes(wl, t, distinct):
+    """Algorithmic HBM bytes of one gdn_beam_step launch at step t.
+
+    Per (request, head): S_ctx once (4 d_v d_k); per beam: q, k, v (e each),
+    alpha, beta (8), the new record (4 + 4 d_v + e d_k) and o_t (4 d_v); per distinct
+    ancestor record referenced: 4 + 4 d_v + e d_k.  Per request: t ancestry indices
+    per beam (4 t W_t).  `distinct[r]` = distinct (step, slot) records request r's
+    beams reference at step t (identical for every head).
+    """
+    e = 2 if wl.io == "bf16" else 4
+    W = wl.width(t)
+    rec = 4 + 4 * wl.d_v + e * wl.d_k
+    per_rh = 4 * wl.d_v * wl.d_k + W * (e * (2 * wl.d_k + wl.d_v) + 8 + rec + 4 * wl.d_v)
+    total = wl.R * wl.H * per_rh + 4 * t * W * wl.R
+    total += wl.H * rec * int(np.sum(distinct))
+    return total
+
+
+def step_flops(wl, t):
+    W = wl.width(t)
+    return wl.R * wl.H * W * (4 * wl.d_v * wl.d_k + t * (4 * wl.d_k + 4 * wl.d_v) + 8 * wl.d_v)
+
+
+def kernel_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(wl_name):
+    """HBM bytes per step-kernel launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source."""
+    f = os.path.join(ROOT, "profiles", f"step_kernel_{wl_name}_traffic.json")
+    if not os.path.exists(f):
+        return None
+    try:
+        d = json.load(open(f))
+    except Exception:
+        return None
+    if d.get("kernel_sha") != kernel_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(args, wl):
+    """Time the float64 FullState oracle on the first requests of the workload."""
+    import resource
+    import oracle
+    from synth import gen
+
+    Wout = gen.wout(wl).value.astype(np.float64)
+    # one request first, to size the sample
+    rs = 0
+    t_tot = 0.0
+    cpu0 = resource.getrusage(resource.RUSAGE_SELF)
+    while True:
+        S = oracle.prefill_request(wl, rs)          # input preparation, not timed
+        inputs = [oracle.run.step_arrays(wl, rs, t) for t in range(wl.T)]
+        forced = [(gen.forced_parents(wl, rs, t), gen.forced_tokens(wl, rs, t)) for t in range(wl.T)]
+        dec = oracle.FullStateDecoder(S.astype(np.float64), wl.width(0))
+        t0 = time.perf_counter()
+        for t in range(wl.T):
+            o, _ = dec.step(t, *inputs[t])
+            fp, ft = forced[t] if args.mode == "forced" else (None, None)
+            dec.select(t, o, Wout, wl.width(t + 1), fp, ft)
+        t_tot += time.perf_counter() - t0
+        rs += 1
+        log(args, f"cpu oracle: {rs} request(s), {t_tot:.1f} s")
+        if rs >= wl.R or t_tot >= args.cpu_seconds or t_tot / rs * (rs + 1) > 2 * args.cpu_seconds:
+            break
+    cpu1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu_s = (cpu1.ru_utime - cpu0.ru_utime) + (cpu1.ru_stime - cpu0.ru_stime)
+    trans = rs * wl.H * sum(wl.width(t) for t in range(wl.T))
+    threads = max(1, round(cpu_s / max(t_tot, 1e-9)))
+    return {"value": trans / t_tot, "unit": "beam-transitions/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rs} of {wl.R} requests (all {wl.H} heads, {wl.T} steps, {args.mode} mode), "
+                      f"float64 FullState numpy, {t_tot:.1f} s; host has "
+                      f"{len(os.sched_getaffinity(0))} cores available"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): requests are "
+              "independent, so the one-GPU rate is one GPU's share of a sharded job.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    from synth import device as sdev
+    from linear_attention_beam_amd import binding as B
+    from linear_attention_beam_amd.decoder import BeamDecoder, prefill
+
+    wl = synth.get(args.workload)
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    log(args, f"workload {wl.name}: {wl.summary}")
+
+    # ---- inputs resident in HBM before timing
+    dec = BeamDecoder(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, wl.io, wl.wout)
+    p = sdev.prompts(wl, dev)
+    S_ctx = torch.empty((wl.R, wl.H, wl.d_v, wl.d_k), dtype=torch.float32, device=dev)
+    t0 = time.perf_counter()
+    prefill(S_ctx, p["k"], p["v"], p["alpha"], p["beta"], p["offsets"])
+    torch.cuda.synchronize()
+    log(args, f"prefill of {p['N']} prompt tokens x {wl.H} heads: {time.perf_counter() - t0:.3f} s")
+    del p
+    Wout = sdev.wout(wl, dev)
+    inputs = [sdev.step_inputs(wl, t, dev) for t in range(wl.T)]
+    outs = [torch.empty((wl.R, wl.H, wl.width(t), wl.d_v), dtype=torch.float32, device=dev)
+            for t in range(wl.T)]
+    sels = [{n: torch.empty((wl.R, wl.width(t + 1)), dtype=dt, device=dev) for n, dt in
+             (("parent", torch.int32), ("token", torch.int32), ("score", torch.float32))}
+            for t in range(wl.T)]
+    forced = [(None, None)] * wl.T
+    if args.mode == "forced":
+        from synth import gen
+        forced = [(torch.from_numpy(np.stack([gen.forced_parents(wl, r, t) for r in range(wl.R)])).to(dev),
+                   torch.from_numpy(np.stack([gen.forced_tokens(wl, r, t) for r in range(wl.R)])).to(dev))
+                  for t in range(wl.T)]
+    torch.cuda.synchronize()
+
+    def decode(ev=None):
+        dec.init(S_ctx, wl.width(0), stream)
+        for t in range(wl.T):
+            x = inputs[t]
+            if ev is not None:
+                ev[t][0].record(stream)
+            dec.step(t, x["q"], x["k"], x["v"], x["alpha"], x["beta"], outs[t], stream)
+            if ev is not None:
+                ev[t][1].record(stream)
+            s = sels[t]
+            dec.select(t, outs[t], Wout, wl.V, wl.width(t + 1), s["parent"], s["token"],
+                       s["score"], forced[t][0], forced[t][1], stream)
+            if ev is not None:
+                ev[t][2].record(stream)
+
+    # ---- distinct ancestor records per step (deterministic: same every decode)
+    distinct = []
+    dec.init(S_ctx, wl.width(0), stream)
+    for t in range(wl.T):
+        anc = dec.export(B.GDN_EXPORT_ANCESTRY).cpu().numpy()
+        W = wl.width(t)
+        d = np.zeros(wl.R, dtype=np.int64)
+        if t > 0:
+            for r in range(wl.R):
+                d[r] = sum(len(np.unique(anc[r, :W, j])) for j in range(t))
+        distinct.append(d)
+        x = inputs[t]
+        dec.step(t, x["q"], x["k"], x["v"], x["alpha"], x["beta"], outs[t], stream)
+        s = sels[t]
+        dec.select(t, outs[t], Wout, wl.V, wl.width(t + 1), s["parent"], s["token"], s["score"],
+                   forced[t][0], forced[t][1], stream)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        decode()
+    torch.cuda.synchronize()
+
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(wl.T)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        decode(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    step_ms = np.zeros(wl.T)
+    sel_ms = np.zeros(wl.T)
+    for i in range(args.steps):
+        for t in range(wl.T):
+            step_ms[t] += evs[i][t][0].elapsed_time(evs[i][t][1])
+            sel_ms[t] += evs[i][t][1].elapsed_time(evs[i][t][2])
+    step_ms /= args.steps
+    sel_ms /= args.steps
+    trans = wl.transitions()
+    value = trans * args.steps / elapsed
+    bytes_t = [step_bytes(wl, t, distinct[t]) for t in range(wl.T)]
+    achieved = sum(bytes_t) / (step_ms.sum() * 1e-3) / 1e9
+    traffic = load_traffic(wl.name)
+    gdn_rate = trans / (step_ms.sum() * 1e-3)
+    flops = sum(step_flops(wl, t) for t in range(wl.T))
+    log(args, f"step kernel ms per SID step: {np.round(step_ms, 4).tolist()}  select ms: "
+              f"{np.round(sel_ms, 4).tolist()}")
+    log(args, f"algorithmic bytes per step launch: {bytes_t}; distinct ancestors per request "
+              f"(mean) {[float(d.mean()) for d in distinct]}")
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "beam-transitions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "R": wl.R, "H": wl.H, "d_k": wl.d_k, "d_v": wl.d_v,
+                   "T": wl.T, "W_t": list(wl.widths), "V": wl.V, "io_dtype": wl.io,
+                   "state_dtype": "f32", "mode": args.mode, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gdn step_kernel", "bytes_per_decode": int(sum(bytes_t)),
+                     "launches_per_decode": wl.T},
+        "gdn_step_rate": gdn_rate,
+        "gdn_step_ms": float(step_ms.sum()),
+        "select_ms": float(sel_ms.sum()),
+        "step_tflops": flops / (step_ms.sum() * 1e-3) / 1e12,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args, wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * gdn_beam.h — large-beam Gated DeltaNet decoding on one AMD Instinct MI355X (gfx950).
+ *
+ * One shared prefill state S_ctx per (request, head); every beam is a chain of
+ * append-only GDN Transition Records r = (alpha, delta, k) in fixed slots, found
+ * through an Ancestry Index.  No per-beam d_v x d_k state is ever built.
+ *
+ * Sources (the pages this follows):
+ *   OneLA reading note (paper-archivist.com, "OneLA: Scaling Linear-Attention
+ *   Decoding to Large Beams in Generative Recommendation"):
+ *     section 1.2 eq. (3)   GDN recurrence and output o_t = S_t q_t
+ *     section 2.1           logical / physical / index layers (S_ctx, GTR slots, ancestry)
+ *     section 2.2 eq. (4-5) rank-1 form and the transition record r_t = (alpha_t, delta_t, k_t)
+ *     section 2.3 eq. (6-8) projection replay along the ancestor chain, then delta_t and o_t
+ *     section 2.4 eq. (9)   ancestry-index update h_t(b, j)
+ *     section 2.5           fused shared-context kernel (S_ctx loaded once, reused across beams)
+ *     section 1.1 eq. (1)   SID probability as a product of per-step conditionals
+ *   RecoGEM (conceptio mirror, "RecoGEM: A Serving System for Production-Scale
+ *   Generative Recommendation"), section 4.3: exact global top-K over a request's
+ *   W x C candidates.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked "host".  Every device pointer must
+ *     be 16-byte aligned.  Arrays are dense, row-major, last index fastest.
+ *   - Calls are asynchronous on `stream` and never synchronise the host.
+ *   - The library never allocates device memory: the caller owns the workspace.
+ *   - Every check runs on the host before any launch; a rejected call changes no
+ *     state and launches nothing.  Nothing aborts or prints.
+ *   - One context serves one stream at a time; separate contexts are independent.
+ *     Calls on one context must be issued in order: init, then for t = 0, 1, ...:
+ *     step(t) then select(t).
+ */
+#ifndef GDN_BEAM_H
+#define GDN_BEAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, bad size or dtype */
+  GDN_ERR_BAD_STATE = 2,    /* call out of order (e.g. select before step, wrong t) */
+  GDN_ERR_CAPACITY = 3,     /* t >= T_max, W > W_max, V > V_max */
+  GDN_ERR_WORKSPACE = 4,    /* workspace smaller than gdn_beam_workspace_bytes() */
+  GDN_ERR_UNSUPPORTED = 5,  /* head dims or dtypes without a compiled kernel */
+  GDN_ERR_HIP = 6           /* a HIP launch or copy failed; see gdn_beam_last_error() */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef struct {
+  int32_t R, H;        /* requests, GDN heads per request                                 */
+  int32_t d_k, d_v;    /* head dims; supported (d_k, d_v): (16,16), (128,128), (128,256)  */
+  int32_t T_max;       /* SID decode steps (1..8)                                         */
+  int32_t W_max;       /* peak beam width = GTR slots per step (1..1024)                  */
+  int32_t V_max;       /* largest codebook passed to select (1..65536)                    */
+  gdn_dtype io_dtype;  /* dtype of q, k, v; keys are stored in the GTR pool in it         */
+  gdn_dtype wout_dtype;/* dtype of the codebook projection Wout                           */
+} gdn_beam_config;
+
+typedef struct gdn_beam_ctx gdn_beam_ctx;   /* opaque, host memory owned by the library */
+
+/* Size in bytes of the workspace a context needs (host only, no GPU call).
+ * Per request it is H*(4*d_v*d_k + T_max*W_max*(4 + 4*d_v + e*d_k)) plus
+ * O(W_max*(T_max + d_v + V_max)) for ancestry, scores and selection scratch
+ * (e = bytes per io element).  No term grows with d_v*d_k*W: this is the
+ * persistent-capacity form of the OneLA reading note, section 2.2 (eq. 5) and
+ * section 4.3 (b), against W*d_v*d_k for one state per beam. */
+gdn_status gdn_beam_workspace_bytes(const gdn_beam_config* cfg, size_t* bytes /* host */);
+
+/* Start a decode.  S_ctx [R,H,d_v,d_k] fp32 is the shared prefill state of each
+ * (request, head) (section 2.1, logical layer); it is read only by the launch this
+ * call makes and may be freed once `stream` has passed it.  W0 beams start at
+ * t = 0, all children of S_ctx with cumulative score 0.  `workspace` (device,
+ * >= gdn_beam_workspace_bytes, 256-byte aligned) must outlive the context.
+ * On success *out (host) receives a new context. */
+gdn_status gdn_beam_init(const gdn_beam_config* cfg, const float* S_ctx, int32_t W0,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         gdn_beam_ctx** out /* host */);
+
+/* One SID step t for all R*H*W_t beams (W_t = beams alive at step t).
+ * Inputs: q, k [R,H,W_t,d_k] and v [R,H,W_t,d_v] in io_dtype; alpha, beta
+ * [R,H,W_t] fp32.  For each beam: u_q = S_ctx q_t and u_k = S_ctx k_t, replayed
+ * along the beam's ancestor records by eqs. (6)-(7); then eq. (8):
+ * delta_t = beta (v - alpha u_k), o_t = alpha u_q + delta_t (k_t . q_t).
+ * Output: o [R,H,W_t,d_v] fp32.  The record (alpha_t, delta_t, k_t) is written
+ * once into slot (t, b) of the GTR pool (section 2.2 eq. 5, section 2.5 step 3).
+ * Valid after init (t = 0) or after select(t-1).  Re-issuing step(t) before
+ * select(t) rewrites the same slots with the same values. */
+gdn_status gdn_beam_step(gdn_beam_ctx* ctx, int32_t t,
+                         const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta,
+                         float* o, hipStream_t stream);
+
+/* Score step t's beams and choose the W_next beams of step t+1.
+ * o [R,H,W_t,d_v] fp32 is the output of step(t).  Wout [d_v,V] in wout_dtype is
+ * the codebook projection shared by all heads.  Per request: z_b = sum_h o_b,
+ * logit_bc = z_b . Wout[:,c], and candidate (b, c) scores
+ * cum_b + (logit_bc - logsumexp_c logit_b)  (log form of eq. 1).
+ * The exact top-W_next over the request's W_t*V candidates, ordered by score
+ * descending then flat index b*V + c ascending, is written to parent, token
+ * [R,W_next] int32 and score [R,W_next] fp32 (RecoGEM section 4.3).
+ * If forced_parent and forced_token [R,W_next] int32 are both non-NULL, the
+ * beams follow them instead and carry the score of the forced candidate; the
+ * top-W is still computed into parent/token/score.  Forced entries out of range
+ * are clamped and flagged in the status word (gdn_beam_export GDN_EXPORT_STATUS).
+ * Then the ancestry is remapped by eq. (9) (section 2.4): only indices move,
+ * never records.  Requires W_next <= W_max, V <= V_max, W_next <= W_t*V. */
+gdn_status gdn_beam_select(gdn_beam_ctx* ctx, int32_t t, const float* o,
+                           const void* Wout, int32_t V, int32_t W_next,
+                           const int32_t* forced_parent, const int32_t* forced_token,
+                           int32_t* parent, int32_t* token, float* score,
+                           hipStream_t stream);
+
+/* Copy internal state to a caller buffer (device) for tests and debugging. */
+typedef enum {
+  GDN_EXPORT_ANCESTRY = 0,  /* [R,W_max,T_max] int32: h_t(b,j) of the coming step        */
+  GDN_EXPORT_TOKENS = 1,    /* [R,W_max,T_max] int32: SID prefix of each live beam       */
+  GDN_EXPORT_CUM = 2,       /* [R,W_max] fp32: cumulative score of each live beam        */
+  GDN_EXPORT_GTR_ALPHA = 3, /* [R,H,T_max,W_max] fp32                                    */
+  GDN_EXPORT_GTR_DELTA = 4, /* [R,H,T_max,W_max,d_v] fp32                                */
+  GDN_EXPORT_GTR_KEY = 5,   /* [R,H,T_max,W_max,d_k] io_dtype                            */
+  GDN_EXPORT_STATUS = 6     /* [1] int32: bit 0 = a forced parent/token was out of range */
+} gdn_export_what;
+gdn_status gdn_beam_export(const gdn_beam_ctx* ctx, int32_t what, void* dst,
+                           size_t dst_bytes, hipStream_t stream);
+
+/* Bytes gdn_beam_export writes for `what` (host only). */
+gdn_status gdn_beam_export_bytes(const gdn_beam_ctx* ctx, int32_t what, size_t* bytes /* host */);
+
+/* Beams alive at the coming step and the step index expected next (host only). */
+gdn_status gdn_beam_query(const gdn_beam_ctx* ctx, int32_t* t_next, int32_t* W_cur /* host */);
+
+/* Free a context (host memory only; the workspace stays the caller's). NULL is a no-op. */
+void gdn_beam_destroy(gdn_beam_ctx* ctx);
+
+/* Static description of a status code. */
+const char* gdn_beam_status_str(gdn_status s);
+
+/* Text of the last GDN_ERR_HIP on the calling thread ("" if none). */
+const char* gdn_beam_last_error(void);
+
+/* Prefill (eq. 3, section 1.2): S_out[r,h] = the state after request r's prompt,
+ * starting from zero.  Prompt tokens of all requests are stacked:
+ * k [N,H,d_k], v [N,H,d_v], alpha, beta [N,H] fp32, request r owning rows
+ * offsets[r] .. offsets[r+1]-1, with offsets [R+1] int32 (device), nondecreasing,
+ * offsets[R] = N.  Offsets are clamped to [0, N] on the device.
+ * S_out [R,H,d_v,d_k] fp32.  Same head dims as the decode. */
+gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t d_k, int32_t d_v, int64_t N,
+                            const float* k, const float* v, const float* alpha,
+                            const float* beta, const int32_t* offsets,
+                            float* S_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_BEAM_H */

@@ -1,0 +1,230 @@
+// Host front end of the C ABI declared in include/gdn_beam.h: argument checks,
+// the per-context state machine (init -> step(t) -> select(t) -> step(t+1) ...),
+// the workspace carve-up, and the hand-off to the kernel launchers.  Every check
+// runs before any launch, so a rejected call leaves the context unchanged.
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "gdn_layout.h"
+
+using namespace gdn;
+
+struct gdn_beam_ctx {
+  gdn_beam_config cfg;
+  Layout L;
+  void* ws;
+  size_t ws_bytes;
+  int t;          // step expected next
+  int stepped;    // step(t) issued, select(t) not yet
+  int W_cur;      // beams alive at step t
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+gdn_status hip_fail(int err, const char* where) {
+  g_last_error = std::string(where) + ": " + hip_error_string(err);
+  return GDN_ERR_HIP;
+}
+
+bool dims_supported(int d_k, int d_v) {
+  return (d_k == 16 && d_v == 16) || (d_k == 128 && d_v == 128) || (d_k == 128 && d_v == 256);
+}
+
+gdn_status check_config(const gdn_beam_config* c) {
+  if (!c) return GDN_ERR_INVALID_ARG;
+  if (c->R < 1 || c->H < 1 || c->T_max < 1 || c->W_max < 1 || c->V_max < 1)
+    return GDN_ERR_INVALID_ARG;
+  if ((c->io_dtype != GDN_F32 && c->io_dtype != GDN_BF16) ||
+      (c->wout_dtype != GDN_F32 && c->wout_dtype != GDN_BF16))
+    return GDN_ERR_INVALID_ARG;
+  if (!dims_supported(c->d_k, c->d_v)) return GDN_ERR_UNSUPPORTED;
+  if (c->T_max > kMaxT || c->W_max > kMaxW || c->V_max > kMaxV) return GDN_ERR_CAPACITY;
+  // flat candidate index b*V + c and per-request scratch sizes must fit in 31 bits
+  if (int64_t(c->W_max) * c->V_max >= (int64_t(1) << 31)) return GDN_ERR_CAPACITY;
+  if (int64_t(c->R) * c->H * c->T_max * c->W_max >= (int64_t(1) << 31)) return GDN_ERR_CAPACITY;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_beam_status_str(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_INVALID_ARG: return "invalid argument";
+    case GDN_ERR_BAD_STATE: return "call out of order";
+    case GDN_ERR_CAPACITY: return "capacity exceeded";
+    case GDN_ERR_WORKSPACE: return "workspace too small";
+    case GDN_ERR_UNSUPPORTED: return "unsupported head dims or dtype";
+    case GDN_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* gdn_beam_last_error(void) { return g_last_error.c_str(); }
+
+gdn_status gdn_beam_workspace_bytes(const gdn_beam_config* cfg, size_t* bytes) {
+  gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!bytes) return GDN_ERR_INVALID_ARG;
+  *bytes = make_layout(*cfg).total;
+  return GDN_OK;
+}
+
+gdn_status gdn_beam_init(const gdn_beam_config* cfg, const float* S_ctx, int32_t W0,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         gdn_beam_ctx** out) {
+  gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!S_ctx || !workspace || !out) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(S_ctx) || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDN_ERR_INVALID_ARG;
+  if (W0 < 1) return GDN_ERR_INVALID_ARG;
+  if (W0 > cfg->W_max) return GDN_ERR_CAPACITY;
+  Layout L = make_layout(*cfg);
+  if (workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+
+  gdn_beam_ctx* ctx = new (std::nothrow) gdn_beam_ctx;
+  if (!ctx) return GDN_ERR_INVALID_ARG;
+  ctx->cfg = *cfg;
+  ctx->L = L;
+  ctx->ws = workspace;
+  ctx->ws_bytes = workspace_bytes;
+  ctx->t = 0;
+  ctx->stepped = 0;
+  ctx->W_cur = W0;
+
+  InitArgs a{cfg->R, cfg->H, cfg->d_k, cfg->d_v, cfg->W_max, cfg->T_max, cfg->io_dtype,
+             S_ctx, workspace, L};
+  int err = launch_init(a, stream);
+  if (err) {
+    delete ctx;
+    return hip_fail(err, "gdn_beam_init");
+  }
+  *out = ctx;
+  return GDN_OK;
+}
+
+gdn_status gdn_beam_step(gdn_beam_ctx* ctx, int32_t t, const void* q, const void* k,
+                         const void* v, const float* alpha, const float* beta, float* o,
+                         hipStream_t stream) {
+  if (!ctx) return GDN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !alpha || !beta || !o) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) ||
+      !aligned16(beta) || !aligned16(o))
+    return GDN_ERR_INVALID_ARG;
+  const gdn_beam_config& c = ctx->cfg;
+  if (t < 0) return GDN_ERR_INVALID_ARG;
+  if (t >= c.T_max) return GDN_ERR_CAPACITY;
+  if (t != ctx->t) return GDN_ERR_BAD_STATE;
+  StepArgs a{c.R, c.H, c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype,
+             q, k, v, alpha, beta, o, ctx->ws, ctx->L};
+  int err = launch_step(a, stream);
+  if (err) return hip_fail(err, "gdn_beam_step");
+  ctx->stepped = 1;
+  return GDN_OK;
+}
+
+gdn_status gdn_beam_select(gdn_beam_ctx* ctx, int32_t t, const float* o, const void* Wout,
+                           int32_t V, int32_t W_next, const int32_t* forced_parent,
+                           const int32_t* forced_token, int32_t* parent, int32_t* token,
+                           float* score, hipStream_t stream) {
+  if (!ctx) return GDN_ERR_INVALID_ARG;
+  if (!o || !Wout || !parent || !token || !score) return GDN_ERR_INVALID_ARG;
+  if ((forced_parent == nullptr) != (forced_token == nullptr)) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(o) || !aligned16(Wout) || !aligned16(parent) || !aligned16(token) ||
+      !aligned16(score))
+    return GDN_ERR_INVALID_ARG;
+  if (forced_parent && (!aligned16(forced_parent) || !aligned16(forced_token)))
+    return GDN_ERR_INVALID_ARG;
+  const gdn_beam_config& c = ctx->cfg;
+  if (t < 0 || V < 1 || W_next < 1) return GDN_ERR_INVALID_ARG;
+  if (t >= c.T_max) return GDN_ERR_CAPACITY;
+  if (t != ctx->t || !ctx->stepped) return GDN_ERR_BAD_STATE;
+  if (V > c.V_max || W_next > c.W_max) return GDN_ERR_CAPACITY;
+  if (int64_t(W_next) > int64_t(ctx->W_cur) * V) return GDN_ERR_INVALID_ARG;
+  SelectArgs a{c.R, c.H, c.d_v, c.W_max, c.V_max, c.T_max, t, ctx->W_cur, V, W_next, c.wout_dtype,
+               o, Wout, forced_parent, forced_token, parent, token, score, ctx->ws, ctx->L};
+  int err = launch_select(a, stream);
+  if (err) return hip_fail(err, "gdn_beam_select");
+  ctx->t = t + 1;
+  ctx->stepped = 0;
+  ctx->W_cur = W_next;
+  return GDN_OK;
+}
+
+gdn_status gdn_beam_export_bytes(const gdn_beam_ctx* ctx, int32_t what, size_t* bytes) {
+  if (!ctx || !bytes) return GDN_ERR_INVALID_ARG;
+  const gdn_beam_config& c = ctx->cfg;
+  const size_t R = c.R, H = c.H, T = c.T_max, W = c.W_max;
+  switch (what) {
+    case GDN_EXPORT_ANCESTRY:
+    case GDN_EXPORT_TOKENS: *bytes = R * W * T * 4; break;
+    case GDN_EXPORT_CUM: *bytes = R * W * 4; break;
+    case GDN_EXPORT_GTR_ALPHA: *bytes = R * H * T * W * 4; break;
+    case GDN_EXPORT_GTR_DELTA: *bytes = R * H * T * W * size_t(c.d_v) * 4; break;
+    case GDN_EXPORT_GTR_KEY: *bytes = R * H * T * W * size_t(c.d_k) * io_bytes(c.io_dtype); break;
+    case GDN_EXPORT_STATUS: *bytes = 4; break;
+    default: return GDN_ERR_INVALID_ARG;
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_beam_export(const gdn_beam_ctx* ctx, int32_t what, void* dst, size_t dst_bytes,
+                           hipStream_t stream) {
+  size_t n = 0;
+  gdn_status st = gdn_beam_export_bytes(ctx, what, &n);
+  if (st != GDN_OK) return st;
+  if (!dst || !aligned16(dst)) return GDN_ERR_INVALID_ARG;
+  if (dst_bytes < n) return GDN_ERR_CAPACITY;
+  const Layout& L = ctx->L;
+  size_t off = 0;
+  const int par = ctx->t & 1;   // buffers of the coming step
+  switch (what) {
+    case GDN_EXPORT_ANCESTRY: off = L.anc[par]; break;
+    case GDN_EXPORT_TOKENS: off = L.tok[par]; break;
+    case GDN_EXPORT_CUM: off = L.cum[par]; break;
+    case GDN_EXPORT_GTR_ALPHA: off = L.gtr_alpha; break;
+    case GDN_EXPORT_GTR_DELTA: off = L.gtr_delta; break;
+    case GDN_EXPORT_GTR_KEY: off = L.gtr_key; break;
+    case GDN_EXPORT_STATUS: off = L.status; break;
+  }
+  int err = copy_d2d(dst, static_cast<const char*>(ctx->ws) + off, n, stream);
+  if (err) return hip_fail(err, "gdn_beam_export");
+  return GDN_OK;
+}
+
+gdn_status gdn_beam_query(const gdn_beam_ctx* ctx, int32_t* t_next, int32_t* W_cur) {
+  if (!ctx || !t_next || !W_cur) return GDN_ERR_INVALID_ARG;
+  *t_next = ctx->t;
+  *W_cur = ctx->W_cur;
+  return GDN_OK;
+}
+
+void gdn_beam_destroy(gdn_beam_ctx* ctx) { delete ctx; }
+
+gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t d_k, int32_t d_v, int64_t N,
+                            const float* k, const float* v, const float* alpha,
+                            const float* beta, const int32_t* offsets, float* S_out,
+                            hipStream_t stream) {
+  if (R < 1 || H < 1 || N < 0) return GDN_ERR_INVALID_ARG;
+  if (!dims_supported(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+  if (!offsets || !S_out) return GDN_ERR_INVALID_ARG;
+  if (N > 0 && (!k || !v || !alpha || !beta)) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(offsets) || !aligned16(S_out)) return GDN_ERR_INVALID_ARG;
+  if (N > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned16(beta)))
+    return GDN_ERR_INVALID_ARG;
+  if (N >= (int64_t(1) << 31)) return GDN_ERR_CAPACITY;
+  PrefillArgs a{R, H, d_k, d_v, N, k, v, alpha, beta, offsets, S_out};
+  int err = launch_prefill(a, stream);
+  if (err) return hip_fail(err, "gdn_beam_prefill");
+  return GDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Internal: workspace layout and launch arguments shared by the host front end
+// (gdn_beam_api.cpp) and the kernels (gdn_beam_kernels.hip).  Not installed.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+#include "../../include/gdn_beam.h"
+
+#if defined(__HIPCC__)
+#define GDN_HD __host__ __device__
+#else
+#define GDN_HD
+#endif
+
+namespace gdn {
+
+constexpr int kMaxT = 8;          // SID steps
+constexpr int kMaxW = 1024;       // beams per step (one sorting workgroup holds them)
+constexpr int kMaxV = 65536;      // codebook
+constexpr int kHistBins = 2048;   // radix digits per selection pass (11 bits)
+constexpr int kSelBlocksMax = 64; // histogram blocks per request
+constexpr int kSelPerBlock = 32768;// candidates per histogram block (before the cap)
+
+// Per-request selection state (device).  Reset at the start of every select.
+// The radix passes bin keys relative to the request's exact key range: each pass
+// splits the current range [lo, lo + 2048 << shift) into 2048 digits.
+struct SelState {
+  uint32_t kmax, kmin;  // largest / smallest candidate key of the request
+  uint32_t lo;          // smallest key of the current range
+  uint32_t hi;          // largest key of the current range
+  int32_t shift;        // digit width (log2) of the next pass; kShiftInit before the first,
+                        // -1 once the threshold key is known
+  uint32_t need;        // winners still to take inside the current range
+  uint32_t done;        // blocks finished in the current pass (last-block detection)
+  uint32_t theta;       // the K-th largest key (valid once shift == -1)
+  uint32_t tie_total;   // candidates whose key equals theta
+  uint32_t n_win;       // collected candidates with key > theta
+  uint32_t n_tie;       // collected candidates with key == theta
+  uint32_t pad[5];
+};
+constexpr int32_t kShiftInit = 99;
+
+// Byte offsets of every region inside the caller's workspace (256-aligned).
+struct Layout {
+  size_t s_frag;      // [R,H] S_ctx in MFMA fragment order, 4*d_vp*d_k bytes each
+  size_t gtr_alpha;   // [R,H,T_max,W_max] f32
+  size_t gtr_delta;   // [R,H,T_max,W_max,d_v] f32
+  size_t gtr_key;     // [R,H,T_max,W_max,d_k] io dtype
+  size_t anc[2];      // [R,W_max,T_max] i32, ping-pong by step parity
+  size_t tok[2];      // [R,W_max,T_max] i32
+  size_t cum[2];      // [R,W_max] f32
+  size_t z;           // [R,W_max,d_v] f32  head-summed outputs
+  size_t woutT;       // [V_max,d_v] wout dtype, codebook transposed
+  size_t logits;      // [R, V_max*W_max] f32, per request [V][W_t]
+  size_t lse_part;    // [R,W_max,n_vgroups] float4 (max, sum of exp, min, 0)
+  size_t lse;         // [R,W_max] f32
+  size_t hist;        // [R,kSelBlocksMax,kHistBins] u32, one histogram per block
+  size_t sel;         // [R] SelState
+  size_t winners;     // [R,W_max] u64 (key<<32 | flat)
+  size_t ties;        // [R, V_max*W_max] u32 flat indices at the threshold key
+  size_t status;      // [64] i32
+  size_t total;
+};
+
+GDN_HD inline int dvp_of(int d_v) { return d_v < 32 ? 32 : d_v; }   // rows padded to one MFMA block
+GDN_HD inline int io_bytes(gdn_dtype d) { return d == GDN_BF16 ? 2 : 4; }
+
+// Codes per logits work unit: a wave covers 32 beams x kCodesPerWave codes.
+constexpr int kCodesPerWave = 256;
+GDN_HD inline int n_vgroups(int V) { return (V + kCodesPerWave - 1) / kCodesPerWave; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline Layout make_layout(const gdn_beam_config& c) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t R = c.R, H = c.H, T = c.T_max, W = c.W_max, V = c.V_max;
+  const size_t dk = c.d_k, dv = c.d_v, e = io_bytes(c.io_dtype), ew = io_bytes(c.wout_dtype);
+  L.s_frag = take(R * H * 4 * size_t(dvp_of(c.d_v)) * dk);
+  L.gtr_alpha = take(R * H * T * W * 4);
+  L.gtr_delta = take(R * H * T * W * dv * 4);
+  L.gtr_key = take(R * H * T * W * dk * e);
+  for (int i = 0; i < 2; ++i) L.anc[i] = take(R * W * T * 4);
+  for (int i = 0; i < 2; ++i) L.tok[i] = take(R * W * T * 4);
+  for (int i = 0; i < 2; ++i) L.cum[i] = take(R * W * 4);
+  L.z = take(R * W * dv * 4);
+  L.woutT = take(V * dv * ew);
+  L.logits = take(R * V * W * 4);
+  L.lse_part = take(R * W * size_t(n_vgroups(c.V_max)) * 16);
+  L.lse = take(R * W * 4);
+  L.hist = take(R * size_t(kSelBlocksMax) * kHistBins * 4);
+  L.sel = take(R * sizeof(SelState));
+  L.winners = take(R * W * 8);
+  L.ties = take(R * V * W * 4);
+  L.status = take(64 * 4);
+  L.total = off;
+  return L;
+}
+
+// ---- launch arguments (host -> kernel TU) ----
+struct InitArgs {
+  int R, H, d_k, d_v, W_max, T_max;
+  gdn_dtype io;
+  const float* S_ctx;
+  void* ws;
+  Layout L;
+};
+
+struct StepArgs {
+  int R, H, d_k, d_v, W_max, T_max, t, W;
+  gdn_dtype io;
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  float* o;
+  void* ws;
+  Layout L;
+};
+
+struct SelectArgs {
+  int R, H, d_v, W_max, V_max, T_max, t, W, V, W_next;
+  gdn_dtype wout_dtype;
+  const float* o;
+  const void* Wout;
+  const int32_t *forced_parent, *forced_token;
+  int32_t *parent, *token;
+  float* score;
+  void* ws;
+  Layout L;
+};
+
+struct PrefillArgs {
+  int R, H, d_k, d_v;
+  int64_t N;
+  const float *k, *v, *alpha, *beta;
+  const int32_t* offsets;
+  float* S_out;
+};
+
+// Kernel launchers (gdn_beam_kernels.hip).  Return a hipError_t value.
+int launch_init(const InitArgs& a, hipStream_t s);
+int launch_step(const StepArgs& a, hipStream_t s);
+int launch_select(const SelectArgs& a, hipStream_t s);
+int launch_prefill(const PrefillArgs& a, hipStream_t s);
+int copy_d2d(void* dst, const void* src, size_t bytes, hipStream_t s);
+const char* hip_error_string(int err);
+
+}  // namespace gdn

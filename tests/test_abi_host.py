@@ -1,0 +1,172 @@
+"""Host-side checks of the C ABI (no GPU): exported symbols, workspace formula,
+and every argument error that is decided before a launch.
+
+Device pointers passed here are never dereferenced: each call below is
+rejected by the host checks before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import synth
+from linear_attention_beam_amd import binding as B
+from oracle import capacity_elements
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gdn_beam.h")
+FAKE = 0x7F0000000000            # 256-aligned, never dereferenced
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:gdn_status|void|const char\*)\s+(gdn_beam_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert set(names) == set(B.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (gdn_beam_\w+)$", out, re.M))
+    missing = set(names) - exported
+    assert not missing, missing
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert getattr(lib, n)
+
+
+def _cfg(**kw):
+    d = dict(R=2, H=3, d_k=128, d_v=128, T_max=4, W_max=256, V_max=1024, io="bf16", wout="bf16")
+    d.update(kw)
+    return B.make_config(**d)
+
+
+def _a(x):
+    return (x + 255) & ~255
+
+
+def expected_bytes(R, H, d_k, d_v, T, W, V, e, ew):
+    """Workspace regions as documented in include/gdn_beam.h, each 256-aligned."""
+    dvp = max(d_v, 32)
+    nvg = -(-V // 256)
+    regions = [R * H * 4 * dvp * d_k, R * H * T * W * 4, R * H * T * W * d_v * 4,
+               R * H * T * W * d_k * e, R * W * T * 4, R * W * T * 4, R * W * T * 4, R * W * T * 4,
+               R * W * 4, R * W * 4, R * W * d_v * 4, V * d_v * ew, R * V * W * 4, R * W * nvg * 16,
+               R * W * 4, R * 64 * 2048 * 4, R * 64, R * W * 8, R * V * W * 4, 64 * 4]
+    return sum(_a(x) for x in regions)
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_workspace_formula(name):
+    wl = synth.get(name)
+    e = 2 if wl.io == "bf16" else 4
+    ew = 2 if wl.wout == "bf16" else 4
+    got = B.gdn_beam_workspace_bytes(B.make_config(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V,
+                                                   wl.io, wl.wout))
+    assert got == expected_bytes(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, e, ew)
+
+
+def test_persistent_state_is_gtr_capacity_and_beats_fullstate():
+    """S_ctx + GTR pool per (request, head) is the capacity form d_v d_k + W T (d_v + d_k + 1)
+    in elements (OneLA reading note, section 4.3 b), and the whole workspace per request
+    stays far below FullState's W d_v d_k fp32 at the stress shape."""
+    wl = synth.get("stress")
+    e = 2
+    cap = capacity_elements(wl.d_k, wl.d_v, W=wl.W_max, T=wl.T)
+    gtr_bytes = 4 * wl.d_v * wl.d_k + wl.T * wl.W_max * (4 + 4 * wl.d_v + e * wl.d_k)
+    assert gtr_bytes == 4 * cap["state"] + wl.T * wl.W_max * (4 * (1 + wl.d_v) + e * wl.d_k)
+    ws = B.gdn_beam_workspace_bytes(B.make_config(1, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V))
+    fullstate = wl.H * wl.W_max * wl.d_v * wl.d_k * 4
+    # the GDN state alone is about 20x smaller; the selection scratch (W x V scores) is extra
+    assert wl.H * gtr_bytes * 18 < fullstate
+    assert ws < fullstate
+
+
+def test_workspace_does_not_grow_with_dv_dk_w():
+    """Doubling W adds a term linear in W (records, scores), never W*d_v*d_k."""
+    b1 = B.gdn_beam_workspace_bytes(_cfg(W_max=256))
+    b2 = B.gdn_beam_workspace_bytes(_cfg(W_max=512))
+    R, H, T, d, V = 2, 3, 4, 128, 1024
+    records = H * T * (4 + 4 * d + 2 * d)              # GTR slots of every head
+    beam_state = 4 * T * 4 + 2 * 4                     # ancestry + SID prefixes, scores
+    scoring = 4 * d + 4 * V + 16 * (V // 256) + 4 + 8 + 4 * V   # z, logits, lse parts, lse, winners, ties
+    per_w = R * (records + beam_state + scoring)
+    assert b2 - b1 <= 256 * per_w + 20 * 256
+    assert b2 - b1 < 256 * 128 * 128 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_k=64), B.GDN_ERR_UNSUPPORTED),
+    (dict(d_k=128, d_v=64), B.GDN_ERR_UNSUPPORTED),
+    (dict(W_max=2048), B.GDN_ERR_CAPACITY),
+    (dict(T_max=9), B.GDN_ERR_CAPACITY),
+    (dict(V_max=70000), B.GDN_ERR_CAPACITY),
+    (dict(R=0), B.GDN_ERR_INVALID_ARG),
+    (dict(H=-1), B.GDN_ERR_INVALID_ARG),
+])
+def test_config_errors(kw, status):
+    cfg = _cfg(**kw)
+    n = ctypes.c_size_t(0)
+    assert B.raw_status("gdn_beam_workspace_bytes", ctypes.byref(cfg), ctypes.byref(n)) == status
+    ctx = ctypes.c_void_p()
+    assert B.raw_status("gdn_beam_init", ctypes.byref(cfg), FAKE, 4, FAKE, 1 << 40, None,
+                        ctypes.byref(ctx)) == status
+    assert ctx.value is None
+
+
+def test_bad_dtype():
+    cfg = _cfg()
+    cfg.io_dtype = 7
+    n = ctypes.c_size_t(0)
+    assert B.raw_status("gdn_beam_workspace_bytes", ctypes.byref(cfg), ctypes.byref(n)) == B.GDN_ERR_INVALID_ARG
+
+
+def test_init_argument_errors():
+    cfg = _cfg()
+    need = B.gdn_beam_workspace_bytes(cfg)
+    ctx = ctypes.c_void_p()
+    st = lambda *a: B.raw_status("gdn_beam_init", ctypes.byref(cfg), *a, ctypes.byref(ctx))
+    assert st(None, 4, FAKE, need, None) == B.GDN_ERR_INVALID_ARG           # null S_ctx
+    assert st(FAKE + 4, 4, FAKE, need, None) == B.GDN_ERR_INVALID_ARG       # misaligned S_ctx
+    assert st(FAKE, 4, FAKE + 16, need, None) == B.GDN_ERR_INVALID_ARG      # workspace not 256-aligned
+    assert st(FAKE, 0, FAKE, need, None) == B.GDN_ERR_INVALID_ARG           # no beams
+    assert st(FAKE, 257, FAKE, need, None) == B.GDN_ERR_CAPACITY            # W0 > W_max
+    assert st(FAKE, 4, FAKE, need - 1, None) == B.GDN_ERR_WORKSPACE         # too small
+    assert B.raw_status("gdn_beam_init", ctypes.byref(cfg), FAKE, 4, FAKE, need, None, None) == \
+        B.GDN_ERR_INVALID_ARG                                                # no out pointer
+    assert ctx.value is None
+
+
+def test_null_context_calls():
+    assert B.raw_status("gdn_beam_step", None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert B.raw_status("gdn_beam_select", None, 0, FAKE, FAKE, 8, 8, None, None, FAKE, FAKE, FAKE,
+                        None) == B.GDN_ERR_INVALID_ARG
+    n = ctypes.c_size_t()
+    assert B.raw_status("gdn_beam_export_bytes", None, 0, ctypes.byref(n)) == B.GDN_ERR_INVALID_ARG
+    assert B.raw_status("gdn_beam_export", None, 0, FAKE, 16, None) == B.GDN_ERR_INVALID_ARG
+    t, w = ctypes.c_int32(), ctypes.c_int32()
+    assert B.raw_status("gdn_beam_query", None, ctypes.byref(t), ctypes.byref(w)) == B.GDN_ERR_INVALID_ARG
+    B.gdn_beam_destroy(None)   # no-op
+
+
+def test_prefill_argument_errors():
+    f = lambda *a: B.raw_status("gdn_beam_prefill", *a)
+    assert f(2, 3, 64, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_UNSUPPORTED
+    assert f(0, 3, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 128, 128, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 128, 128, 10, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 128, 128, 1 << 31, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_CAPACITY
+
+
+def test_status_strings():
+    for s in range(7):
+        assert B.gdn_beam_status_str(s)
+    assert B.gdn_beam_status_str(99) == "unknown status"
+    assert B.gdn_beam_last_error() == ""
+
+
+def test_single_hip_runtime():
+    """The library shares PyTorch's HIP runtime: exactly one libamdhip64 is mapped."""
+    assert len(B._hip_runtimes()) == 1

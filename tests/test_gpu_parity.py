@@ -1,0 +1,306 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (stated by the workload definitions): o_t and delta_t within 1e-4 max
+per-vector relative error for fp32 io, 2e-2 for bf16 io; ancestry, SID prefixes
+and slot contents bit-exact whenever parent maps are fixed; selected sets equal
+except for candidates within 1e-6 (relative to max(1, |threshold|)) of the
+threshold score.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import gen
+from linear_attention_beam_amd import binding as B
+from gpu_harness import GpuDecode, TOL, check_selection, rel_err, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _eq9(anc, parent, t):
+    return oracle.ancestry_update(anc, parent, t)
+
+
+def _cmp_gdn(wl, dec, g, r, t, o, dpool, tol, heads=None):
+    x = g.step_inputs64(r, t)
+    if heads is not None:
+        x = tuple(a[list(heads)] for a in x)
+    o_ref, d_ref = dec.step(t, *x)
+    hs = list(range(wl.H)) if heads is None else list(heads)
+    W = wl.width(t)
+    eo = rel_err(o[r][hs], o_ref)
+    ed = rel_err(dpool[r][hs][:, t, :W], d_ref)
+    say(f"r={r} t={t} rel err o={eo:.3e} delta={ed:.3e}")
+    assert eo <= tol and ed <= tol, (eo, ed)
+    return o_ref
+
+
+@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2)])
+def test_prefill_matches_oracle(name, R):
+    from synth import device as sdev
+    from linear_attention_beam_amd.decoder import prefill
+    wl = synth.get(name)
+    dev = torch.device("cuda")
+    p = sdev.prompts(wl, dev, R=R)
+    for r in range(R):
+        sdev.upload_prompt(p, wl, r)
+    S = torch.empty((R, wl.H, wl.d_v, wl.d_k), dtype=torch.float32, device=dev)
+    say(f"gdn_beam_prefill {name} R={R} N={p['N']}")
+    prefill(S, p["k"], p["v"], p["alpha"], p["beta"], p["offsets"])
+    torch.cuda.synchronize()
+    S = to_np(S)
+    for r in range(R):
+        ref = oracle.prefill_request(wl, r)
+        e = rel_err(S[r], ref)
+        say(f"prefill r={r} rel err {e:.3e}")
+        assert e <= 1e-4
+
+
+@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2)])
+def test_forced_parents_parity(name, R):
+    wl = synth.get(name)
+    g = GpuDecode(wl, R=R, exact=range(R))
+    tol = TOL[wl.io]
+    decs = {r: oracle.FullStateDecoder(g.S_exact[r].astype(np.float64), wl.width(0)) for r in range(R)}
+    g.init()
+    for t in range(wl.T):
+        o = to_np(g.step(t))
+        cum_before = g.export(B.GDN_EXPORT_CUM)
+        fp, ft = g.forced_maps(t)
+        sel = g.select(t, forced=(fp, ft))
+        dpool = g.export(B.GDN_EXPORT_GTR_DELTA)
+        anc = g.export(B.GDN_EXPORT_ANCESTRY)
+        tok = g.export(B.GDN_EXPORT_TOKENS)
+        cum = g.export(B.GDN_EXPORT_CUM)
+        K = wl.width(t + 1)
+        for r in range(R):
+            o_ref = _cmp_gdn(wl, decs[r], g, r, t, o, dpool, tol)
+            sel_r = {k: v[r] for k, v in sel.items()}
+            check_selection(o[r], cum_before[r][:wl.width(t)], g.Wout64, K, sel_r, f"r={r} t={t}")
+            decs[r].select(t, o_ref, g.Wout64, K, fp[r], ft[r])
+            np.testing.assert_array_equal(anc[r][:K, :t + 1], decs[r].anc)
+            np.testing.assert_array_equal(tok[r][:K, :t + 1], decs[r].tokens)
+            assert np.all(np.abs(cum[r][:K] - decs[r].cum) <= tol * np.maximum(1, np.abs(decs[r].cum)))
+    assert g.export(B.GDN_EXPORT_STATUS)[0] == 0
+
+
+@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2)])
+def test_select_mode_parity(name, R):
+    """Top-W drives the beams.  The oracle follows the GPU's choice (teacher forcing)
+    after the selection itself has been checked against the exact top-W."""
+    wl = synth.get(name)
+    g = GpuDecode(wl, R=R, exact=range(R))
+    tol = TOL[wl.io]
+    decs = {r: oracle.FullStateDecoder(g.S_exact[r].astype(np.float64), wl.width(0)) for r in range(R)}
+    g.init()
+    swaps = 0
+    for t in range(wl.T):
+        o = to_np(g.step(t))
+        cum_before = g.export(B.GDN_EXPORT_CUM)
+        sel = g.select(t)
+        dpool = g.export(B.GDN_EXPORT_GTR_DELTA)
+        anc = g.export(B.GDN_EXPORT_ANCESTRY)
+        tok = g.export(B.GDN_EXPORT_TOKENS)
+        cum = g.export(B.GDN_EXPORT_CUM)
+        K = wl.width(t + 1)
+        for r in range(R):
+            o_ref = _cmp_gdn(wl, decs[r], g, r, t, o, dpool, tol)
+            sel_r = {k: v[r] for k, v in sel.items()}
+            check_selection(o[r], cum_before[r][:wl.width(t)], g.Wout64, K, sel_r, f"r={r} t={t}")
+            s_ref = oracle.step_scores(o_ref, g.Wout64, decs[r].cum)
+            rp, rt, rs = oracle.top_w(s_ref, K)
+            V = wl.V
+            d = set((rp.astype(np.int64) * V + rt).tolist()) ^ set(
+                (sel_r["parent"].astype(np.int64) * V + sel_r["token"]).tolist())
+            swaps += len(d)
+            for f in d:   # end to end, only candidates at the boundary may differ
+                assert abs(s_ref.reshape(-1)[f] - rs[-1]) <= 10 * tol * max(1.0, abs(rs[-1]))
+            decs[r].advance(t, sel_r["parent"], sel_r["token"], s_ref[sel_r["parent"], sel_r["token"]])
+            np.testing.assert_array_equal(anc[r][:K, :t + 1], decs[r].anc)
+            np.testing.assert_array_equal(tok[r][:K, :t + 1], decs[r].tokens)
+            assert np.all(np.abs(cum[r][:K] - decs[r].cum) <= tol * np.maximum(1, np.abs(decs[r].cum)))
+    say(f"end-to-end boundary swaps vs the oracle's own top-W: {swaps}")
+
+
+@pytest.mark.parametrize("name", ["batch", "stress", "growing"])
+def test_full_size_forced_sampled(name):
+    """Full-size launch; sampled (request, head) pairs against single-head FullState,
+    every request's ancestry against eq. (9) on its parent maps, and the selection of
+    sampled requests against exact float64 rescoring."""
+    wl = synth.get(name)
+    R = wl.R
+    exact = (0, R - 1)
+    heads = (0, wl.H - 1)
+    g = GpuDecode(wl, exact=exact)
+    tol = TOL[wl.io]
+    decs = {r: oracle.FullStateDecoder(g.S_exact[r][list(heads)].astype(np.float64), wl.width(0))
+            for r in exact}
+    anc_ref = [np.zeros((wl.width(0), 0), np.int32) for _ in range(R)]
+    g.init()
+    for t in range(wl.T):
+        o = to_np(g.step(t))
+        cum_before = g.export(B.GDN_EXPORT_CUM)
+        fp, ft = g.forced_maps(t)
+        sel = g.select(t, forced=(fp, ft))
+        dpool = g.export(B.GDN_EXPORT_GTR_DELTA)
+        anc = g.export(B.GDN_EXPORT_ANCESTRY)
+        K = wl.width(t + 1)
+        for r in exact:
+            _cmp_gdn(wl, decs[r], g, r, t, o, dpool, tol, heads=heads)
+            decs[r].advance(t, fp[r], ft[r], np.zeros(K))
+            sel_r = {k: v[r] for k, v in sel.items()}
+            check_selection(o[r], cum_before[r][:wl.width(t)], g.Wout64, K, sel_r, f"r={r} t={t}")
+        for r in range(R):
+            anc_ref[r] = _eq9(anc_ref[r], fp[r], t)
+            assert np.array_equal(anc[r][:K, :t + 1], anc_ref[r]), f"ancestry r={r} t={t}"
+    assert g.export(B.GDN_EXPORT_STATUS)[0] == 0
+
+
+@pytest.mark.parametrize("name", ["batch"])
+def test_full_size_select_teacher_forced(name):
+    """Full-size select mode; request 0 against the full (all heads) FullState oracle."""
+    wl = synth.get(name)
+    g = GpuDecode(wl, exact=(0,))
+    tol = TOL[wl.io]
+    dec = oracle.FullStateDecoder(g.S_exact[0].astype(np.float64), wl.width(0))
+    g.init()
+    for t in range(wl.T):
+        o = to_np(g.step(t))
+        cum_before = g.export(B.GDN_EXPORT_CUM)
+        sel = g.select(t)
+        dpool = g.export(B.GDN_EXPORT_GTR_DELTA)
+        anc = g.export(B.GDN_EXPORT_ANCESTRY)
+        K = wl.width(t + 1)
+        o_ref = _cmp_gdn(wl, dec, g, 0, t, o, dpool, tol)
+        for r in (0, wl.R - 1):
+            sel_r = {k: v[r] for k, v in sel.items()}
+            check_selection(o[r], cum_before[r][:wl.width(t)], g.Wout64, K, sel_r, f"r={r} t={t}")
+        s_ref = oracle.step_scores(o_ref, g.Wout64, dec.cum)
+        p0, t0 = sel["parent"][0], sel["token"][0]
+        dec.advance(t, p0, t0, s_ref[p0, t0])
+        np.testing.assert_array_equal(anc[0][:K, :t + 1], dec.anc)
+
+
+@pytest.mark.parametrize("name", ["stress", "growing"])
+def test_full_size_select_properties(name):
+    """Full-size select mode: exact selection on sampled requests (float64 rescoring of
+    the GPU's own outputs) and eq. (9) ancestry for every request."""
+    wl = synth.get(name)
+    R = wl.R
+    g = GpuDecode(wl, exact=())
+    anc_ref = [np.zeros((wl.width(0), 0), np.int32) for _ in range(R)]
+    g.init()
+    for t in range(wl.T):
+        o = to_np(g.step(t))
+        cum_before = g.export(B.GDN_EXPORT_CUM)
+        sel = g.select(t)
+        anc = g.export(B.GDN_EXPORT_ANCESTRY)
+        K = wl.width(t + 1)
+        for r in (0, R // 2, R - 1):
+            sel_r = {k: v[r] for k, v in sel.items()}
+            nd = check_selection(o[r], cum_before[r][:wl.width(t)], g.Wout64, K, sel_r, f"r={r} t={t}")
+            say(f"r={r} t={t} near-tie differences: {nd}")
+        for r in range(R):
+            anc_ref[r] = _eq9(anc_ref[r], sel["parent"][r], t)
+            assert np.array_equal(anc[r][:K, :t + 1], anc_ref[r]), f"ancestry r={r} t={t}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "single"])
+def test_all_scores_tied(name):
+    """Wout = 0: every candidate of a request scores cum - log V; the top-W is then the
+    W smallest flat indices, in order (the tie-break), at every step."""
+    wl = synth.get(name)
+    g = GpuDecode(wl, R=1, exact=(0,))
+    g.Wout.zero_()
+    g.Wout64[:] = 0
+    g.init()
+    for t in range(wl.T):
+        g.step(t)
+        sel = g.select(t)
+        K = wl.width(t + 1)
+        flat = sel["parent"][0].astype(np.int64) * wl.V + sel["token"][0]
+        np.testing.assert_array_equal(flat, np.arange(K))
+        expect = np.float32(-(t + 1) * np.log(wl.V))
+        assert np.all(np.abs(sel["score"][0] - expect) <= 1e-5 * abs(expect))
+
+
+def test_step_reissue_and_write_once():
+    """Re-issuing step t rewrites the same values; records of earlier steps never change;
+    slots beyond W_t of the current step are never written."""
+    wl = synth.get("single")
+    g = GpuDecode(wl, R=1, exact=(0,))
+    g.init()
+    g.dec.export(B.GDN_EXPORT_GTR_DELTA)  # warm
+    snap = None
+    for t in range(wl.T):
+        o1 = to_np(g.step(t)).copy()
+        p1 = g.export(B.GDN_EXPORT_GTR_DELTA)
+        o2 = to_np(g.step(t))
+        p2 = g.export(B.GDN_EXPORT_GTR_DELTA)
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(p1, p2)
+        if snap is not None:
+            np.testing.assert_array_equal(p2[:, :, :t], snap[:, :, :t])
+        snap = p2
+        g.select(t)
+
+
+def test_state_machine_errors():
+    wl = synth.get("tiny")
+    g = GpuDecode(wl, R=1, exact=(0,))
+    g.init()
+    d = g.dec
+    x = g.inputs[0]
+    s = g.sel[0]
+
+    def sel_status(t):
+        return B.raw_status("gdn_beam_select", d.ctx, t, g.o[0].data_ptr(), g.Wout.data_ptr(), wl.V,
+                            wl.width(1), None, None, s["parent"].data_ptr(), s["token"].data_ptr(),
+                            s["score"].data_ptr(), torch.cuda.current_stream().cuda_stream)
+
+    def step_status(t):
+        return B.raw_status("gdn_beam_step", d.ctx, t, x["q"].data_ptr(), x["k"].data_ptr(),
+                            x["v"].data_ptr(), x["alpha"].data_ptr(), x["beta"].data_ptr(),
+                            g.o[0].data_ptr(), torch.cuda.current_stream().cuda_stream)
+
+    assert sel_status(0) == B.GDN_ERR_BAD_STATE          # select before step
+    assert step_status(1) == B.GDN_ERR_BAD_STATE         # skipping ahead
+    assert step_status(wl.T) == B.GDN_ERR_CAPACITY       # beyond T_max
+    assert step_status(0) == B.GDN_OK
+    assert sel_status(1) == B.GDN_ERR_BAD_STATE          # wrong t
+    big = B.raw_status("gdn_beam_select", d.ctx, 0, g.o[0].data_ptr(), g.Wout.data_ptr(), wl.V + 1,
+                       wl.width(1), None, None, s["parent"].data_ptr(), s["token"].data_ptr(),
+                       s["score"].data_ptr(), None)
+    assert big == B.GDN_ERR_CAPACITY                     # V > V_max
+    assert sel_status(0) == B.GDN_OK
+    assert d.query() == (1, wl.width(1))
+    assert step_status(0) == B.GDN_ERR_BAD_STATE         # step 0 again after its select
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["tiny", "single", "batch"])
+def test_step_closed_forms(name):
+    """Eq. (8) at t = 0 with one term switched off (closed forms of eqs. 3-4):
+    S_ctx = 0 gives delta = beta v and o = beta v (k . q);
+    beta = 0 gives delta = 0 and o = alpha S_ctx q."""
+    wl = synth.get(name)
+    g = GpuDecode(wl, R=1, exact=(0,))
+    tol = TOL[wl.io]
+    q, k, v, al, be = g.step_inputs64(0, 0)
+    S = g.S_exact[0].astype(np.float64)
+    g.S_ctx.zero_()
+    g.init()
+    o = to_np(g.step(0))[0]
+    d = g.export(B.GDN_EXPORT_GTR_DELTA)[0][:, 0, :wl.width(0)]
+    kq = np.sum(k * q, axis=-1)
+    assert rel_err(d, be[..., None] * v) <= tol
+    assert rel_err(o, be[..., None] * v * kq[..., None]) <= tol
+    g.S_ctx.copy_(torch.from_numpy(g.S_exact[0][None]).to(g.dev))
+    g.inputs[0]["beta"].zero_()
+    g.init()
+    o = to_np(g.step(0))[0]
+    d = g.export(B.GDN_EXPORT_GTR_DELTA)[0][:, 0, :wl.width(0)]
+    assert np.all(d == 0)
+    assert rel_err(o, al[..., None] * np.einsum("hvk,hbk->hbv", S, q)) <= tol
