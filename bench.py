@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU oracle time")
     p.add_argument("--quiet", action="store_true")
+    p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                   help="first copy MIB MiB device-to-device 3 times (a plain copy of known size "
+                        "for scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -144,6 +147,15 @@ def main():
     wl = synth.get(args.workload)
     dev = torch.device("cuda")
     stream = torch.cuda.current_stream()
+    if args.copy_calib:
+        n = args.copy_calib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(args, f"copy calibration: 3 x {args.copy_calib} MiB device-to-device")
+        del src, dst
     log(args, f"workload {wl.name}: {wl.summary}")
 
     # ---- inputs resident in HBM before timing

@@ -13,12 +13,13 @@
 //   wout_t_kernel    codebook transpose Wout[d_v,V] -> [V,d_v] (MFMA operand order).
 //   logits_kernel    logits = z Wout on MFMA, stored [V][W_t]; online log-sum-exp parts.
 //   lse_kernel       combines the parts into logsumexp per beam.
-//   hist_kernel      one 11-bit radix pass over the candidate keys, relative to the
-//                    request's key range; the last block of a request picks the digit
-//                    (three passes give the exact K-th largest key).
-//   collect_kernel   gathers candidates above / at the threshold key.
-//   finalize_kernel  resolves ties by flat index, sorts the winners, writes the
-//                    top-W, and remaps ancestry, SID prefixes and scores (eq. 9).
+//   hist_kernel      first radix pass over every candidate key, 2048 digits spread over
+//                    the request's exact key range (one histogram per block).
+//   digit_kernel     sums a request's histograms and picks the boundary digit.
+//   compact_kernel   keys above the boundary digit -> winners; keys inside it -> kept.
+//   finalize_kernel  finishes the radix select on the kept keys, breaks ties by flat
+//                    index, sorts the winners, writes the top-W, and remaps ancestry,
+//                    SID prefixes and scores (eq. 9).
 //   prefill_kernel   eq. (3) over each request's prompt (the state S_ctx).
 #include <hip/hip_runtime.h>
 #include <cstdint>
@@ -190,6 +191,15 @@ __device__ __forceinline__ float dot_half(const typename IoT<BF16>::vec* a,
 // chunk at a time: lane l is beam l%32 and half l/32 of its d_k (B operand) and of
 // each 32-row block of d_v (accumulator), so the replay and eq. (8) run directly on
 // the MFMA accumulators with no hand-off.
+// Rows [row0, row0 + 16) of beam `beam` for the replay and eq. (8): the delta_j rows of
+// every ancestor record and the v_t rows, as raw vectors (loads only, no waiting).
+template <int DV, bool BF16, int NJ>
+struct RowLoads {
+  f32x4 d[NJ > 0 ? NJ : 1][4];
+  u32x4 vb[2];     // bf16 v: 16 values
+  f32x4 vf[4];     // fp32 v
+};
+
 template <int DK, int DV, bool BF16, int NWAVES, int TT>
 __global__ void __launch_bounds__(NWAVES * 64, 2) step_kernel(StepK a) {
   constexpr int DVP = DV < 32 ? 32 : DV;
@@ -198,24 +208,37 @@ __global__ void __launch_bounds__(NWAVES * 64, 2) step_kernel(StepK a) {
   constexpr int P = IoT<BF16>::per;
   constexpr int NC = HK / P;                      // io vectors per lane half
   constexpr int FRAG_BYTES = 4 * DVP * DK;
+  constexpr int NT = NWAVES * 64;
+  constexpr int NFILL = FRAG_BYTES / 16;
+  constexpr int t = TT;                           // step index, fixed at compile time
+  constexpr int NJ = TT;                          // ancestor records replayed
   using IV = typename IoT<BF16>::vec;
-  __shared__ u32x4 lds[FRAG_BYTES / 16];
+  __shared__ u32x4 lds[NFILL];
 
   const int work = xcd_work_id();
   const int rh = work / a.nwg, part = work % a.nwg;
   if (rh >= a.nrh) return;                        // whole block, before any barrier
 
-  {
+  {  // S_ctx fragments -> LDS, every load in flight before the first LDS write
+    constexpr int PER = (NFILL + NT - 1) / NT;
     const u32x4* src = reinterpret_cast<const u32x4*>(a.s_frag + size_t(rh) * FRAG_BYTES);
-    for (int i = threadIdx.x; i < FRAG_BYTES / 16; i += NWAVES * 64) lds[i] = src[i];
+    u32x4 tmp[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + i * NT;
+      if (NFILL % NT == 0 || idx < NFILL) tmp[i] = src[idx];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + i * NT;
+      if (NFILL % NT == 0 || idx < NFILL) lds[idx] = tmp[i];
+    }
   }
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 31, hf = lane >> 5;
   const int W = a.W;
-  constexpr int t = TT;                           // step index, fixed at compile time
-  constexpr int NJ = TT > 0 ? TT : 1;             // ancestor records replayed (t of them)
   const int r = rh / a.H;
   const int nchunk = (W + 31) >> 5;
   const IV* qg = static_cast<const IV*>(a.q);
@@ -228,42 +251,74 @@ __global__ void __launch_bounds__(NWAVES * 64, 2) step_kernel(StepK a) {
     if (chunk >= nchunk) break;
     const int b = chunk * 32 + m;
     const bool valid = b < W;
-    const size_t beam = size_t(rh) * W + b;
+    // lanes past W read beam 0's inputs (valid memory); their MFMA columns are
+    // independent of the others and nothing of theirs is stored
+    const size_t beam = size_t(rh) * W + (valid ? b : 0);
 
+    // round 1: q_t, k_t, gates and the ancestry indices
     IV qv[NC], kv[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      qv[c] = valid ? qg[beam * (DK / P) + hf * NC + c] : IV{};
-      kv[c] = valid ? kg[beam * (DK / P) + hf * NC + c] : IV{};
+      qv[c] = qg[beam * (DK / P) + hf * NC + c];
+      kv[c] = kg[beam * (DK / P) + hf * NC + c];
     }
-    const float al = valid ? a.alpha[beam] : 0.0f;
-    const float be = valid ? a.beta[beam] : 0.0f;
-
-    // k_t . q_t and the replay coefficients k_j . q_t, k_j . k_t of every ancestor j < t
-    float kq = dot_half<BF16, NC>(kv, qv);
-    kq += __shfl_xor(kq, 32);
-    int sj[NJ];
-    float aj[NJ], cq[NJ], ck[NJ];
+    const float al = a.alpha[beam];
+    const float be = a.beta[beam];
+    int sj[NJ > 0 ? NJ : 1];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      if (j < t) {
-        int s = valid ? a.anc[(size_t(r) * a.W_max + b) * a.T_max + j] : 0;
-        s = s < 0 ? 0 : (s >= a.W_max ? a.W_max - 1 : s);
-        sj[j] = s;
-        const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + s;
-        aj[j] = a.gtr_alpha[rec];
-        IV kj[NC];
+      int s = a.anc[(size_t(r) * a.W_max + (valid ? b : 0)) * a.T_max + j];
+      sj[j] = s < 0 ? 0 : (s >= a.W_max ? a.W_max - 1 : s);
+    }
+
+    auto load_rows = [&](int rb, RowLoads<DV, BF16, NJ>& L) {
+      const int row0 = min(32 * rb + 16 * hf, DV - 16);   // in range; rows >= DV unused
 #pragma unroll
-        for (int c = 0; c < NC; ++c) kj[c] = keyg[rec * (DK / P) + hf * NC + c];
-        float x = dot_half<BF16, NC>(kj, qv);
-        float y = dot_half<BF16, NC>(kj, kv);
-        cq[j] = x + __shfl_xor(x, 32);
-        ck[j] = y + __shfl_xor(y, 32);
+      for (int j = 0; j < NJ; ++j) {
+        const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + sj[j];
+        const f32x4* dp = reinterpret_cast<const f32x4*>(a.gtr_delta + rec * DV + row0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) L.d[j][c] = dp[c];
       }
+      if constexpr (BF16) {
+        const u32x4* vp = static_cast<const u32x4*>(a.v) + (beam * DV + row0) / 8;
+        L.vb[0] = vp[0];
+        L.vb[1] = vp[1];
+      } else {
+        const f32x4* vp = static_cast<const f32x4*>(a.v) + (beam * DV + row0) / 4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) L.vf[c] = vp[c];
+      }
+    };
+
+    // round 2: ancestor keys and gates, and the first row block's rows, all in flight
+    float aj[NJ > 0 ? NJ : 1];
+    IV kj[NJ > 0 ? NJ : 1][NC];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + sj[j];
+      aj[j] = a.gtr_alpha[rec];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kj[j][c] = keyg[rec * (DK / P) + hf * NC + c];
+    }
+    RowLoads<DV, BF16, NJ> rows;
+    load_rows(0, rows);
+
+    // k_t . q_t and the replay coefficients k_j . q_t, k_j . k_t (halves summed across lanes)
+    float kq = dot_half<BF16, NC>(kv, qv);
+    kq += __shfl_xor(kq, 32);
+    float cq[NJ > 0 ? NJ : 1], ck[NJ > 0 ? NJ : 1];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const float x = dot_half<BF16, NC>(kj[j], qv);
+      const float y = dot_half<BF16, NC>(kj[j], kv);
+      cq[j] = x + __shfl_xor(x, 32);
+      ck[j] = y + __shfl_xor(y, 32);
     }
 
 #pragma unroll 1
     for (int rb = 0; rb < NRB; ++rb) {
+      if (rb > 0) load_rows(rb, rows);     // in flight while this block's MFMAs run
       f32x16 accq = {}, acck = {};
       if constexpr (BF16) {
         const u32x4* fr = lds + rb * (DK / 16) * 2 * 64;
@@ -295,35 +350,26 @@ __global__ void __launch_bounds__(NWAVES * 64, 2) step_kernel(StepK a) {
       if (row0 < DV && valid) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          if (j < t) {
-            const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + sj[j];
-            const f32x4* dp = reinterpret_cast<const f32x4*>(a.gtr_delta + rec * DV + row0);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const f32x4 d = dp[c];
+          for (int c = 0; c < 4; ++c) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                accq[4 * c + i] = fmaf(d[i], cq[j], aj[j] * accq[4 * c + i]);   // eq. (6)
-                acck[4 * c + i] = fmaf(d[i], ck[j], aj[j] * acck[4 * c + i]);   // eq. (7)
-              }
+            for (int i = 0; i < 4; ++i) {
+              accq[4 * c + i] = fmaf(rows.d[j][c][i], cq[j], aj[j] * accq[4 * c + i]);   // eq. (6)
+              acck[4 * c + i] = fmaf(rows.d[j][c][i], ck[j], aj[j] * acck[4 * c + i]);   // eq. (7)
             }
           }
         }
         float vin[16];
         if constexpr (BF16) {
-          const u32x4* vp = static_cast<const u32x4*>(a.v) + (beam * DV + row0) / 8;
-          unpack8(vp[0], vin);
-          unpack8(vp[1], vin + 8);
+          unpack8(rows.vb[0], vin);
+          unpack8(rows.vb[1], vin + 8);
         } else {
-          const f32x4* vp = static_cast<const f32x4*>(a.v) + (beam * DV + row0) / 4;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const f32x4 x = vp[c];
-            for (int i = 0; i < 4; ++i) vin[4 * c + i] = x[i];
-          }
+          for (int c = 0; c < 4; ++c)
+            for (int i = 0; i < 4; ++i) vin[4 * c + i] = rows.vf[c][i];
         }
         f32x4* dout = reinterpret_cast<f32x4*>(a.gtr_delta + (slot_t * a.W_max + b) * DV + row0);
-        f32x4* oout = reinterpret_cast<f32x4*>(a.o + beam * DV + row0);
+        f32x4* oout = reinterpret_cast<f32x4*>(a.o + (size_t(rh) * W + b) * DV + row0);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           f32x4 dt, ot;
@@ -367,7 +413,6 @@ __global__ void zsum_kernel(const float* __restrict__ o, float* __restrict__ z, 
       SelState st{};
       st.kmax = 0u;
       st.kmin = 0xFFFFFFFFu;
-      st.shift = kShiftInit;
       st.need = uint32_t(K);
       sel[r] = st;
     }
@@ -542,21 +587,23 @@ struct SelK {
   const float* logits;   // per request [V][W]
   const float* lse;      // [R,W_max]
   const float* cum;      // [R,W_max] of step t
-  uint32_t* hist;        // [R,kHistBins]
+  uint32_t* hist;        // [R,kSelBlocksMax,kHistBins], one histogram per block
   SelState* sel;
-  uint64_t* winners;     // [R,W_max]
-  uint32_t* ties;        // [R,logits_stride]
+  uint64_t* winners;     // [R,W_max]: key << 32 | flat, keys above the boundary digit
+  uint32_t* cand;        // [R,logits_stride]: flat indices inside the boundary digit
 };
 
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t cand_key(const float* lg, const float* lse, const float* cum,
+                                             int W, int b, int c) {
+  return f2key(cand_score(cum[b], lg[size_t(c) * W + b], lse[b]));
 }
 
-// Candidates of one request are [V][W] logits; block `blk` of the request covers codes
-// [c0, c1).  Thread layout: with W >= 256 a thread owns beams tid + 256 i for every code;
-// with W < 256 it owns beam tid % W for every (256 / W)-th code.  No division per candidate.
+// Candidates of one request are its [V][W] logits; block `blk` covers codes [c0, c1).
+// With W >= 256 a thread owns beams tid + 256 i for every code; with W < 256 it owns
+// beam tid % W for every (256 / W)-th code.  Loads are issued eight at a time.
 template <typename F>
 __device__ __forceinline__ void for_each_candidate(const SelK& a, int r, int blk, F&& f) {
+  constexpr int U = 8;
   const int tid = threadIdx.x;
   const int W = a.W;
   const int cpb = (a.V + a.nblk - 1) / a.nblk;
@@ -564,43 +611,44 @@ __device__ __forceinline__ void for_each_candidate(const SelK& a, int r, int blk
   const float* lg = a.logits + size_t(r) * a.logits_stride;
   const float* lse = a.lse + size_t(r) * a.W_max;
   const float* cum = a.cum + size_t(r) * a.W_max;
+  int b0, bstep, cs, cstep;
   if (W >= 256) {
-    for (int b = tid; b < W; b += 256) {
-      const float cb = cum[b], lb = lse[b];
-      for (int c = c0; c < c1; ++c) f(f2key(cand_score(cb, lg[size_t(c) * W + b], lb)), b, c);
-    }
+    b0 = tid; bstep = 256; cs = c0; cstep = 1;
   } else {
     const int G = 256 / W;
     if (tid >= G * W) return;
-    const int b = tid % W, g = tid / W;
+    b0 = tid % W; bstep = W; cs = c0 + tid / W; cstep = G;
+  }
+  for (int b = b0; b < W; b += bstep) {
     const float cb = cum[b], lb = lse[b];
-    for (int c = c0 + g; c < c1; c += G) f(f2key(cand_score(cb, lg[size_t(c) * W + b], lb)), b, c);
+    int c = cs;
+    for (; c + (U - 1) * cstep < c1; c += U * cstep) {
+      float x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = lg[size_t(c + u * cstep) * W + b];
+#pragma unroll
+      for (int u = 0; u < U; ++u) f(f2key(cand_score(cb, x[u], lb)), b, c + u * cstep);
+    }
+    for (; c < c1; c += cstep) f(f2key(cand_score(cb, lg[size_t(c) * W + b], lb)), b, c);
   }
 }
 
-// One radix pass over a request's candidate keys.  The current range [lo, hi] is split
-// into 2048 digits of width 2^shift ((key - lo) >> shift); the first pass takes the
-// range from the exact key bounds, so the digits spread over the values present.  Each
-// block stores its own histogram; the last block to finish sums them, picks the digit
-// holding the need-th largest key and narrows the range to that digit.  Keys are 32
-// bits and each pass resolves 11, so three passes end on a single key (theta).
+// First radix pass over all candidates of a request.  The range [kmin, kmax] (exact
+// key bounds) is split into 2048 digits of width 2^shift; each block stores its own
+// histogram (plain stores: the next kernel reads them, so no fence is needed).
+__device__ __forceinline__ int first_shift(uint32_t lo, uint32_t hi) {
+  const uint32_t span = hi - lo;
+  const int bits = span ? 32 - __clz(span) : 0;
+  return bits > 11 ? bits - 11 : 0;
+}
+
 __global__ void __launch_bounds__(256) hist_kernel(SelK a) {
   __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t scan[256];
-  __shared__ int is_last;
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
-  SelState* st = a.sel + r;
-  int32_t shift = st->shift;
-  if (shift < 0) return;                       // threshold already found (uniform per request)
-  uint32_t lo = st->lo, hi = st->hi;
-  if (shift == kShiftInit) {
-    lo = st->kmin;
-    hi = st->kmax;
-    const uint32_t span = hi - lo;
-    const int bits = span ? 32 - __clz(span) : 0;
-    shift = bits > 11 ? bits - 11 : 0;
-  }
+  const SelState* st = a.sel + r;
+  const uint32_t lo = st->kmin, hi = st->kmax;
+  const int shift = first_shift(lo, hi);
   for (int i = tid; i < kHistBins; i += 256) h[i] = 0;
   __syncthreads();
   for_each_candidate(a, r, blockIdx.x, [&](uint32_t key, int, int) {
@@ -609,26 +657,34 @@ __global__ void __launch_bounds__(256) hist_kernel(SelK a) {
   __syncthreads();
   uint32_t* gh = a.hist + (size_t(r) * kSelBlocksMax + blockIdx.x) * kHistBins;
   for (int i = tid; i < kHistBins; i += 256) gh[i] = h[i];
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = (atomicAdd(&st->done, 1u) == uint32_t(a.nblk - 1));
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+}
 
-  // last block of this request: digit d with above(d) < need <= above(d) + count(d)
-  constexpr int PER = kHistBins / 256;
-  const uint32_t need = st->need;
+// One block per request: sum the block histograms and pick the digit d holding the
+// K-th largest key: keys above d are winners, keys inside d go on to the finish.
+__global__ void __launch_bounds__(256) digit_kernel(SelK a) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t scan[256];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  SelState* st = a.sel + r;
+  const uint32_t lo = st->kmin, hi = st->kmax;
+  const int shift = first_shift(lo, hi);
   const uint32_t* rh = a.hist + size_t(r) * kSelBlocksMax * kHistBins;
+  for (int d = tid; d < kHistBins; d += 256) {
+    uint32_t c = 0;
+#pragma unroll 8
+    for (int bk = 0; bk < a.nblk; ++bk) c += rh[size_t(bk) * kHistBins + d];
+    h[d] = c;
+  }
+  __syncthreads();
+  constexpr int PER = kHistBins / 256;
+  const uint32_t need = uint32_t(a.K);
   uint32_t cnt[PER];
   uint32_t tot = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {          // thread tid owns digits from the top down
-    const int d = kHistBins - 1 - (tid * PER + i);
-    uint32_t c = 0;
-    for (int bk = 0; bk < a.nblk; ++bk) c += ld_agent(&rh[size_t(bk) * kHistBins + d]);
-    cnt[i] = c;
-    tot += c;
+    cnt[i] = h[kHistBins - 1 - (tid * PER + i)];
+    tot += cnt[i];
   }
   scan[tid] = tot;
   __syncthreads();
@@ -649,35 +705,29 @@ __global__ void __launch_bounds__(256) hist_kernel(SelK a) {
         st->lo = nlo;
         st->hi = top < hi ? uint32_t(top) : hi;
         st->need = need - above;
-        if (shift == 0) {
-          st->theta = nlo;
-          st->tie_total = cnt[i];
-          st->shift = -1;
-        } else {
-          st->shift = shift > 11 ? shift - 11 : 0;
-        }
+        st->shift = shift == 0 ? -1 : (shift > 11 ? shift - 11 : 0);
       }
       above += cnt[i];
     }
   }
-  __syncthreads();
-  if (tid == 0) st->done = 0;
 }
 
-__global__ void __launch_bounds__(256) collect_kernel(SelK a) {
+// Split the candidates by the boundary digit [lo, hi]: keys above it are winners,
+// keys inside it are kept (flat index) for the finish kernel.
+__global__ void __launch_bounds__(256) compact_kernel(SelK a) {
   const int r = blockIdx.y;
   SelState* st = a.sel + r;
-  const uint32_t theta = st->theta;
+  const uint32_t lo = st->lo, hi = st->hi;
   const size_t cap = size_t(a.V) * a.W;
   for_each_candidate(a, r, blockIdx.x, [&](uint32_t key, int b, int c) {
-    if (key >= theta) {
+    if (key >= lo) {
       const uint32_t flat = uint32_t(b) * uint32_t(a.V) + uint32_t(c);
-      if (key > theta) {
+      if (key > hi) {
         const uint32_t i = atomicAdd(&st->n_win, 1u);
         if (i < uint32_t(a.W_max)) a.winners[size_t(r) * a.W_max + i] = (uint64_t(key) << 32) | flat;
       } else {
-        const uint32_t i = atomicAdd(&st->n_tie, 1u);
-        if (i < cap) a.ties[size_t(r) * a.logits_stride + i] = flat;
+        const uint32_t i = atomicAdd(&st->n_cand, 1u);
+        if (i < cap) a.cand[size_t(r) * a.logits_stride + i] = flat;
       }
     }
   });
@@ -696,76 +746,136 @@ struct FinK {
   int32_t* tok_next;
   const SelState* sel;
   const uint64_t* winners;
-  const uint32_t* ties;
+  const uint32_t* cand;
   const int32_t *forced_parent, *forced_token;
   int32_t *parent, *token;
   float* score;
   int32_t* status;
 };
 
-// One 1024-thread block per request.
+// One 1024-thread block per request: finish the radix select inside the boundary
+// digit (at most two more 11-bit passes over its candidates), keep the `need`
+// smallest flat indices among keys equal to the threshold, sort the K winners by
+// score descending then flat index ascending, write the top-W, and remap ancestry,
+// SID prefixes and cumulative scores by eq. (9).
 __global__ void __launch_bounds__(1024) finalize_kernel(FinK a) {
   __shared__ uint64_t s[kMaxW];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t cnt, phi_s, need_s;
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t scan[1024];
+  __shared__ uint32_t cnt, sh_lo, sh_hi, sh_need;
+  __shared__ int sh_shift;
   const int r = blockIdx.x, tid = threadIdx.x;
   const SelState st = a.sel[r];
-  const uint32_t theta = st.theta;
-  const uint32_t n_win = st.n_win < uint32_t(a.K) ? st.n_win : uint32_t(a.K);
-  const uint32_t n_tie = st.n_tie;
-  const uint32_t need = st.need;
-  const uint32_t* ties = a.ties + size_t(r) * a.logits_stride;
+  const float* lg = a.logits + size_t(r) * a.logits_stride;
+  const float* lse = a.lse + size_t(r) * a.W_max;
+  const float* cum = a.cum + size_t(r) * a.W_max;
+  const uint32_t* cand = a.cand + size_t(r) * a.logits_stride;
+  const uint32_t n_cand = min(st.n_cand, uint32_t(a.V) * uint32_t(a.W));
+  const uint32_t n_win = min(st.n_win, uint32_t(a.K));
+  const uint32_t V = uint32_t(a.V);
+  auto key_of = [&](uint32_t flat) {
+    return cand_key(lg, lse, cum, a.W, int(flat / V), int(flat % V));
+  };
 
-  // ties at the threshold key: keep the `need` smallest flat indices
+  // radix passes inside [lo, hi] until a single key remains (theta = lo = hi)
+  uint32_t lo = st.lo, hi = st.hi, need = st.need;
+  int shift = st.shift;
+  while (shift >= 0) {
+    for (int i = tid; i < kHistBins; i += 1024) hist[i] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < n_cand; i += 1024) {
+      const uint32_t key = key_of(cand[i]);
+      if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    const uint32_t c0 = hist[kHistBins - 1 - 2 * tid], c1 = hist[kHistBins - 2 - 2 * tid];
+    scan[tid] = c0 + c1;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const uint32_t x = tid >= off ? scan[tid - off] : 0u;
+      __syncthreads();
+      scan[tid] += x;
+      __syncthreads();
+    }
+    uint32_t above = scan[tid] - (c0 + c1);
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t ci = i ? c1 : c0;
+      if (above < need && need <= above + ci) {
+        const uint32_t d = uint32_t(kHistBins - 1 - (2 * tid + i));
+        const uint32_t nlo = lo + (d << shift);
+        const uint64_t top = uint64_t(nlo) + (uint64_t(1) << shift) - 1;
+        sh_lo = nlo;
+        sh_hi = top < hi ? uint32_t(top) : hi;
+        sh_need = need - above;
+        sh_shift = shift == 0 ? -1 : (shift > 11 ? shift - 11 : 0);
+      }
+      above += ci;
+    }
+    __syncthreads();
+    lo = sh_lo; hi = sh_hi; need = sh_need; shift = sh_shift;
+    __syncthreads();
+  }
+  const uint32_t theta = lo;
+
+  // ties at theta: keep the `need` smallest flat indices (radix over the flat index)
+  if (tid == 0) cnt = 0;
+  __syncthreads();
+  for (uint32_t i = tid; i < n_cand; i += 1024)
+    if (key_of(cand[i]) == theta) atomicAdd(&cnt, 1u);
+  __syncthreads();
+  const uint32_t n_eq = cnt;
   uint32_t phi = 0xFFFFFFFFu;
-  if (need < n_tie) {
+  if (need < n_eq) {
     uint32_t pre = 0, nd = need;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int sh = 24; sh >= 0; sh -= 8) {
       for (int i = tid; i < 256; i += 1024) hist[i] = 0;
       __syncthreads();
-      const uint32_t himask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-      for (uint32_t i = tid; i < n_tie; i += 1024) {
-        const uint32_t f = ties[i];
-        if ((f & himask) == (pre & himask)) atomicAdd(&hist[(f >> shift) & 255u], 1u);
+      const uint32_t himask = sh == 24 ? 0u : (0xFFFFFFFFu << (sh + 8));
+      for (uint32_t i = tid; i < n_cand; i += 1024) {
+        const uint32_t f = cand[i];
+        if ((f & himask) == (pre & himask) && key_of(f) == theta) atomicAdd(&hist[(f >> sh) & 255u], 1u);
       }
       __syncthreads();
       if (tid == 0) {
         uint32_t below = 0;
         for (int d = 0; d < 256; ++d) {
           if (below < nd && nd <= below + hist[d]) {
-            pre |= uint32_t(d) << shift;
+            pre |= uint32_t(d) << sh;
             nd -= below;
             break;
           }
           below += hist[d];
         }
-        phi_s = pre;
-        need_s = nd;
+        sh_lo = pre;
+        sh_need = nd;
       }
       __syncthreads();
-      pre = phi_s;
-      nd = need_s;
+      pre = sh_lo;
+      nd = sh_need;
       __syncthreads();
     }
     phi = pre;
   }
+
+  // gather the K winners
   if (tid == 0) cnt = 0;
   __syncthreads();
   for (uint32_t i = tid; i < n_win; i += 1024) {
     const uint32_t j = atomicAdd(&cnt, 1u);
     if (j < uint32_t(kMaxW)) s[j] = a.winners[size_t(r) * a.W_max + i];
   }
-  for (uint32_t i = tid; i < n_tie; i += 1024) {
-    const uint32_t f = ties[i];
-    if (f <= phi) {
+  for (uint32_t i = tid; i < n_cand; i += 1024) {
+    const uint32_t f = cand[i];
+    const uint32_t key = key_of(f);
+    if (key > theta || (key == theta && f <= phi)) {
       const uint32_t j = atomicAdd(&cnt, 1u);
-      if (j < uint32_t(kMaxW)) s[j] = (uint64_t(theta) << 32) | f;
+      if (j < uint32_t(kMaxW)) s[j] = (uint64_t(key) << 32) | f;
     }
   }
   __syncthreads();
   const uint32_t got = cnt;
   if (tid == 0 && got != uint32_t(a.K)) atomicOr(a.status, 2);
-  // pad to a power of two with the smallest possible entry, then sort descending by
+  // pad to a power of two with the smallest entry, then sort descending by
   // (key, ~flat): score descending, flat index ascending
   int n = 1;
   while (n < a.K) n <<= 1;
@@ -787,13 +897,10 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinK a) {
       __syncthreads();
     }
   }
-  const float* lg = a.logits + size_t(r) * a.logits_stride;
-  const float* lse = a.lse + size_t(r) * a.W_max;
-  const float* cum = a.cum + size_t(r) * a.W_max;
   for (int i = tid; i < a.K; i += 1024) {
     const uint64_t e = s[i];
     const uint32_t flat = 0xFFFFFFFFu - uint32_t(e);
-    int p = int(flat / uint32_t(a.V)), c = int(flat % uint32_t(a.V));
+    int p = int(flat / V), c = int(flat % V);
     if (uint32_t(i) >= got || p >= a.W) {   // only if fewer than K were gathered (flagged)
       p = 0;
       c = 0;
@@ -905,11 +1012,10 @@ static int launch_step_t(const StepArgs& a, hipStream_t s) {
   constexpr int NW = DV >= 256 ? 8 : 4;
   const int nchunk = (a.W + 31) / 32;
   const int nrh = a.R * a.H;
-  // chunks per wave: enough workgroups to fill 256 CUs several times over, while
-  // the S_ctx fragments are fetched once per workgroup
-  int cpw = 1;
-  while (cpw < 4 && size_t(nrh) * ((nchunk + NW * cpw * 2 - 1) / (NW * cpw * 2)) >= 2048) cpw *= 2;
-  const int nwg = (nchunk + NW * cpw - 1) / (NW * cpw);
+  // one workgroup per (request, head) takes all of its beams, so S_ctx is fetched from
+  // HBM once per (request, head) and reused from LDS by every beam
+  const int cpw = (nchunk + NW - 1) / NW;
+  const int nwg = 1;
   const long total = long(nrh) * nwg;
   const long grid = (total + 7) / 8 * 8;
   char* ws = static_cast<char*>(a.ws);
@@ -954,7 +1060,7 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   float4* lse_part = reinterpret_cast<float4*>(ws + L.lse_part);
   float* lse = reinterpret_cast<float*>(ws + L.lse);
   uint64_t* winners = reinterpret_cast<uint64_t*>(ws + L.winners);
-  uint32_t* ties = reinterpret_cast<uint32_t*>(ws + L.ties);
+  uint32_t* cand = reinterpret_cast<uint32_t*>(ws + L.cand);
   float* cum = reinterpret_cast<float*>(ws + L.cum[par]);
   float* cum_next = reinterpret_cast<float*>(ws + L.cum[par ^ 1]);
   int32_t* anc = reinterpret_cast<int32_t*>(ws + L.anc[par]);
@@ -1003,16 +1109,16 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
     nblk = nblk < 1 ? 1 : (nblk > kSelBlocksMax ? kSelBlocksMax : nblk);
     nblk = nblk > a.V ? a.V : nblk;                      // every block owns >= 1 code
     SelK k{a.W, a.W_max, a.V, a.W_next, int(nblk), a.T_max, a.t, stride, logits, lse, cum,
-           hist, sel, winners, ties};
+           hist, sel, winners, cand};
     dim3 grid(nblk, a.R);
-    for (int pass = 0; pass < 3; ++pass)   // 32-bit keys, 11 bits per pass
-      hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, k);
-    hipLaunchKernelGGL(collect_kernel, grid, dim3(256), 0, s, k);
+    hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, k);
+    hipLaunchKernelGGL(digit_kernel, dim3(a.R), dim3(256), 0, s, k);
+    hipLaunchKernelGGL(compact_kernel, grid, dim3(256), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
   {  // order, write the top-W, remap ancestry (eq. 9)
     FinK k{a.W, a.W_max, a.V, a.W_next, a.T_max, a.t, stride, logits, lse, cum, cum_next,
-           anc, anc_next, tok, tok_next, sel, winners, ties, a.forced_parent, a.forced_token,
+           anc, anc_next, tok, tok_next, sel, winners, cand, a.forced_parent, a.forced_token,
            a.parent, a.token, a.score, status};
     hipLaunchKernelGGL(finalize_kernel, dim3(a.R), dim3(1024), 0, s, k);
     if ((err = last_launch_error())) return err;

@@ -18,26 +18,20 @@ constexpr int kMaxW = 1024;       // beams per step (one sorting workgroup holds
 constexpr int kMaxV = 65536;      // codebook
 constexpr int kHistBins = 2048;   // radix digits per selection pass (11 bits)
 constexpr int kSelBlocksMax = 64; // histogram blocks per request
-constexpr int kSelPerBlock = 32768;// candidates per histogram block (before the cap)
+constexpr int kSelPerBlock = 8192; // candidates per histogram block (before the cap)
 
 // Per-request selection state (device).  Reset at the start of every select.
 // The radix passes bin keys relative to the request's exact key range: each pass
 // splits the current range [lo, lo + 2048 << shift) into 2048 digits.
 struct SelState {
   uint32_t kmax, kmin;  // largest / smallest candidate key of the request
-  uint32_t lo;          // smallest key of the current range
-  uint32_t hi;          // largest key of the current range
-  int32_t shift;        // digit width (log2) of the next pass; kShiftInit before the first,
-                        // -1 once the threshold key is known
-  uint32_t need;        // winners still to take inside the current range
-  uint32_t done;        // blocks finished in the current pass (last-block detection)
-  uint32_t theta;       // the K-th largest key (valid once shift == -1)
-  uint32_t tie_total;   // candidates whose key equals theta
-  uint32_t n_win;       // collected candidates with key > theta
-  uint32_t n_tie;       // collected candidates with key == theta
-  uint32_t pad[5];
+  uint32_t lo, hi;      // boundary digit [lo, hi] chosen by the first pass
+  int32_t shift;        // digit width (log2) for the next pass inside [lo, hi]; -1: lo == hi
+  uint32_t need;        // winners still to take inside [lo, hi]
+  uint32_t n_win;       // collected candidates with key > hi
+  uint32_t n_cand;      // collected candidates with key in [lo, hi]
+  uint32_t pad[8];
 };
-constexpr int32_t kShiftInit = 99;
 
 // Byte offsets of every region inside the caller's workspace (256-aligned).
 struct Layout {
@@ -56,7 +50,7 @@ struct Layout {
   size_t hist;        // [R,kSelBlocksMax,kHistBins] u32, one histogram per block
   size_t sel;         // [R] SelState
   size_t winners;     // [R,W_max] u64 (key<<32 | flat)
-  size_t ties;        // [R, V_max*W_max] u32 flat indices at the threshold key
+  size_t cand;        // [R, V_max*W_max] u32 flat indices inside the boundary digit
   size_t status;      // [64] i32
   size_t total;
 };
@@ -91,7 +85,7 @@ inline Layout make_layout(const gdn_beam_config& c) {
   L.hist = take(R * size_t(kSelBlocksMax) * kHistBins * 4);
   L.sel = take(R * sizeof(SelState));
   L.winners = take(R * W * 8);
-  L.ties = take(R * V * W * 4);
+  L.cand = take(R * V * W * 4);
   L.status = take(64 * 4);
   L.total = off;
   return L;
