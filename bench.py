@@ -76,6 +76,25 @@ def step_flops(wl, t):
     return wl.R * wl.H * W * (4 * wl.d_v * wl.d_k + t * (4 * wl.d_k + 4 * wl.d_v) + 8 * wl.d_v)
 
 
+def copy_bandwidth(torch, dev, mib=1024, reps=10):
+    """Read+write GB/s of a plain device-to-device copy: the bandwidth a kernel with
+    mixed reads and writes can reach on this GPU (context for the 8 TB/s peak)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
 def kernel_hash():
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
@@ -157,6 +176,8 @@ def main():
         log(args, f"copy calibration: 3 x {args.copy_calib} MiB device-to-device")
         del src, dst
     log(args, f"workload {wl.name}: {wl.summary}")
+    copy_gbs = copy_bandwidth(torch, dev)
+    log(args, f"device copy (read + write): {copy_gbs:.0f} GB/s")
 
     # ---- inputs resident in HBM before timing
     dec = BeamDecoder(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, wl.io, wl.wout)
@@ -259,6 +280,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gdn step_kernel", "bytes_per_decode": int(sum(bytes_t)),
+                     "copy_GBs": copy_gbs,
                      "launches_per_decode": wl.T},
         "gdn_step_rate": gdn_rate,
         "gdn_step_ms": float(step_ms.sum()),

@@ -4,7 +4,7 @@ Argument marshalling only.  Every pointer argument accepts an int (device
 address), None (NULL), or an object with .data_ptr() (a torch tensor).
 Streams accept an int handle, None (the null stream) or an object with
 .cuda_stream.  Non-OK statuses raise GdnBeamError.  The library must be built
-(python -m linear_attention_beam_amd.build); importing this module without it
+(python linear_attention_beam_amd/build.py); importing this module without it
 raises ImportError, there is no fallback.
 """
 from __future__ import annotations
@@ -53,7 +53,7 @@ def _hip_runtimes():
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run python -m linear_attention_beam_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run python linear_attention_beam_amd/build.py")
     # One process must hold one HIP runtime.  PyTorch ships its own copy (same SONAME,
     # different file); loading torch first makes this library bind to that copy.  The
     # other order would map two runtimes that both drive the GPU.

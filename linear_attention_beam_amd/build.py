@@ -1,6 +1,6 @@
 """Build libgdnbeam.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m linear_attention_beam_amd.build      # or build() from Python
+    python linear_attention_beam_amd/build.py      # or __graft_entry__.build()
 
 Packed fp32 VALU forms are switched off for all device code.
 """

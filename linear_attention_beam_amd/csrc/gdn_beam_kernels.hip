@@ -316,9 +316,9 @@ __global__ void __launch_bounds__(NWAVES * 64, 2) step_kernel(StepK a) {
       ck[j] = y + __shfl_xor(y, 32);
     }
 
-#pragma unroll 1
-    for (int rb = 0; rb < NRB; ++rb) {
-      if (rb > 0) load_rows(rb, rows);     // in flight while this block's MFMAs run
+    // one row block: MFMAs, replay, eq. (8), stores.  The next block's rows are issued
+    // before this block's stores, so waiting for them never waits on those stores.
+    auto row_block = [&](int rb, const RowLoads<DV, BF16, NJ>& R) {
       f32x16 accq = {}, acck = {};
       if constexpr (BF16) {
         const u32x4* fr = lds + rb * (DK / 16) * 2 * 64;
@@ -354,19 +354,19 @@ __global__ void __launch_bounds__(NWAVES * 64, 2) step_kernel(StepK a) {
           for (int c = 0; c < 4; ++c) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              accq[4 * c + i] = fmaf(rows.d[j][c][i], cq[j], aj[j] * accq[4 * c + i]);   // eq. (6)
-              acck[4 * c + i] = fmaf(rows.d[j][c][i], ck[j], aj[j] * acck[4 * c + i]);   // eq. (7)
+              accq[4 * c + i] = fmaf(R.d[j][c][i], cq[j], aj[j] * accq[4 * c + i]);   // eq. (6)
+              acck[4 * c + i] = fmaf(R.d[j][c][i], ck[j], aj[j] * acck[4 * c + i]);   // eq. (7)
             }
           }
         }
         float vin[16];
         if constexpr (BF16) {
-          unpack8(rows.vb[0], vin);
-          unpack8(rows.vb[1], vin + 8);
+          unpack8(R.vb[0], vin);
+          unpack8(R.vb[1], vin + 8);
         } else {
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            for (int i = 0; i < 4; ++i) vin[4 * c + i] = rows.vf[c][i];
+            for (int i = 0; i < 4; ++i) vin[4 * c + i] = R.vf[c][i];
         }
         f32x4* dout = reinterpret_cast<f32x4*>(a.gtr_delta + (slot_t * a.W_max + b) * DV + row0);
         f32x4* oout = reinterpret_cast<f32x4*>(a.o + (size_t(rh) * W + b) * DV + row0);
@@ -382,6 +382,24 @@ __global__ void __launch_bounds__(NWAVES * 64, 2) step_kernel(StepK a) {
           dout[c] = dt;
           oout[c] = ot;
         }
+      }
+    };
+    if constexpr (NRB == 1) {
+      row_block(0, rows);
+    } else if constexpr (NJ > 2) {       // registers allow one row buffer only
+#pragma unroll 1
+      for (int rb = 0; rb < NRB; ++rb) {
+        if (rb > 0) load_rows(rb, rows);
+        row_block(rb, rows);
+      }
+    } else {
+      RowLoads<DV, BF16, NJ> rows1;
+#pragma unroll 1
+      for (int rb = 0; rb < NRB; rb += 2) {
+        load_rows(rb + 1, rows1);
+        row_block(rb, rows);
+        if (rb + 2 < NRB) load_rows(rb + 2, rows);
+        row_block(rb + 1, rows1);
       }
     }
     // append the rest of record r_t = (alpha_t, delta_t, k_t) at slot (t, b)
@@ -661,7 +679,7 @@ __global__ void __launch_bounds__(256) hist_kernel(SelK a) {
 
 // One block per request: sum the block histograms and pick the digit d holding the
 // K-th largest key: keys above d are winners, keys inside d go on to the finish.
-__global__ void __launch_bounds__(256) digit_kernel(SelK a) {
+__global__ void __launch_bounds__(1024) digit_kernel(SelK a) {
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t scan[256];
   const int r = blockIdx.x;
@@ -670,30 +688,33 @@ __global__ void __launch_bounds__(256) digit_kernel(SelK a) {
   const uint32_t lo = st->kmin, hi = st->kmax;
   const int shift = first_shift(lo, hi);
   const uint32_t* rh = a.hist + size_t(r) * kSelBlocksMax * kHistBins;
-  for (int d = tid; d < kHistBins; d += 256) {
+  for (int d = tid; d < kHistBins; d += 1024) {
     uint32_t c = 0;
 #pragma unroll 8
     for (int bk = 0; bk < a.nblk; ++bk) c += rh[size_t(bk) * kHistBins + d];
     h[d] = c;
   }
   __syncthreads();
+  // digit scan on the first 256 threads (all threads take part in the barriers)
   constexpr int PER = kHistBins / 256;
   const uint32_t need = uint32_t(a.K);
+  const bool act = tid < 256;
   uint32_t cnt[PER];
   uint32_t tot = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {          // thread tid owns digits from the top down
-    cnt[i] = h[kHistBins - 1 - (tid * PER + i)];
+    cnt[i] = act ? h[kHistBins - 1 - (tid * PER + i)] : 0u;
     tot += cnt[i];
   }
-  scan[tid] = tot;
+  if (act) scan[tid] = tot;
   __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t x = tid >= off ? scan[tid - off] : 0u;
+    const uint32_t x = (act && tid >= off) ? scan[tid - off] : 0u;
     __syncthreads();
-    scan[tid] += x;
+    if (act) scan[tid] += x;
     __syncthreads();
   }
+  if (!act) return;
   uint32_t above = scan[tid] - tot;
   if (above < need && need <= above + tot) {
 #pragma unroll
@@ -1112,7 +1133,7 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
            hist, sel, winners, cand};
     dim3 grid(nblk, a.R);
     hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, k);
-    hipLaunchKernelGGL(digit_kernel, dim3(a.R), dim3(256), 0, s, k);
+    hipLaunchKernelGGL(digit_kernel, dim3(a.R), dim3(1024), 0, s, k);
     hipLaunchKernelGGL(compact_kernel, grid, dim3(256), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
