@@ -139,7 +139,7 @@ __global__ void init_kernel(InitArgs a) {
 // ---------------------------------------------------------------- step
 
 struct StepK {
-  int H, W, W_max, T_max, t, nwg, cpw, nrh;
+  int H, W, W_max, T_max, t, nrh;
   const void *q, *k, *v;
   const float *alpha, *beta;
   float* o;
@@ -150,265 +150,312 @@ struct StepK {
   const int32_t* anc;
 };
 
-template <bool BF16> struct IoT;
-template <> struct IoT<true> { using vec = u32x4; static constexpr int per = 8; };   // 8 bf16
-template <> struct IoT<false> { using vec = f32x4; static constexpr int per = 4; };  // 4 f32
+// Sizes of the fused step for head dims (DK, DV) and io dtype.
+template <int DK, int DV, bool BF16>
+struct StepCfg {
+  static constexpr int DVP = DV < 32 ? 32 : DV;
+  static constexpr int NW = DVP / 32;            // one wave per 32-row block of d_v
+  static constexpr int NT = NW * 64;
+  static constexpr int E = BF16 ? 2 : 4;         // bytes per io element
+  static constexpr int QB = DK * E;              // bytes of one q / k row
+  static constexpr int VB = DV * E;              // bytes of one v row
+  static constexpr int QROW = QB + 16;           // padded LDS rows (bank spread)
+  static constexpr int VROW = VB + 16;
+  static constexpr int QU = 32 * QB / 16 / NT;   // 16-byte staging units per thread
+  static constexpr int VU = 32 * VB / 16 / NT;
+  static constexpr int TPB = NT / 32;            // threads per beam in the dot phase
+  static constexpr int SEGB = QB / TPB;          // bytes of q / k each of them takes
+  static constexpr int SLOT = 32 * (2 * QROW + VROW) + 2 * 32 * 4 + 32 * kMaxT * 4;
+  static_assert(QU >= 1 && VU >= 1 && SEGB >= 16 && SEGB % 16 == 0, "unsupported shape");
+};
 
 template <bool BF16>
-__device__ __forceinline__ void vec_to_f(const typename IoT<BF16>::vec& x, float* f) {
-  if constexpr (BF16) unpack8(x, f);
-  else { for (int i = 0; i < 4; ++i) f[i] = x[i]; }
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// partial dot product over this lane's half of d_k (bf16 pairs go through v_dot2)
-template <bool BF16, int N>
-__device__ __forceinline__ float dot_half(const typename IoT<BF16>::vec* a,
-                                          const typename IoT<BF16>::vec* b) {
-  // (bit-cast whole vectors, never single elements of one: hipcc lowers a bit-cast of an
-  // ext-vector element to element 0)
-  float s = 0.0f;
+__device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float s) {
+  if constexpr (BF16) {
+    // (bit-cast whole vectors, never single elements of one: hipcc lowers a bit-cast
+    // of an ext-vector element to element 0)
+    const bf16x8 x = __builtin_bit_cast(bf16x8, a);
+    const bf16x8 y = __builtin_bit_cast(bf16x8, b);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x.s01, y.s01, s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x.s23, y.s23, s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x.s45, y.s45, s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x.s67, y.s67, s, false);
+  } else {
+    const f32x4 x = __builtin_bit_cast(f32x4, a);
+    const f32x4 y = __builtin_bit_cast(f32x4, b);
 #pragma unroll
-  for (int c = 0; c < N; ++c) {
-    if constexpr (BF16) {
-      const bf16x8 x = __builtin_bit_cast(bf16x8, a[c]);
-      const bf16x8 y = __builtin_bit_cast(bf16x8, b[c]);
-      s = __builtin_amdgcn_fdot2_f32_bf16(x.s01, y.s01, s, false);
-      s = __builtin_amdgcn_fdot2_f32_bf16(x.s23, y.s23, s, false);
-      s = __builtin_amdgcn_fdot2_f32_bf16(x.s45, y.s45, s, false);
-      s = __builtin_amdgcn_fdot2_f32_bf16(x.s67, y.s67, s, false);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(a[c][i], b[c][i], s);
-    }
+    for (int i = 0; i < 4; ++i) s = fmaf(x[i], y[i], s);
   }
   return s;
 }
 
-// One workgroup = one (request, head) x a range of 32-beam chunks; S_ctx fragments
-// live in LDS and are reused by every beam the workgroup handles.  A wave owns one
-// chunk at a time: lane l is beam l%32 and half l/32 of its d_k (B operand) and of
-// each 32-row block of d_v (accumulator), so the replay and eq. (8) run directly on
-// the MFMA accumulators with no hand-off.
-// Rows [row0, row0 + 16) of beam `beam` for the replay and eq. (8): the delta_j rows of
-// every ancestor record and the v_t rows, as raw vectors (loads only, no waiting).
-template <int DV, bool BF16, int NJ>
-struct RowLoads {
-  f32x4 d[NJ > 0 ? NJ : 1][4];
-  u32x4 vb[2];     // bf16 v: 16 values
-  f32x4 vf[4];     // fp32 v
-};
+// Fused SID step (OneLA reading note, sections 2.3-2.5).  One workgroup per
+// (request, head); wave w owns rows [32 w, 32 w + 32) of d_v and keeps that block of
+// S_ctx (bf16 hi/lo, or fp32) as MFMA A fragments in registers for every beam.  Beams
+// go through in chunks of 32: a chunk's q, k, v, gates and ancestry indices are
+// loaded with contiguous reads into registers while the previous chunk computes, then
+// written to a double-buffered LDS slot.  Per chunk:
+//   dots     threads cooperate per beam on k_t.q_t and, for each ancestor record j,
+//            k_j.q_t and k_j.k_t (contiguous reads of the records' keys);
+//   per wave U = S_block [q|k] on MFMA (B fragments from LDS), the delta_j rows of
+//            the ancestors gathered meanwhile; then eqs. (6)-(7) on the accumulators
+//            and eq. (8); delta_t and o_t rows stored;
+//   append   k_t rows copied from LDS to slot (t, b) of the record pool, alpha_t.
+template <int DK, int DV, bool BF16, int TT>
+__global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(StepK a) {
+  using C = StepCfg<DK, DV, BF16>;
+  constexpr int NT = C::NT, QROW = C::QROW, VROW = C::VROW, TPB = C::TPB;
+  constexpr int UPQ = C::QB / 16, UPV = C::VB / 16;      // 16-byte units per row
+  constexpr int NJ = TT;                                 // ancestor records replayed
+  constexpr int NJ1 = NJ > 0 ? NJ : 1;
+  constexpr int HK = DK / 2;
+  constexpr int SCN = 1 + 3 * NJ;                        // kq, alpha_j, cq_j, ck_j
+  __shared__ __align__(16) unsigned char lds[2 * C::SLOT + 32 * SCN * 4];
+  float* sc = reinterpret_cast<float*>(lds + 2 * C::SLOT);
 
-template <int DK, int DV, bool BF16, int NWAVES, int TT>
-__global__ void __launch_bounds__(NWAVES * 64, 2) step_kernel(StepK a) {
-  constexpr int DVP = DV < 32 ? 32 : DV;
-  constexpr int NRB = DVP / 32;
-  constexpr int HK = DK / 2;                      // d_k elements per lane half
-  constexpr int P = IoT<BF16>::per;
-  constexpr int NC = HK / P;                      // io vectors per lane half
-  constexpr int FRAG_BYTES = 4 * DVP * DK;
-  constexpr int NT = NWAVES * 64;
-  constexpr int NFILL = FRAG_BYTES / 16;
-  constexpr int t = TT;                           // step index, fixed at compile time
-  constexpr int NJ = TT;                          // ancestor records replayed
-  using IV = typename IoT<BF16>::vec;
-  __shared__ u32x4 lds[NFILL];
+  const int rh = xcd_work_id();
+  if (rh >= a.nrh) return;                                // whole block, before any barrier
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int m = lane & 31, hf = lane >> 5;
+  const int W = a.W, r = rh / a.H;
+  const int nch = (W + 31) >> 5;
+  const size_t slot_t = size_t(rh) * a.T_max + TT;       // (r,h,t) row of the record pool
+  const unsigned char* qg = static_cast<const unsigned char*>(a.q);
+  const unsigned char* kg = static_cast<const unsigned char*>(a.k);
+  const unsigned char* vg = static_cast<const unsigned char*>(a.v);
+  unsigned char* keyg = static_cast<unsigned char*>(a.gtr_key);
 
-  const int work = xcd_work_id();
-  const int rh = work / a.nwg, part = work % a.nwg;
-  if (rh >= a.nrh) return;                        // whole block, before any barrier
-
-  {  // S_ctx fragments -> LDS, every load in flight before the first LDS write
-    constexpr int PER = (NFILL + NT - 1) / NT;
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.s_frag + size_t(rh) * FRAG_BYTES);
-    u32x4 tmp[PER];
+  // this wave's block of S_ctx as A fragments (layout written by init_kernel)
+  constexpr int NA = BF16 ? 2 * (DK / 16) : DK / 8;
+  u32x4 afr[NA];
+  {
+    const u32x4* fr = reinterpret_cast<const u32x4*>(a.s_frag + size_t(rh) * 4 * C::DVP * DK);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = threadIdx.x + i * NT;
-      if (NFILL % NT == 0 || idx < NFILL) tmp[i] = src[idx];
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = threadIdx.x + i * NT;
-      if (NFILL % NT == 0 || idx < NFILL) lds[idx] = tmp[i];
-    }
+    for (int i = 0; i < NA; ++i) afr[i] = fr[(w * NA + i) * 64 + lane];
   }
+
+  // ---- staging of one chunk: registers <- global (contiguous), LDS <- registers
+  u32x4 sq[C::QU], sk[C::QU], sv[C::VU];
+  float sab = 0.0f;
+  constexpr int NAI = (32 * NJ1 + NT - 1) / NT;
+  int sanc[NAI];
+  auto stage_load = [&](int c) {
+    const int c0 = c * 32, nb = min(32, W - c0);
+    const size_t base = size_t(rh) * W + c0;
+#pragma unroll
+    for (int i = 0; i < C::QU; ++i) {
+      const int u = tid + i * NT;
+      if (u / UPQ < nb) {
+        sq[i] = *reinterpret_cast<const u32x4*>(qg + base * C::QB + size_t(u) * 16);
+        sk[i] = *reinterpret_cast<const u32x4*>(kg + base * C::QB + size_t(u) * 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::VU; ++i) {
+      const int u = tid + i * NT;
+      if (u / UPV < nb) sv[i] = *reinterpret_cast<const u32x4*>(vg + base * C::VB + size_t(u) * 16);
+    }
+    if (tid < 64 && (tid & 31) < nb) sab = tid < 32 ? a.alpha[base + tid] : a.beta[base + tid - 32];
+#pragma unroll
+    for (int i = 0; i < NAI; ++i) {
+      const int e = tid + i * NT, bb = e / NJ1, j = e % NJ1;
+      if (NJ > 0 && e < 32 * NJ && bb < nb) sanc[i] = a.anc[(size_t(r) * a.W_max + c0 + bb) * a.T_max + j];
+    }
+  };
+  auto stage_store = [&](int slot) {
+    unsigned char* L = lds + slot * C::SLOT;
+#pragma unroll
+    for (int i = 0; i < C::QU; ++i) {
+      const int u = tid + i * NT, bb = u / UPQ, o = (u % UPQ) * 16;
+      *reinterpret_cast<u32x4*>(L + bb * QROW + o) = sq[i];
+      *reinterpret_cast<u32x4*>(L + 32 * QROW + bb * QROW + o) = sk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::VU; ++i) {
+      const int u = tid + i * NT, bb = u / UPV, o = (u % UPV) * 16;
+      *reinterpret_cast<u32x4*>(L + 64 * QROW + bb * VROW + o) = sv[i];
+    }
+    float* ab = reinterpret_cast<float*>(L + 64 * QROW + 32 * VROW);
+    if (tid < 64) ab[tid] = sab;
+    int* an = reinterpret_cast<int*>(L + 64 * QROW + 32 * VROW + 256);
+#pragma unroll
+    for (int i = 0; i < NAI; ++i) {
+      const int e = tid + i * NT, bb = e / NJ1, j = e % NJ1;
+      if (NJ > 0 && e < 32 * NJ) {
+        const int s = sanc[i];
+        an[bb * kMaxT + j] = s < 0 ? 0 : (s >= a.W_max ? a.W_max - 1 : s);
+      }
+    }
+  };
+
+  stage_load(0);
+  stage_store(0);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m = lane & 31, hf = lane >> 5;
-  const int W = a.W;
-  const int r = rh / a.H;
-  const int nchunk = (W + 31) >> 5;
-  const IV* qg = static_cast<const IV*>(a.q);
-  const IV* kg = static_cast<const IV*>(a.k);
-  IV* keyg = static_cast<IV*>(a.gtr_key);
-  const size_t slot_t = size_t(rh) * a.T_max + t;          // (r,h,t) slot row
+  for (int c = 0; c < nch; ++c) {
+    const int c0 = c * 32, nb = min(32, W - c0);
+    const unsigned char* L = lds + (c & 1) * C::SLOT;
+    const unsigned char* Lq = L;
+    const unsigned char* Lk = L + 32 * QROW;
+    const unsigned char* Lv = L + 64 * QROW;
+    const float* Lab = reinterpret_cast<const float*>(L + 64 * QROW + 32 * VROW);
+    const int* Lan = reinterpret_cast<const int*>(L + 64 * QROW + 32 * VROW + 256);
 
-  for (int ci = 0; ci < a.cpw; ++ci) {
-    const int chunk = (part * a.cpw + ci) * NWAVES + wave;
-    if (chunk >= nchunk) break;
-    const int b = chunk * 32 + m;
-    const bool valid = b < W;
-    // lanes past W read beam 0's inputs (valid memory); their MFMA columns are
-    // independent of the others and nothing of theirs is stored
-    const size_t beam = size_t(rh) * W + (valid ? b : 0);
-
-    // round 1: q_t, k_t, gates and the ancestry indices
-    IV qv[NC], kv[NC];
+    // ---- dots: TPB threads per beam, SEGB bytes of d_k each
+    {
+      const int bm = tid / TPB, sg = tid % TPB;
+      const bool ok = bm < nb;
+      constexpr int SV = C::SEGB / 16;
+      u32x4 xq[SV], xk[SV];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      qv[c] = qg[beam * (DK / P) + hf * NC + c];
-      kv[c] = kg[beam * (DK / P) + hf * NC + c];
-    }
-    const float al = a.alpha[beam];
-    const float be = a.beta[beam];
-    int sj[NJ > 0 ? NJ : 1];
+      for (int i = 0; i < SV; ++i) {
+        xq[i] = *reinterpret_cast<const u32x4*>(Lq + bm * QROW + sg * C::SEGB + 16 * i);
+        xk[i] = *reinterpret_cast<const u32x4*>(Lk + bm * QROW + sg * C::SEGB + 16 * i);
+      }
+      float kq = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      int s = a.anc[(size_t(r) * a.W_max + (valid ? b : 0)) * a.T_max + j];
-      sj[j] = s < 0 ? 0 : (s >= a.W_max ? a.W_max - 1 : s);
-    }
-
-    auto load_rows = [&](int rb, RowLoads<DV, BF16, NJ>& L) {
-      const int row0 = min(32 * rb + 16 * hf, DV - 16);   // in range; rows >= DV unused
+      for (int i = 0; i < SV; ++i) kq = dot16<BF16>(xk[i], xq[i], kq);
+      float aj[NJ1], cq[NJ1], ck[NJ1];
+      u32x4 kj[NJ1][SV];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + sj[j];
-        const f32x4* dp = reinterpret_cast<const f32x4*>(a.gtr_delta + rec * DV + row0);
+        const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (ok ? Lan[bm * kMaxT + j] : 0);
+        aj[j] = a.gtr_alpha[rec];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) L.d[j][c] = dp[c];
+        for (int i = 0; i < SV; ++i)
+          kj[j][i] = *reinterpret_cast<const u32x4*>(keyg + rec * C::QB + sg * C::SEGB + 16 * i);
       }
-      if constexpr (BF16) {
-        const u32x4* vp = static_cast<const u32x4*>(a.v) + (beam * DV + row0) / 8;
-        L.vb[0] = vp[0];
-        L.vb[1] = vp[1];
-      } else {
-        const f32x4* vp = static_cast<const f32x4*>(a.v) + (beam * DV + row0) / 4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) L.vf[c] = vp[c];
+      for (int j = 0; j < NJ; ++j) {
+        cq[j] = 0.0f;
+        ck[j] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < SV; ++i) {
+          cq[j] = dot16<BF16>(kj[j][i], xq[i], cq[j]);
+          ck[j] = dot16<BF16>(kj[j][i], xk[i], ck[j]);
+        }
       }
-    };
-
-    // round 2: ancestor keys and gates, and the first row block's rows, all in flight
-    float aj[NJ > 0 ? NJ : 1];
-    IV kj[NJ > 0 ? NJ : 1][NC];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + sj[j];
-      aj[j] = a.gtr_alpha[rec];
+      for (int off = 1; off < TPB; off <<= 1) {
+        kq += __shfl_xor(kq, off);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kj[j][c] = keyg[rec * (DK / P) + hf * NC + c];
+        for (int j = 0; j < NJ; ++j) {
+          cq[j] += __shfl_xor(cq[j], off);
+          ck[j] += __shfl_xor(ck[j], off);
+        }
+      }
+      if (sg == 0) {
+        sc[bm * SCN] = kq;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          sc[bm * SCN + 1 + j] = aj[j];
+          sc[bm * SCN + 1 + NJ + j] = cq[j];
+          sc[bm * SCN + 1 + 2 * NJ + j] = ck[j];
+        }
+      }
     }
-    RowLoads<DV, BF16, NJ> rows;
-    load_rows(0, rows);
+    __syncthreads();
 
-    // k_t . q_t and the replay coefficients k_j . q_t, k_j . k_t (halves summed across lanes)
-    float kq = dot_half<BF16, NC>(kv, qv);
-    kq += __shfl_xor(kq, 32);
-    float cq[NJ > 0 ? NJ : 1], ck[NJ > 0 ? NJ : 1];
+    // ---- this wave's row block for the chunk's 32 beams (lane: beam m, rows half hf)
+    {
+      const bool valid = m < nb;
+      const int b = c0 + m;
+      const int row0 = 32 * w + 16 * hf;
+      const int rowl = min(row0, DV - 16);               // in range (rows >= DV unused)
+      f32x4 dj[NJ1][4];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const float x = dot_half<BF16, NC>(kj[j], qv);
-      const float y = dot_half<BF16, NC>(kj[j], kv);
-      cq[j] = x + __shfl_xor(x, 32);
-      ck[j] = y + __shfl_xor(y, 32);
-    }
+      for (int j = 0; j < NJ; ++j) {
+        const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (valid ? Lan[m * kMaxT + j] : 0);
+        const f32x4* dp = reinterpret_cast<const f32x4*>(a.gtr_delta + rec * DV + rowl);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) dj[j][q4] = dp[q4];
+      }
+      if (c + 1 < nch) stage_load(c + 1);               // in flight until the end of the chunk
 
-    // one row block: MFMAs, replay, eq. (8), stores.  The next block's rows are issued
-    // before this block's stores, so waiting for them never waits on those stores.
-    auto row_block = [&](int rb, const RowLoads<DV, BF16, NJ>& R) {
       f32x16 accq = {}, acck = {};
       if constexpr (BF16) {
-        const u32x4* fr = lds + rb * (DK / 16) * 2 * 64;
 #pragma unroll
         for (int kk = 0; kk < DK / 16; ++kk) {
-          const bf16x8 ahi = __builtin_bit_cast(bf16x8, fr[(kk * 2 + 0) * 64 + lane]);
-          const bf16x8 alo = __builtin_bit_cast(bf16x8, fr[(kk * 2 + 1) * 64 + lane]);
-          const bf16x8 bq = __builtin_bit_cast(bf16x8, qv[kk]);
-          const bf16x8 bk = __builtin_bit_cast(bf16x8, kv[kk]);
+          const int off = m * QROW + (HK * hf + 8 * kk) * 2;
+          const bf16x8 bq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lq + off));
+          const bf16x8 bk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lk + off));
+          const bf16x8 ahi = __builtin_bit_cast(bf16x8, afr[2 * kk]);
+          const bf16x8 alo = __builtin_bit_cast(bf16x8, afr[2 * kk + 1]);
           accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bq, accq, 0, 0, 0);
           acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bk, acck, 0, 0, 0);
           accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bq, accq, 0, 0, 0);
           acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bk, acck, 0, 0, 0);
         }
       } else {
-        const f32x4* fr = reinterpret_cast<const f32x4*>(lds) + rb * (DK / 8) * 64;
 #pragma unroll
         for (int kk4 = 0; kk4 < DK / 8; ++kk4) {
-          const f32x4 af = fr[kk4 * 64 + lane];
+          const int off = m * QROW + (HK * hf + 4 * kk4) * 4;
+          const f32x4 bq = *reinterpret_cast<const f32x4*>(Lq + off);
+          const f32x4 bk = *reinterpret_cast<const f32x4*>(Lk + off);
+          const f32x4 af = __builtin_bit_cast(f32x4, afr[kk4]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            accq = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], qv[kk4][i], accq, 0, 0, 0);
-            acck = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], kv[kk4][i], acck, 0, 0, 0);
+            accq = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bq[i], accq, 0, 0, 0);
+            acck = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bk[i], acck, 0, 0, 0);
           }
         }
       }
-      // accumulator register i of this lane = physical row 32 rb + 16 hf + i of beam b
-      const int row0 = 32 * rb + 16 * hf;
+
+      // accumulator register i of this lane = physical row row0 + i of beam b
       if (row0 < DV && valid) {
+        const float* s = sc + m * SCN;
+        const float kq = s[0];
+        const float al = Lab[m], be = Lab[32 + m];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
+          const float ajj = s[1 + j], cqj = s[1 + NJ + j], ckj = s[1 + 2 * NJ + j];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int q4 = 0; q4 < 4; ++q4) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              accq[4 * c + i] = fmaf(R.d[j][c][i], cq[j], aj[j] * accq[4 * c + i]);   // eq. (6)
-              acck[4 * c + i] = fmaf(R.d[j][c][i], ck[j], aj[j] * acck[4 * c + i]);   // eq. (7)
+              accq[4 * q4 + i] = fmaf(dj[j][q4][i], cqj, ajj * accq[4 * q4 + i]);   // eq. (6)
+              acck[4 * q4 + i] = fmaf(dj[j][q4][i], ckj, ajj * acck[4 * q4 + i]);   // eq. (7)
             }
           }
         }
         float vin[16];
         if constexpr (BF16) {
-          unpack8(R.vb[0], vin);
-          unpack8(R.vb[1], vin + 8);
+          const u32x4* vp = reinterpret_cast<const u32x4*>(Lv + m * VROW + row0 * 2);
+          unpack8(vp[0], vin);
+          unpack8(vp[1], vin + 8);
         } else {
+          const f32x4* vp = reinterpret_cast<const f32x4*>(Lv + m * VROW + row0 * 4);
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            for (int i = 0; i < 4; ++i) vin[4 * c + i] = R.vf[c][i];
+          for (int q4 = 0; q4 < 4; ++q4)
+            for (int i = 0; i < 4; ++i) vin[4 * q4 + i] = vp[q4][i];
         }
         f32x4* dout = reinterpret_cast<f32x4*>(a.gtr_delta + (slot_t * a.W_max + b) * DV + row0);
         f32x4* oout = reinterpret_cast<f32x4*>(a.o + (size_t(rh) * W + b) * DV + row0);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int q4 = 0; q4 < 4; ++q4) {
           f32x4 dt, ot;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int e = 4 * c + i;
+            const int e = 4 * q4 + i;
             dt[i] = be * (vin[e] - al * acck[e]);              // eq. (8) delta_t
             ot[i] = fmaf(dt[i], kq, al * accq[e]);             // eq. (8) o_t
           }
-          dout[c] = dt;
-          oout[c] = ot;
+          dout[q4] = dt;
+          oout[q4] = ot;
         }
       }
-    };
-    if constexpr (NRB == 1) {
-      row_block(0, rows);
-    } else if constexpr (NJ > 2) {       // registers allow one row buffer only
-#pragma unroll 1
-      for (int rb = 0; rb < NRB; ++rb) {
-        if (rb > 0) load_rows(rb, rows);
-        row_block(rb, rows);
-      }
-    } else {
-      RowLoads<DV, BF16, NJ> rows1;
-#pragma unroll 1
-      for (int rb = 0; rb < NRB; rb += 2) {
-        load_rows(rb + 1, rows1);
-        row_block(rb, rows);
-        if (rb + 2 < NRB) load_rows(rb + 2, rows);
-        row_block(rb + 1, rows1);
-      }
     }
-    // append the rest of record r_t = (alpha_t, delta_t, k_t) at slot (t, b)
-    if (valid) {
-      const size_t rec = slot_t * a.W_max + b;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) keyg[rec * (DK / P) + hf * NC + c] = kv[c];
-      if (hf == 0) a.gtr_alpha[rec] = al;
+
+    // ---- append: k_t rows (contiguous slots c0..c0+nb-1) and alpha_t
+    {
+      unsigned char* dst = keyg + (slot_t * a.W_max + c0) * C::QB;
+      for (int u = tid; u < nb * UPQ; u += NT)
+        *reinterpret_cast<u32x4*>(dst + size_t(u) * 16) =
+            *reinterpret_cast<const u32x4*>(Lk + (u / UPQ) * QROW + (u % UPQ) * 16);
+      if (tid < nb) a.gtr_alpha[slot_t * a.W_max + c0 + tid] = Lab[tid];
     }
+    if (c + 1 < nch) stage_store((c + 1) & 1);
+    __syncthreads();
   }
 }
 
@@ -1014,37 +1061,27 @@ int launch_init(const InitArgs& a, hipStream_t s) {
   return last_launch_error();
 }
 
-template <int DK, int DV, bool BF16, int NW>
-static void launch_step_tt(const StepArgs& a, const StepK& k, dim3 grid, hipStream_t s) {
-  switch (a.t) {
-    case 0: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, NW, 0>), grid, dim3(NW * 64), 0, s, k); break;
-    case 1: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, NW, 1>), grid, dim3(NW * 64), 0, s, k); break;
-    case 2: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, NW, 2>), grid, dim3(NW * 64), 0, s, k); break;
-    case 3: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, NW, 3>), grid, dim3(NW * 64), 0, s, k); break;
-    case 4: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, NW, 4>), grid, dim3(NW * 64), 0, s, k); break;
-    case 5: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, NW, 5>), grid, dim3(NW * 64), 0, s, k); break;
-    case 6: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, NW, 6>), grid, dim3(NW * 64), 0, s, k); break;
-    default: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, NW, 7>), grid, dim3(NW * 64), 0, s, k); break;
-  }
-}
-
 template <int DK, int DV, bool BF16>
 static int launch_step_t(const StepArgs& a, hipStream_t s) {
-  constexpr int NW = DV >= 256 ? 8 : 4;
-  const int nchunk = (a.W + 31) / 32;
+  constexpr int NT = StepCfg<DK, DV, BF16>::NT;
   const int nrh = a.R * a.H;
-  // one workgroup per (request, head) takes all of its beams, so S_ctx is fetched from
-  // HBM once per (request, head) and reused from LDS by every beam
-  const int cpw = (nchunk + NW - 1) / NW;
-  const int nwg = 1;
-  const long total = long(nrh) * nwg;
-  const long grid = (total + 7) / 8 * 8;
+  // one workgroup per (request, head): S_ctx is read once and kept in registers
+  const long grid = (long(nrh) + 7) / 8 * 8;
   char* ws = static_cast<char*>(a.ws);
-  StepK k{a.H, a.W, a.W_max, a.T_max, a.t, nwg, cpw, nrh, a.q, a.k, a.v, a.alpha, a.beta, a.o,
+  StepK k{a.H, a.W, a.W_max, a.T_max, a.t, nrh, a.q, a.k, a.v, a.alpha, a.beta, a.o,
           ws + a.L.s_frag, reinterpret_cast<float*>(ws + a.L.gtr_alpha),
           reinterpret_cast<float*>(ws + a.L.gtr_delta), ws + a.L.gtr_key,
           reinterpret_cast<const int32_t*>(ws + a.L.anc[a.t & 1])};
-  launch_step_tt<DK, DV, BF16, NW>(a, k, dim3(grid), s);
+  switch (a.t) {
+    case 0: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 0>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 1: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 1>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 2: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 2>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 3: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 3>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 4: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 4>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 5: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 5>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 6: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 6>), dim3(grid), dim3(NT), 0, s, k); break;
+    default: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 7>), dim3(grid), dim3(NT), 0, s, k); break;
+  }
   return last_launch_error();
 }
 
