@@ -195,11 +195,12 @@ __device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float s) 
 // go through in chunks of 32: a chunk's q, k, v, gates and ancestry indices are
 // loaded with contiguous reads into registers while the previous chunk computes, then
 // written to a double-buffered LDS slot.  Per chunk:
+//   issue    the ancestor records' keys (for the dots) and delta rows (for the
+//            replay), then the next chunk's inputs;
 //   dots     threads cooperate per beam on k_t.q_t and, for each ancestor record j,
 //            k_j.q_t and k_j.k_t (contiguous reads of the records' keys);
-//   per wave U = S_block [q|k] on MFMA (B fragments from LDS), the delta_j rows of
-//            the ancestors gathered meanwhile; then eqs. (6)-(7) on the accumulators
-//            and eq. (8); delta_t and o_t rows stored;
+//   per wave U = S_block [q|k] on MFMA (B fragments from LDS), then eqs. (6)-(7) on
+//            the accumulators and eq. (8); delta_t and o_t stored;
 //   append   k_t rows copied from LDS to slot (t, b) of the record pool, alpha_t.
 template <int DK, int DV, bool BF16, int TT>
 __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(StepK a) {
@@ -301,11 +302,37 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     const float* Lab = reinterpret_cast<const float*>(L + 64 * QROW + 32 * VROW);
     const int* Lan = reinterpret_cast<const int*>(L + 64 * QROW + 32 * VROW + 256);
 
+    // Issue order for the chunk (loads complete in issue order): the ancestor keys for
+    // the dot products, the ancestors' delta rows for this wave's replay, the next
+    // chunk's inputs.  The dots wait only for the keys.
+    const int bm = tid / TPB, sg = tid % TPB;             // dot-phase role
+    constexpr int SV = C::SEGB / 16;
+    u32x4 kj[NJ1][SV];
+    float aj[NJ1];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (bm < nb ? Lan[bm * kMaxT + j] : 0);
+      aj[j] = a.gtr_alpha[rec];
+#pragma unroll
+      for (int i = 0; i < SV; ++i)
+        kj[j][i] = *reinterpret_cast<const u32x4*>(keyg + rec * C::QB + sg * C::SEGB + 16 * i);
+    }
+    const bool valid = m < nb;
+    const int b = c0 + m;
+    const int row0 = 32 * w + 16 * hf;
+    const int rowl = min(row0, DV - 16);                 // in range (rows >= DV unused)
+    f32x4 dj[NJ1][4];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (valid ? Lan[m * kMaxT + j] : 0);
+      const f32x4* dp = reinterpret_cast<const f32x4*>(a.gtr_delta + rec * DV + rowl);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) dj[j][q4] = dp[q4];
+    }
+    if (c + 1 < nch) stage_load(c + 1);                  // in flight until the end of the chunk
+
     // ---- dots: TPB threads per beam, SEGB bytes of d_k each
     {
-      const int bm = tid / TPB, sg = tid % TPB;
-      const bool ok = bm < nb;
-      constexpr int SV = C::SEGB / 16;
       u32x4 xq[SV], xk[SV];
 #pragma unroll
       for (int i = 0; i < SV; ++i) {
@@ -315,16 +342,7 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
       float kq = 0.0f;
 #pragma unroll
       for (int i = 0; i < SV; ++i) kq = dot16<BF16>(xk[i], xq[i], kq);
-      float aj[NJ1], cq[NJ1], ck[NJ1];
-      u32x4 kj[NJ1][SV];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (ok ? Lan[bm * kMaxT + j] : 0);
-        aj[j] = a.gtr_alpha[rec];
-#pragma unroll
-        for (int i = 0; i < SV; ++i)
-          kj[j][i] = *reinterpret_cast<const u32x4*>(keyg + rec * C::QB + sg * C::SEGB + 16 * i);
-      }
+      float cq[NJ1], ck[NJ1];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         cq[j] = 0.0f;
@@ -357,50 +375,36 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     __syncthreads();
 
     // ---- this wave's row block for the chunk's 32 beams (lane: beam m, rows half hf)
+    f32x16 accq = {}, acck = {};
+    if constexpr (BF16) {
+#pragma unroll
+      for (int kk = 0; kk < DK / 16; ++kk) {
+        const int off = m * QROW + (HK * hf + 8 * kk) * 2;
+        const bf16x8 bq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lq + off));
+        const bf16x8 bk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lk + off));
+        const bf16x8 ahi = __builtin_bit_cast(bf16x8, afr[2 * kk]);
+        const bf16x8 alo = __builtin_bit_cast(bf16x8, afr[2 * kk + 1]);
+        accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bq, accq, 0, 0, 0);
+        acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bk, acck, 0, 0, 0);
+        accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bq, accq, 0, 0, 0);
+        acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bk, acck, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kk4 = 0; kk4 < DK / 8; ++kk4) {
+        const int off = m * QROW + (HK * hf + 4 * kk4) * 4;
+        const f32x4 bq = *reinterpret_cast<const f32x4*>(Lq + off);
+        const f32x4 bk = *reinterpret_cast<const f32x4*>(Lk + off);
+        const f32x4 af = __builtin_bit_cast(f32x4, afr[kk4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          accq = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bq[i], accq, 0, 0, 0);
+          acck = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bk[i], acck, 0, 0, 0);
+        }
+      }
+    }
+
     {
-      const bool valid = m < nb;
-      const int b = c0 + m;
-      const int row0 = 32 * w + 16 * hf;
-      const int rowl = min(row0, DV - 16);               // in range (rows >= DV unused)
-      f32x4 dj[NJ1][4];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (valid ? Lan[m * kMaxT + j] : 0);
-        const f32x4* dp = reinterpret_cast<const f32x4*>(a.gtr_delta + rec * DV + rowl);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) dj[j][q4] = dp[q4];
-      }
-      if (c + 1 < nch) stage_load(c + 1);               // in flight until the end of the chunk
-
-      f32x16 accq = {}, acck = {};
-      if constexpr (BF16) {
-#pragma unroll
-        for (int kk = 0; kk < DK / 16; ++kk) {
-          const int off = m * QROW + (HK * hf + 8 * kk) * 2;
-          const bf16x8 bq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lq + off));
-          const bf16x8 bk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lk + off));
-          const bf16x8 ahi = __builtin_bit_cast(bf16x8, afr[2 * kk]);
-          const bf16x8 alo = __builtin_bit_cast(bf16x8, afr[2 * kk + 1]);
-          accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bq, accq, 0, 0, 0);
-          acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bk, acck, 0, 0, 0);
-          accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bq, accq, 0, 0, 0);
-          acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bk, acck, 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int kk4 = 0; kk4 < DK / 8; ++kk4) {
-          const int off = m * QROW + (HK * hf + 4 * kk4) * 4;
-          const f32x4 bq = *reinterpret_cast<const f32x4*>(Lq + off);
-          const f32x4 bk = *reinterpret_cast<const f32x4*>(Lk + off);
-          const f32x4 af = __builtin_bit_cast(f32x4, afr[kk4]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            accq = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bq[i], accq, 0, 0, 0);
-            acck = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bk[i], acck, 0, 0, 0);
-          }
-        }
-      }
-
       // accumulator register i of this lane = physical row row0 + i of beam b
       if (row0 < DV && valid) {
         const float* s = sc + m * SCN;
