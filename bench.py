@@ -29,7 +29,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GDN beam-transitions/sec (R×H×W per SID step) at 1 MI355X; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "linear_attention_beam_amd", "csrc", "gdn_beam_kernels.hip")
+# the step kernel and everything it includes: counter runs taken on other sources are stale
+STEP_SOURCES = [os.path.join(ROOT, "linear_attention_beam_amd", "csrc", f)
+                for f in ("gdn_step.hip", "gdn_device.h", "gdn_layout.h")]
 
 
 def parse():
@@ -96,7 +98,10 @@ def copy_bandwidth(torch, dev, mib=1024, reps=10):
 
 
 def kernel_hash():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in STEP_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(wl_name):

@@ -1,5 +1,5 @@
 // Internal: workspace layout and launch arguments shared by the host front end
-// (gdn_beam_api.cpp) and the kernels (gdn_beam_kernels.hip).  Not installed.
+// (gdn_beam_api.cpp) and the kernels (gdn_step.hip, gdn_select.hip).  Not installed.
 #pragma once
 #include <cstddef>
 #include <cstdint>
@@ -59,7 +59,7 @@ GDN_HD inline int dvp_of(int d_v) { return d_v < 32 ? 32 : d_v; }   // rows padd
 GDN_HD inline int io_bytes(gdn_dtype d) { return d == GDN_BF16 ? 2 : 4; }
 
 // Codes per logits work unit: a wave covers 32 beams x kCodesPerWave codes.
-constexpr int kCodesPerWave = 256;
+constexpr int kCodesPerWave = 128;
 GDN_HD inline int n_vgroups(int V) { return (V + kCodesPerWave - 1) / kCodesPerWave; }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -130,7 +130,7 @@ struct PrefillArgs {
   float* S_out;
 };
 
-// Kernel launchers (gdn_beam_kernels.hip).  Return a hipError_t value.
+// Kernel launchers (gdn_step.hip, gdn_select.hip).  Return a hipError_t value.
 int launch_init(const InitArgs& a, hipStream_t s);
 int launch_step(const StepArgs& a, hipStream_t s);
 int launch_select(const SelectArgs& a, hipStream_t s);

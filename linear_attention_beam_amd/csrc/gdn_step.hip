@@ -1,0 +1,501 @@
+// Step-side HIP kernels for large-beam Gated DeltaNet decoding on gfx950 (CDNA4).
+//
+// OneLA reading note (paper-archivist.com), sections 2.1-2.5: one shared state
+// S_ctx per (request, head), append-only transition records (alpha, delta, k) in
+// fixed slots, an ancestry index, and a fused shared-context step.
+//
+// Kernels
+//   init_kernel      S_ctx -> MFMA fragment order in the workspace; clear beam state.
+//   step_kernel      fused step: S_ctx [q|k] on MFMA (eqs. 6-7 initial terms), replay
+//                    along the ancestor records (eqs. 6-7), eq. (8), record append.
+//   prefill_kernel   eq. (3) over each request's prompt (the state S_ctx).
+#include "gdn_device.h"
+
+namespace gdn {
+
+// ---------------------------------------------------------------- init
+
+// S_frag per (r,h): bf16 io: blocks (rb, kk, part) of 64 lanes x 8 bf16,
+//   lane l -> S[32 rb + frag_row(l%32)][d_k/2*(l/32) + 8 kk + i], part 0 = hi, 1 = lo.
+// f32 io: blocks (rb, kk4) of 64 lanes x 4 f32, lane l -> S[..][d_k/2*(l/32) + 4 kk4 + i].
+__global__ void init_kernel(InitArgs a) {
+  const int rh = blockIdx.x;
+  const int r = rh / a.H, h = rh % a.H;
+  const int dk = a.d_k, dv = a.d_v, dvp = dvp_of(dv), nrb = dvp / 32;
+  char* ws = static_cast<char*>(a.ws);
+  const float* S = a.S_ctx + size_t(rh) * dv * dk;
+  u32x4* dst = reinterpret_cast<u32x4*>(ws + a.L.s_frag + size_t(rh) * 4 * dvp * dk);
+  if (a.io == GDN_BF16) {
+    const int nkk = dk / 16;
+    const int nchunk = nrb * nkk * 2 * 64;
+    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+      const int lane = c & 63, blk = c >> 6;
+      const int part = blk & 1, kk = (blk >> 1) % nkk, rb = (blk >> 1) / nkk;
+      const int row = 32 * rb + frag_row(lane & 31);
+      const int k0 = (dk / 2) * (lane >> 5) + 8 * kk;
+      uint32_t b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = row < dv ? S[size_t(row) * dk + k0 + i] : 0.0f;
+        const uint32_t hi = f2bf(x);
+        b[i] = part == 0 ? hi : f2bf(x - bf2f(hi));
+      }
+      dst[c] = pack8(b);
+    }
+  } else {
+    const int nkk4 = dk / 8;
+    const int nchunk = nrb * nkk4 * 64;
+    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+      const int lane = c & 63, blk = c >> 6;
+      const int kk4 = blk % nkk4, rb = blk / nkk4;
+      const int row = 32 * rb + frag_row(lane & 31);
+      const int k0 = (dk / 2) * (lane >> 5) + 4 * kk4;
+      f32x4 f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = row < dv ? S[size_t(row) * dk + k0 + i] : 0.0f;
+      reinterpret_cast<f32x4*>(dst)[c] = f;
+    }
+  }
+  if (h == 0) {  // beam state of request r: cumulative scores 0, empty ancestry
+    float* cum = reinterpret_cast<float*>(ws + a.L.cum[0]) + size_t(r) * a.W_max;
+    int32_t* anc = reinterpret_cast<int32_t*>(ws + a.L.anc[0]) + size_t(r) * a.W_max * a.T_max;
+    int32_t* tok = reinterpret_cast<int32_t*>(ws + a.L.tok[0]) + size_t(r) * a.W_max * a.T_max;
+    for (int i = threadIdx.x; i < a.W_max; i += blockDim.x) cum[i] = 0.0f;
+    for (int i = threadIdx.x; i < a.W_max * a.T_max; i += blockDim.x) anc[i] = tok[i] = 0;
+  }
+  if (rh == 0 && threadIdx.x < 64)
+    reinterpret_cast<int32_t*>(ws + a.L.status)[threadIdx.x] = 0;
+}
+
+// ---------------------------------------------------------------- step
+
+struct StepK {
+  int H, W, W_max, T_max, t, nrh;
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  float* o;
+  const char* s_frag;
+  float* gtr_alpha;
+  float* gtr_delta;
+  void* gtr_key;
+  const int32_t* anc;
+};
+
+// Sizes of the fused step for head dims (DK, DV) and io dtype.
+template <int DK, int DV, bool BF16>
+struct StepCfg {
+  static constexpr int DVP = DV < 32 ? 32 : DV;
+  static constexpr int NW = DVP / 32;            // one wave per 32-row block of d_v
+  static constexpr int NT = NW * 64;
+  static constexpr int E = BF16 ? 2 : 4;         // bytes per io element
+  static constexpr int QB = DK * E;              // bytes of one q / k row
+  static constexpr int VB = DV * E;              // bytes of one v row
+  static constexpr int QROW = QB + 16;           // padded LDS rows (bank spread)
+  static constexpr int VROW = VB + 16;
+  static constexpr int QU = 32 * QB / 16 / NT;   // 16-byte staging units per thread
+  static constexpr int VU = 32 * VB / 16 / NT;
+  static constexpr int TPB = NT / 32;            // threads per beam in the dot phase
+  static constexpr int SEGB = QB / TPB;          // bytes of q / k each of them takes
+  static constexpr int SLOT = 32 * (2 * QROW + VROW) + 2 * 32 * 4 + 32 * kMaxT * 4;
+  static_assert(QU >= 1 && VU >= 1 && SEGB >= 16 && SEGB % 16 == 0, "unsupported shape");
+};
+
+template <bool BF16>
+__device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float s) {
+  if constexpr (BF16) {
+    // (bit-cast whole vectors, never single elements of one: hipcc lowers a bit-cast
+    // of an ext-vector element to element 0)
+    const bf16x8 x = __builtin_bit_cast(bf16x8, a);
+    const bf16x8 y = __builtin_bit_cast(bf16x8, b);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x.s01, y.s01, s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x.s23, y.s23, s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x.s45, y.s45, s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x.s67, y.s67, s, false);
+  } else {
+    const f32x4 x = __builtin_bit_cast(f32x4, a);
+    const f32x4 y = __builtin_bit_cast(f32x4, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = fmaf(x[i], y[i], s);
+  }
+  return s;
+}
+
+// Fused SID step (OneLA reading note, sections 2.3-2.5).  One workgroup per
+// (request, head); wave w owns rows [32 w, 32 w + 32) of d_v and keeps that block of
+// S_ctx (bf16 hi/lo, or fp32) as MFMA A fragments in registers for every beam.  Beams
+// go through in chunks of 32: a chunk's q, k, v, gates and ancestry indices are
+// loaded with contiguous reads into registers while the previous chunk computes, then
+// written to a double-buffered LDS slot.  Per chunk:
+//   issue    the ancestor records' keys (for the dots) and delta rows (for the
+//            replay), then the next chunk's inputs;
+//   dots     threads cooperate per beam on k_t.q_t and, for each ancestor record j,
+//            k_j.q_t and k_j.k_t (contiguous reads of the records' keys);
+//   per wave U = S_block [q|k] on MFMA (B fragments from LDS), then eqs. (6)-(7) on
+//            the accumulators and eq. (8); delta_t and o_t stored;
+//   append   k_t rows copied from LDS to slot (t, b) of the record pool, alpha_t.
+template <int DK, int DV, bool BF16, int TT>
+__global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(StepK a) {
+  using C = StepCfg<DK, DV, BF16>;
+  constexpr int NT = C::NT, QROW = C::QROW, VROW = C::VROW, TPB = C::TPB;
+  constexpr int UPQ = C::QB / 16, UPV = C::VB / 16;      // 16-byte units per row
+  constexpr int NJ = TT;                                 // ancestor records replayed
+  constexpr int NJ1 = NJ > 0 ? NJ : 1;
+  constexpr int HK = DK / 2;
+  constexpr int SCN = 1 + 3 * NJ;                        // kq, alpha_j, cq_j, ck_j
+  __shared__ __align__(16) unsigned char lds[2 * C::SLOT + 32 * SCN * 4];
+  float* sc = reinterpret_cast<float*>(lds + 2 * C::SLOT);
+
+  const int rh = xcd_work_id();
+  if (rh >= a.nrh) return;                                // whole block, before any barrier
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int m = lane & 31, hf = lane >> 5;
+  const int W = a.W, r = rh / a.H;
+  const int nch = (W + 31) >> 5;
+  const size_t slot_t = size_t(rh) * a.T_max + TT;       // (r,h,t) row of the record pool
+  const unsigned char* qg = static_cast<const unsigned char*>(a.q);
+  const unsigned char* kg = static_cast<const unsigned char*>(a.k);
+  const unsigned char* vg = static_cast<const unsigned char*>(a.v);
+  unsigned char* keyg = static_cast<unsigned char*>(a.gtr_key);
+
+  // this wave's block of S_ctx as A fragments (layout written by init_kernel)
+  constexpr int NA = BF16 ? 2 * (DK / 16) : DK / 8;
+  u32x4 afr[NA];
+  {
+    const u32x4* fr = reinterpret_cast<const u32x4*>(a.s_frag + size_t(rh) * 4 * C::DVP * DK);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) afr[i] = fr[(w * NA + i) * 64 + lane];
+  }
+
+  // ---- staging of one chunk: registers <- global (contiguous), LDS <- registers
+  u32x4 sq[C::QU], sk[C::QU], sv[C::VU];
+  float sab = 0.0f;
+  constexpr int NAI = (32 * NJ1 + NT - 1) / NT;
+  int sanc[NAI];
+  auto stage_load = [&](int c) {
+    const int c0 = c * 32, nb = min(32, W - c0);
+    const size_t base = size_t(rh) * W + c0;
+#pragma unroll
+    for (int i = 0; i < C::QU; ++i) {
+      const int u = tid + i * NT;
+      if (u / UPQ < nb) {
+        sq[i] = *reinterpret_cast<const u32x4*>(qg + base * C::QB + size_t(u) * 16);
+        sk[i] = *reinterpret_cast<const u32x4*>(kg + base * C::QB + size_t(u) * 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::VU; ++i) {
+      const int u = tid + i * NT;
+      if (u / UPV < nb) sv[i] = *reinterpret_cast<const u32x4*>(vg + base * C::VB + size_t(u) * 16);
+    }
+    if (tid < 64 && (tid & 31) < nb) sab = tid < 32 ? a.alpha[base + tid] : a.beta[base + tid - 32];
+#pragma unroll
+    for (int i = 0; i < NAI; ++i) {
+      const int e = tid + i * NT, bb = e / NJ1, j = e % NJ1;
+      if (NJ > 0 && e < 32 * NJ && bb < nb) sanc[i] = a.anc[(size_t(r) * a.W_max + c0 + bb) * a.T_max + j];
+    }
+  };
+  auto stage_store = [&](int slot) {
+    unsigned char* L = lds + slot * C::SLOT;
+#pragma unroll
+    for (int i = 0; i < C::QU; ++i) {
+      const int u = tid + i * NT, bb = u / UPQ, o = (u % UPQ) * 16;
+      *reinterpret_cast<u32x4*>(L + bb * QROW + o) = sq[i];
+      *reinterpret_cast<u32x4*>(L + 32 * QROW + bb * QROW + o) = sk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::VU; ++i) {
+      const int u = tid + i * NT, bb = u / UPV, o = (u % UPV) * 16;
+      *reinterpret_cast<u32x4*>(L + 64 * QROW + bb * VROW + o) = sv[i];
+    }
+    float* ab = reinterpret_cast<float*>(L + 64 * QROW + 32 * VROW);
+    if (tid < 64) ab[tid] = sab;
+    int* an = reinterpret_cast<int*>(L + 64 * QROW + 32 * VROW + 256);
+#pragma unroll
+    for (int i = 0; i < NAI; ++i) {
+      const int e = tid + i * NT, bb = e / NJ1, j = e % NJ1;
+      if (NJ > 0 && e < 32 * NJ) {
+        const int s = sanc[i];
+        an[bb * kMaxT + j] = s < 0 ? 0 : (s >= a.W_max ? a.W_max - 1 : s);
+      }
+    }
+  };
+
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    const int c0 = c * 32, nb = min(32, W - c0);
+    const unsigned char* L = lds + (c & 1) * C::SLOT;
+    const unsigned char* Lq = L;
+    const unsigned char* Lk = L + 32 * QROW;
+    const unsigned char* Lv = L + 64 * QROW;
+    const float* Lab = reinterpret_cast<const float*>(L + 64 * QROW + 32 * VROW);
+    const int* Lan = reinterpret_cast<const int*>(L + 64 * QROW + 32 * VROW + 256);
+
+    // Issue order for the chunk (loads complete in issue order): the ancestor keys for
+    // the dot products, the ancestors' delta rows for this wave's replay, the next
+    // chunk's inputs.  The dots wait only for the keys.
+    const int bm = tid / TPB, sg = tid % TPB;             // dot-phase role
+    constexpr int SV = C::SEGB / 16;
+    u32x4 kj[NJ1][SV];
+    float aj[NJ1];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (bm < nb ? Lan[bm * kMaxT + j] : 0);
+      aj[j] = a.gtr_alpha[rec];
+#pragma unroll
+      for (int i = 0; i < SV; ++i)
+        kj[j][i] = *reinterpret_cast<const u32x4*>(keyg + rec * C::QB + sg * C::SEGB + 16 * i);
+    }
+    const bool valid = m < nb;
+    const int b = c0 + m;
+    const int row0 = 32 * w + 16 * hf;
+    const int rowl = min(row0, DV - 16);                 // in range (rows >= DV unused)
+    f32x4 dj[NJ1][4];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (valid ? Lan[m * kMaxT + j] : 0);
+      const f32x4* dp = reinterpret_cast<const f32x4*>(a.gtr_delta + rec * DV + rowl);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) dj[j][q4] = dp[q4];
+    }
+    if (c + 1 < nch) stage_load(c + 1);                  // in flight until the end of the chunk
+
+    // ---- dots: TPB threads per beam, SEGB bytes of d_k each
+    {
+      u32x4 xq[SV], xk[SV];
+#pragma unroll
+      for (int i = 0; i < SV; ++i) {
+        xq[i] = *reinterpret_cast<const u32x4*>(Lq + bm * QROW + sg * C::SEGB + 16 * i);
+        xk[i] = *reinterpret_cast<const u32x4*>(Lk + bm * QROW + sg * C::SEGB + 16 * i);
+      }
+      float kq = 0.0f;
+#pragma unroll
+      for (int i = 0; i < SV; ++i) kq = dot16<BF16>(xk[i], xq[i], kq);
+      float cq[NJ1], ck[NJ1];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        cq[j] = 0.0f;
+        ck[j] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < SV; ++i) {
+          cq[j] = dot16<BF16>(kj[j][i], xq[i], cq[j]);
+          ck[j] = dot16<BF16>(kj[j][i], xk[i], ck[j]);
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < TPB; off <<= 1) {
+        kq += __shfl_xor(kq, off);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          cq[j] += __shfl_xor(cq[j], off);
+          ck[j] += __shfl_xor(ck[j], off);
+        }
+      }
+      if (sg == 0) {
+        sc[bm * SCN] = kq;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          sc[bm * SCN + 1 + j] = aj[j];
+          sc[bm * SCN + 1 + NJ + j] = cq[j];
+          sc[bm * SCN + 1 + 2 * NJ + j] = ck[j];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- this wave's row block for the chunk's 32 beams (lane: beam m, rows half hf)
+    f32x16 accq = {}, acck = {};
+    if constexpr (BF16) {
+#pragma unroll
+      for (int kk = 0; kk < DK / 16; ++kk) {
+        const int off = m * QROW + (HK * hf + 8 * kk) * 2;
+        const bf16x8 bq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lq + off));
+        const bf16x8 bk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lk + off));
+        const bf16x8 ahi = __builtin_bit_cast(bf16x8, afr[2 * kk]);
+        const bf16x8 alo = __builtin_bit_cast(bf16x8, afr[2 * kk + 1]);
+        accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bq, accq, 0, 0, 0);
+        acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bk, acck, 0, 0, 0);
+        accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bq, accq, 0, 0, 0);
+        acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bk, acck, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kk4 = 0; kk4 < DK / 8; ++kk4) {
+        const int off = m * QROW + (HK * hf + 4 * kk4) * 4;
+        const f32x4 bq = *reinterpret_cast<const f32x4*>(Lq + off);
+        const f32x4 bk = *reinterpret_cast<const f32x4*>(Lk + off);
+        const f32x4 af = __builtin_bit_cast(f32x4, afr[kk4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          accq = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bq[i], accq, 0, 0, 0);
+          acck = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bk[i], acck, 0, 0, 0);
+        }
+      }
+    }
+
+    {
+      // accumulator register i of this lane = physical row row0 + i of beam b
+      if (row0 < DV && valid) {
+        const float* s = sc + m * SCN;
+        const float kq = s[0];
+        const float al = Lab[m], be = Lab[32 + m];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const float ajj = s[1 + j], cqj = s[1 + NJ + j], ckj = s[1 + 2 * NJ + j];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              accq[4 * q4 + i] = fmaf(dj[j][q4][i], cqj, ajj * accq[4 * q4 + i]);   // eq. (6)
+              acck[4 * q4 + i] = fmaf(dj[j][q4][i], ckj, ajj * acck[4 * q4 + i]);   // eq. (7)
+            }
+          }
+        }
+        float vin[16];
+        if constexpr (BF16) {
+          const u32x4* vp = reinterpret_cast<const u32x4*>(Lv + m * VROW + row0 * 2);
+          unpack8(vp[0], vin);
+          unpack8(vp[1], vin + 8);
+        } else {
+          const f32x4* vp = reinterpret_cast<const f32x4*>(Lv + m * VROW + row0 * 4);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            for (int i = 0; i < 4; ++i) vin[4 * q4 + i] = vp[q4][i];
+        }
+        f32x4* dout = reinterpret_cast<f32x4*>(a.gtr_delta + (slot_t * a.W_max + b) * DV + row0);
+        f32x4* oout = reinterpret_cast<f32x4*>(a.o + (size_t(rh) * W + b) * DV + row0);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 dt, ot;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * q4 + i;
+            dt[i] = be * (vin[e] - al * acck[e]);              // eq. (8) delta_t
+            ot[i] = fmaf(dt[i], kq, al * accq[e]);             // eq. (8) o_t
+          }
+          dout[q4] = dt;
+          oout[q4] = ot;
+        }
+      }
+    }
+
+    // ---- append: k_t rows (contiguous slots c0..c0+nb-1) and alpha_t
+    {
+      unsigned char* dst = keyg + (slot_t * a.W_max + c0) * C::QB;
+      for (int u = tid; u < nb * UPQ; u += NT)
+        *reinterpret_cast<u32x4*>(dst + size_t(u) * 16) =
+            *reinterpret_cast<const u32x4*>(Lk + (u / UPQ) * QROW + (u % UPQ) * 16);
+      if (tid < nb) a.gtr_alpha[slot_t * a.W_max + c0 + tid] = Lab[tid];
+    }
+    if (c + 1 < nch) stage_store((c + 1) & 1);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- prefill (eq. 3)
+
+// One workgroup per (request, head); thread (row, half) holds S[row][half*DK/2 ..] in
+// registers.  Each token: u = S k (row dot, reduced over the row's lanes),
+// S <- alpha S + beta (v - alpha u) k^T.
+template <int DK, int DV>
+__global__ void __launch_bounds__(DV < 32 ? 256 : 2 * DV) prefill_kernel(PrefillArgs a) {
+  constexpr int TPR = DV < 32 ? 256 / DV : 2;        // lanes per row
+  constexpr int COLS = DK / TPR;
+  const int rh = blockIdx.x, r = rh / a.H, h = rh % a.H;
+  const int row = threadIdx.x / TPR, cp = threadIdx.x % TPR;
+  int beg = a.offsets[r], end = a.offsets[r + 1];
+  beg = beg < 0 ? 0 : (beg > a.N ? int(a.N) : beg);
+  end = end < beg ? beg : (end > a.N ? int(a.N) : end);
+  float S[COLS];
+#pragma unroll
+  for (int c = 0; c < COLS; ++c) S[c] = 0.0f;
+  float kc[COLS];
+  float vn = 0.0f, an = 0.0f, bn = 0.0f;
+  auto load = [&](int i, float* kk, float& vv, float& aa, float& bb) {
+    const float* kp = a.k + (size_t(i) * a.H + h) * DK + cp * COLS;
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) kk[c] = kp[c];
+    vv = a.v[(size_t(i) * a.H + h) * DV + row];
+    aa = a.alpha[size_t(i) * a.H + h];
+    bb = a.beta[size_t(i) * a.H + h];
+  };
+  if (beg < end) load(beg, kc, vn, an, bn);
+  for (int i = beg; i < end; ++i) {
+    float kcur[COLS];
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) kcur[c] = kc[c];
+    const float vv = vn, aa = an, bb = bn;
+    if (i + 1 < end) load(i + 1, kc, vn, an, bn);
+    float u = 0.0f;
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) u = fmaf(S[c], kcur[c], u);
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) u += __shfl_xor(u, off);
+    const float d = bb * (vv - aa * u);
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) S[c] = fmaf(d, kcur[c], aa * S[c]);
+  }
+  float* out = a.S_out + ((size_t(rh) * DV + row) * DK) + cp * COLS;
+#pragma unroll
+  for (int c = 0; c < COLS; ++c) out[c] = S[c];
+}
+
+// ---------------------------------------------------------------- launchers
+
+int launch_init(const InitArgs& a, hipStream_t s) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(init_kernel, dim3(a.R * a.H), dim3(256), 0, s, a);
+  return last_launch_error();
+}
+
+template <int DK, int DV, bool BF16>
+static int launch_step_t(const StepArgs& a, hipStream_t s) {
+  constexpr int NT = StepCfg<DK, DV, BF16>::NT;
+  const int nrh = a.R * a.H;
+  // one workgroup per (request, head): S_ctx is read once and kept in registers
+  const long grid = (long(nrh) + 7) / 8 * 8;
+  char* ws = static_cast<char*>(a.ws);
+  StepK k{a.H, a.W, a.W_max, a.T_max, a.t, nrh, a.q, a.k, a.v, a.alpha, a.beta, a.o,
+          ws + a.L.s_frag, reinterpret_cast<float*>(ws + a.L.gtr_alpha),
+          reinterpret_cast<float*>(ws + a.L.gtr_delta), ws + a.L.gtr_key,
+          reinterpret_cast<const int32_t*>(ws + a.L.anc[a.t & 1])};
+  switch (a.t) {
+    case 0: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 0>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 1: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 1>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 2: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 2>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 3: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 3>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 4: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 4>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 5: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 5>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 6: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 6>), dim3(grid), dim3(NT), 0, s, k); break;
+    default: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 7>), dim3(grid), dim3(NT), 0, s, k); break;
+  }
+  return last_launch_error();
+}
+
+int launch_step(const StepArgs& a, hipStream_t s) {
+  (void)hipGetLastError();
+  const bool bf = a.io == GDN_BF16;
+  if (a.d_k == 16 && a.d_v == 16) return bf ? launch_step_t<16, 16, true>(a, s) : launch_step_t<16, 16, false>(a, s);
+  if (a.d_k == 128 && a.d_v == 128) return bf ? launch_step_t<128, 128, true>(a, s) : launch_step_t<128, 128, false>(a, s);
+  if (a.d_k == 128 && a.d_v == 256) return bf ? launch_step_t<128, 256, true>(a, s) : launch_step_t<128, 256, false>(a, s);
+  return int(hipErrorInvalidValue);
+}
+
+template <int DK, int DV>
+static int launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
+  constexpr int threads = DV < 32 ? 256 : 2 * DV;
+  hipLaunchKernelGGL((prefill_kernel<DK, DV>), dim3(a.R * a.H), dim3(threads), 0, s, a);
+  return last_launch_error();
+}
+
+int launch_prefill(const PrefillArgs& a, hipStream_t s) {
+  (void)hipGetLastError();
+  if (a.d_k == 16 && a.d_v == 16) return launch_prefill_t<16, 16>(a, s);
+  if (a.d_k == 128 && a.d_v == 128) return launch_prefill_t<128, 128>(a, s);
+  if (a.d_k == 128 && a.d_v == 256) return launch_prefill_t<128, 256>(a, s);
+  return int(hipErrorInvalidValue);
+}
+
+}  // namespace gdn

@@ -49,7 +49,7 @@ def _a(x):
 def expected_bytes(R, H, d_k, d_v, T, W, V, e, ew):
     """Workspace regions as documented in include/gdn_beam.h, each 256-aligned."""
     dvp = max(d_v, 32)
-    nvg = -(-V // 256)
+    nvg = -(-V // 128)
     regions = [R * H * 4 * dvp * d_k, R * H * T * W * 4, R * H * T * W * d_v * 4,
                R * H * T * W * d_k * e, R * W * T * 4, R * W * T * 4, R * W * T * 4, R * W * T * 4,
                R * W * 4, R * W * 4, R * W * d_v * 4, V * d_v * ew, R * V * W * 4, R * W * nvg * 16,
@@ -90,7 +90,7 @@ def test_workspace_does_not_grow_with_dv_dk_w():
     R, H, T, d, V = 2, 3, 4, 128, 1024
     records = H * T * (4 + 4 * d + 2 * d)              # GTR slots of every head
     beam_state = 4 * T * 4 + 2 * 4                     # ancestry + SID prefixes, scores
-    scoring = 4 * d + 4 * V + 16 * (V // 256) + 4 + 8 + 4 * V   # z, logits, lse parts, lse, winners, ties
+    scoring = 4 * d + 4 * V + 16 * (V // 128) + 4 + 8 + 4 * V   # z, logits, lse parts, lse, winners, ties
     per_w = R * (records + beam_state + scoring)
     assert b2 - b1 <= 256 * per_w + 20 * 256
     assert b2 - b1 < 256 * 128 * 128 * 4
