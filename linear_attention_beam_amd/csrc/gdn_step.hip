@@ -18,52 +18,57 @@ namespace gdn {
 // S_frag per (r,h): bf16 io: blocks (rb, kk, part) of 64 lanes x 8 bf16,
 //   lane l -> S[32 rb + frag_row(l%32)][d_k/2*(l/32) + 8 kk + i], part 0 = hi, 1 = lo.
 // f32 io: blocks (rb, kk4) of 64 lanes x 4 f32, lane l -> S[..][d_k/2*(l/32) + 4 kk4 + i].
-__global__ void init_kernel(InitArgs a) {
-  const int rh = blockIdx.x;
-  const int r = rh / a.H, h = rh % a.H;
+// One thread per 16-byte fragment position: it loads the 8 (bf16 io) or 4 (f32 io)
+// source values once and writes every part, so all loads of the grid are independent.
+__global__ void __launch_bounds__(256) init_kernel(InitArgs a) {
   const int dk = a.d_k, dv = a.d_v, dvp = dvp_of(dv), nrb = dvp / 32;
+  const bool bf = a.io == GDN_BF16;
+  const int nkk = bf ? dk / 16 : dk / 8;           // fragment columns per 32-row block
+  const int per_rh = nrb * nkk * 64;
+  const size_t n = size_t(a.R) * a.H * per_rh;
   char* ws = static_cast<char*>(a.ws);
-  const float* S = a.S_ctx + size_t(rh) * dv * dk;
-  u32x4* dst = reinterpret_cast<u32x4*>(ws + a.L.s_frag + size_t(rh) * 4 * dvp * dk);
-  if (a.io == GDN_BF16) {
-    const int nkk = dk / 16;
-    const int nchunk = nrb * nkk * 2 * 64;
-    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
-      const int lane = c & 63, blk = c >> 6;
-      const int part = blk & 1, kk = (blk >> 1) % nkk, rb = (blk >> 1) / nkk;
-      const int row = 32 * rb + frag_row(lane & 31);
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t g = size_t(blockIdx.x) * blockDim.x + threadIdx.x; g < n; g += stride) {
+    const size_t rh = g / per_rh;
+    const int c = int(g % per_rh);
+    const int lane = c & 63, blk = c >> 6;           // blk = rb * nkk + kk
+    const int kk = blk % nkk, rb = blk / nkk;
+    const int row = 32 * rb + frag_row(lane & 31);
+    const float* S = a.S_ctx + rh * dv * dk;
+    u32x4* dst = reinterpret_cast<u32x4*>(ws + a.L.s_frag + rh * 4 * dvp * dk);
+    if (bf) {
       const int k0 = (dk / 2) * (lane >> 5) + 8 * kk;
-      uint32_t b[8];
+      f32x4 x0 = {}, x1 = {};
+      if (row < dv) {
+        x0 = *reinterpret_cast<const f32x4*>(S + size_t(row) * dk + k0);
+        x1 = *reinterpret_cast<const f32x4*>(S + size_t(row) * dk + k0 + 4);
+      }
+      uint32_t hi[8], lo[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x = row < dv ? S[size_t(row) * dk + k0 + i] : 0.0f;
-        const uint32_t hi = f2bf(x);
-        b[i] = part == 0 ? hi : f2bf(x - bf2f(hi));
+        const float x = i < 4 ? x0[i] : x1[i - 4];
+        hi[i] = f2bf(x);
+        lo[i] = f2bf(x - bf2f(hi[i]));
       }
-      dst[c] = pack8(b);
-    }
-  } else {
-    const int nkk4 = dk / 8;
-    const int nchunk = nrb * nkk4 * 64;
-    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
-      const int lane = c & 63, blk = c >> 6;
-      const int kk4 = blk % nkk4, rb = blk / nkk4;
-      const int row = 32 * rb + frag_row(lane & 31);
-      const int k0 = (dk / 2) * (lane >> 5) + 4 * kk4;
-      f32x4 f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = row < dv ? S[size_t(row) * dk + k0 + i] : 0.0f;
+      dst[(2 * blk) * 64 + lane] = pack8(hi);
+      dst[(2 * blk + 1) * 64 + lane] = pack8(lo);
+    } else {
+      const int k0 = (dk / 2) * (lane >> 5) + 4 * kk;
+      f32x4 f = {};
+      if (row < dv) f = *reinterpret_cast<const f32x4*>(S + size_t(row) * dk + k0);
       reinterpret_cast<f32x4*>(dst)[c] = f;
     }
   }
-  if (h == 0) {  // beam state of request r: cumulative scores 0, empty ancestry
-    float* cum = reinterpret_cast<float*>(ws + a.L.cum[0]) + size_t(r) * a.W_max;
-    int32_t* anc = reinterpret_cast<int32_t*>(ws + a.L.anc[0]) + size_t(r) * a.W_max * a.T_max;
-    int32_t* tok = reinterpret_cast<int32_t*>(ws + a.L.tok[0]) + size_t(r) * a.W_max * a.T_max;
-    for (int i = threadIdx.x; i < a.W_max; i += blockDim.x) cum[i] = 0.0f;
-    for (int i = threadIdx.x; i < a.W_max * a.T_max; i += blockDim.x) anc[i] = tok[i] = 0;
+  // beam state: cumulative scores 0, empty ancestry and SID prefixes, clear status
+  const size_t nb = size_t(a.R) * a.W_max * a.T_max;
+  float* cum = reinterpret_cast<float*>(ws + a.L.cum[0]);
+  int32_t* anc = reinterpret_cast<int32_t*>(ws + a.L.anc[0]);
+  int32_t* tok = reinterpret_cast<int32_t*>(ws + a.L.tok[0]);
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nb; i += stride) {
+    anc[i] = tok[i] = 0;
+    if (i < size_t(a.R) * a.W_max) cum[i] = 0.0f;
   }
-  if (rh == 0 && threadIdx.x < 64)
+  if (blockIdx.x == 0 && threadIdx.x < 64)
     reinterpret_cast<int32_t*>(ws + a.L.status)[threadIdx.x] = 0;
 }
 
@@ -446,7 +451,11 @@ __global__ void __launch_bounds__(DV < 32 ? 256 : 2 * DV) prefill_kernel(Prefill
 
 int launch_init(const InitArgs& a, hipStream_t s) {
   (void)hipGetLastError();
-  hipLaunchKernelGGL(init_kernel, dim3(a.R * a.H), dim3(256), 0, s, a);
+  const int nkk = a.io == GDN_BF16 ? a.d_k / 16 : a.d_k / 8;
+  const size_t n = size_t(a.R) * a.H * (dvp_of(a.d_v) / 32) * nkk * 64;
+  size_t blocks = (n + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 16384 ? 16384 : blocks);
+  hipLaunchKernelGGL(init_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, a);
   return last_launch_error();
 }
 
