@@ -17,20 +17,13 @@ constexpr int kMaxT = 8;          // SID steps
 constexpr int kMaxW = 1024;       // beams per step (one sorting workgroup holds them)
 constexpr int kMaxV = 65536;      // codebook
 constexpr int kHistBins = 2048;   // radix digits per selection pass (11 bits)
-constexpr int kSelBlocksMax = 64; // histogram blocks per request
-constexpr int kSelPerBlock = 8192; // candidates per histogram block (before the cap)
 
-// Per-request selection state (device).  Reset at the start of every select.
-// The radix passes bin keys relative to the request's exact key range: each pass
-// splits the current range [lo, lo + 2048 << shift) into 2048 digits.
+// Per-request selection results handed from the tile choice to the refinement.
 struct SelState {
-  uint32_t kmax, kmin;  // largest / smallest candidate key of the request
-  uint32_t lo, hi;      // boundary digit [lo, hi] chosen by the first pass
-  int32_t shift;        // digit width (log2) for the next pass inside [lo, hi]; -1: lo == hi
-  uint32_t need;        // winners still to take inside [lo, hi]
-  uint32_t n_win;       // collected candidates with key > hi
-  uint32_t n_cand;      // collected candidates with key in [lo, hi]
-  uint32_t pad[8];
+  uint32_t n_tiles;     // tiles chosen for refinement
+  uint32_t n_groups;    // refinement groups (code tile x up to 32 beams)
+  uint32_t theta;       // key of the K-th chosen tile (0: fewer than K tiles exist)
+  uint32_t pad;
 };
 
 // Byte offsets of every region inside the caller's workspace (256-aligned).
@@ -42,15 +35,18 @@ struct Layout {
   size_t anc[2];      // [R,W_max,T_max] i32, ping-pong by step parity
   size_t tok[2];      // [R,W_max,T_max] i32
   size_t cum[2];      // [R,W_max] f32
-  size_t z;           // [R,W_max,d_v] f32  head-summed outputs
+  size_t z;           // [R,W_max,d_v] f32  head-summed outputs (fp32 codebook)
+  size_t zf;          // [R,n_chunks(W_max),d_v/16,3,64] u32x4: z as bf16 hi/mid/lo MFMA operand
   size_t woutT;       // [V_max,d_v] wout dtype, codebook transposed
-  size_t logits;      // [R, V_max*W_max] f32, per request [V][W_t]
-  size_t lse_part;    // [R,W_max,n_vgroups] float4 (max, sum of exp, min, 0)
+  size_t tmax;        // [R, n_tiles(V_max)*W_max] f32, per request [n_tiles(V)][W_t]
+  size_t lse_part;    // [R,W_max,n_vgroups(V_max)] float4 (max, sum of exp, min tile max, 0)
   size_t lse;         // [R,W_max] f32
-  size_t hist;        // [R,kSelBlocksMax,kHistBins] u32, one histogram per block
   size_t sel;         // [R] SelState
-  size_t winners;     // [R,W_max] u64 (key<<32 | flat)
-  size_t cand;        // [R, V_max*W_max] u32 flat indices inside the boundary digit
+  size_t cand;        // [R, n_tiles(V_max)*W_max] u32 flat tiles inside the boundary digit
+  size_t tiles;       // [R,W_max] u32 chosen flat tiles, grouped by code tile
+  size_t groups;      // [R,max_groups] u32 refinement groups
+  size_t gtiles;      // [R,max_groups,32] u32 the tiles of each group
+  size_t rkeys;       // [R,W_max,kTile] u32 keys of the chosen tiles' candidates
   size_t status;      // [64] i32
   size_t total;
 };
@@ -58,7 +54,16 @@ struct Layout {
 GDN_HD inline int dvp_of(int d_v) { return d_v < 32 ? 32 : d_v; }   // rows padded to one MFMA block
 GDN_HD inline int io_bytes(gdn_dtype d) { return d == GDN_BF16 ? 2 : 4; }
 
-// Codes per logits work unit: a wave covers 32 beams x kCodesPerWave codes.
+// Codes per tile: one 32-row MFMA block.  The selection keeps one maximum per
+// (beam, tile) and refines at most W_next tiles.
+constexpr int kTile = 32;
+GDN_HD inline int n_tiles(int V) { return (V + kTile - 1) / kTile; }
+GDN_HD inline int n_chunks(int W) { return (W + 31) / 32; }   // 32-beam MFMA columns
+// refinement groups: sum over code tiles of ceil(beams / 32) <= ceil(K/32) + min(Vt, K)
+GDN_HD inline int max_groups(int W_max, int Vt_max) {
+  return n_chunks(W_max) + 1 + (Vt_max < W_max ? Vt_max : W_max);
+}
+// First-pass work unit: 32 beams x (128 .. 1024) codes; log-sum-exp parts per unit.
 constexpr int kCodesPerWave = 128;
 GDN_HD inline int n_vgroups(int V) { return (V + kCodesPerWave - 1) / kCodesPerWave; }
 
@@ -77,15 +82,19 @@ inline Layout make_layout(const gdn_beam_config& c) {
   for (int i = 0; i < 2; ++i) L.anc[i] = take(R * W * T * 4);
   for (int i = 0; i < 2; ++i) L.tok[i] = take(R * W * T * 4);
   for (int i = 0; i < 2; ++i) L.cum[i] = take(R * W * 4);
+  const size_t Vt = size_t(n_tiles(c.V_max));
   L.z = take(R * W * dv * 4);
+  L.zf = take(R * size_t(n_chunks(c.W_max)) * 32 * dv * 6);
   L.woutT = take(V * dv * ew);
-  L.logits = take(R * V * W * 4);
+  L.tmax = take(R * Vt * W * 4);
   L.lse_part = take(R * W * size_t(n_vgroups(c.V_max)) * 16);
   L.lse = take(R * W * 4);
-  L.hist = take(R * size_t(kSelBlocksMax) * kHistBins * 4);
   L.sel = take(R * sizeof(SelState));
-  L.winners = take(R * W * 8);
-  L.cand = take(R * V * W * 4);
+  L.cand = take(R * Vt * W * 4);
+  L.tiles = take(R * W * 4);
+  L.groups = take(R * size_t(max_groups(c.W_max, n_tiles(c.V_max))) * 4);
+  L.gtiles = take(R * size_t(max_groups(c.W_max, n_tiles(c.V_max))) * 32 * 4);
+  L.rkeys = take(R * W * kTile * 4);
   L.status = take(64 * 4);
   L.total = off;
   return L;

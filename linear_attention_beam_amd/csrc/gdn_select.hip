@@ -1,394 +1,656 @@
 // Selection-side HIP kernels for large-beam Gated DeltaNet decoding on gfx950.
 //
 // Scoring follows the beam-search objective of OneLA (paper-archivist.com) section 2.1
-// and eq. (1); the request-level exact top-K follows RecoGEM (conceptio mirror)
-// section 4.3; the ancestry remap is OneLA eq. (9).
+// and eq. (1); the exact request-level top-K with a per-row precut follows RecoGEM
+// (conceptio mirror) section 4.3; the ancestry remap is OneLA eq. (9).
+//
+// No score matrix is materialised.  Codes are cut into tiles of 32 (one MFMA block of
+// rows).  The first pass keeps, per (beam, tile), the largest logit, and per beam the
+// log-sum-exp.  The exact top-K of the tiles, ranked by the score of their largest
+// logit, must contain every tile that holds one of the top-K candidates: each chosen
+// tile owns a candidate that ranks at or above its tile-mates, so any candidate of an
+// unchosen tile has K distinct candidates ahead of it.  Only the chosen tiles are
+// recomputed, with the same MFMA sequence (bit-identical logits), and the exact top-K
+// is taken over their 32 K candidates.
 //
 // Kernels
-//   zsum_kernel      z_b = sum_h o_b; resets the per-request selection state.
-//   wout_t_kernel    codebook transpose Wout[d_v,V] -> [V,d_v] (MFMA operand order).
-//   logits_kernel    logits = z Wout on MFMA, stored [V][W_t]; online log-sum-exp parts.
-//   lse_kernel       combines the parts into logsumexp per beam.
-//   hist_kernel      first radix pass over every candidate key, 2048 digits spread over
-//                    the request's exact key range (one histogram per block).
-//   digit_kernel     sums a request's histograms and picks the boundary digit.
-//   compact_kernel   keys above the boundary digit -> winners; keys inside it -> kept.
-//   finalize_kernel  finishes the radix select on the kept keys, breaks ties by flat
-//                    index, sorts the winners, writes the top-W, and remaps ancestry,
-//                    SID prefixes and scores (eq. 9).
+//   zsum_kernel      z_b = sum_h o_b, stored as the bf16 hi/mid/lo MFMA operand (bf16
+//                    codebook) or fp32 (fp32 codebook); its last grid row transposes
+//                    the codebook Wout[d_v,V] -> [V,d_v] (MFMA operand order).
+//   logits_kernel    first pass on MFMA: per (beam, tile) largest logit, online
+//                    log-sum-exp parts per code group.
+//   tile_select_kernel  one block per request: log-sum-exp per beam, then the exact
+//                    top-K tiles by two streaming radix passes over the tile maxima and a
+//                    finish inside the boundary digit; groups the chosen tiles by code tile.
+//   refine_kernel    recomputes the chosen tiles' logits (one MFMA block per group) and
+//                    writes their 32 candidate keys each.
+//   final_kernel     exact top-K over the refined keys in LDS, ties by flat index,
+//                    sort, the top-W outputs, and the remap of ancestry, SID prefixes
+//                    and cumulative scores (eq. 9).
 #include "gdn_device.h"
 
 namespace gdn {
 
-// ---------------------------------------------------------------- select: z, Wout^T
+constexpr float kLog2e = 1.4426950408889634f;
 
-// z[r,b,:] = sum_h o[r,h,b,:]; thread 0.. also reset the selection state of the request.
-__global__ void zsum_kernel(const float* __restrict__ o, float* __restrict__ z, int H, int W,
-                           int W_max, int d_v, int K, uint32_t* hist, SelState* sel, int R) {
-  const int r = blockIdx.y;
-  const int n4 = W * d_v / 4;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
-    f32x4 s = {};
-    for (int h = 0; h < H; ++h)
-      s += reinterpret_cast<const f32x4*>(o + (size_t(r) * H + h) * W * d_v)[i];
-    const int b = (4 * i) / d_v, c = (4 * i) % d_v;
-    *reinterpret_cast<f32x4*>(z + (size_t(r) * W_max + b) * d_v + c) = s;
+// ---------------------------------------------------------------- z and its operand
+
+// zf per request: [chunk][kk][term][lane] u32x4, chunk = b / 32, kk < d_v / 16, term
+// 0/1/2 = hi/mid/lo bf16 parts of z, lane l -> beam 32 chunk + l % 32 and elements
+// d = d_v / 2 * (l / 32) + 8 kk + i (i < 8): the B operand of the logits MFMA.
+__device__ __forceinline__ size_t zf_lane_base(int r, int nch_max, int d_v, int b, int hf) {
+  return (size_t(r) * nch_max + (b >> 5)) * size_t(d_v / 16) * 3 * 64 + (b & 31) + 32 * hf;
+}
+
+struct ZsumK {
+  int R, H, W, W_max, d_v, V, nch_max;
+  int split;            // bf16 codebook: write zf; fp32 codebook: write z
+  const float* o;       // [R,H,W,d_v]
+  float* z;             // [R,W_max,d_v]
+  u32x4* zf;
+  const void* wout;     // [d_v,V]
+  void* woutT;          // [V,d_v]
+};
+
+// 32 x 32 tiles of Wout[d_v,V] -> Wout^T[V,d_v] through LDS, one tile per step.
+template <typename WT>
+__device__ void transpose_codebook(const WT* __restrict__ w, WT* __restrict__ wt, int d_v, int V) {
+  __shared__ WT tile[32][33];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 256 threads: 32 x 8
+  const int ntc = (V + 31) / 32, nt = ntc * ((d_v + 31) / 32);
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const int c0 = (t % ntc) * 32, i0 = (t / ntc) * 32;
+    for (int y = ty; y < 32; y += 8) {
+      const int i = i0 + y, c = c0 + tx;
+      tile[y][tx] = (i < d_v && c < V) ? w[size_t(i) * V + c] : WT{};
+    }
+    __syncthreads();
+    for (int y = ty; y < 32; y += 8) {
+      const int c = c0 + y, i = i0 + tx;
+      if (c < V && i < d_v) wt[size_t(c) * d_v + i] = tile[tx][y];
+    }
+    __syncthreads();
   }
-  if (blockIdx.x == 0) {
-    if (threadIdx.x == 0) {
-      SelState st{};
-      st.kmax = 0u;
-      st.kmin = 0xFFFFFFFFu;
-      st.need = uint32_t(K);
-      sel[r] = st;
+}
+
+// Rows y < R: one thread per 8 consecutive elements of one beam (beams padded to a
+// multiple of 32 with zeros); the head sum runs in head order.  Row y = R: codebook
+// transpose.
+__global__ void __launch_bounds__(256) zsum_kernel(ZsumK a) {
+  const int r = blockIdx.y;
+  if (r == a.R) {
+    if (a.split)
+      transpose_codebook(static_cast<const uint16_t*>(a.wout), static_cast<uint16_t*>(a.woutT), a.d_v, a.V);
+    else
+      transpose_codebook(static_cast<const float*>(a.wout), static_cast<float*>(a.woutT), a.d_v, a.V);
+    return;
+  }
+  const int g8 = a.d_v / 8, HV = a.d_v / 2;
+  const int n = ((a.W + 31) & ~31) * g8;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const int b = i / g8, d0 = 8 * (i % g8);
+    f32x4 s0 = {}, s1 = {};
+    if (b < a.W) {
+      // heads eight at a time: all loads of a batch in flight, then the sums in head order
+      const float* p0 = a.o + (size_t(r) * a.H * a.W + b) * a.d_v + d0;
+      const size_t hstride = size_t(a.W) * a.d_v;
+      for (int h0 = 0; h0 < a.H; h0 += 8) {
+        f32x4 x0[8], x1[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float* p = p0 + size_t(h0 + u < a.H ? h0 + u : h0) * hstride;
+          x0[u] = *reinterpret_cast<const f32x4*>(p);
+          x1[u] = *reinterpret_cast<const f32x4*>(p + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (h0 + u < a.H) { s0 += x0[u]; s1 += x1[u]; }
+      }
+    }
+    if (a.split) {
+      uint32_t bh[8], bm[8], bl[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float x = k < 4 ? s0[k] : s1[k - 4];
+        bh[k] = f2bf(x);
+        const float r1 = x - bf2f(bh[k]);
+        bm[k] = f2bf(r1);
+        bl[k] = f2bf(r1 - bf2f(bm[k]));
+      }
+      const int hf = d0 / HV, kk = (d0 % HV) / 8;
+      u32x4* dst = a.zf + zf_lane_base(r, a.nch_max, a.d_v, b, hf) + size_t(kk) * 3 * 64;
+      dst[0] = pack8(bh);
+      dst[64] = pack8(bm);
+      dst[128] = pack8(bl);
+    } else if (b < a.W) {
+      float* dst = a.z + (size_t(r) * a.W_max + b) * a.d_v + d0;
+      *reinterpret_cast<f32x4*>(dst) = s0;
+      *reinterpret_cast<f32x4*>(dst + 4) = s1;
     }
   }
 }
 
-template <typename WT>
-__global__ void wout_t_kernel(const WT* __restrict__ w, WT* __restrict__ wt, int d_v, int V) {
-  __shared__ WT tile[32][33];
-  const int c0 = blockIdx.x * 32, i0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 256 threads: 32 x 8
-  for (int y = ty; y < 32; y += 8) {
-    const int i = i0 + y, c = c0 + tx;
-    tile[y][tx] = (i < d_v && c < V) ? w[size_t(i) * V + c] : WT{};
-  }
-  __syncthreads();
-  for (int y = ty; y < 32; y += 8) {
-    const int c = c0 + y, i = i0 + tx;
-    if (c < V && i < d_v) wt[size_t(c) * d_v + i] = tile[tx][y];
-  }
+// ---------------------------------------------------------------- one 32 x 32 logits block
+
+// A = codebook rows (codes c0 + lane % 32), B = z columns (32 beams); lane half hf
+// holds elements d_v/2 * hf + ...  acc[i] -> code c0 + 8 (i / 4) + 4 hf + i % 4,
+// beam = column lane % 32.  Both passes call exactly these, so a candidate's logit has
+// the same bits in both.
+template <int DV>
+__device__ __forceinline__ void load_codes_bf16(const u32x4* wt, int code, int V, int hf, u32x4* w) {
+  constexpr int KS = DV / 16, HV = DV / 2;
+  const size_t row = size_t(code < V ? code : 0) * DV + HV * hf;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) w[kk] = code < V ? wt[row / 8 + kk] : u32x4{};
 }
 
-// ---------------------------------------------------------------- select: logits
+template <int KS>
+__device__ __forceinline__ f32x16 block_mfma_bf16(const u32x4* w, const u32x4* zh, const u32x4* zm,
+                                                  const u32x4* zl, f32x16 acc = {}) {
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, w[kk]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, __builtin_bit_cast(bf16x8, zl[kk]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, __builtin_bit_cast(bf16x8, zm[kk]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, __builtin_bit_cast(bf16x8, zh[kk]), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+template <int DV>
+__device__ __forceinline__ f32x16 block_mfma_f32(const float* wt, int code, int V, int hf,
+                                                 const float* zv) {
+  constexpr int HV = DV / 2;
+  const bool cv = code < V;
+  const float* wr = wt + size_t(cv ? code : 0) * DV + HV * hf;
+  f32x16 acc = {};
+#pragma unroll
+  for (int kk = 0; kk < HV; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(cv ? wr[kk] : 0.0f, zv[kk], acc, 0, 0, 0);
+  return acc;
+}
+
+// ---------------------------------------------------------------- first pass
 
 struct LogitsK {
-  int W, W_max, V, nchunk, nvg;
-  const float* z;       // [R,W_max,DV]
-  const void* woutT;    // [V,DV]
-  float* logits;        // per request [V][W]
-  float4* lse_part;     // [R,W_max,nvg]: max, sum of exp(x - max), min
-  size_t logits_stride; // elements per request
+  int W, W_max, V, nchunk, nvg, cpw, nch_max;
+  const float* z;        // [R,W_max,DV]      fp32 codebook
+  const u32x4* zf;       // operand fragments bf16 codebook
+  const void* woutT;     // [V,DV]
+  float* tmax;           // per request [n_tiles(V)][W]: largest logit of each tile
+  size_t tmax_stride;    // elements per request
+  float4* lse_part;      // [R,W_max,nvg]: max, sum of exp(x - max), min tile max
 };
 
-// One wave: 32 beams x kCodesPerWave codes.  A = Wout^T rows (codes), B = z columns
-// (beams), so lane l keeps beam l%32 and can fold its 16 codes per tile into a running
-// log-sum-exp without cross-lane traffic.  bf16 codebook: z is split into three bf16
-// terms (hi, mid, lo), exact products against the bf16 codebook, fp32 accumulation.
+// One wave: 32 beams x cpw codes.  Lane l keeps beam l % 32 and folds its 16 codes of
+// every tile into the tile maximum (with its partner half) and a running log-sum-exp.
 template <int DV, bool WBF16>
 __global__ void __launch_bounds__(256) logits_kernel(LogitsK a) {
   constexpr int HV = DV / 2;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int per_req = a.nchunk * a.nvg;
   const int r = blockIdx.y;
-  if (gw >= per_req) return;
+  if (gw >= a.nchunk * a.nvg) return;
   const int chunk = gw / a.nvg, vg = gw % a.nvg;
   const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
   const int b = chunk * 32 + m;
   const bool bvalid = b < a.W;
-  const float* zr = a.z + (size_t(r) * a.W_max + (bvalid ? b : 0)) * DV + HV * hf;
-  float* lg = a.logits + size_t(r) * a.logits_stride;
+  float* tm_r = a.tmax + size_t(r) * a.tmax_stride;
+  const int code_lo = vg * a.cpw;
+  const int code_hi = min(a.V, code_lo + a.cpw);
 
   float mrun = -INFINITY, srun = 0.0f, nrun = INFINITY;
-  const int code_lo = vg * kCodesPerWave;
-  const int code_hi = min(a.V, code_lo + kCodesPerWave);
+  auto fold = [&](const f32x16& acc, int c0) {
+    float tm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (c0 + 8 * (i >> 2) + 4 * hf + (i & 3) < a.V) tm = fmaxf(tm, acc[i]);
+    tm = fmaxf(tm, __shfl_xor(tm, 32));            // code c0 is valid: tm is finite
+    if (hf == 0 && bvalid) tm_r[size_t(c0 >> 5) * a.W + b] = tm;
+    nrun = fminf(nrun, tm);
+    if (tm > mrun) {
+      srun = mrun == -INFINITY ? 0.0f : srun * __builtin_amdgcn_exp2f((mrun - tm) * kLog2e);
+      mrun = tm;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (c0 + 8 * (i >> 2) + 4 * hf + (i & 3) < a.V)
+        srun += __builtin_amdgcn_exp2f((acc[i] - mrun) * kLog2e);
+  };
 
   if constexpr (WBF16) {
     constexpr int KS = DV / 16;
+    const u32x4* zb = a.zf + zf_lane_base(r, a.nch_max, DV, chunk * 32, hf) + m;
     u32x4 zh[KS], zm[KS], zl[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      uint32_t bh[8], bm[8], bl[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = bvalid ? zr[8 * kk + i] : 0.0f;
-        bh[i] = f2bf(x);
-        const float r1 = x - bf2f(bh[i]);
-        bm[i] = f2bf(r1);
-        bl[i] = f2bf(r1 - bf2f(bm[i]));
-      }
-      zh[kk] = pack8(bh); zm[kk] = pack8(bm); zl[kk] = pack8(bl);
+      zh[kk] = zb[(3 * kk) * 64];
+      zm[kk] = zb[(3 * kk + 1) * 64];
+      zl[kk] = zb[(3 * kk + 2) * 64];
     }
     const u32x4* wt = static_cast<const u32x4*>(a.woutT);
-    // codebook fragments of the current tile; the next tile's are loaded during its MFMAs
-    auto load_w = [&](int c0, u32x4* wf) {
-      const int code = c0 + m;
-      const size_t row = size_t(code < a.V ? code : 0) * DV + HV * hf;
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) wf[kk] = code < a.V ? wt[row / 8 + kk] : u32x4{};
-    };
     u32x4 wcur[KS], wnext[KS];
-    load_w(code_lo, wcur);
+    load_codes_bf16<DV>(wt, code_lo + m, a.V, hf, wcur);
     for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
-      if (c0 + 32 < code_hi) load_w(c0 + 32, wnext);
-      f32x16 acc = {};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const bf16x8 w = __builtin_bit_cast(bf16x8, wcur[kk]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, __builtin_bit_cast(bf16x8, zl[kk]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, __builtin_bit_cast(bf16x8, zm[kk]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, __builtin_bit_cast(bf16x8, zh[kk]), acc, 0, 0, 0);
-      }
-      // acc[i]: code c0 + 8*(i/4) + 4*hf + i%4, beam b
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int cc = c0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (cc < a.V) {
-          tmax = fmaxf(tmax, acc[i]);
-          nrun = fminf(nrun, acc[i]);
-          if (bvalid) lg[size_t(cc) * a.W + b] = acc[i];
-        }
-      }
-      if (tmax > mrun) { srun = (mrun == -INFINITY) ? 0.0f : srun * expf(mrun - tmax); mrun = tmax; }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int cc = c0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (cc < a.V) srun += expf(acc[i] - mrun);
-      }
+      if (c0 + 32 < code_hi) load_codes_bf16<DV>(wt, c0 + 32 + m, a.V, hf, wnext);
+      fold(block_mfma_bf16<KS>(wcur, zh, zm, zl), c0);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) wcur[kk] = wnext[kk];
     }
   } else {
+    const float* zr = a.z + (size_t(r) * a.W_max + (bvalid ? b : 0)) * DV + HV * hf;
+    float zv[HV];
+#pragma unroll
+    for (int i = 0; i < HV; ++i) zv[i] = bvalid ? zr[i] : 0.0f;
     const float* wt = static_cast<const float*>(a.woutT);
-    float zf[HV];
-#pragma unroll
-    for (int i = 0; i < HV; ++i) zf[i] = bvalid ? zr[i] : 0.0f;
-    for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
-      const int code = c0 + m;
-      const bool cv = code < a.V;
-      const float* wr = wt + size_t(cv ? code : 0) * DV + HV * hf;
-      f32x16 acc = {};
-#pragma unroll
-      for (int kk = 0; kk < HV; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(cv ? wr[kk] : 0.0f, zf[kk], acc, 0, 0, 0);
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int cc = c0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (cc < a.V) {
-          tmax = fmaxf(tmax, acc[i]);
-          nrun = fminf(nrun, acc[i]);
-          if (bvalid) lg[size_t(cc) * a.W + b] = acc[i];
-        }
-      }
-      if (tmax > mrun) { srun = (mrun == -INFINITY) ? 0.0f : srun * expf(mrun - tmax); mrun = tmax; }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int cc = c0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (cc < a.V) srun += expf(acc[i] - mrun);
-      }
-    }
+    for (int c0 = code_lo; c0 < code_hi; c0 += 32)
+      fold(block_mfma_f32<DV>(wt, c0 + m, a.V, hf, zv), c0);
   }
   // merge the two lane halves of beam b
   const float mo = __shfl_xor(mrun, 32), so = __shfl_xor(srun, 32);
   const float mm = fmaxf(mrun, mo);
   float ss = 0.0f;
-  if (mrun != -INFINITY) ss += srun * expf(mrun - mm);
-  if (mo != -INFINITY) ss += so * expf(mo - mm);
-  const float nn = fminf(nrun, __shfl_xor(nrun, 32));
-  if (hf == 0 && bvalid) a.lse_part[(size_t(r) * a.W_max + b) * a.nvg + vg] = make_float4(mm, ss, nn, 0.0f);
+  if (mrun != -INFINITY) ss += srun * __builtin_amdgcn_exp2f((mrun - mm) * kLog2e);
+  if (mo != -INFINITY) ss += so * __builtin_amdgcn_exp2f((mo - mm) * kLog2e);
+  if (hf == 0 && bvalid) a.lse_part[(size_t(r) * a.W_max + b) * a.nvg + vg] = make_float4(mm, ss, nrun, 0.0f);
 }
 
-// logsumexp per beam, and the request's exact key range: the score is monotone in
-// the logit, so the row's largest / smallest logits give its largest / smallest keys.
-__global__ void __launch_bounds__(256) lse_kernel(const float4* __restrict__ part,
-                                                  float* __restrict__ lse,
-                                                  const float* __restrict__ cum, SelState* sel,
-                                                  int W, int W_max, int nvg) {
-  const int r = blockIdx.y;
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-  if (b < W) {
-    const float4* p = part + (size_t(r) * W_max + b) * nvg;
-    float mm = -INFINITY, mn = INFINITY;
-    for (int g = 0; g < nvg; ++g) {
-      mm = fmaxf(mm, p[g].x);
-      mn = fminf(mn, p[g].z);
-    }
-    float s = 0.0f;
-    for (int g = 0; g < nvg; ++g)
-      if (p[g].x != -INFINITY) s += p[g].y * expf(p[g].x - mm);
-    const float l = mm + logf(s);
-    lse[size_t(r) * W_max + b] = l;
-    const float c = cum[size_t(r) * W_max + b];
-    kmax = f2key(cand_score(c, mm, l));
-    kmin = f2key(cand_score(c, mn, l));
-  }
-  // one atomic per wave (all lanes of a block belong to request r)
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), off)));
-    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), off)));
-  }
-  if ((threadIdx.x & 63) == 0) {
-    atomicMax(&sel[r].kmax, kmax);
-    atomicMin(&sel[r].kmin, kmin);
-  }
-}
+// ---------------------------------------------------------------- block-wide radix helpers
 
-// ---------------------------------------------------------------- select: radix passes
-
-struct SelK {
-  int W, W_max, V, K, nblk, T_max, t;
-  size_t logits_stride;
-  const float* logits;   // per request [V][W]
-  const float* lse;      // [R,W_max]
-  const float* cum;      // [R,W_max] of step t
-  uint32_t* hist;        // [R,kSelBlocksMax,kHistBins], one histogram per block
-  SelState* sel;
-  uint64_t* winners;     // [R,W_max]: key << 32 | flat, keys above the boundary digit
-  uint32_t* cand;        // [R,logits_stride]: flat indices inside the boundary digit
-};
-
-__device__ __forceinline__ uint32_t cand_key(const float* lg, const float* lse, const float* cum,
-                                             int W, int b, int c) {
-  return f2key(cand_score(cum[b], lg[size_t(c) * W + b], lse[b]));
-}
-
-// Candidates of one request are its [V][W] logits; block `blk` covers codes [c0, c1).
-// With W >= 256 a thread owns beams tid + 256 i for every code; with W < 256 it owns
-// beam tid % W for every (256 / W)-th code.  Loads are issued eight at a time.
-template <typename F>
-__device__ __forceinline__ void for_each_candidate(const SelK& a, int r, int blk, F&& f) {
-  constexpr int U = 8;
-  const int tid = threadIdx.x;
-  const int W = a.W;
-  const int cpb = (a.V + a.nblk - 1) / a.nblk;
-  const int c0 = blk * cpb, c1 = min(a.V, c0 + cpb);
-  const float* lg = a.logits + size_t(r) * a.logits_stride;
-  const float* lse = a.lse + size_t(r) * a.W_max;
-  const float* cum = a.cum + size_t(r) * a.W_max;
-  int b0, bstep, cs, cstep;
-  if (W >= 256) {
-    b0 = tid; bstep = 256; cs = c0; cstep = 1;
-  } else {
-    const int G = 256 / W;
-    if (tid >= G * W) return;
-    b0 = tid % W; bstep = W; cs = c0 + tid / W; cstep = G;
-  }
-  for (int b = b0; b < W; b += bstep) {
-    const float cb = cum[b], lb = lse[b];
-    int c = cs;
-    for (; c + (U - 1) * cstep < c1; c += U * cstep) {
-      float x[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = lg[size_t(c + u * cstep) * W + b];
-#pragma unroll
-      for (int u = 0; u < U; ++u) f(f2key(cand_score(cb, x[u], lb)), b, c + u * cstep);
-    }
-    for (; c < c1; c += cstep) f(f2key(cand_score(cb, lg[size_t(c) * W + b], lb)), b, c);
-  }
-}
-
-// First radix pass over all candidates of a request.  The range [kmin, kmax] (exact
-// key bounds) is split into 2048 digits of width 2^shift; each block stores its own
-// histogram (plain stores: the next kernel reads them, so no fence is needed).
+// The range [lo, hi] is split into 2048 digits of width 2^shift.
 __device__ __forceinline__ int first_shift(uint32_t lo, uint32_t hi) {
   const uint32_t span = hi - lo;
   const int bits = span ? 32 - __clz(span) : 0;
   return bits > 11 ? bits - 11 : 0;
 }
 
-__global__ void __launch_bounds__(256) hist_kernel(SelK a) {
-  __shared__ uint32_t h[kHistBins];
-  const int r = blockIdx.y;
-  const int tid = threadIdx.x;
-  const SelState* st = a.sel + r;
-  const uint32_t lo = st->kmin, hi = st->kmax;
-  const int shift = first_shift(lo, hi);
-  for (int i = tid; i < kHistBins; i += 256) h[i] = 0;
-  __syncthreads();
-  for_each_candidate(a, r, blockIdx.x, [&](uint32_t key, int, int) {
-    if (key >= lo && key <= hi) atomicAdd(&h[(key - lo) >> shift], 1u);
-  });
-  __syncthreads();
-  uint32_t* gh = a.hist + (size_t(r) * kSelBlocksMax + blockIdx.x) * kHistBins;
-  for (int i = tid; i < kHistBins; i += 256) gh[i] = h[i];
+// Shared scalars of the 1024-thread select blocks.
+struct RadixSh {
+  uint32_t lo, hi, need, cnt;
+  int shift;
+};
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = uint32_t(__shfl_up(int(x), off));
+    if (lane >= off) x += y;
+  }
+  return x;
 }
 
-// One block per request: sum the block histograms and pick the digit d holding the
-// K-th largest key: keys above d are winners, keys inside d go on to the finish.
-__global__ void __launch_bounds__(1024) digit_kernel(SelK a) {
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t scan[256];
-  const int r = blockIdx.x;
+// Exclusive prefix sum of v over a 1024-thread block in thread order; `total` gets
+// the block sum.  Two barriers; wsum[16] is scratch.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(v);
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  const uint32_t wx = wave_incl_scan(lane < 16 ? wsum[lane] : 0u);
+  const uint32_t before = uint32_t(__shfl(int(wx), (wv + 63) & 63));
+  total = uint32_t(__shfl(int(wx), 15));
+  __syncthreads();
+  return x - v + (wv ? before : 0u);
+}
+
+// Block of 1024 threads, hist[2048] complete: find the digit of [lo, lo + 2048 << shift)
+// that holds the need-th largest key and leave in sh its range, the count still to take
+// inside it and the next digit width (-1 once the digit is a single value).  Thread t
+// owns digits 2047 - 2t and 2046 - 2t: the keys above them are a prefix sum.
+__device__ void pick_digit(const uint32_t* hist, uint32_t* wsum, uint32_t lo, uint32_t hi, int shift,
+                           uint32_t need, RadixSh& sh) {
   const int tid = threadIdx.x;
-  SelState* st = a.sel + r;
-  const uint32_t lo = st->kmin, hi = st->kmax;
-  const int shift = first_shift(lo, hi);
-  const uint32_t* rh = a.hist + size_t(r) * kSelBlocksMax * kHistBins;
-  for (int d = tid; d < kHistBins; d += 1024) {
-    uint32_t c = 0;
-#pragma unroll 8
-    for (int bk = 0; bk < a.nblk; ++bk) c += rh[size_t(bk) * kHistBins + d];
-    h[d] = c;
+  const uint32_t c0 = hist[kHistBins - 1 - 2 * tid], c1 = hist[kHistBins - 2 - 2 * tid];
+  uint32_t total;
+  uint32_t above = block_excl_scan(c0 + c1, wsum, total);
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t ci = i ? c1 : c0;
+    if (above < need && need <= above + ci) {
+      const uint32_t d = uint32_t(kHistBins - 1 - (2 * tid + i));
+      const uint32_t nlo = lo + (d << shift);
+      const uint64_t top = uint64_t(nlo) + (uint64_t(1) << shift) - 1;
+      sh.lo = nlo;
+      sh.hi = top < hi ? uint32_t(top) : hi;
+      sh.need = need - above;
+      sh.shift = shift == 0 ? -1 : (shift > 11 ? shift - 11 : 0);
+    }
+    above += ci;
   }
   __syncthreads();
-  // digit scan on the first 256 threads (all threads take part in the barriers)
-  constexpr int PER = kHistBins / 256;
-  const uint32_t need = uint32_t(a.K);
-  const bool act = tid < 256;
-  uint32_t cnt[PER];
-  uint32_t tot = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {          // thread tid owns digits from the top down
-    cnt[i] = act ? h[kHistBins - 1 - (tid * PER + i)] : 0u;
-    tot += cnt[i];
+}
+
+// Radix passes inside [lo, hi] over n keys (key_at(i)) until one key value remains:
+// returns theta, the value of the need-th largest key; `need` becomes the number of
+// keys equal to theta still to take.  Every thread of the 1024-thread block calls it.
+template <typename KeyAt>
+__device__ uint32_t radix_finish(KeyAt key_at, uint32_t n, uint32_t lo, uint32_t hi, uint32_t& need,
+                                 int shift, uint32_t* hist, uint32_t* wsum, RadixSh& sh) {
+  const int tid = threadIdx.x;
+  while (shift >= 0) {
+    for (int i = tid; i < kHistBins; i += 1024) hist[i] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += 1024) {
+      const uint32_t key = key_at(i);
+      if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    pick_digit(hist, wsum, lo, hi, shift, need, sh);
+    lo = sh.lo; hi = sh.hi; need = sh.need; shift = sh.shift;
+    __syncthreads();
   }
-  if (act) scan[tid] = tot;
+  return lo;
+}
+
+// Among the keys equal to theta, the need-th smallest flat index (radix over the flat
+// index, 8 bits a pass); all of them when need covers every tie (returns ~0).
+template <typename KeyAt, typename FlatAt>
+__device__ uint32_t tie_cut(KeyAt key_at, FlatAt flat_at, uint32_t n, uint32_t theta, uint32_t need,
+                            uint32_t* hist, RadixSh& sh) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.cnt = 0;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t x = (act && tid >= off) ? scan[tid - off] : 0u;
+  uint32_t mine = 0;
+  for (uint32_t i = tid; i < n; i += 1024) mine += key_at(i) == theta;
+  if (mine) atomicAdd(&sh.cnt, mine);
+  __syncthreads();
+  const uint32_t n_eq = sh.cnt;
+  __syncthreads();
+  if (need >= n_eq) return 0xFFFFFFFFu;
+  uint32_t pre = 0, nd = need;
+  for (int s = 24; s >= 0; s -= 8) {
+    for (int i = tid; i < 256; i += 1024) hist[i] = 0;
     __syncthreads();
-    if (act) scan[tid] += x;
+    const uint32_t himask = s == 24 ? 0u : (0xFFFFFFFFu << (s + 8));
+    for (uint32_t i = tid; i < n; i += 1024) {
+      if (key_at(i) != theta) continue;
+      const uint32_t f = flat_at(i);
+      if ((f & himask) == (pre & himask)) atomicAdd(&hist[(f >> s) & 255u], 1u);
+    }
     __syncthreads();
-  }
-  if (!act) return;
-  uint32_t above = scan[tid] - tot;
-  if (above < need && need <= above + tot) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (above < need && need <= above + cnt[i]) {
-        const uint32_t d = uint32_t(kHistBins - 1 - (tid * PER + i));
-        const uint32_t nlo = lo + (d << shift);
-        const uint64_t top = uint64_t(nlo) + (uint64_t(1) << shift) - 1;
-        st->lo = nlo;
-        st->hi = top < hi ? uint32_t(top) : hi;
-        st->need = need - above;
-        st->shift = shift == 0 ? -1 : (shift > 11 ? shift - 11 : 0);
+    if (tid == 0) {
+      uint32_t below = 0;
+      for (int d = 0; d < 256; ++d) {
+        if (below < nd && nd <= below + hist[d]) {
+          pre |= uint32_t(d) << s;
+          nd -= below;
+          break;
+        }
+        below += hist[d];
       }
-      above += cnt[i];
+      sh.lo = pre;
+      sh.need = nd;
+    }
+    __syncthreads();
+    pre = sh.lo;
+    nd = sh.need;
+    __syncthreads();
+  }
+  return pre;
+}
+
+// ---------------------------------------------------------------- tile select
+
+struct TileSelK {
+  int W, W_max, Vt, K, K_full, G_max, nvg;
+  size_t stride;           // tile maxima / kept tiles per request (n_tiles(V_max) * W_max)
+  const float* tmax;       // per request [Vt][W]
+  const float4* lse_part;  // [R,W_max,nvg]
+  const float* cum;        // [R,W_max] of step t
+  float* lse;              // [R,W_max] out
+  SelState* sel;           // n_tiles, n_groups out
+  uint32_t* cand;          // [R,stride] tiles inside the boundary digit
+  uint32_t* tiles;         // [R,W_max] chosen flat tiles b * Vt + j, grouped by j
+  uint32_t* groups;        // [R,G_max] start | count << 10 | j << 16
+  uint32_t* gtiles;        // [R,G_max,32] the tiles of each group (refinement operands)
+  int32_t* status;
+};
+
+// One 1024-thread block per request.
+//  1. log-sum-exp of every beam from its parts; the request's tile-key range (the
+//     score is monotone in the logit: the largest logit and the smallest tile maximum
+//     of each row bound its tile keys).
+//  2. Pass over all tile keys: 2048-digit histogram over that exact range; the digit
+//     holding the K-th largest key.
+//  3. Pass: keys above the digit are chosen, keys inside it are kept.
+//  4. Radix finish inside the digit over the kept tiles, ties by flat tile index.
+//  5. Counting sort of the K chosen tiles by code tile j, cut into groups of at most
+//     32 beams: one MFMA block of the refinement each.
+__global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
+  __shared__ float lse_s[kMaxW], cum_s[kMaxW];
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t fill[kHistBins];
+  __shared__ uint32_t jstart[kHistBins];
+  __shared__ uint32_t chosen[kMaxW];
+  __shared__ uint32_t wsum[16];
+  __shared__ RadixSh sh;
+  __shared__ uint32_t kmin_sh, kmax_sh, nwin_sh, ncand_sh;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int W = a.W;
+  const uint32_t Vt = uint32_t(a.Vt), K = uint32_t(a.K);
+  const float* tm = a.tmax + size_t(r) * a.stride;
+  uint32_t* cand = a.cand + size_t(r) * a.stride;
+  const size_t cap = size_t(Vt) * W;
+
+  if (tid == 0) { kmin_sh = 0xFFFFFFFFu; kmax_sh = 0u; nwin_sh = 0u; ncand_sh = 0u; }
+  for (int i = tid; i < kHistBins; i += 1024) hist[i] = 0;
+  __syncthreads();
+  {
+    uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
+    if (tid < W) {
+      const float4* p = a.lse_part + (size_t(r) * a.W_max + tid) * a.nvg;
+      float mm = -INFINITY, mn = INFINITY, s = 0.0f;
+      for (int g0 = 0; g0 < a.nvg; g0 += 8) {
+        float4 q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          q[u] = g0 + u < a.nvg ? p[g0 + u] : make_float4(-INFINITY, 0.0f, INFINITY, 0.0f);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          mn = fminf(mn, q[u].z);
+          if (q[u].x > mm) {
+            s = mm == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f((mm - q[u].x) * kLog2e);
+            mm = q[u].x;
+          }
+          if (q[u].x != -INFINITY) s += q[u].y * __builtin_amdgcn_exp2f((q[u].x - mm) * kLog2e);
+        }
+      }
+      const float l = mm + logf(s);
+      const float c = a.cum[size_t(r) * a.W_max + tid];
+      lse_s[tid] = l;
+      cum_s[tid] = c;
+      a.lse[size_t(r) * a.W_max + tid] = l;
+      kmx = f2key(cand_score(c, mm, l));
+      kmn = f2key(cand_score(c, mn, l));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      kmx = max(kmx, uint32_t(__shfl_xor(int(kmx), off)));
+      kmn = min(kmn, uint32_t(__shfl_xor(int(kmn), off)));
+    }
+    if ((tid & 63) == 0) { atomicMax(&kmax_sh, kmx); atomicMin(&kmin_sh, kmn); }
+  }
+  __syncthreads();
+  const uint32_t kmin = kmin_sh, kmax = kmax_sh;
+  const int shift0 = first_shift(kmin, kmax);
+
+  // thread -> one beam b and every G-th tile from jg; loads issued U at a time
+  const int G = 1024 / W;
+  const bool act = tid < G * W;
+  const int b = act ? tid % W : 0, jg = act ? tid / W : 0;
+  const float cb = cum_s[b], lb = lse_s[b];
+  auto stream = [&](auto&& f) {
+    if (!act) return;
+    constexpr int U = 16;
+    for (int j = jg; j < a.Vt; j += U * G) {
+      float x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int jj = j + u * G;
+        x[u] = jj < a.Vt ? tm[size_t(jj) * W + b] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int jj = j + u * G;
+        if (jj < a.Vt) f(f2key(cand_score(cb, x[u], lb)), jj);
+      }
+    }
+  };
+  stream([&](uint32_t key, int) { atomicAdd(&hist[(key - kmin) >> shift0], 1u); });
+  __syncthreads();
+  pick_digit(hist, wsum, kmin, kmax, shift0, K, sh);
+  const uint32_t lo = sh.lo, hi = sh.hi;
+  uint32_t need = sh.need;
+  const int shift1 = sh.shift;
+  __syncthreads();
+  stream([&](uint32_t key, int j) {
+    if (key < lo) return;
+    const uint32_t flat = uint32_t(b) * Vt + uint32_t(j);
+    if (key > hi) {
+      const uint32_t p = atomicAdd(&nwin_sh, 1u);
+      if (p < uint32_t(kMaxW)) chosen[p] = flat;
+    } else {
+      const uint32_t p = atomicAdd(&ncand_sh, 1u);
+      if (p < cap) cand[p] = flat;
+    }
+  });
+  __syncthreads();
+  const uint32_t n_cand = min(ncand_sh, uint32_t(cap));
+  auto key_at = [&](uint32_t i) {
+    const uint32_t f = cand[i];
+    const uint32_t bb = f / Vt;
+    return f2key(cand_score(cum_s[bb], tm[size_t(f % Vt) * W + bb], lse_s[bb]));
+  };
+  auto flat_at = [&](uint32_t i) { return cand[i]; };
+  const uint32_t theta = radix_finish(key_at, n_cand, lo, hi, need, shift1, hist, wsum, sh);
+  const uint32_t phi = tie_cut(key_at, flat_at, n_cand, theta, need, hist, sh);
+  // the K-th tile key bounds the K-th candidate key from below when K tiles are chosen
+  if (tid == 0) a.sel[r].theta = a.K == a.K_full ? theta : 0u;
+  for (uint32_t i = tid; i < n_cand; i += 1024) {
+    const uint32_t f = cand[i];
+    const uint32_t key = key_at(i);
+    if (key > theta || (key == theta && f <= phi)) {
+      const uint32_t p = atomicAdd(&nwin_sh, 1u);
+      if (p < uint32_t(kMaxW)) chosen[p] = f;
+    }
+  }
+  for (int j = tid; j < kHistBins; j += 1024) hist[j] = 0;
+  __syncthreads();
+  const uint32_t got = min(nwin_sh, K);
+  if (tid == 0 && nwin_sh != K) atomicOr(a.status, 2);
+  for (uint32_t p = tid; p < got; p += 1024) atomicAdd(&hist[chosen[p] % Vt], 1u);
+  __syncthreads();
+  // exclusive scans over j of the counts (low 16 bits) and the group counts (high 16)
+  const uint32_t n0 = hist[2 * tid], n1 = hist[2 * tid + 1];
+  const uint32_t g0 = (n0 + 31) / 32, g1 = (n1 + 31) / 32;
+  const uint32_t v = (n0 + n1) | ((g0 + g1) << 16);
+  uint32_t total;
+  const uint32_t ex = block_excl_scan(v, wsum, total);
+  const uint32_t s0 = ex & 0xFFFFu, gs0 = ex >> 16;
+  const uint32_t s1 = s0 + n0, gs1 = gs0 + g0;
+  if (tid == 0) {
+    a.sel[r].n_groups = total >> 16;
+    a.sel[r].n_tiles = got;
+  }
+  fill[2 * tid] = s0;
+  fill[2 * tid + 1] = s1;
+  jstart[2 * tid] = s0;
+  jstart[2 * tid + 1] = s1;
+  hist[2 * tid] = gs0;                          // first group of code tile j
+  hist[2 * tid + 1] = gs1;
+  uint32_t* grp = a.groups + size_t(r) * a.G_max;
+  for (uint32_t q = 0; q < g0; ++q)
+    grp[gs0 + q] = (s0 + 32 * q) | (min(32u, n0 - 32 * q) << 10) | (uint32_t(2 * tid) << 16);
+  for (uint32_t q = 0; q < g1; ++q)
+    grp[gs1 + q] = (s1 + 32 * q) | (min(32u, n1 - 32 * q) << 10) | (uint32_t(2 * tid + 1) << 16);
+  __syncthreads();
+  uint32_t* tl = a.tiles + size_t(r) * a.W_max;
+  uint32_t* gt = a.gtiles + size_t(r) * a.G_max * 32;
+  for (uint32_t p = tid; p < got; p += 1024) {
+    const uint32_t f = chosen[p], j = f % Vt;
+    const uint32_t q = atomicAdd(&fill[j], 1u), off = q - jstart[j];
+    tl[q] = f;
+    gt[(hist[j] + off / 32) * 32 + off % 32] = f;
+  }
+}
+
+// ---------------------------------------------------------------- refinement
+
+struct RefineK {
+  int W, W_max, V, Vt, G_max, nch_max;
+  const float* z;
+  const u32x4* zf;
+  const void* woutT;
+  const float* lse;
+  const float* cum;
+  const SelState* sel;
+  const uint32_t* groups;
+  const uint32_t* gtiles;
+  uint32_t* rkeys;       // [R,W_max,32]: keys of the chosen tiles' candidates (0: no code)
+};
+
+// One wave per group: code tile j against up to 32 beams that chose it.  Columns are
+// independent in the MFMA, so every logit equals the first pass's bit for bit.
+template <int DV, bool WBF16>
+__global__ void __launch_bounds__(256, 2) refine_kernel(RefineK a) {
+  constexpr int HV = DV / 2;
+  const int r = blockIdx.y;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);      // < G_max by the launch
+  const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
+  const uint32_t ng = a.sel[r].n_groups;
+  const uint32_t desc = a.groups[size_t(r) * a.G_max + g];
+  const uint32_t f = a.gtiles[(size_t(r) * a.G_max + g) * 32 + m];
+  if (g >= int(ng)) return;
+  const int start = int(desc & 1023u), cnt = int((desc >> 10) & 63u), j = int(desc >> 16);
+  const bool valid = m < cnt;
+  const int b = valid ? int(f / uint32_t(a.Vt)) : 0;
+  const int c0 = 32 * j;
+  f32x16 acc;
+  if constexpr (WBF16) {
+    // the same MFMA sequence as the first pass (kk ascending), operands held for at
+    // most eight kk at a time
+    constexpr int KS = DV / 16, KP = KS > 8 ? 8 : KS;
+    const u32x4* zb = a.zf + zf_lane_base(r, a.nch_max, DV, b, hf);
+    const u32x4* wt = static_cast<const u32x4*>(a.woutT);
+    const int code = c0 + m;
+    const size_t row = size_t(code < a.V ? code : 0) * DV + HV * hf;
+    acc = f32x16{};
+#pragma unroll 1
+    for (int k0 = 0; k0 < KS; k0 += KP) {
+      u32x4 zh[KP], zm[KP], zl[KP], w[KP];
+#pragma unroll
+      for (int kk = 0; kk < KP; ++kk) {
+        zh[kk] = valid ? zb[(3 * (k0 + kk)) * 64] : u32x4{};
+        zm[kk] = valid ? zb[(3 * (k0 + kk) + 1) * 64] : u32x4{};
+        zl[kk] = valid ? zb[(3 * (k0 + kk) + 2) * 64] : u32x4{};
+        w[kk] = code < a.V ? wt[row / 8 + k0 + kk] : u32x4{};
+      }
+      acc = block_mfma_bf16<KP>(w, zh, zm, zl, acc);
+    }
+  } else {
+    const float* zr = a.z + (size_t(r) * a.W_max + b) * DV + HV * hf;
+    float zv[HV];
+#pragma unroll
+    for (int i = 0; i < HV; ++i) zv[i] = valid ? zr[i] : 0.0f;
+    acc = block_mfma_f32<DV>(static_cast<const float*>(a.woutT), c0 + m, a.V, hf, zv);
+  }
+  if (valid) {
+    const float cb = a.cum[size_t(r) * a.W_max + b], lb = a.lse[size_t(r) * a.W_max + b];
+    uint32_t* out = a.rkeys + (size_t(r) * a.W_max + start + m) * kTile;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int o = 8 * (i >> 2) + 4 * hf + (i & 3);
+      out[o] = c0 + o < a.V ? f2key(cand_score(cb, acc[i], lb)) : 0u;
     }
   }
 }
 
-// Split the candidates by the boundary digit [lo, hi]: keys above it are winners,
-// keys inside it are kept (flat index) for the finish kernel.
-__global__ void __launch_bounds__(256) compact_kernel(SelK a) {
-  const int r = blockIdx.y;
-  SelState* st = a.sel + r;
-  const uint32_t lo = st->lo, hi = st->hi;
-  const size_t cap = size_t(a.V) * a.W;
-  for_each_candidate(a, r, blockIdx.x, [&](uint32_t key, int b, int c) {
-    if (key >= lo) {
-      const uint32_t flat = uint32_t(b) * uint32_t(a.V) + uint32_t(c);
-      if (key > hi) {
-        const uint32_t i = atomicAdd(&st->n_win, 1u);
-        if (i < uint32_t(a.W_max)) a.winners[size_t(r) * a.W_max + i] = (uint64_t(key) << 32) | flat;
-      } else {
-        const uint32_t i = atomicAdd(&st->n_cand, 1u);
-        if (i < cap) a.cand[size_t(r) * a.logits_stride + i] = flat;
-      }
-    }
-  });
-}
+// ---------------------------------------------------------------- final select
 
 struct FinK {
-  int W, W_max, V, K, T_max, t;
-  size_t logits_stride;
-  const float* logits;
+  int W, W_max, V, Vt, K, Kt, T_max, t, d_v, nch_max, split;
+  const SelState* sel;
+  const uint32_t* rkeys;
+  const uint32_t* tiles;
   const float* lse;
   const float* cum;        // step t
   float* cum_next;
@@ -396,168 +658,182 @@ struct FinK {
   int32_t* anc_next;
   const int32_t* tok;
   int32_t* tok_next;
-  const SelState* sel;
-  const uint64_t* winners;
-  const uint32_t* cand;
+  const float* z;
+  const u32x4* zf;
+  const void* woutT;
   const int32_t *forced_parent, *forced_token;
   int32_t *parent, *token;
   float* score;
   int32_t* status;
 };
 
-// One 1024-thread block per request: finish the radix select inside the boundary
-// digit (at most two more 11-bit passes over its candidates), keep the `need`
-// smallest flat indices among keys equal to the threshold, sort the K winners by
-// score descending then flat index ascending, write the top-W, and remap ancestry,
-// SID prefixes and cumulative scores by eq. (9).
-__global__ void __launch_bounds__(1024) finalize_kernel(FinK a) {
-  __shared__ uint64_t s[kMaxW];
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t scan[1024];
-  __shared__ uint32_t cnt, sh_lo, sh_hi, sh_need;
-  __shared__ int sh_shift;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const SelState st = a.sel[r];
-  const float* lg = a.logits + size_t(r) * a.logits_stride;
+// logit of one (beam, code) for a forced candidate: fp32 dot product of z (rebuilt
+// exactly from its three bf16 parts for a bf16 codebook) and the code's row.
+__device__ float forced_logit(const FinK& a, int r, int b, int c) {
+  float s = 0.0f;
+  const int HV = a.d_v / 2;
+  for (int d = 0; d < a.d_v; ++d) {
+    float zd, wd;
+    if (a.split) {
+      const int hf = d / HV, kk = (d % HV) / 8, i = d % 8;
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(a.zf + zf_lane_base(r, a.nch_max, a.d_v, b, hf) +
+                                                            size_t(kk) * 3 * 64);
+      auto part = [&](int term) {
+        const uint32_t w = p[size_t(term) * 64 * 4 + i / 2];
+        return bf2f(i & 1 ? (w >> 16) : (w & 0xFFFFu));
+      };
+      zd = (part(0) + part(1)) + part(2);
+      wd = bf2f(static_cast<const uint16_t*>(a.woutT)[size_t(c) * a.d_v + d]);
+    } else {
+      zd = a.z[(size_t(r) * a.W_max + b) * a.d_v + d];
+      wd = static_cast<const float*>(a.woutT)[size_t(c) * a.d_v + d];
+    }
+    s = fmaf(zd, wd, s);
+  }
+  return s;
+}
+
+// Refined keys kept in LDS by the final select; more than this many keys at or above
+// the tile threshold (massive ties) are read from global memory instead.
+constexpr int kFinCap = 8192;
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(v)), m));
+  const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(v >> 32)), m));
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// One 1024-thread block per request.  Only refined keys at or above the K-th tile key
+// can be among the top K (when K tiles were chosen: their maxima are K candidates);
+// they are compacted into LDS.  Then the exact top-K (score descending, flat index
+// b * V + c ascending), a bitonic sort with one entry per thread (exchanges inside a
+// wave by shuffles, across waves through LDS), the top-W outputs, and the eq. (9)
+// remap of ancestry, SID prefixes and cumulative scores.
+__global__ void __launch_bounds__(1024) final_kernel(FinK a) {
+  __shared__ uint32_t ck[kFinCap], ce[kFinCap];
+  __shared__ uint32_t tl[kMaxW];
+  __shared__ union {
+    uint32_t hist[kHistBins];
+    uint64_t s[kMaxW];
+  } u;
+  __shared__ uint32_t wsum[16];
+  __shared__ RadixSh sh;
+  __shared__ uint32_t kmax_sh, m_sh;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const uint32_t n = uint32_t(a.Kt) * kTile;
+  const uint32_t V = uint32_t(a.V), Vt = uint32_t(a.Vt);
+  const uint32_t lo = max(a.sel[r].theta, 1u);            // key 0 marks a padding code
+  const uint32_t* rk = a.rkeys + size_t(r) * a.W_max * kTile;
+  if (tid == 0) { kmax_sh = 0u; m_sh = 0u; }
+  for (int p = tid; p < a.Kt; p += 1024) tl[p] = a.tiles[size_t(r) * a.W_max + p];
+  __syncthreads();
+  {
+    constexpr int IT = kMaxW * kTile / 4 / 1024;         // u32x4 loads per thread, all issued first
+    const u32x4* src = reinterpret_cast<const u32x4*>(rk);
+    u32x4 kv[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const uint32_t q = uint32_t(it) * 1024 + tid;
+      kv[it] = q < n / 4 ? src[q] : u32x4{0u, 0u, 0u, 0u};
+    }
+    uint32_t lmax = 0u;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = kv[it][e];
+        const bool keep = key >= lo;
+        lmax = keep ? max(lmax, key) : lmax;
+        const uint64_t mask = __ballot(keep);
+        if (mask) {
+          uint32_t base = 0u;
+          if (lane == 0) base = atomicAdd(&m_sh, uint32_t(__popcll(mask)));
+          base = uint32_t(__shfl(int(base), 0));
+          if (keep) {
+            const uint32_t p = base + uint32_t(__popcll(mask & ((1ull << lane) - 1ull)));
+            if (p < uint32_t(kFinCap)) { ck[p] = key; ce[p] = 4 * (uint32_t(it) * 1024 + tid) + e; }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lmax = max(lmax, uint32_t(__shfl_xor(int(lmax), off)));
+    if (lane == 0) atomicMax(&kmax_sh, lmax);
+  }
+  __syncthreads();
+  const uint32_t m = m_sh, hi = kmax_sh;
+  const bool inl = m <= uint32_t(kFinCap);
+  const uint32_t ns = inl ? m : n;
+  auto key_at = [&](uint32_t i) { return inl ? ck[i] : rk[i]; };
+  auto flat_at = [&](uint32_t i) {
+    const uint32_t e = inl ? ce[i] : i;
+    const uint32_t f = tl[e >> 5];
+    return (f / Vt) * V + (f % Vt) * kTile + (e & 31u);
+  };
+  uint32_t need = uint32_t(a.K);
+  const uint32_t theta = radix_finish(key_at, ns, lo, hi, need, first_shift(lo, hi), u.hist, wsum, sh);
+  const uint32_t phi = tie_cut(key_at, flat_at, ns, theta, need, u.hist, sh);
+
+  // gather the K winners as (key, ~flat): sorting these descending ranks by score
+  // descending, then flat index ascending
+  if (tid == 0) sh.cnt = 0;
+  __syncthreads();
+  for (uint32_t i0 = 0; i0 < ns; i0 += 1024) {
+    const uint32_t i = i0 + tid;
+    bool win = false;
+    uint64_t ent = 0;
+    if (i < ns) {
+      const uint32_t key = key_at(i);
+      if (key >= theta) {
+        const uint32_t f = flat_at(i);
+        win = key > theta || f <= phi;
+        ent = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - f);
+      }
+    }
+    const uint64_t mask = __ballot(win);
+    if (mask) {
+      uint32_t base = 0u;
+      if (lane == 0) base = atomicAdd(&sh.cnt, uint32_t(__popcll(mask)));
+      base = uint32_t(__shfl(int(base), 0));
+      if (win) {
+        const uint32_t p = base + uint32_t(__popcll(mask & ((1ull << lane) - 1ull)));
+        if (p < uint32_t(kMaxW)) u.s[p] = ent;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t got = min(sh.cnt, uint32_t(kMaxW));
+  if (tid == 0 && sh.cnt != uint32_t(a.K)) atomicOr(a.status, 2);
+  uint64_t v = uint32_t(tid) < got ? u.s[tid] : 0ull;    // padding sorts last
+  int np = 1;
+  while (np < a.K) np <<= 1;
+  for (int k = 2; k <= np; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint64_t o;
+      if (j >= 64) {
+        __syncthreads();
+        u.s[tid] = v;
+        __syncthreads();
+        o = u.s[tid ^ j];
+      } else {
+        o = shfl_xor_u64(v, j);
+      }
+      const bool desc = (tid & k) == 0, lower = (tid & j) == 0;
+      v = (desc == lower) ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  }
+  // thread i holds rank i
   const float* lse = a.lse + size_t(r) * a.W_max;
   const float* cum = a.cum + size_t(r) * a.W_max;
-  const uint32_t* cand = a.cand + size_t(r) * a.logits_stride;
-  const uint32_t n_cand = min(st.n_cand, uint32_t(a.V) * uint32_t(a.W));
-  const uint32_t n_win = min(st.n_win, uint32_t(a.K));
-  const uint32_t V = uint32_t(a.V);
-  auto key_of = [&](uint32_t flat) {
-    return cand_key(lg, lse, cum, a.W, int(flat / V), int(flat % V));
-  };
-
-  // radix passes inside [lo, hi] until a single key remains (theta = lo = hi)
-  uint32_t lo = st.lo, hi = st.hi, need = st.need;
-  int shift = st.shift;
-  while (shift >= 0) {
-    for (int i = tid; i < kHistBins; i += 1024) hist[i] = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < n_cand; i += 1024) {
-      const uint32_t key = key_of(cand[i]);
-      if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> shift], 1u);
-    }
-    __syncthreads();
-    const uint32_t c0 = hist[kHistBins - 1 - 2 * tid], c1 = hist[kHistBins - 2 - 2 * tid];
-    scan[tid] = c0 + c1;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const uint32_t x = tid >= off ? scan[tid - off] : 0u;
-      __syncthreads();
-      scan[tid] += x;
-      __syncthreads();
-    }
-    uint32_t above = scan[tid] - (c0 + c1);
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t ci = i ? c1 : c0;
-      if (above < need && need <= above + ci) {
-        const uint32_t d = uint32_t(kHistBins - 1 - (2 * tid + i));
-        const uint32_t nlo = lo + (d << shift);
-        const uint64_t top = uint64_t(nlo) + (uint64_t(1) << shift) - 1;
-        sh_lo = nlo;
-        sh_hi = top < hi ? uint32_t(top) : hi;
-        sh_need = need - above;
-        sh_shift = shift == 0 ? -1 : (shift > 11 ? shift - 11 : 0);
-      }
-      above += ci;
-    }
-    __syncthreads();
-    lo = sh_lo; hi = sh_hi; need = sh_need; shift = sh_shift;
-    __syncthreads();
-  }
-  const uint32_t theta = lo;
-
-  // ties at theta: keep the `need` smallest flat indices (radix over the flat index)
-  if (tid == 0) cnt = 0;
-  __syncthreads();
-  for (uint32_t i = tid; i < n_cand; i += 1024)
-    if (key_of(cand[i]) == theta) atomicAdd(&cnt, 1u);
-  __syncthreads();
-  const uint32_t n_eq = cnt;
-  uint32_t phi = 0xFFFFFFFFu;
-  if (need < n_eq) {
-    uint32_t pre = 0, nd = need;
-    for (int sh = 24; sh >= 0; sh -= 8) {
-      for (int i = tid; i < 256; i += 1024) hist[i] = 0;
-      __syncthreads();
-      const uint32_t himask = sh == 24 ? 0u : (0xFFFFFFFFu << (sh + 8));
-      for (uint32_t i = tid; i < n_cand; i += 1024) {
-        const uint32_t f = cand[i];
-        if ((f & himask) == (pre & himask) && key_of(f) == theta) atomicAdd(&hist[(f >> sh) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t below = 0;
-        for (int d = 0; d < 256; ++d) {
-          if (below < nd && nd <= below + hist[d]) {
-            pre |= uint32_t(d) << sh;
-            nd -= below;
-            break;
-          }
-          below += hist[d];
-        }
-        sh_lo = pre;
-        sh_need = nd;
-      }
-      __syncthreads();
-      pre = sh_lo;
-      nd = sh_need;
-      __syncthreads();
-    }
-    phi = pre;
-  }
-
-  // gather the K winners
-  if (tid == 0) cnt = 0;
-  __syncthreads();
-  for (uint32_t i = tid; i < n_win; i += 1024) {
-    const uint32_t j = atomicAdd(&cnt, 1u);
-    if (j < uint32_t(kMaxW)) s[j] = a.winners[size_t(r) * a.W_max + i];
-  }
-  for (uint32_t i = tid; i < n_cand; i += 1024) {
-    const uint32_t f = cand[i];
-    const uint32_t key = key_of(f);
-    if (key > theta || (key == theta && f <= phi)) {
-      const uint32_t j = atomicAdd(&cnt, 1u);
-      if (j < uint32_t(kMaxW)) s[j] = (uint64_t(key) << 32) | f;
-    }
-  }
-  __syncthreads();
-  const uint32_t got = cnt;
-  if (tid == 0 && got != uint32_t(a.K)) atomicOr(a.status, 2);
-  // pad to a power of two with the smallest entry, then sort descending by
-  // (key, ~flat): score descending, flat index ascending
-  int n = 1;
-  while (n < a.K) n <<= 1;
-  for (int i = tid; i < n; i += 1024) {
-    if (uint32_t(i) >= got) s[i] = 0;
-    else s[i] = (s[i] & 0xFFFFFFFF00000000ull) | uint64_t(0xFFFFFFFFu - uint32_t(s[i]));
-  }
-  __syncthreads();
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < n; i += 1024) {
-        const int p = i ^ j;
-        if (p > i) {
-          const bool desc = (i & k) == 0;
-          const uint64_t x = s[i], y = s[p];
-          if (desc ? (x < y) : (x > y)) { s[i] = y; s[p] = x; }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < a.K; i += 1024) {
-    const uint64_t e = s[i];
-    const uint32_t flat = 0xFFFFFFFFu - uint32_t(e);
+  if (tid < a.K) {
+    const int i = tid;
+    const uint32_t flat = 0xFFFFFFFFu - uint32_t(v);
     int p = int(flat / V), c = int(flat % V);
     if (uint32_t(i) >= got || p >= a.W) {   // only if fewer than K were gathered (flagged)
       p = 0;
       c = 0;
     }
-    const float sc = key2f(uint32_t(e >> 32));
+    const float sc = key2f(uint32_t(v >> 32));
     const size_t o = size_t(r) * a.K + i;
     a.parent[o] = p;
     a.token[o] = c;
@@ -572,7 +848,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinK a) {
         fp = fp < 0 ? 0 : (fp >= a.W ? a.W - 1 : fp);
         fc = fc < 0 ? 0 : (fc >= a.V ? a.V - 1 : fc);
       }
-      fs = cand_score(cum[fp], lg[size_t(fc) * a.W + fp], lse[fp]) + 0.0f;
+      fs = cand_score(cum[fp], forced_logit(a, r, fp, fc), lse[fp]) + 0.0f;
     }
     // eq. (9): the child copies its parent's ancestry and appends the parent's slot
     const int32_t* ap = a.anc + (size_t(r) * a.W_max + fp) * a.T_max;
@@ -590,30 +866,52 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinK a) {
 // ---------------------------------------------------------------- launchers
 
 template <int DV>
-static int launch_logits_t(const SelectArgs& a, const LogitsK& k, hipStream_t s) {
-  const int per_req = k.nchunk * k.nvg;
-  dim3 grid((per_req + 3) / 4, a.R);
-  if (a.wout_dtype == GDN_BF16)
-    hipLaunchKernelGGL((logits_kernel<DV, true>), grid, dim3(256), 0, s, k);
-  else
-    hipLaunchKernelGGL((logits_kernel<DV, false>), grid, dim3(256), 0, s, k);
+static int launch_dv(const SelectArgs& a, const LogitsK& lk, const RefineK& rk, int groups,
+                     hipStream_t s, bool refine) {
+  const bool bf = a.wout_dtype == GDN_BF16;
+  if (!refine) {
+    dim3 grid((lk.nchunk * lk.nvg + 3) / 4, a.R);
+    if (bf) hipLaunchKernelGGL((logits_kernel<DV, true>), grid, dim3(256), 0, s, lk);
+    else hipLaunchKernelGGL((logits_kernel<DV, false>), grid, dim3(256), 0, s, lk);
+  } else {
+    dim3 grid((groups + 3) / 4, a.R);
+    if (bf) hipLaunchKernelGGL((refine_kernel<DV, true>), grid, dim3(256), 0, s, rk);
+    else hipLaunchKernelGGL((refine_kernel<DV, false>), grid, dim3(256), 0, s, rk);
+  }
   return last_launch_error();
+}
+
+static int launch_by_dv(const SelectArgs& a, const LogitsK& lk, const RefineK& rk, int groups,
+                        hipStream_t s, bool refine) {
+  if (a.d_v == 16) return launch_dv<16>(a, lk, rk, groups, s, refine);
+  if (a.d_v == 128) return launch_dv<128>(a, lk, rk, groups, s, refine);
+  if (a.d_v == 256) return launch_dv<256>(a, lk, rk, groups, s, refine);
+  return int(hipErrorInvalidValue);
 }
 
 int launch_select(const SelectArgs& a, hipStream_t s) {
   (void)hipGetLastError();
   char* ws = static_cast<char*>(a.ws);
   const Layout& L = a.L;
-  const size_t stride = size_t(a.W_max) * size_t(a.V_max);   // per-request candidates
   const int par = a.t & 1;
+  const int Vt = n_tiles(a.V);
+  const int nch = n_chunks(a.W), nch_max = n_chunks(a.W_max);
+  const int Kt = int(a.W_next < int64_t(a.W) * Vt ? a.W_next : int64_t(a.W) * Vt);
+  const size_t tstride = size_t(n_tiles(a.V_max)) * a.W_max;
+  const int G_max = max_groups(a.W_max, n_tiles(a.V_max));
+  const int split = a.wout_dtype == GDN_BF16;
   float* z = reinterpret_cast<float*>(ws + L.z);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
-  SelState* sel = reinterpret_cast<SelState*>(ws + L.sel);
-  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  u32x4* zf = reinterpret_cast<u32x4*>(ws + L.zf);
+  void* woutT = ws + L.woutT;
+  float* tmax = reinterpret_cast<float*>(ws + L.tmax);
   float4* lse_part = reinterpret_cast<float4*>(ws + L.lse_part);
   float* lse = reinterpret_cast<float*>(ws + L.lse);
-  uint64_t* winners = reinterpret_cast<uint64_t*>(ws + L.winners);
+  SelState* sel = reinterpret_cast<SelState*>(ws + L.sel);
   uint32_t* cand = reinterpret_cast<uint32_t*>(ws + L.cand);
+  uint32_t* tiles = reinterpret_cast<uint32_t*>(ws + L.tiles);
+  uint32_t* groups = reinterpret_cast<uint32_t*>(ws + L.groups);
+  uint32_t* gtiles = reinterpret_cast<uint32_t*>(ws + L.gtiles);
+  uint32_t* rkeys = reinterpret_cast<uint32_t*>(ws + L.rkeys);
   float* cum = reinterpret_cast<float*>(ws + L.cum[par]);
   float* cum_next = reinterpret_cast<float*>(ws + L.cum[par ^ 1]);
   int32_t* anc = reinterpret_cast<int32_t*>(ws + L.anc[par]);
@@ -623,56 +921,39 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
   int err;
 
-  {  // head sum, selection-state reset
-    const int n4 = a.W * a.d_v / 4;
-    int gx = (n4 + 255) / 256;
+  {  // head sum into the MFMA operand; codebook transpose in the last grid row
+    ZsumK k{a.R, a.H, a.W, a.W_max, a.d_v, a.V, nch_max, split, a.o, z, zf, a.Wout, woutT};
+    const int n = nch * 32 * (a.d_v / 8);
+    const int ntr = ((a.V + 31) / 32) * ((a.d_v + 31) / 32);   // transpose tiles
+    int gx = (n + 255) / 256;
+    gx = gx < ntr ? ntr : gx;
     gx = gx < 1 ? 1 : (gx > 1024 ? 1024 : gx);
-    hipLaunchKernelGGL(zsum_kernel, dim3(gx, a.R), dim3(256), 0, s, a.o, z, a.H, a.W, a.W_max,
-                       a.d_v, a.W_next, hist, sel, a.R);
+    hipLaunchKernelGGL(zsum_kernel, dim3(gx, a.R + 1), dim3(256), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
-  {  // codebook transpose
-    dim3 grid((a.V + 31) / 32, (a.d_v + 31) / 32);
-    if (a.wout_dtype == GDN_BF16)
-      hipLaunchKernelGGL((wout_t_kernel<uint16_t>), grid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(a.Wout), reinterpret_cast<uint16_t*>(ws + L.woutT), a.d_v, a.V);
-    else
-      hipLaunchKernelGGL((wout_t_kernel<float>), grid, dim3(256), 0, s,
-                         static_cast<const float*>(a.Wout), reinterpret_cast<float*>(ws + L.woutT), a.d_v, a.V);
+  // codes per wave: 128 .. 1024, larger while the grid keeps >= 16384 waves, so that
+  // the z operand is reloaded fewer times on large codebooks
+  int cpw = 128;
+  while (cpw < 1024 && cpw < a.V && int64_t(a.R) * nch * ((a.V + 2 * cpw - 1) / (2 * cpw)) >= 16384) cpw *= 2;
+  const int nvg = (a.V + cpw - 1) / cpw;
+  LogitsK lk{a.W, a.W_max, a.V, nch, nvg, cpw, nch_max, z, zf, woutT, tmax, tstride, lse_part};
+  RefineK rk{a.W, a.W_max, a.V, Vt, G_max, nch_max, z, zf, woutT, lse, cum, sel, groups, gtiles, rkeys};
+  if ((err = launch_by_dv(a, lk, rk, 0, s, false))) return err;
+  {
+    TileSelK k{a.W, a.W_max, Vt, Kt, a.W_next, G_max, nvg, tstride, tmax, lse_part, cum, lse, sel,
+               cand, tiles, groups, gtiles, status};
+    hipLaunchKernelGGL(tile_select_kernel, dim3(a.R), dim3(1024), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
-  const int nvg = n_vgroups(a.V);
-  {  // logits and log-sum-exp parts
-    LogitsK k{a.W, a.W_max, a.V, (a.W + 31) / 32, nvg, z, ws + L.woutT, logits, lse_part, stride};
-    if (a.d_v == 16) err = launch_logits_t<16>(a, k, s);
-    else if (a.d_v == 128) err = launch_logits_t<128>(a, k, s);
-    else if (a.d_v == 256) err = launch_logits_t<256>(a, k, s);
-    else return int(hipErrorInvalidValue);
-    if (err) return err;
+  {  // groups <= ceil(Kt / 32) + min(Vt, Kt) <= G_max
+    const int gmax = (Kt + 31) / 32 + (Vt < Kt ? Vt : Kt);
+    if ((err = launch_by_dv(a, lk, rk, gmax, s, true))) return err;
   }
   {
-    hipLaunchKernelGGL(lse_kernel, dim3((a.W + 255) / 256, a.R), dim3(256), 0, s, lse_part, lse,
-                       cum, sel, a.W, a.W_max, nvg);
-    if ((err = last_launch_error())) return err;
-  }
-  {  // exact top-W_next: three radix passes, then gather
-    const size_t N = size_t(a.V) * a.W;
-    long nblk = long((N + kSelPerBlock - 1) / kSelPerBlock);
-    nblk = nblk < 1 ? 1 : (nblk > kSelBlocksMax ? kSelBlocksMax : nblk);
-    nblk = nblk > a.V ? a.V : nblk;                      // every block owns >= 1 code
-    SelK k{a.W, a.W_max, a.V, a.W_next, int(nblk), a.T_max, a.t, stride, logits, lse, cum,
-           hist, sel, winners, cand};
-    dim3 grid(nblk, a.R);
-    hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, k);
-    hipLaunchKernelGGL(digit_kernel, dim3(a.R), dim3(1024), 0, s, k);
-    hipLaunchKernelGGL(compact_kernel, grid, dim3(256), 0, s, k);
-    if ((err = last_launch_error())) return err;
-  }
-  {  // order, write the top-W, remap ancestry (eq. 9)
-    FinK k{a.W, a.W_max, a.V, a.W_next, a.T_max, a.t, stride, logits, lse, cum, cum_next,
-           anc, anc_next, tok, tok_next, sel, winners, cand, a.forced_parent, a.forced_token,
-           a.parent, a.token, a.score, status};
-    hipLaunchKernelGGL(finalize_kernel, dim3(a.R), dim3(1024), 0, s, k);
+    FinK k{a.W, a.W_max, a.V, Vt, a.W_next, Kt, a.T_max, a.t, a.d_v, nch_max, split, sel, rkeys, tiles,
+           lse, cum, cum_next, anc, anc_next, tok, tok_next, z, zf, woutT, a.forced_parent,
+           a.forced_token, a.parent, a.token, a.score, status};
+    hipLaunchKernelGGL(final_kernel, dim3(a.R), dim3(1024), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
   return 0;

@@ -50,10 +50,14 @@ def expected_bytes(R, H, d_k, d_v, T, W, V, e, ew):
     """Workspace regions as documented in include/gdn_beam.h, each 256-aligned."""
     dvp = max(d_v, 32)
     nvg = -(-V // 128)
+    Vt = -(-V // 32)                      # 32-code tiles
+    nch = -(-W // 32)                     # 32-beam MFMA columns
+    groups = nch + 1 + min(Vt, W)
     regions = [R * H * 4 * dvp * d_k, R * H * T * W * 4, R * H * T * W * d_v * 4,
                R * H * T * W * d_k * e, R * W * T * 4, R * W * T * 4, R * W * T * 4, R * W * T * 4,
-               R * W * 4, R * W * 4, R * W * d_v * 4, V * d_v * ew, R * V * W * 4, R * W * nvg * 16,
-               R * W * 4, R * 64 * 2048 * 4, R * 64, R * W * 8, R * V * W * 4, 64 * 4]
+               R * W * 4, R * W * 4, R * W * d_v * 4, R * nch * 32 * d_v * 6, V * d_v * ew,
+               R * Vt * W * 4, R * W * nvg * 16, R * W * 4, R * 16, R * Vt * W * 4, R * W * 4,
+               R * groups * 4, R * groups * 32 * 4, R * W * 32 * 4, 64 * 4]
     return sum(_a(x) for x in regions)
 
 
@@ -78,7 +82,8 @@ def test_persistent_state_is_gtr_capacity_and_beats_fullstate():
     assert gtr_bytes == 4 * cap["state"] + wl.T * wl.W_max * (4 * (1 + wl.d_v) + e * wl.d_k)
     ws = B.gdn_beam_workspace_bytes(B.make_config(1, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V))
     fullstate = wl.H * wl.W_max * wl.d_v * wl.d_k * 4
-    # the GDN state alone is about 20x smaller; the selection scratch (W x V scores) is extra
+    # the GDN state alone is about 20x smaller; the selection scratch (W x V / 32 tile
+    # maxima) is extra
     assert wl.H * gtr_bytes * 18 < fullstate
     assert ws < fullstate
 
@@ -90,7 +95,9 @@ def test_workspace_does_not_grow_with_dv_dk_w():
     R, H, T, d, V = 2, 3, 4, 128, 1024
     records = H * T * (4 + 4 * d + 2 * d)              # GTR slots of every head
     beam_state = 4 * T * 4 + 2 * 4                     # ancestry + SID prefixes, scores
-    scoring = 4 * d + 4 * V + 16 * (V // 128) + 4 + 8 + 4 * V   # z, logits, lse parts, lse, winners, ties
+    # z (fp32 and operand), tile maxima, lse parts, lse, kept tiles, chosen tiles,
+    # groups and their tiles, refined keys
+    scoring = 4 * d + 6 * d + 4 * (V // 32) + 16 * (V // 128) + 4 + 4 * (V // 32) + 4 + 4 + 128 + 128
     per_w = R * (records + beam_state + scoring)
     assert b2 - b1 <= 256 * per_w + 20 * 256
     assert b2 - b1 < 256 * 128 * 128 * 4
