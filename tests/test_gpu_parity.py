@@ -18,6 +18,25 @@ from gpu_harness import GpuDecode, TOL, check_selection, rel_err, say, to_np
 
 pytestmark = pytest.mark.gpu
 
+# Shapes the named workloads do not reach, derived from them: a codebook that is not a
+# multiple of the 32-code tile, beam counts that are not multiples of 32, fewer
+# (beam, tile) pairs than the next beam count, and enough tied keys to exceed the
+# final select's on-chip list.
+DERIVED = {
+    "tiny_v37": ("tiny", dict(V=37)),
+    "tiny_odd_w": ("tiny", dict(widths=(5, 13, 7), V=37)),
+    "tiny_few_tiles": ("tiny", dict(widths=(4, 8, 16), V=32)),
+    "single_v300": ("single", dict(V=300)),
+    "ties_w512": ("tiny", dict(widths=(512, 512, 512), V=64)),
+}
+
+
+def _wl(name):
+    if name in DERIVED:
+        base, kw = DERIVED[name]
+        return synth.get(base).scaled(name=name, **kw)
+    return synth.get(name)
+
 
 def _eq9(anc, parent, t):
     return oracle.ancestry_update(anc, parent, t)
@@ -86,11 +105,12 @@ def test_forced_parents_parity(name, R):
     assert g.export(B.GDN_EXPORT_STATUS)[0] == 0
 
 
-@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2)])
+@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_v37", 1),
+                                    ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("single_v300", 1)])
 def test_select_mode_parity(name, R):
     """Top-W drives the beams.  The oracle follows the GPU's choice (teacher forcing)
     after the selection itself has been checked against the exact top-W."""
-    wl = synth.get(name)
+    wl = _wl(name)
     g = GpuDecode(wl, R=R, exact=range(R))
     tol = TOL[wl.io]
     decs = {r: oracle.FullStateDecoder(g.S_exact[r].astype(np.float64), wl.width(0)) for r in range(R)}
@@ -207,11 +227,11 @@ def test_full_size_select_properties(name):
             assert np.array_equal(anc[r][:K, :t + 1], anc_ref[r]), f"ancestry r={r} t={t}"
 
 
-@pytest.mark.parametrize("name", ["tiny", "single"])
+@pytest.mark.parametrize("name", ["tiny", "single", "ties_w512"])
 def test_all_scores_tied(name):
     """Wout = 0: every candidate of a request scores cum - log V; the top-W is then the
     W smallest flat indices, in order (the tie-break), at every step."""
-    wl = synth.get(name)
+    wl = _wl(name)
     g = GpuDecode(wl, R=1, exact=(0,))
     g.Wout.zero_()
     g.Wout64[:] = 0
