@@ -105,8 +105,9 @@ def kernel_hash():
 
 
 def load_traffic(wl_name):
-    """HBM bytes per step-kernel launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source."""
+    """HBM bytes of the step kernel per decode (summed over its T launches, like
+    bytes_per_decode) from committed rocprofv3 counter runs, if they were taken on the
+    current kernel source."""
     f = os.path.join(ROOT, "profiles", f"step_kernel_{wl_name}_traffic.json")
     if not os.path.exists(f):
         return None
@@ -116,7 +117,7 @@ def load_traffic(wl_name):
         return None
     if d.get("kernel_sha") != kernel_hash():
         return None
-    return d.get("bytes_per_launch")
+    return d.get("bytes_per_decode")
 
 
 def cpu_baseline(args, wl):

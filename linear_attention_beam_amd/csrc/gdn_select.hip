@@ -135,13 +135,15 @@ __global__ void __launch_bounds__(256) zsum_kernel(ZsumK a) {
 // A = codebook rows (codes c0 + lane % 32), B = z columns (32 beams); lane half hf
 // holds elements d_v/2 * hf + ...  acc[i] -> code c0 + 8 (i / 4) + 4 hf + i % 4,
 // beam = column lane % 32.  Both passes call exactly these, so a candidate's logit has
-// the same bits in both.
+// the same bits in both.  Rows past the codebook load code 0 and columns past the
+// beams load beam 0 of the chunk: MFMA rows and columns are independent, and those
+// results are never used.
 template <int DV>
 __device__ __forceinline__ void load_codes_bf16(const u32x4* wt, int code, int V, int hf, u32x4* w) {
   constexpr int KS = DV / 16, HV = DV / 2;
   const size_t row = size_t(code < V ? code : 0) * DV + HV * hf;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) w[kk] = code < V ? wt[row / 8 + kk] : u32x4{};
+  for (int kk = 0; kk < KS; ++kk) w[kk] = wt[row / 8 + kk];
 }
 
 template <int KS>
@@ -161,12 +163,11 @@ template <int DV>
 __device__ __forceinline__ f32x16 block_mfma_f32(const float* wt, int code, int V, int hf,
                                                  const float* zv) {
   constexpr int HV = DV / 2;
-  const bool cv = code < V;
-  const float* wr = wt + size_t(cv ? code : 0) * DV + HV * hf;
+  const float* wr = wt + size_t(code < V ? code : 0) * DV + HV * hf;
   f32x16 acc = {};
 #pragma unroll
   for (int kk = 0; kk < HV; ++kk)
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(cv ? wr[kk] : 0.0f, zv[kk], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wr[kk], zv[kk], acc, 0, 0, 0);
   return acc;
 }
 
@@ -182,28 +183,41 @@ struct LogitsK {
   float4* lse_part;      // [R,W_max,nvg]: max, sum of exp(x - max), min tile max
 };
 
-// One wave: 32 beams x cpw codes.  Lane l keeps beam l % 32 and folds its 16 codes of
-// every tile into the tile maximum (with its partner half) and a running log-sum-exp.
+// Beam chunks (waves) per first-pass block; the block shares one code group.
+constexpr int kLogitsWaves = 8;
+
+// Block: kLogitsWaves chunks of 32 beams x one group of cpw codes.  Each 32-code tile of
+// the codebook is staged once per block in LDS (double-buffered, one barrier per tile)
+// and read by every wave as its A operand.  Lane l keeps beam l % 32 and folds its 16
+// codes of every tile into the tile maximum (with its partner half) and a running
+// log-sum-exp.  Waves past the last chunk follow the barriers and store nothing.
 template <int DV, bool WBF16>
-__global__ void __launch_bounds__(256) logits_kernel(LogitsK a) {
+__global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   constexpr int HV = DV / 2;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int vg = blockIdx.x % a.nvg;
+  const int chunk = (blockIdx.x / a.nvg) * kLogitsWaves + wave;
+  const bool wvalid = chunk < a.nchunk;
   const int r = blockIdx.y;
-  if (gw >= a.nchunk * a.nvg) return;
-  const int chunk = gw / a.nvg, vg = gw % a.nvg;
   const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
-  const int b = chunk * 32 + m;
-  const bool bvalid = b < a.W;
+  const int b = (wvalid ? chunk : 0) * 32 + m;
+  const bool bvalid = wvalid && b < a.W;
   float* tm_r = a.tmax + size_t(r) * a.tmax_stride;
   const int code_lo = vg * a.cpw;
   const int code_hi = min(a.V, code_lo + a.cpw);
 
   float mrun = -INFINITY, srun = 0.0f, nrun = INFINITY;
   auto fold = [&](const f32x16& acc, int c0) {
+    const bool full = c0 + 32 <= a.V;              // block-uniform
     float tm = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (c0 + 8 * (i >> 2) + 4 * hf + (i & 3) < a.V) tm = fmaxf(tm, acc[i]);
+      for (int i = 0; i < 16; ++i) tm = fmaxf(tm, acc[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (c0 + 8 * (i >> 2) + 4 * hf + (i & 3) < a.V) tm = fmaxf(tm, acc[i]);
+    }
     tm = fmaxf(tm, __shfl_xor(tm, 32));            // code c0 is valid: tm is finite
     if (hf == 0 && bvalid) tm_r[size_t(c0 >> 5) * a.W + b] = tm;
     nrun = fminf(nrun, tm);
@@ -211,15 +225,48 @@ __global__ void __launch_bounds__(256) logits_kernel(LogitsK a) {
       srun = mrun == -INFINITY ? 0.0f : srun * __builtin_amdgcn_exp2f((mrun - tm) * kLog2e);
       mrun = tm;
     }
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (c0 + 8 * (i >> 2) + 4 * hf + (i & 3) < a.V)
-        srun += __builtin_amdgcn_exp2f((acc[i] - mrun) * kLog2e);
+      for (int i = 0; i < 16; ++i) srun += __builtin_amdgcn_exp2f((acc[i] - mrun) * kLog2e);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (c0 + 8 * (i >> 2) + 4 * hf + (i & 3) < a.V)
+          srun += __builtin_amdgcn_exp2f((acc[i] - mrun) * kLog2e);
+    }
   };
 
   if constexpr (WBF16) {
     constexpr int KS = DV / 16;
-    const u32x4* zb = a.zf + zf_lane_base(r, a.nch_max, DV, chunk * 32, hf) + m;
+    constexpr int RS = DV / 8 + 1;                 // LDS row stride in u32x4 (16 B pad)
+    constexpr int NE = 32 * DV / 8;                // u32x4 per codebook tile
+    constexpr int PT = (NE + 64 * kLogitsWaves - 1) / (64 * kLogitsWaves);
+    __shared__ u32x4 tile[2][32 * RS];
+    const u32x4* wt = static_cast<const u32x4*>(a.woutT);
+    // thread e-th entry of a tile: row e / (DV / 8), column e % (DV / 8); rows past the
+    // codebook load code 0 (never used)
+    u32x4 stg[PT];
+    auto fetch = [&](int c0) {
+#pragma unroll
+      for (int u = 0; u < PT; ++u) {
+        const int e = threadIdx.x + u * 64 * kLogitsWaves;
+        if (e < NE) {
+          const int row = c0 + e / (DV / 8);
+          stg[u] = wt[size_t(row < a.V ? row : 0) * (DV / 8) + e % (DV / 8)];
+        }
+      }
+    };
+    auto put = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < PT; ++u) {
+        const int e = threadIdx.x + u * 64 * kLogitsWaves;
+        if (e < NE) tile[buf][(e / (DV / 8)) * RS + e % (DV / 8)] = stg[u];
+      }
+    };
+    // the first tile's loads go out before the z operand's (loads complete in order, so
+    // staging the tile then waits for those alone)
+    fetch(code_lo);
+    const u32x4* zb = a.zf + zf_lane_base(r, a.nch_max, DV, (wvalid ? chunk : 0) * 32, hf) + m;
     u32x4 zh[KS], zm[KS], zl[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -227,14 +274,22 @@ __global__ void __launch_bounds__(256) logits_kernel(LogitsK a) {
       zm[kk] = zb[(3 * kk + 1) * 64];
       zl[kk] = zb[(3 * kk + 2) * 64];
     }
-    const u32x4* wt = static_cast<const u32x4*>(a.woutT);
-    u32x4 wcur[KS], wnext[KS];
-    load_codes_bf16<DV>(wt, code_lo + m, a.V, hf, wcur);
+    put(0);
+    // wait for the whole z operand here, so that inside the loop only the prefetched
+    // tile is waited for, after the MFMAs
+    asm volatile("" ::"v"(zl[KS - 1][0]));
+    __syncthreads();
+    int buf = 0;
     for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
-      if (c0 + 32 < code_hi) load_codes_bf16<DV>(wt, c0 + 32 + m, a.V, hf, wnext);
-      fold(block_mfma_bf16<KS>(wcur, zh, zm, zl), c0);
+      const bool more = c0 + 32 < code_hi;         // block-uniform
+      if (more) fetch(c0 + 32);
+      u32x4 w[KS];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) wcur[kk] = wnext[kk];
+      for (int kk = 0; kk < KS; ++kk) w[kk] = tile[buf][m * RS + (HV / 8) * hf + kk];
+      fold(block_mfma_bf16<KS>(w, zh, zm, zl), c0);
+      if (more) put(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
     }
   } else {
     const float* zr = a.z + (size_t(r) * a.W_max + (bvalid ? b : 0)) * DV + HV * hf;
@@ -296,10 +351,19 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
 // Block of 1024 threads, hist[2048] complete: find the digit of [lo, lo + 2048 << shift)
 // that holds the need-th largest key and leave in sh its range, the count still to take
 // inside it and the next digit width (-1 once the digit is a single value).  Thread t
-// owns digits 2047 - 2t and 2046 - 2t: the keys above them are a prefix sum.
+// owns digits 2047 - 2t and 2046 - 2t: the keys above them are a prefix sum.  If the
+// histogram holds fewer than `need` keys (inconsistent input, e.g. NaN scores), sh ends
+// the search (shift -1, nothing more to take): every caller's loop terminates and the
+// shortfall shows up as fewer winners than asked for.
 __device__ void pick_digit(const uint32_t* hist, uint32_t* wsum, uint32_t lo, uint32_t hi, int shift,
                            uint32_t need, RadixSh& sh) {
   const int tid = threadIdx.x;
+  if (tid == 0) {
+    sh.lo = lo;
+    sh.hi = lo;
+    sh.need = 0u;
+    sh.shift = -1;
+  }
   const uint32_t c0 = hist[kHistBins - 1 - 2 * tid], c1 = hist[kHistBins - 2 - 2 * tid];
   uint32_t total;
   uint32_t above = block_excl_scan(c0 + c1, wsum, total);
@@ -495,7 +559,9 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
       }
     }
   };
-  stream([&](uint32_t key, int) { atomicAdd(&hist[(key - kmin) >> shift0], 1u); });
+  stream([&](uint32_t key, int) {
+    if (key >= kmin && key <= kmax) atomicAdd(&hist[(key - kmin) >> shift0], 1u);
+  });
   __syncthreads();
   pick_digit(hist, wsum, kmin, kmax, shift0, K, sh);
   const uint32_t lo = sh.lo, hi = sh.hi;
@@ -596,12 +662,13 @@ __global__ void __launch_bounds__(256, 2) refine_kernel(RefineK a) {
   const int r = blockIdx.y;
   const int g = blockIdx.x * 4 + (threadIdx.x >> 6);      // < G_max by the launch
   const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
+  // no early exit: the three loads issue together; a wave past the last group works
+  // on clamped operands and stores nothing
   const uint32_t ng = a.sel[r].n_groups;
   const uint32_t desc = a.groups[size_t(r) * a.G_max + g];
   const uint32_t f = a.gtiles[(size_t(r) * a.G_max + g) * 32 + m];
-  if (g >= int(ng)) return;
   const int start = int(desc & 1023u), cnt = int((desc >> 10) & 63u), j = int(desc >> 16);
-  const bool valid = m < cnt;
+  const bool valid = g < int(ng) && m < cnt;
   const int b = valid ? int(f / uint32_t(a.Vt)) : 0;
   const int c0 = 32 * j;
   f32x16 acc;
@@ -619,27 +686,34 @@ __global__ void __launch_bounds__(256, 2) refine_kernel(RefineK a) {
       u32x4 zh[KP], zm[KP], zl[KP], w[KP];
 #pragma unroll
       for (int kk = 0; kk < KP; ++kk) {
-        zh[kk] = valid ? zb[(3 * (k0 + kk)) * 64] : u32x4{};
-        zm[kk] = valid ? zb[(3 * (k0 + kk) + 1) * 64] : u32x4{};
-        zl[kk] = valid ? zb[(3 * (k0 + kk) + 2) * 64] : u32x4{};
-        w[kk] = code < a.V ? wt[row / 8 + k0 + kk] : u32x4{};
+        zh[kk] = zb[(3 * (k0 + kk)) * 64];
+        zm[kk] = zb[(3 * (k0 + kk) + 1) * 64];
+        zl[kk] = zb[(3 * (k0 + kk) + 2) * 64];
+        w[kk] = wt[row / 8 + k0 + kk];
       }
+      __builtin_amdgcn_sched_barrier(0);          // every operand load issued before the MFMAs
       acc = block_mfma_bf16<KP>(w, zh, zm, zl, acc);
     }
   } else {
     const float* zr = a.z + (size_t(r) * a.W_max + b) * DV + HV * hf;
     float zv[HV];
 #pragma unroll
-    for (int i = 0; i < HV; ++i) zv[i] = valid ? zr[i] : 0.0f;
+    for (int i = 0; i < HV; ++i) zv[i] = zr[i];
     acc = block_mfma_f32<DV>(static_cast<const float*>(a.woutT), c0 + m, a.V, hf, zv);
   }
   if (valid) {
+    // lane half hf holds codes 8 q + 4 hf + (0..3): four 16-byte runs of the row
     const float cb = a.cum[size_t(r) * a.W_max + b], lb = a.lse[size_t(r) * a.W_max + b];
-    uint32_t* out = a.rkeys + (size_t(r) * a.W_max + start + m) * kTile;
+    u32x4* out = reinterpret_cast<u32x4*>(a.rkeys + (size_t(r) * a.W_max + start + m) * kTile);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int o = 8 * (i >> 2) + 4 * hf + (i & 3);
-      out[o] = c0 + o < a.V ? f2key(cand_score(cb, acc[i], lb)) : 0u;
+    for (int q = 0; q < 4; ++q) {
+      u32x4 kq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = f2key(cand_score(cb, acc[4 * q + e], lb));
+        kq[e] = c0 + 8 * q + 4 * hf + e < a.V ? key : 0u;
+      }
+      out[2 * q + hf] = kq;
     }
   }
 }
@@ -870,9 +944,9 @@ static int launch_dv(const SelectArgs& a, const LogitsK& lk, const RefineK& rk, 
                      hipStream_t s, bool refine) {
   const bool bf = a.wout_dtype == GDN_BF16;
   if (!refine) {
-    dim3 grid((lk.nchunk * lk.nvg + 3) / 4, a.R);
-    if (bf) hipLaunchKernelGGL((logits_kernel<DV, true>), grid, dim3(256), 0, s, lk);
-    else hipLaunchKernelGGL((logits_kernel<DV, false>), grid, dim3(256), 0, s, lk);
+    dim3 grid(((lk.nchunk + kLogitsWaves - 1) / kLogitsWaves) * lk.nvg, a.R);
+    if (bf) hipLaunchKernelGGL((logits_kernel<DV, true>), grid, dim3(64 * kLogitsWaves), 0, s, lk);
+    else hipLaunchKernelGGL((logits_kernel<DV, false>), grid, dim3(64 * kLogitsWaves), 0, s, lk);
   } else {
     dim3 grid((groups + 3) / 4, a.R);
     if (bf) hipLaunchKernelGGL((refine_kernel<DV, true>), grid, dim3(256), 0, s, rk);
