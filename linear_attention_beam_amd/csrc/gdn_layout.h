@@ -35,6 +35,8 @@ struct Layout {
   size_t anc[2];      // [R,W_max,T_max] i32, ping-pong by step parity
   size_t tok[2];      // [R,W_max,T_max] i32
   size_t cum[2];      // [R,W_max] f32
+  size_t order[2];    // [R,W_max] i32 beam processing order of a step (siblings adjacent)
+  size_t opos[2];     // [R,W_max] i32 position of each beam in that order
   size_t z;           // [R,W_max,d_v] f32  head-summed outputs (fp32 codebook)
   size_t zf;          // [R,n_chunks(W_max),d_v/16,3,64] u32x4: z as bf16 hi/mid/lo MFMA operand
   size_t woutT;       // [V_max,d_v] wout dtype, codebook transposed
@@ -82,6 +84,8 @@ inline Layout make_layout(const gdn_beam_config& c) {
   for (int i = 0; i < 2; ++i) L.anc[i] = take(R * W * T * 4);
   for (int i = 0; i < 2; ++i) L.tok[i] = take(R * W * T * 4);
   for (int i = 0; i < 2; ++i) L.cum[i] = take(R * W * 4);
+  for (int i = 0; i < 2; ++i) L.order[i] = take(R * W * 4);
+  for (int i = 0; i < 2; ++i) L.opos[i] = take(R * W * 4);
   const size_t Vt = size_t(n_tiles(c.V_max));
   L.z = take(R * W * dv * 4);
   L.zf = take(R * size_t(n_chunks(c.W_max)) * 32 * dv * 6);

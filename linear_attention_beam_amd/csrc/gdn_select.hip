@@ -732,6 +732,9 @@ struct FinK {
   int32_t* anc_next;
   const int32_t* tok;
   int32_t* tok_next;
+  const int32_t* opos;     // [R,W_max] position of each beam in step t's processing order
+  int32_t* order_next;     // [R,W_max] processing order of step t + 1
+  int32_t* opos_next;
   const float* z;
   const u32x4* zf;
   const void* woutT;
@@ -899,6 +902,7 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
   // thread i holds rank i
   const float* lse = a.lse + size_t(r) * a.W_max;
   const float* cum = a.cum + size_t(r) * a.W_max;
+  int okey = 0;                                           // parent's position (order below)
   if (tid < a.K) {
     const int i = tid;
     const uint32_t flat = 0xFFFFFFFFu - uint32_t(v);
@@ -934,6 +938,24 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
       tn[j] = j < a.t ? tp[j] : (j == a.t ? fc : 0);
     }
     a.cum_next[size_t(r) * a.W_max + i] = fs;
+    okey = a.t == 0 ? fp : a.opos[size_t(r) * a.W_max + fp];
+  }
+  // processing order of step t + 1: a counting sort of the beams by their parent's
+  // position in step t's order, so children of one parent are adjacent and subtrees
+  // stay contiguous (any order is correct; this one makes shared records cache hits)
+  __syncthreads();
+  u.hist[tid] = 0u;
+  __syncthreads();
+  if (tid < a.K) atomicAdd(&u.hist[okey], 1u);
+  __syncthreads();
+  uint32_t total;
+  const uint32_t start = block_excl_scan(u.hist[tid], wsum, total);
+  u.hist[tid] = start;
+  __syncthreads();
+  if (tid < a.K) {
+    const uint32_t p = atomicAdd(&u.hist[okey], 1u);
+    a.order_next[size_t(r) * a.W_max + p] = tid;
+    a.opos_next[size_t(r) * a.W_max + tid] = int32_t(p);
   }
 }
 
@@ -993,6 +1015,9 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   int32_t* tok = reinterpret_cast<int32_t*>(ws + L.tok[par]);
   int32_t* tok_next = reinterpret_cast<int32_t*>(ws + L.tok[par ^ 1]);
   int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
+  const int32_t* opos = reinterpret_cast<const int32_t*>(ws + L.opos[par]);
+  int32_t* order_next = reinterpret_cast<int32_t*>(ws + L.order[par ^ 1]);
+  int32_t* opos_next = reinterpret_cast<int32_t*>(ws + L.opos[par ^ 1]);
   int err;
 
   {  // head sum into the MFMA operand; codebook transpose in the last grid row
@@ -1025,7 +1050,8 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   }
   {
     FinK k{a.W, a.W_max, a.V, Vt, a.W_next, Kt, a.T_max, a.t, a.d_v, nch_max, split, sel, rkeys, tiles,
-           lse, cum, cum_next, anc, anc_next, tok, tok_next, z, zf, woutT, a.forced_parent,
+           lse, cum, cum_next, anc, anc_next, tok, tok_next, opos, order_next, opos_next, z, zf,
+           woutT, a.forced_parent,
            a.forced_token, a.parent, a.token, a.score, status};
     hipLaunchKernelGGL(final_kernel, dim3(a.R), dim3(1024), 0, s, k);
     if ((err = last_launch_error())) return err;

@@ -84,6 +84,7 @@ struct StepK {
   float* gtr_delta;
   void* gtr_key;
   const int32_t* anc;
+  const int32_t* order;    // [R,W_max] processing order of the beams (steps t >= 1)
 };
 
 // Sizes of the fused step for head dims (DK, DV) and io dtype.
@@ -138,6 +139,9 @@ __device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float s) 
 //   per wave U = S_block [q|k] on MFMA (B fragments from LDS), then eqs. (6)-(7) on
 //            the accumulators and eq. (8); delta_t and o_t stored;
 //   append   k_t rows copied from LDS to slot (t, b) of the record pool, alpha_t.
+// From t = 1 on, chunks take the beams in the order the selection left (children of
+// one parent adjacent, subtrees contiguous), so the records that siblings and cousins
+// share are gathered back to back, from cache.
 template <int DK, int DV, bool BF16, int TT>
 __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(StepK a) {
   using C = StepCfg<DK, DV, BF16>;
@@ -148,6 +152,7 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
   constexpr int HK = DK / 2;
   constexpr int SCN = 1 + 3 * NJ;                        // kq, alpha_j, cq_j, ck_j
   __shared__ __align__(16) unsigned char lds[2 * C::SLOT + 32 * SCN * 4];
+  __shared__ int ord[NJ > 0 ? kMaxW : 1];
   float* sc = reinterpret_cast<float*>(lds + 2 * C::SLOT);
 
   const int rh = xcd_work_id();
@@ -161,6 +166,14 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
   const unsigned char* kg = static_cast<const unsigned char*>(a.k);
   const unsigned char* vg = static_cast<const unsigned char*>(a.v);
   unsigned char* keyg = static_cast<unsigned char*>(a.gtr_key);
+
+  if constexpr (NJ > 0) {
+    for (int i = tid; i < W; i += NT) {
+      const int x = a.order[size_t(r) * a.W_max + i];
+      ord[i] = x < 0 ? 0 : (x >= W ? W - 1 : x);
+    }
+  }
+  auto beam_of = [&](int x) { return NJ > 0 ? ord[x] : x; };
 
   // this wave's block of S_ctx as A fragments (layout written by init_kernel)
   constexpr int NA = BF16 ? 2 * (DK / 16) : DK / 8;
@@ -178,25 +191,31 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
   int sanc[NAI];
   auto stage_load = [&](int c) {
     const int c0 = c * 32, nb = min(32, W - c0);
-    const size_t base = size_t(rh) * W + c0;
+    const size_t base = size_t(rh) * W;
 #pragma unroll
     for (int i = 0; i < C::QU; ++i) {
       const int u = tid + i * NT;
       if (u / UPQ < nb) {
-        sq[i] = *reinterpret_cast<const u32x4*>(qg + base * C::QB + size_t(u) * 16);
-        sk[i] = *reinterpret_cast<const u32x4*>(kg + base * C::QB + size_t(u) * 16);
+        const size_t row = base + beam_of(c0 + u / UPQ);
+        sq[i] = *reinterpret_cast<const u32x4*>(qg + row * C::QB + size_t(u % UPQ) * 16);
+        sk[i] = *reinterpret_cast<const u32x4*>(kg + row * C::QB + size_t(u % UPQ) * 16);
       }
     }
 #pragma unroll
     for (int i = 0; i < C::VU; ++i) {
       const int u = tid + i * NT;
-      if (u / UPV < nb) sv[i] = *reinterpret_cast<const u32x4*>(vg + base * C::VB + size_t(u) * 16);
+      if (u / UPV < nb)
+        sv[i] = *reinterpret_cast<const u32x4*>(vg + (base + beam_of(c0 + u / UPV)) * C::VB + size_t(u % UPV) * 16);
     }
-    if (tid < 64 && (tid & 31) < nb) sab = tid < 32 ? a.alpha[base + tid] : a.beta[base + tid - 32];
+    if (tid < 64 && (tid & 31) < nb) {
+      const size_t bi = base + beam_of(c0 + (tid & 31));
+      sab = tid < 32 ? a.alpha[bi] : a.beta[bi];
+    }
 #pragma unroll
     for (int i = 0; i < NAI; ++i) {
       const int e = tid + i * NT, bb = e / NJ1, j = e % NJ1;
-      if (NJ > 0 && e < 32 * NJ && bb < nb) sanc[i] = a.anc[(size_t(r) * a.W_max + c0 + bb) * a.T_max + j];
+      if (NJ > 0 && e < 32 * NJ && bb < nb)
+        sanc[i] = a.anc[(size_t(r) * a.W_max + beam_of(c0 + bb)) * a.T_max + j];
     }
   };
   auto stage_store = [&](int slot) {
@@ -225,6 +244,7 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     }
   };
 
+  if constexpr (NJ > 0) __syncthreads();                  // ord complete
   stage_load(0);
   stage_store(0);
   __syncthreads();
@@ -254,7 +274,7 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
         kj[j][i] = *reinterpret_cast<const u32x4*>(keyg + rec * C::QB + sg * C::SEGB + 16 * i);
     }
     const bool valid = m < nb;
-    const int b = c0 + m;
+    const int b = valid ? beam_of(c0 + m) : 0;
     const int row0 = 32 * w + 16 * hf;
     const int rowl = min(row0, DV - 16);                 // in range (rows >= DV unused)
     f32x4 dj[NJ1][4];
@@ -386,13 +406,12 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
       }
     }
 
-    // ---- append: k_t rows (contiguous slots c0..c0+nb-1) and alpha_t
+    // ---- append: k_t rows to slots (t, b) of the chunk's beams, and alpha_t
     {
-      unsigned char* dst = keyg + (slot_t * a.W_max + c0) * C::QB;
       for (int u = tid; u < nb * UPQ; u += NT)
-        *reinterpret_cast<u32x4*>(dst + size_t(u) * 16) =
+        *reinterpret_cast<u32x4*>(keyg + (slot_t * a.W_max + beam_of(c0 + u / UPQ)) * C::QB + (u % UPQ) * 16) =
             *reinterpret_cast<const u32x4*>(Lk + (u / UPQ) * QROW + (u % UPQ) * 16);
-      if (tid < nb) a.gtr_alpha[slot_t * a.W_max + c0 + tid] = Lab[tid];
+      if (tid < nb) a.gtr_alpha[slot_t * a.W_max + beam_of(c0 + tid)] = Lab[tid];
     }
     if (c + 1 < nch) stage_store((c + 1) & 1);
     __syncthreads();
@@ -469,7 +488,8 @@ static int launch_step_t(const StepArgs& a, hipStream_t s) {
   StepK k{a.H, a.W, a.W_max, a.T_max, a.t, nrh, a.q, a.k, a.v, a.alpha, a.beta, a.o,
           ws + a.L.s_frag, reinterpret_cast<float*>(ws + a.L.gtr_alpha),
           reinterpret_cast<float*>(ws + a.L.gtr_delta), ws + a.L.gtr_key,
-          reinterpret_cast<const int32_t*>(ws + a.L.anc[a.t & 1])};
+          reinterpret_cast<const int32_t*>(ws + a.L.anc[a.t & 1]),
+          reinterpret_cast<const int32_t*>(ws + a.L.order[a.t & 1])};
   switch (a.t) {
     case 0: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 0>), dim3(grid), dim3(NT), 0, s, k); break;
     case 1: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 1>), dim3(grid), dim3(NT), 0, s, k); break;

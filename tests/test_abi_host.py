@@ -55,7 +55,7 @@ def expected_bytes(R, H, d_k, d_v, T, W, V, e, ew):
     groups = nch + 1 + min(Vt, W)
     regions = [R * H * 4 * dvp * d_k, R * H * T * W * 4, R * H * T * W * d_v * 4,
                R * H * T * W * d_k * e, R * W * T * 4, R * W * T * 4, R * W * T * 4, R * W * T * 4,
-               R * W * 4, R * W * 4, R * W * d_v * 4, R * nch * 32 * d_v * 6, V * d_v * ew,
+               R * W * 4, R * W * 4, R * W * 4, R * W * 4, R * W * 4, R * W * 4, R * W * d_v * 4, R * nch * 32 * d_v * 6, V * d_v * ew,
                R * Vt * W * 4, R * W * nvg * 16, R * W * 4, R * 16, R * Vt * W * 4, R * W * 4,
                R * groups * 4, R * groups * 32 * 4, R * W * 32 * 4, 64 * 4]
     return sum(_a(x) for x in regions)
@@ -94,7 +94,7 @@ def test_workspace_does_not_grow_with_dv_dk_w():
     b2 = B.gdn_beam_workspace_bytes(_cfg(W_max=512))
     R, H, T, d, V = 2, 3, 4, 128, 1024
     records = H * T * (4 + 4 * d + 2 * d)              # GTR slots of every head
-    beam_state = 4 * T * 4 + 2 * 4                     # ancestry + SID prefixes, scores
+    beam_state = 4 * T * 4 + 2 * 4 + 4 * 4             # ancestry + SID prefixes, scores, order
     # z (fp32 and operand), tile maxima, lse parts, lse, kept tiles, chosen tiles,
     # groups and their tiles, refined keys
     scoring = 4 * d + 6 * d + 4 * (V // 32) + 16 * (V // 128) + 4 + 4 * (V // 32) + 4 + 4 + 128 + 128
