@@ -44,6 +44,7 @@ __device__ __forceinline__ size_t zf_lane_base(int r, int nch_max, int d_v, int 
 
 struct ZsumK {
   int R, H, W, W_max, d_v, V, nch_max;
+  int zblocks;          // blocks of the head sum; the blocks after them transpose
   int split;            // bf16 codebook: write zf; fp32 codebook: write z
   const float* o;       // [R,H,W,d_v]
   float* z;             // [R,W_max,d_v]
@@ -52,13 +53,14 @@ struct ZsumK {
   void* woutT;          // [V,d_v]
 };
 
-// 32 x 32 tiles of Wout[d_v,V] -> Wout^T[V,d_v] through LDS, one tile per step.
+// 32 x 32 tiles of Wout[d_v,V] -> Wout^T[V,d_v] through LDS, tiles t0, t0 + nb, ...
 template <typename WT>
-__device__ void transpose_codebook(const WT* __restrict__ w, WT* __restrict__ wt, int d_v, int V) {
+__device__ void transpose_codebook(const WT* __restrict__ w, WT* __restrict__ wt, int d_v, int V,
+                                   int t0, int nb) {
   __shared__ WT tile[32][33];
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 256 threads: 32 x 8
   const int ntc = (V + 31) / 32, nt = ntc * ((d_v + 31) / 32);
-  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+  for (int t = t0; t < nt; t += nb) {
     const int c0 = (t % ntc) * 32, i0 = (t / ntc) * 32;
     for (int y = ty; y < 32; y += 8) {
       const int i = i0 + y, c = c0 + tx;
@@ -73,37 +75,39 @@ __device__ void transpose_codebook(const WT* __restrict__ w, WT* __restrict__ wt
   }
 }
 
-// Rows y < R: one thread per 8 consecutive elements of one beam (beams padded to a
-// multiple of 32 with zeros); the head sum runs in head order.  Row y = R: codebook
+// Blocks [0, zblocks): one thread per 8 consecutive elements of one beam of one
+// request (beams padded to a multiple of 32 with zeros); all heads' loads are in
+// flight at once (up to 16), the sum runs in head order.  Later blocks: codebook
 // transpose.
 __global__ void __launch_bounds__(256) zsum_kernel(ZsumK a) {
-  const int r = blockIdx.y;
-  if (r == a.R) {
+  if (int(blockIdx.x) >= a.zblocks) {
+    const int t0 = blockIdx.x - a.zblocks, nb = gridDim.x - a.zblocks;
     if (a.split)
-      transpose_codebook(static_cast<const uint16_t*>(a.wout), static_cast<uint16_t*>(a.woutT), a.d_v, a.V);
+      transpose_codebook(static_cast<const uint16_t*>(a.wout), static_cast<uint16_t*>(a.woutT), a.d_v, a.V, t0, nb);
     else
-      transpose_codebook(static_cast<const float*>(a.wout), static_cast<float*>(a.woutT), a.d_v, a.V);
+      transpose_codebook(static_cast<const float*>(a.wout), static_cast<float*>(a.woutT), a.d_v, a.V, t0, nb);
     return;
   }
   const int g8 = a.d_v / 8, HV = a.d_v / 2;
-  const int n = ((a.W + 31) & ~31) * g8;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
-    const int b = i / g8, d0 = 8 * (i % g8);
+  const int per_req = ((a.W + 31) & ~31) * g8;
+  const int n = a.R * per_req;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += a.zblocks * blockDim.x) {
+    const int r = i / per_req, e = i % per_req;
+    const int b = e / g8, d0 = 8 * (e % g8);
     f32x4 s0 = {}, s1 = {};
     if (b < a.W) {
-      // heads eight at a time: all loads of a batch in flight, then the sums in head order
       const float* p0 = a.o + (size_t(r) * a.H * a.W + b) * a.d_v + d0;
       const size_t hstride = size_t(a.W) * a.d_v;
-      for (int h0 = 0; h0 < a.H; h0 += 8) {
-        f32x4 x0[8], x1[8];
+      for (int h0 = 0; h0 < a.H; h0 += 16) {
+        f32x4 x0[16], x1[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const float* p = p0 + size_t(h0 + u < a.H ? h0 + u : h0) * hstride;
           x0[u] = *reinterpret_cast<const f32x4*>(p);
           x1[u] = *reinterpret_cast<const f32x4*>(p + 4);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
           if (h0 + u < a.H) { s0 += x0[u]; s1 += x1[u]; }
       }
     }
@@ -495,6 +499,18 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   uint32_t* cand = a.cand + size_t(r) * a.stride;
   const size_t cap = size_t(Vt) * W;
 
+  // thread -> one beam b and every G-th tile from jg; its first U tiles are loaded now,
+  // under the log-sum-exp phase, and kept for both passes
+  constexpr int U = 16;
+  const int G = 1024 / W;
+  const bool act = tid < G * W;
+  const int b = act ? tid % W : 0, jg = act ? tid / W : 0;
+  float x0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int jj = jg + u * G;
+    x0[u] = act && jj < a.Vt ? tm[size_t(jj) * W + b] : 0.0f;
+  }
   if (tid == 0) { kmin_sh = 0xFFFFFFFFu; kmax_sh = 0u; nwin_sh = 0u; ncand_sh = 0u; }
   for (int i = tid; i < kHistBins; i += 1024) hist[i] = 0;
   __syncthreads();
@@ -537,15 +553,15 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   const uint32_t kmin = kmin_sh, kmax = kmax_sh;
   const int shift0 = first_shift(kmin, kmax);
 
-  // thread -> one beam b and every G-th tile from jg; loads issued U at a time
-  const int G = 1024 / W;
-  const bool act = tid < G * W;
-  const int b = act ? tid % W : 0, jg = act ? tid / W : 0;
   const float cb = cum_s[b], lb = lse_s[b];
   auto stream = [&](auto&& f) {
     if (!act) return;
-    constexpr int U = 16;
-    for (int j = jg; j < a.Vt; j += U * G) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = jg + u * G;
+      if (jj < a.Vt) f(f2key(cand_score(cb, x0[u], lb)), jj);
+    }
+    for (int j = jg + U * G; j < a.Vt; j += U * G) {
       float x[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -774,10 +790,76 @@ __device__ float forced_logit(const FinK& a, int r, int b, int c) {
 // the tile threshold (massive ties) are read from global memory instead.
 constexpr int kFinCap = 8192;
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(v)), m));
-  const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(v >> 32)), m));
-  return (uint64_t(hi) << 32) | lo;
+// Value of lane (lane ^ J) of the wave.  J = 1, 2: DPP quad permutes; 4: DPP row
+// shifts by 4 either way; 8: DPP row rotate by 8; 16: swizzle (xor mode); 32: LDS
+// permute.  The DPP forms are plain VALU moves.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, false));
+  else if constexpr (J == 2) return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xF, 0xF, false));
+  else if constexpr (J == 4) {
+    const uint32_t up = uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x104, 0xF, 0xF, false));
+    const uint32_t dn = uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x114, 0xF, 0xF, false));
+    return (threadIdx.x & 4) ? dn : up;
+  } else if constexpr (J == 8) return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x128, 0xF, 0xF, false));
+  else if constexpr (J == 16) return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), (16 << 10) | 0x1F));
+  else return uint32_t(__shfl_xor(int(v), 32));
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
+  return (uint64_t(lane_xor<J>(uint32_t(v >> 32))) << 32) | lane_xor<J>(uint32_t(v));
+}
+
+// One compare-exchange stage of a bitonic sort, one entry per thread of the block,
+// descending within blocks of k where (tid & k) == 0: partner tid ^ J inside the wave,
+// through LDS (two barriers) across waves.
+template <int J>
+__device__ __forceinline__ uint64_t bitonic_stage(uint64_t v, int k, uint64_t* xs) {
+  const int tid = threadIdx.x;
+  uint64_t o;
+  if constexpr (J >= 64) {
+    __syncthreads();
+    xs[tid] = v;
+    __syncthreads();
+    o = xs[tid ^ J];
+  } else {
+    o = lane_xor64<J>(v);
+  }
+  const bool desc = (tid & k) == 0, lower = (tid & J) == 0;
+  return (desc == lower) ? (v > o ? v : o) : (v < o ? v : o);
+}
+
+template <int LK>
+__device__ __forceinline__ uint64_t bitonic_merge(uint64_t v, uint64_t* xs) {
+  constexpr int k = 1 << LK;
+  if constexpr (LK >= 10) v = bitonic_stage<512>(v, k, xs);
+  if constexpr (LK >= 9) v = bitonic_stage<256>(v, k, xs);
+  if constexpr (LK >= 8) v = bitonic_stage<128>(v, k, xs);
+  if constexpr (LK >= 7) v = bitonic_stage<64>(v, k, xs);
+  if constexpr (LK >= 6) v = bitonic_stage<32>(v, k, xs);
+  if constexpr (LK >= 5) v = bitonic_stage<16>(v, k, xs);
+  if constexpr (LK >= 4) v = bitonic_stage<8>(v, k, xs);
+  if constexpr (LK >= 3) v = bitonic_stage<4>(v, k, xs);
+  if constexpr (LK >= 2) v = bitonic_stage<2>(v, k, xs);
+  v = bitonic_stage<1>(v, k, xs);
+  return v;
+}
+
+// Sort the first np (a power of two <= 1024) entries of the block descending, entry i
+// held by thread i; threads past np sort their own entries among themselves.
+__device__ __forceinline__ uint64_t bitonic_sort_desc(uint64_t v, int np, uint64_t* xs) {
+  if (np >= 2) v = bitonic_merge<1>(v, xs);
+  if (np >= 4) v = bitonic_merge<2>(v, xs);
+  if (np >= 8) v = bitonic_merge<3>(v, xs);
+  if (np >= 16) v = bitonic_merge<4>(v, xs);
+  if (np >= 32) v = bitonic_merge<5>(v, xs);
+  if (np >= 64) v = bitonic_merge<6>(v, xs);
+  if (np >= 128) v = bitonic_merge<7>(v, xs);
+  if (np >= 256) v = bitonic_merge<8>(v, xs);
+  if (np >= 512) v = bitonic_merge<9>(v, xs);
+  if (np >= 1024) v = bitonic_merge<10>(v, xs);
+  return v;
 }
 
 // One 1024-thread block per request.  Only refined keys at or above the K-th tile key
@@ -802,10 +884,10 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
   const uint32_t lo = max(a.sel[r].theta, 1u);            // key 0 marks a padding code
   const uint32_t* rk = a.rkeys + size_t(r) * a.W_max * kTile;
   if (tid == 0) { kmax_sh = 0u; m_sh = 0u; }
-  for (int p = tid; p < a.Kt; p += 1024) tl[p] = a.tiles[size_t(r) * a.W_max + p];
-  __syncthreads();
   {
-    constexpr int IT = kMaxW * kTile / 4 / 1024;         // u32x4 loads per thread, all issued first
+    // the tile list and every key load go out together; one barrier then waits for all
+    for (int p = tid; p < a.Kt; p += 1024) tl[p] = a.tiles[size_t(r) * a.W_max + p];
+    constexpr int IT = kMaxW * kTile / 4 / 1024;         // u32x4 loads per thread
     const u32x4* src = reinterpret_cast<const u32x4*>(rk);
     u32x4 kv[IT];
 #pragma unroll
@@ -813,6 +895,7 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
       const uint32_t q = uint32_t(it) * 1024 + tid;
       kv[it] = q < n / 4 ? src[q] : u32x4{0u, 0u, 0u, 0u};
     }
+    __syncthreads();
     uint32_t lmax = 0u;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -884,21 +967,7 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
   uint64_t v = uint32_t(tid) < got ? u.s[tid] : 0ull;    // padding sorts last
   int np = 1;
   while (np < a.K) np <<= 1;
-  for (int k = 2; k <= np; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      uint64_t o;
-      if (j >= 64) {
-        __syncthreads();
-        u.s[tid] = v;
-        __syncthreads();
-        o = u.s[tid ^ j];
-      } else {
-        o = shfl_xor_u64(v, j);
-      }
-      const bool desc = (tid & k) == 0, lower = (tid & j) == 0;
-      v = (desc == lower) ? (v > o ? v : o) : (v < o ? v : o);
-    }
-  }
+  v = bitonic_sort_desc(v, np, u.s);
   // thread i holds rank i
   const float* lse = a.lse + size_t(r) * a.W_max;
   const float* cum = a.cum + size_t(r) * a.W_max;
@@ -1021,13 +1090,13 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   int err;
 
   {  // head sum into the MFMA operand; codebook transpose in the last grid row
-    ZsumK k{a.R, a.H, a.W, a.W_max, a.d_v, a.V, nch_max, split, a.o, z, zf, a.Wout, woutT};
-    const int n = nch * 32 * (a.d_v / 8);
+    const long n = long(a.R) * nch * 32 * (a.d_v / 8);
     const int ntr = ((a.V + 31) / 32) * ((a.d_v + 31) / 32);   // transpose tiles
-    int gx = (n + 255) / 256;
-    gx = gx < ntr ? ntr : gx;
-    gx = gx < 1 ? 1 : (gx > 1024 ? 1024 : gx);
-    hipLaunchKernelGGL(zsum_kernel, dim3(gx, a.R + 1), dim3(256), 0, s, k);
+    long zb = (n + 255) / 256;
+    zb = zb < 1 ? 1 : (zb > 8192 ? 8192 : zb);
+    const int tb = ntr < 256 ? ntr : 256;
+    ZsumK k{a.R, a.H, a.W, a.W_max, a.d_v, a.V, nch_max, int(zb), split, a.o, z, zf, a.Wout, woutT};
+    hipLaunchKernelGGL(zsum_kernel, dim3(unsigned(zb + tb)), dim3(256), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
   // codes per wave: 128 .. 1024, larger while the grid keeps >= 16384 waves, so that
