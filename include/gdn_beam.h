@@ -67,8 +67,9 @@ typedef struct gdn_beam_ctx gdn_beam_ctx;   /* opaque, host memory owned by the 
 
 /* Size in bytes of the workspace a context needs (host only, no GPU call).
  * Per request it is H*(4*d_v*d_k + T_max*W_max*(4 + 4*d_v + e*d_k)) plus
- * O(W_max*(T_max + d_v + V_max)) for ancestry, scores and selection scratch
- * (e = bytes per io element).  No term grows with d_v*d_k*W: this is the
+ * O(W_max*(T_max + d_v + V_max/32)) for ancestry, scores and selection scratch
+ * (e = bytes per io element; the selection keeps one value per 32 codes of a
+ * beam, never a W x V score matrix).  No term grows with d_v*d_k*W: this is the
  * persistent-capacity form of the OneLA reading note, section 2.2 (eq. 5) and
  * section 4.3 (b), against W*d_v*d_k for one state per beam. */
 gdn_status gdn_beam_workspace_bytes(const gdn_beam_config* cfg, size_t* bytes /* host */);
