@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="batch")
     p.add_argument("--mode", choices=["select", "forced"], default="select")
+    p.add_argument("--path", choices=["records", "fullstate"], default="records",
+                   help="records: transition records and replay (gdn_beam_step); fullstate: "
+                        "the per-beam state baseline (gdn_fullstate_step)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU oracle time")
     p.add_argument("--quiet", action="store_true")
@@ -71,6 +74,18 @@ def step_bytes(wl, t, distinct):
     total = wl.R * wl.H * per_rh + 4 * t * W * wl.R
     total += wl.H * rec * int(np.sum(distinct))
     return total
+
+
+def fullstate_bytes(wl, t):
+    """Algorithmic HBM bytes of one gdn_fullstate_step launch at step t: per beam the
+    parent's state (4 d_v d_k; at t = 0 the shared S_ctx, once per (request, head)),
+    the new state (4 d_v d_k), q, k, v (e each), alpha, beta (8) and o_t (4 d_v); per
+    request the parent indices (4 W_t)."""
+    e = 2 if wl.io == "bf16" else 4
+    W = wl.width(t)
+    st = 4 * wl.d_v * wl.d_k
+    per_rh = W * (st + e * (2 * wl.d_k + wl.d_v) + 8 + 4 * wl.d_v) + (st if t == 0 else W * st)
+    return wl.R * wl.H * per_rh + (4 * W * wl.R if t > 0 else 0)
 
 
 def step_flops(wl, t):
@@ -209,13 +224,22 @@ def main():
                   for t in range(wl.T)]
     torch.cuda.synchronize()
 
+    states = dec.alloc_states() if args.path == "fullstate" else None
+
+    def gdn_step(t, x):
+        if states is None:
+            dec.step(t, x["q"], x["k"], x["v"], x["alpha"], x["beta"], outs[t], stream)
+        else:
+            dec.fullstate_step(t, S_ctx if t == 0 else None, x["q"], x["k"], x["v"], x["alpha"],
+                               x["beta"], outs[t], states, stream)
+
     def decode(ev=None):
         dec.init(S_ctx, wl.width(0), stream)
         for t in range(wl.T):
             x = inputs[t]
             if ev is not None:
                 ev[t][0].record(stream)
-            dec.step(t, x["q"], x["k"], x["v"], x["alpha"], x["beta"], outs[t], stream)
+            gdn_step(t, x)
             if ev is not None:
                 ev[t][1].record(stream)
             s = sels[t]
@@ -236,7 +260,7 @@ def main():
                 d[r] = sum(len(np.unique(anc[r, :W, j])) for j in range(t))
         distinct.append(d)
         x = inputs[t]
-        dec.step(t, x["q"], x["k"], x["v"], x["alpha"], x["beta"], outs[t], stream)
+        gdn_step(t, x)
         s = sels[t]
         dec.select(t, outs[t], Wout, wl.V, wl.width(t + 1), s["parent"], s["token"], s["score"],
                    forced[t][0], forced[t][1], stream)
@@ -265,11 +289,17 @@ def main():
     sel_ms /= args.steps
     trans = wl.transitions()
     value = trans * args.steps / elapsed
-    bytes_t = [step_bytes(wl, t, distinct[t]) for t in range(wl.T)]
+    if states is None:
+        bytes_t = [step_bytes(wl, t, distinct[t]) for t in range(wl.T)]
+    else:
+        bytes_t = [fullstate_bytes(wl, t) for t in range(wl.T)]
     achieved = sum(bytes_t) / (step_ms.sum() * 1e-3) / 1e9
-    traffic = load_traffic(wl.name)
+    traffic = load_traffic(wl.name) if states is None else None
     gdn_rate = trans / (step_ms.sum() * 1e-3)
-    flops = sum(step_flops(wl, t) for t in range(wl.T))
+    if states is None:
+        flops = sum(step_flops(wl, t) for t in range(wl.T))
+    else:   # P k and P q, alpha P + delta k^T per state element
+        flops = sum(wl.R * wl.H * wl.width(t) * 6 * wl.d_v * wl.d_k for t in range(wl.T))
     log(args, f"step kernel ms per SID step: {np.round(step_ms, 4).tolist()}  select ms: "
               f"{np.round(sel_ms, 4).tolist()}")
     log(args, f"algorithmic bytes per step launch: {bytes_t}; distinct ancestors per request "
@@ -282,10 +312,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "R": wl.R, "H": wl.H, "d_k": wl.d_k, "d_v": wl.d_v,
                    "T": wl.T, "W_t": list(wl.widths), "V": wl.V, "io_dtype": wl.io,
-                   "state_dtype": "f32", "mode": args.mode, "parallelism": "single GPU"},
+                   "state_dtype": "f32", "mode": args.mode, "path": args.path,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gdn step_kernel", "bytes_per_decode": int(sum(bytes_t)),
+                     "kernel": "gdn step_kernel" if states is None else "gdn fullstate_kernel",
+                     "bytes_per_decode": int(sum(bytes_t)),
                      "copy_GBs": copy_gbs,
                      "launches_per_decode": wl.T},
         "gdn_step_rate": gdn_rate,

@@ -118,6 +118,29 @@ gdn_status gdn_beam_select(gdn_beam_ctx* ctx, int32_t t, const float* o,
                            int32_t* parent, int32_t* token, float* score,
                            hipStream_t stream);
 
+/* Bytes of the state buffer gdn_fullstate_step needs (host only):
+ * 2 * R*H*W_max*d_v*d_k*4, two generations of one fp32 d_v x d_k state per
+ * (request, head, beam). */
+gdn_status gdn_fullstate_bytes(const gdn_beam_config* cfg, size_t* bytes /* host */);
+
+/* The FullState baseline of the OneLA reading note (section 1.3, Fig. 2; eq. 4 of
+ * section 2.2): every beam carries its own state, copied on reorder.  Same inputs,
+ * output and state machine as gdn_beam_step, in its place (select(t) follows):
+ * beam b reads its parent's state P (S_ctx at t = 0, else the state this call wrote
+ * at step t-1 for slot pi_t(b), from the ancestry the selection left), and writes
+ * S_{t,b} = alpha P + delta k^T with delta = beta (v - alpha P k), and
+ * o = S_{t,b} q [R,H,W_t,d_v] fp32.  It writes no transition records, so a decode
+ * uses either this call or gdn_beam_step for all its steps (mixing them is
+ * GDN_ERR_BAD_STATE).
+ * states: device, >= gdn_fullstate_bytes, 16-byte aligned, owned by the caller, the
+ * same buffer for every step of the decode (steps alternate its two halves).
+ * S_ctx [R,H,d_v,d_k] fp32 (device) is read at t = 0 only (may be NULL later).
+ * Errors as gdn_beam_step; a short buffer is GDN_ERR_WORKSPACE. */
+gdn_status gdn_fullstate_step(gdn_beam_ctx* ctx, int32_t t, const float* S_ctx,
+                              const void* q, const void* k, const void* v,
+                              const float* alpha, const float* beta, float* o,
+                              void* states, size_t states_bytes, hipStream_t stream);
+
 /* Copy internal state to a caller buffer (device) for tests and debugging. */
 typedef enum {
   GDN_EXPORT_ANCESTRY = 0,  /* [R,W_max,T_max] int32: h_t(b,j) of the coming step        */

@@ -24,7 +24,8 @@ GDN_F32, GDN_BF16 = 0, 1
 # every entry point the header declares
 EXPORTS = ("gdn_beam_workspace_bytes", "gdn_beam_init", "gdn_beam_step", "gdn_beam_select",
            "gdn_beam_export", "gdn_beam_export_bytes", "gdn_beam_query", "gdn_beam_destroy",
-           "gdn_beam_status_str", "gdn_beam_last_error", "gdn_beam_prefill")
+           "gdn_beam_status_str", "gdn_beam_last_error", "gdn_beam_prefill",
+           "gdn_fullstate_bytes", "gdn_fullstate_step")
 
 
 class gdn_beam_config(ctypes.Structure):
@@ -78,6 +79,8 @@ def _load():
         "gdn_beam_status_str": (c_char_p, [st]),
         "gdn_beam_last_error": (c_char_p, []),
         "gdn_beam_prefill": (st, [i32, i32, i32, i32, c_int64, vp, vp, vp, vp, vp, vp, vp]),
+        "gdn_fullstate_bytes": (st, [POINTER(gdn_beam_config), POINTER(c_size_t)]),
+        "gdn_fullstate_step": (st, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -171,6 +174,18 @@ def gdn_beam_last_error() -> str:
 def gdn_beam_prefill(R, H, d_k, d_v, N, k, v, alpha, beta, offsets, S_out, stream=None):
     _check(_lib.gdn_beam_prefill(R, H, d_k, d_v, N, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                  _ptr(offsets), _ptr(S_out), _stream(stream)), "gdn_beam_prefill")
+
+
+def gdn_fullstate_bytes(cfg: gdn_beam_config) -> int:
+    n = c_size_t(0)
+    _check(_lib.gdn_fullstate_bytes(byref(cfg), byref(n)), "gdn_fullstate_bytes")
+    return n.value
+
+
+def gdn_fullstate_step(ctx, t, S_ctx, q, k, v, alpha, beta, o, states, states_bytes, stream=None):
+    _check(_lib.gdn_fullstate_step(ctx, t, _ptr(S_ctx), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                   _ptr(beta), _ptr(o), _ptr(states), states_bytes,
+                                   _stream(stream)), "gdn_fullstate_step")
 
 
 def raw_status(name: str, *args) -> int:

@@ -19,6 +19,8 @@ struct gdn_beam_ctx {
   int t;          // step expected next
   int stepped;    // step(t) issued, select(t) not yet
   int W_cur;      // beams alive at step t
+  int mode;       // steps of this decode: 0 none yet, 1 transition records, 2 full states
+  const void* states;   // state buffer of a full-state decode
 };
 
 namespace {
@@ -99,6 +101,8 @@ gdn_status gdn_beam_init(const gdn_beam_config* cfg, const float* S_ctx, int32_t
   ctx->t = 0;
   ctx->stepped = 0;
   ctx->W_cur = W0;
+  ctx->mode = 0;
+  ctx->states = nullptr;
 
   InitArgs a{cfg->R, cfg->H, cfg->d_k, cfg->d_v, cfg->W_max, cfg->T_max, cfg->io_dtype,
              S_ctx, workspace, L};
@@ -122,12 +126,49 @@ gdn_status gdn_beam_step(gdn_beam_ctx* ctx, int32_t t, const void* q, const void
   const gdn_beam_config& c = ctx->cfg;
   if (t < 0) return GDN_ERR_INVALID_ARG;
   if (t >= c.T_max) return GDN_ERR_CAPACITY;
-  if (t != ctx->t) return GDN_ERR_BAD_STATE;
+  if (t != ctx->t || ctx->mode == 2) return GDN_ERR_BAD_STATE;
   StepArgs a{c.R, c.H, c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype,
              q, k, v, alpha, beta, o, ctx->ws, ctx->L};
   int err = launch_step(a, stream);
   if (err) return hip_fail(err, "gdn_beam_step");
   ctx->stepped = 1;
+  ctx->mode = 1;
+  return GDN_OK;
+}
+
+gdn_status gdn_fullstate_bytes(const gdn_beam_config* cfg, size_t* bytes) {
+  if (!bytes) return GDN_ERR_INVALID_ARG;
+  const gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  *bytes = 2 * fullstate_half_bytes(*cfg);
+  return GDN_OK;
+}
+
+gdn_status gdn_fullstate_step(gdn_beam_ctx* ctx, int32_t t, const float* S_ctx, const void* q,
+                              const void* k, const void* v, const float* alpha,
+                              const float* beta, float* o, void* states, size_t states_bytes,
+                              hipStream_t stream) {
+  if (!ctx) return GDN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !alpha || !beta || !o || !states) return GDN_ERR_INVALID_ARG;
+  if (t == 0 && !S_ctx) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) ||
+      !aligned16(beta) || !aligned16(o) || !aligned16(states) || (S_ctx && !aligned16(S_ctx)))
+    return GDN_ERR_INVALID_ARG;
+  const gdn_beam_config& c = ctx->cfg;
+  if (t < 0) return GDN_ERR_INVALID_ARG;
+  if (t >= c.T_max) return GDN_ERR_CAPACITY;
+  const size_t half = fullstate_half_bytes(c);
+  if (states_bytes < 2 * half) return GDN_ERR_WORKSPACE;
+  if (t != ctx->t || ctx->mode == 1) return GDN_ERR_BAD_STATE;
+  if (t > 0 && states != ctx->states) return GDN_ERR_BAD_STATE;   // parents live in it
+  FullStepArgs a{c.R, c.H, c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype, S_ctx,
+                 q, k, v, alpha, beta, o, states, half,
+                 reinterpret_cast<const int32_t*>(static_cast<char*>(ctx->ws) + ctx->L.anc[t & 1])};
+  int err = launch_fullstate(a, stream);
+  if (err) return hip_fail(err, "gdn_fullstate_step");
+  ctx->stepped = 1;
+  ctx->mode = 2;
+  ctx->states = states;
   return GDN_OK;
 }
 

@@ -143,11 +143,29 @@ struct PrefillArgs {
   float* S_out;
 };
 
-// Kernel launchers (gdn_step.hip, gdn_select.hip).  Return a hipError_t value.
+struct FullStepArgs {
+  int R, H, d_k, d_v, W_max, T_max, t, W;
+  gdn_dtype io;
+  const float* S_ctx;
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  float* o;
+  void* states;           // two generations of R*H*W_max*d_v*d_k fp32 states
+  size_t half_bytes;      // bytes of one generation
+  const int32_t* anc;     // ancestry of step t in the workspace
+};
+
+inline size_t fullstate_half_bytes(const gdn_beam_config& c) {
+  return size_t(c.R) * c.H * c.W_max * size_t(c.d_v) * c.d_k * 4;
+}
+
+// Kernel launchers (gdn_step.hip, gdn_select.hip, gdn_fullstate.hip).  Return a
+// hipError_t value.
 int launch_init(const InitArgs& a, hipStream_t s);
 int launch_step(const StepArgs& a, hipStream_t s);
 int launch_select(const SelectArgs& a, hipStream_t s);
 int launch_prefill(const PrefillArgs& a, hipStream_t s);
+int launch_fullstate(const FullStepArgs& a, hipStream_t s);
 int copy_d2d(void* dst, const void* src, size_t bytes, hipStream_t s);
 const char* hip_error_string(int err);
 

@@ -790,22 +790,6 @@ __device__ float forced_logit(const FinK& a, int r, int b, int c) {
 // the tile threshold (massive ties) are read from global memory instead.
 constexpr int kFinCap = 8192;
 
-// Value of lane (lane ^ J) of the wave.  J = 1, 2: DPP quad permutes; 4: DPP row
-// shifts by 4 either way; 8: DPP row rotate by 8; 16: swizzle (xor mode); 32: LDS
-// permute.  The DPP forms are plain VALU moves.
-template <int J>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  if constexpr (J == 1) return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, false));
-  else if constexpr (J == 2) return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xF, 0xF, false));
-  else if constexpr (J == 4) {
-    const uint32_t up = uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x104, 0xF, 0xF, false));
-    const uint32_t dn = uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x114, 0xF, 0xF, false));
-    return (threadIdx.x & 4) ? dn : up;
-  } else if constexpr (J == 8) return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x128, 0xF, 0xF, false));
-  else if constexpr (J == 16) return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), (16 << 10) | 0x1F));
-  else return uint32_t(__shfl_xor(int(v), 32));
-}
-
 template <int J>
 __device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
   return (uint64_t(lane_xor<J>(uint32_t(v >> 32))) << 32) | lane_xor<J>(uint32_t(v));

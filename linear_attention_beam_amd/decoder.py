@@ -38,6 +38,18 @@ class BeamDecoder:
     def step(self, t, q, k, v, alpha, beta, o, stream=None):
         B.gdn_beam_step(self.ctx, t, q, k, v, alpha, beta, o, self._stream(stream))
 
+    def fullstate_step(self, t, S_ctx, q, k, v, alpha, beta, o, states, stream=None):
+        """The FullState baseline in place of step(t); `states` is a device buffer of
+        fullstate_bytes() bytes (see alloc_states)."""
+        B.gdn_fullstate_step(self.ctx, t, S_ctx, q, k, v, alpha, beta, o, states,
+                             states.numel() * states.element_size(), self._stream(stream))
+
+    def fullstate_bytes(self):
+        return B.gdn_fullstate_bytes(self.cfg)
+
+    def alloc_states(self):
+        return torch.empty(self.fullstate_bytes() // 4, dtype=torch.float32, device=self.device)
+
     def select(self, t, o, Wout, V, W_next, parent, token, score, forced_parent=None,
                forced_token=None, stream=None):
         B.gdn_beam_select(self.ctx, t, o, Wout, V, W_next, forced_parent, forced_token,

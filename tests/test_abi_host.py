@@ -21,14 +21,14 @@ FAKE = 0x7F0000000000            # 256-aligned, never dereferenced
 
 def header_functions():
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:gdn_status|void|const char\*)\s+(gdn_beam_\w+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:gdn_status|void|const char\*)\s+(gdn_\w+)\s*\(", txt, re.M)))
 
 
 def test_header_symbols_exported():
     names = header_functions()
     assert set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r" T (gdn_beam_\w+)$", out, re.M))
+    exported = set(re.findall(r" T (gdn_\w+)$", out, re.M))
     missing = set(names) - exported
     assert not missing, missing
     lib = ctypes.CDLL(B.LIB_PATH)
@@ -177,3 +177,24 @@ def test_status_strings():
 def test_single_hip_runtime():
     """The library shares PyTorch's HIP runtime: exactly one libamdhip64 is mapped."""
     assert len(B._hip_runtimes()) == 1
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_fullstate_bytes_formula(name):
+    """Two generations of one fp32 d_v x d_k state per (request, head, beam): the
+    FullState capacity of the OneLA reading note (section 1.3, Fig. 2)."""
+    wl = synth.get(name)
+    cfg = B.make_config(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, wl.io, wl.wout)
+    assert B.gdn_fullstate_bytes(cfg) == 2 * wl.R * wl.H * wl.W_max * wl.d_v * wl.d_k * 4
+
+
+def test_fullstate_argument_errors():
+    n = ctypes.c_size_t(0)
+    assert B.raw_status("gdn_fullstate_bytes", None, ctypes.byref(n)) == B.GDN_ERR_INVALID_ARG
+    cfg = _cfg(d_k=64)
+    assert B.raw_status("gdn_fullstate_bytes", ctypes.byref(cfg), ctypes.byref(n)) == B.GDN_ERR_UNSUPPORTED
+    cfg = _cfg()
+    assert B.raw_status("gdn_fullstate_bytes", ctypes.byref(cfg), None) == B.GDN_ERR_INVALID_ARG
+    # a null context is rejected before anything touches the device
+    assert B.raw_status("gdn_fullstate_step", None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, 1 << 30, None) == B.GDN_ERR_INVALID_ARG
