@@ -64,6 +64,10 @@ def wout(wl: Workload, device) -> torch.Tensor:
     return _to_dev(gen.wout(wl), device).contiguous()
 
 
+def wout_step(wl: Workload, t: int, V: int, device) -> torch.Tensor:
+    return _to_dev(gen.wout_step(wl, t, V), device).contiguous()
+
+
 def prompts(wl: Workload, device, R=None, lengths=None) -> dict:
     """Stacked prompt tokens of R requests: k [N,H,d_k], v [N,H,d_v], alpha, beta [N,H], offsets [R+1]."""
     R = wl.R if R is None else R

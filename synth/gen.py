@@ -109,6 +109,14 @@ def wout(wl: Workload) -> Tensor:
     return Tensor(w.astype(np.float32), wl.wout)
 
 
+def wout_step(wl: Workload, t: int, V: int) -> Tensor:
+    """A step's own codebook projection [d_v, V] (per-step vocabularies), same law as
+    wout(); step t draws its own stream."""
+    g = _rng(wl, _WOUT, 0, t + 1)
+    w = g.standard_normal((wl.d_v, V), dtype=np.float32) / np.float32(np.sqrt(wl.d_v))
+    return Tensor(w.astype(np.float32), wl.wout)
+
+
 def forced_parents(wl: Workload, r: int, t: int) -> np.ndarray:
     """Seed-fixed parent map for the selection after step t: W_{t+1} children of W_t parents.
 

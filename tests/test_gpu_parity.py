@@ -28,6 +28,9 @@ DERIVED = {
     "tiny_few_tiles": ("tiny", dict(widths=(4, 8, 16), V=32)),
     "single_v300": ("single", dict(V=300)),
     "ties_w512": ("tiny", dict(widths=(512, 512, 512), V=64)),
+    # six SID steps (five ancestor records at the last step)
+    "tiny_t6": ("tiny", dict(T=6, widths=(8,) * 6)),
+    "single_bf16_t6": ("single", dict(T=6, widths=(128,) * 6, io="bf16", wout="bf16")),
 }
 
 
@@ -77,9 +80,10 @@ def test_prefill_matches_oracle(name, R):
         assert e <= 1e-4
 
 
-@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2)])
+@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_t6", 1),
+                                    ("single_bf16_t6", 1)])
 def test_forced_parents_parity(name, R):
-    wl = synth.get(name)
+    wl = _wl(name)
     g = GpuDecode(wl, R=R, exact=range(R))
     tol = TOL[wl.io]
     decs = {r: oracle.FullStateDecoder(g.S_exact[r].astype(np.float64), wl.width(0)) for r in range(R)}
@@ -106,7 +110,8 @@ def test_forced_parents_parity(name, R):
 
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_v37", 1),
-                                    ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("single_v300", 1)])
+                                    ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("single_v300", 1),
+                                    ("single_bf16_t6", 1)])
 def test_select_mode_parity(name, R):
     """Top-W drives the beams.  The oracle follows the GPU's choice (teacher forcing)
     after the selection itself has been checked against the exact top-W."""
@@ -324,3 +329,36 @@ def test_step_closed_forms(name):
     d = g.export(B.GDN_EXPORT_GTR_DELTA)[0][:, 0, :wl.width(0)]
     assert np.all(d == 0)
     assert rel_err(o, al[..., None] * np.einsum("hvk,hbk->hbv", S, q)) <= tol
+
+
+@pytest.mark.parametrize("name", ["tiny", "single"])
+def test_per_step_codebooks(name):
+    """Each step scores against its own codebook and vocabulary size (step-specific
+    vocabularies): V_t = V_max, ~0.6 V_max (not a multiple of 32), V_max."""
+    from synth import device as sdev
+    wl = synth.get(name)
+    g = GpuDecode(wl, R=1, exact=(0,))
+    tol = TOL[wl.io]
+    Vs = [wl.V, (wl.V * 3) // 5 | 1, wl.V][:wl.T]
+    dec = oracle.FullStateDecoder(g.S_exact[0].astype(np.float64), wl.width(0))
+    g.init()
+    for t in range(wl.T):
+        V = Vs[t]
+        W_t = sdev.wout_step(wl, t, V, g.dev)
+        W64 = gen.wout_step(wl, t, V).value.astype(np.float64)
+        o = to_np(g.step(t))
+        cum_before = g.export(B.GDN_EXPORT_CUM)
+        K = wl.width(t + 1)
+        s = g.sel[t]
+        say(f"gdn_beam_select t={t} V={V} (own codebook)")
+        g.dec.select(t, g.o[t], W_t, V, K, s["parent"], s["token"], s["score"])
+        torch.cuda.synchronize()
+        sel = {k: to_np(v)[0] for k, v in s.items()}
+        o_ref, _ = dec.step(t, *g.step_inputs64(0, t))
+        assert rel_err(o[0], o_ref) <= tol
+        check_selection(o[0], cum_before[0][:wl.width(t)], W64, K, sel, f"t={t} V={V}")
+        assert np.all(sel["token"] < V)
+        s_ref = oracle.step_scores(o_ref, W64, dec.cum)
+        dec.advance(t, sel["parent"], sel["token"], s_ref[sel["parent"], sel["token"]])
+        anc = g.export(B.GDN_EXPORT_ANCESTRY)
+        np.testing.assert_array_equal(anc[0][:K, :t + 1], dec.anc)
