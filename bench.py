@@ -201,7 +201,7 @@ def main():
     log(args, f"device copy (read + write): {copy_gbs:.0f} GB/s")
 
     # ---- inputs resident in HBM before timing
-    dec = BeamDecoder(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, wl.io, wl.wout)
+    dec = BeamDecoder(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, wl.io, wl.wout, H_K=wl.H_K)
     p = sdev.prompts(wl, dev)
     S_ctx = torch.empty((wl.R, wl.H, wl.d_v, wl.d_k), dtype=torch.float32, device=dev)
     t0 = time.perf_counter()

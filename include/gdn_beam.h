@@ -54,13 +54,16 @@ typedef enum {
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 typedef struct {
-  int32_t R, H;        /* requests, GDN heads per request                                 */
+  int32_t R, H;        /* requests, GDN value heads per request                           */
   int32_t d_k, d_v;    /* head dims; supported (d_k, d_v): (16,16), (128,128), (128,256)  */
   int32_t T_max;       /* SID decode steps (1..8)                                         */
   int32_t W_max;       /* peak beam width = GTR slots per step (1..1024)                  */
   int32_t V_max;       /* largest codebook passed to select (1..65536)                    */
   gdn_dtype io_dtype;  /* dtype of q, k, v; keys are stored in the GTR pool in it         */
   gdn_dtype wout_dtype;/* dtype of the codebook projection Wout                           */
+  int32_t H_K;         /* key heads (0: H).  Grouped value heads: H = g * H_K, value head */
+                       /* h uses q, k of key head h / g; S_ctx, v, gates, o and the      */
+                       /* records' delta are per value head, q, k and keys per key head  */
 } gdn_beam_config;
 
 typedef struct gdn_beam_ctx gdn_beam_ctx;   /* opaque, host memory owned by the library */
@@ -85,7 +88,7 @@ gdn_status gdn_beam_init(const gdn_beam_config* cfg, const float* S_ctx, int32_t
                          gdn_beam_ctx** out /* host */);
 
 /* One SID step t for all R*H*W_t beams (W_t = beams alive at step t).
- * Inputs: q, k [R,H,W_t,d_k] and v [R,H,W_t,d_v] in io_dtype; alpha, beta
+ * Inputs: q, k [R,H_K,W_t,d_k] and v [R,H,W_t,d_v] in io_dtype; alpha, beta
  * [R,H,W_t] fp32.  For each beam: u_q = S_ctx q_t and u_k = S_ctx k_t, replayed
  * along the beam's ancestor records by eqs. (6)-(7); then eq. (8):
  * delta_t = beta (v - alpha u_k), o_t = alpha u_q + delta_t (k_t . q_t).
@@ -148,7 +151,7 @@ typedef enum {
   GDN_EXPORT_CUM = 2,       /* [R,W_max] fp32: cumulative score of each live beam        */
   GDN_EXPORT_GTR_ALPHA = 3, /* [R,H,T_max,W_max] fp32                                    */
   GDN_EXPORT_GTR_DELTA = 4, /* [R,H,T_max,W_max,d_v] fp32                                */
-  GDN_EXPORT_GTR_KEY = 5,   /* [R,H,T_max,W_max,d_k] io_dtype                            */
+  GDN_EXPORT_GTR_KEY = 5,   /* [R,H_K,T_max,W_max,d_k] io_dtype                          */
   GDN_EXPORT_STATUS = 6     /* [1] int32: bit 0 = a forced parent/token was out of range */
 } gdn_export_what;
 gdn_status gdn_beam_export(const gdn_beam_ctx* ctx, int32_t what, void* dst,
@@ -171,11 +174,11 @@ const char* gdn_beam_last_error(void);
 
 /* Prefill (eq. 3, section 1.2): S_out[r,h] = the state after request r's prompt,
  * starting from zero.  Prompt tokens of all requests are stacked:
- * k [N,H,d_k], v [N,H,d_v], alpha, beta [N,H] fp32, request r owning rows
+ * k [N,H_K,d_k] (H_K = 0: H), v [N,H,d_v], alpha, beta [N,H] fp32, request r owning rows
  * offsets[r] .. offsets[r+1]-1, with offsets [R+1] int32 (device), nondecreasing,
  * offsets[R] = N.  Offsets are clamped to [0, N] on the device.
  * S_out [R,H,d_v,d_k] fp32.  Same head dims as the decode. */
-gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t d_k, int32_t d_v, int64_t N,
+gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t H_K, int32_t d_k, int32_t d_v, int64_t N,
                             const float* k, const float* v, const float* alpha,
                             const float* beta, const int32_t* offsets,
                             float* S_out, hipStream_t stream);

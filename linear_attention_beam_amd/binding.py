@@ -31,7 +31,7 @@ EXPORTS = ("gdn_beam_workspace_bytes", "gdn_beam_init", "gdn_beam_step", "gdn_be
 class gdn_beam_config(ctypes.Structure):
     _fields_ = [("R", c_int32), ("H", c_int32), ("d_k", c_int32), ("d_v", c_int32),
                 ("T_max", c_int32), ("W_max", c_int32), ("V_max", c_int32),
-                ("io_dtype", c_int), ("wout_dtype", c_int)]
+                ("io_dtype", c_int), ("wout_dtype", c_int), ("H_K", c_int32)]
 
 
 class GdnBeamError(RuntimeError):
@@ -78,7 +78,7 @@ def _load():
         "gdn_beam_destroy": (None, [vp]),
         "gdn_beam_status_str": (c_char_p, [st]),
         "gdn_beam_last_error": (c_char_p, []),
-        "gdn_beam_prefill": (st, [i32, i32, i32, i32, c_int64, vp, vp, vp, vp, vp, vp, vp]),
+        "gdn_beam_prefill": (st, [i32, i32, i32, i32, i32, c_int64, vp, vp, vp, vp, vp, vp, vp]),
         "gdn_fullstate_bytes": (st, [POINTER(gdn_beam_config), POINTER(c_size_t)]),
         "gdn_fullstate_step": (st, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp]),
     }
@@ -113,9 +113,9 @@ def _check(status: int, where: str):
         raise GdnBeamError(status, where)
 
 
-def make_config(R, H, d_k, d_v, T_max, W_max, V_max, io="bf16", wout="bf16") -> gdn_beam_config:
+def make_config(R, H, d_k, d_v, T_max, W_max, V_max, io="bf16", wout="bf16", H_K=0) -> gdn_beam_config:
     dt = {"f32": GDN_F32, "bf16": GDN_BF16}
-    return gdn_beam_config(R, H, d_k, d_v, T_max, W_max, V_max, dt[io], dt[wout])
+    return gdn_beam_config(R, H, d_k, d_v, T_max, W_max, V_max, dt[io], dt[wout], H_K)
 
 
 def gdn_beam_workspace_bytes(cfg: gdn_beam_config) -> int:
@@ -171,8 +171,8 @@ def gdn_beam_last_error() -> str:
     return _lib.gdn_beam_last_error().decode()
 
 
-def gdn_beam_prefill(R, H, d_k, d_v, N, k, v, alpha, beta, offsets, S_out, stream=None):
-    _check(_lib.gdn_beam_prefill(R, H, d_k, d_v, N, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+def gdn_beam_prefill(R, H, H_K, d_k, d_v, N, k, v, alpha, beta, offsets, S_out, stream=None):
+    _check(_lib.gdn_beam_prefill(R, H, H_K, d_k, d_v, N, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                  _ptr(offsets), _ptr(S_out), _stream(stream)), "gdn_beam_prefill")
 
 

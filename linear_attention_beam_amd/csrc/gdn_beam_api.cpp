@@ -45,6 +45,7 @@ gdn_status check_config(const gdn_beam_config* c) {
   if ((c->io_dtype != GDN_F32 && c->io_dtype != GDN_BF16) ||
       (c->wout_dtype != GDN_F32 && c->wout_dtype != GDN_BF16))
     return GDN_ERR_INVALID_ARG;
+  if (c->H_K < 0 || (c->H_K > 0 && c->H % c->H_K != 0)) return GDN_ERR_INVALID_ARG;
   if (!dims_supported(c->d_k, c->d_v)) return GDN_ERR_UNSUPPORTED;
   if (c->T_max > kMaxT || c->W_max > kMaxW || c->V_max > kMaxV) return GDN_ERR_CAPACITY;
   // flat candidate index b*V + c and per-request scratch sizes must fit in 31 bits
@@ -127,7 +128,7 @@ gdn_status gdn_beam_step(gdn_beam_ctx* ctx, int32_t t, const void* q, const void
   if (t < 0) return GDN_ERR_INVALID_ARG;
   if (t >= c.T_max) return GDN_ERR_CAPACITY;
   if (t != ctx->t || ctx->mode == 2) return GDN_ERR_BAD_STATE;
-  StepArgs a{c.R, c.H, c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype,
+  StepArgs a{c.R, c.H, key_heads(c), c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype,
              q, k, v, alpha, beta, o, ctx->ws, ctx->L};
   int err = launch_step(a, stream);
   if (err) return hip_fail(err, "gdn_beam_step");
@@ -161,7 +162,7 @@ gdn_status gdn_fullstate_step(gdn_beam_ctx* ctx, int32_t t, const float* S_ctx, 
   if (states_bytes < 2 * half) return GDN_ERR_WORKSPACE;
   if (t != ctx->t || ctx->mode == 1) return GDN_ERR_BAD_STATE;
   if (t > 0 && states != ctx->states) return GDN_ERR_BAD_STATE;   // parents live in it
-  FullStepArgs a{c.R, c.H, c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype, S_ctx,
+  FullStepArgs a{c.R, c.H, key_heads(c), c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype, S_ctx,
                  q, k, v, alpha, beta, o, states, half,
                  reinterpret_cast<const int32_t*>(static_cast<char*>(ctx->ws) + ctx->L.anc[t & 1])};
   int err = launch_fullstate(a, stream);
@@ -210,7 +211,7 @@ gdn_status gdn_beam_export_bytes(const gdn_beam_ctx* ctx, int32_t what, size_t* 
     case GDN_EXPORT_CUM: *bytes = R * W * 4; break;
     case GDN_EXPORT_GTR_ALPHA: *bytes = R * H * T * W * 4; break;
     case GDN_EXPORT_GTR_DELTA: *bytes = R * H * T * W * size_t(c.d_v) * 4; break;
-    case GDN_EXPORT_GTR_KEY: *bytes = R * H * T * W * size_t(c.d_k) * io_bytes(c.io_dtype); break;
+    case GDN_EXPORT_GTR_KEY: *bytes = R * size_t(key_heads(c)) * T * W * size_t(c.d_k) * io_bytes(c.io_dtype); break;
     case GDN_EXPORT_STATUS: *bytes = 4; break;
     default: return GDN_ERR_INVALID_ARG;
   }
@@ -250,11 +251,13 @@ gdn_status gdn_beam_query(const gdn_beam_ctx* ctx, int32_t* t_next, int32_t* W_c
 
 void gdn_beam_destroy(gdn_beam_ctx* ctx) { delete ctx; }
 
-gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t d_k, int32_t d_v, int64_t N,
+gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t H_K, int32_t d_k, int32_t d_v, int64_t N,
                             const float* k, const float* v, const float* alpha,
                             const float* beta, const int32_t* offsets, float* S_out,
                             hipStream_t stream) {
-  if (R < 1 || H < 1 || N < 0) return GDN_ERR_INVALID_ARG;
+  if (R < 1 || H < 1 || N < 0 || H_K < 0) return GDN_ERR_INVALID_ARG;
+  if (H_K == 0) H_K = H;
+  if (H % H_K != 0) return GDN_ERR_INVALID_ARG;
   if (!dims_supported(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
   if (!offsets || !S_out) return GDN_ERR_INVALID_ARG;
   if (N > 0 && (!k || !v || !alpha || !beta)) return GDN_ERR_INVALID_ARG;
@@ -262,7 +265,7 @@ gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t d_k, int32_t d_v, int6
   if (N > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned16(beta)))
     return GDN_ERR_INVALID_ARG;
   if (N >= (int64_t(1) << 31)) return GDN_ERR_CAPACITY;
-  PrefillArgs a{R, H, d_k, d_v, N, k, v, alpha, beta, offsets, S_out};
+  PrefillArgs a{R, H, H_K, d_k, d_v, N, k, v, alpha, beta, offsets, S_out};
   int err = launch_prefill(a, stream);
   if (err) return hip_fail(err, "gdn_beam_prefill");
   return GDN_OK;

@@ -11,7 +11,7 @@
 namespace gdn {
 
 struct FullK {
-  int H, W, W_max, T_max, t;
+  int H, HK, W, W_max, T_max, t;
   const float* S_ctx;          // [R,H,DV,DK] fp32
   const void *q, *k, *v;       // [R,H,W,DK|DV] io dtype
   const float *alpha, *beta;   // [R,H,W]
@@ -73,8 +73,9 @@ __global__ void __launch_bounds__(256) fullstate_kernel(FullK a) {
   }
   float* S = a.next + (rh * a.W_max + b) * DV * DK;
   const size_t beam = rh * a.W + b;
-  const f32x4 k4 = load4<BF16>(a.k, beam * DK + 4 * lr);
-  const f32x4 q4 = load4<BF16>(a.q, beam * DK + 4 * lr);
+  const size_t kbeam = (size_t(r) * a.HK + int(rh % a.H) / (a.H / a.HK)) * a.W + b;   // key head
+  const f32x4 k4 = load4<BF16>(a.k, kbeam * DK + 4 * lr);
+  const f32x4 q4 = load4<BF16>(a.q, kbeam * DK + 4 * lr);
   const float al = a.alpha[beam], be = a.beta[beam];
   f32x4 pr[IT];
   float vr[IT];
@@ -107,7 +108,7 @@ static int launch_full_t(const FullStepArgs& s, hipStream_t st) {
   const float* prev = reinterpret_cast<const float*>(static_cast<const char*>(s.states) +
                                                      ((s.t + 1) & 1) * s.half_bytes);
   float* next = reinterpret_cast<float*>(static_cast<char*>(s.states) + (s.t & 1) * s.half_bytes);
-  FullK k{s.H, s.W, s.W_max, s.T_max, s.t, s.S_ctx, s.q, s.k, s.v, s.alpha, s.beta, s.o, prev,
+  FullK k{s.H, s.HK, s.W, s.W_max, s.T_max, s.t, s.S_ctx, s.q, s.k, s.v, s.alpha, s.beta, s.o, prev,
           next, s.anc};
   const size_t blocks = size_t(s.R) * s.H * s.W;
   hipLaunchKernelGGL((fullstate_kernel<DK, DV, BF16>), dim3(unsigned(blocks)), dim3(256), 0, st, k);

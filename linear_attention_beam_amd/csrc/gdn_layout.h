@@ -71,6 +71,8 @@ GDN_HD inline int n_vgroups(int V) { return (V + kCodesPerWave - 1) / kCodesPerW
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+inline int key_heads(const gdn_beam_config& c) { return c.H_K > 0 ? c.H_K : c.H; }
+
 inline Layout make_layout(const gdn_beam_config& c) {
   Layout L{};
   size_t off = 0;
@@ -80,7 +82,7 @@ inline Layout make_layout(const gdn_beam_config& c) {
   L.s_frag = take(R * H * 4 * size_t(dvp_of(c.d_v)) * dk);
   L.gtr_alpha = take(R * H * T * W * 4);
   L.gtr_delta = take(R * H * T * W * dv * 4);
-  L.gtr_key = take(R * H * T * W * dk * e);
+  L.gtr_key = take(R * size_t(key_heads(c)) * T * W * dk * e);
   for (int i = 0; i < 2; ++i) L.anc[i] = take(R * W * T * 4);
   for (int i = 0; i < 2; ++i) L.tok[i] = take(R * W * T * 4);
   for (int i = 0; i < 2; ++i) L.cum[i] = take(R * W * 4);
@@ -114,7 +116,7 @@ struct InitArgs {
 };
 
 struct StepArgs {
-  int R, H, d_k, d_v, W_max, T_max, t, W;
+  int R, H, HK, d_k, d_v, W_max, T_max, t, W;
   gdn_dtype io;
   const void *q, *k, *v;
   const float *alpha, *beta;
@@ -136,7 +138,7 @@ struct SelectArgs {
 };
 
 struct PrefillArgs {
-  int R, H, d_k, d_v;
+  int R, H, HK, d_k, d_v;
   int64_t N;
   const float *k, *v, *alpha, *beta;
   const int32_t* offsets;
@@ -144,7 +146,7 @@ struct PrefillArgs {
 };
 
 struct FullStepArgs {
-  int R, H, d_k, d_v, W_max, T_max, t, W;
+  int R, H, HK, d_k, d_v, W_max, T_max, t, W;
   gdn_dtype io;
   const float* S_ctx;
   const void *q, *k, *v;

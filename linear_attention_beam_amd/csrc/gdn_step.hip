@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(256) init_kernel(InitArgs a) {
 // ---------------------------------------------------------------- step
 
 struct StepK {
-  int H, W, W_max, T_max, t, nrh;
+  int H, HK, W, W_max, T_max, t, nrh;
   const void *q, *k, *v;
   const float *alpha, *beta;
   float* o;
@@ -160,8 +160,13 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m = lane & 31, hf = lane >> 5;
   const int W = a.W, r = rh / a.H;
+  // grouped value heads: q, k and the records' keys belong to key head h / (H / HK)
+  const int grp = a.H / a.HK, hv = rh % a.H;
+  const int rk = r * a.HK + hv / grp;
+  const bool key_writer = hv % grp == 0;
   const int nch = (W + 31) >> 5;
   const size_t slot_t = size_t(rh) * a.T_max + TT;       // (r,h,t) row of the record pool
+  const size_t kslot_t = size_t(rk) * a.T_max + TT;      // (r,h_k,t) row of the key pool
   const unsigned char* qg = static_cast<const unsigned char*>(a.q);
   const unsigned char* kg = static_cast<const unsigned char*>(a.k);
   const unsigned char* vg = static_cast<const unsigned char*>(a.v);
@@ -191,12 +196,12 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
   int sanc[NAI];
   auto stage_load = [&](int c) {
     const int c0 = c * 32, nb = min(32, W - c0);
-    const size_t base = size_t(rh) * W;
+    const size_t base = size_t(rh) * W, kbase = size_t(rk) * W;
 #pragma unroll
     for (int i = 0; i < C::QU; ++i) {
       const int u = tid + i * NT;
       if (u / UPQ < nb) {
-        const size_t row = base + beam_of(c0 + u / UPQ);
+        const size_t row = kbase + beam_of(c0 + u / UPQ);
         sq[i] = *reinterpret_cast<const u32x4*>(qg + row * C::QB + size_t(u % UPQ) * 16);
         sk[i] = *reinterpret_cast<const u32x4*>(kg + row * C::QB + size_t(u % UPQ) * 16);
       }
@@ -267,11 +272,13 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     float aj[NJ1];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (bm < nb ? Lan[bm * kMaxT + j] : 0);
+      const int sl = bm < nb ? Lan[bm * kMaxT + j] : 0;
+      const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + sl;
+      const size_t krec = (size_t(rk) * a.T_max + j) * a.W_max + sl;
       aj[j] = a.gtr_alpha[rec];
 #pragma unroll
       for (int i = 0; i < SV; ++i)
-        kj[j][i] = *reinterpret_cast<const u32x4*>(keyg + rec * C::QB + sg * C::SEGB + 16 * i);
+        kj[j][i] = *reinterpret_cast<const u32x4*>(keyg + krec * C::QB + sg * C::SEGB + 16 * i);
     }
     const bool valid = m < nb;
     const int b = valid ? beam_of(c0 + m) : 0;
@@ -406,11 +413,13 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
       }
     }
 
-    // ---- append: k_t rows to slots (t, b) of the chunk's beams, and alpha_t
+    // ---- append: k_t rows to slots (t, b) of the chunk's beams (once per key head),
+    // and alpha_t
     {
-      for (int u = tid; u < nb * UPQ; u += NT)
-        *reinterpret_cast<u32x4*>(keyg + (slot_t * a.W_max + beam_of(c0 + u / UPQ)) * C::QB + (u % UPQ) * 16) =
-            *reinterpret_cast<const u32x4*>(Lk + (u / UPQ) * QROW + (u % UPQ) * 16);
+      if (key_writer)
+        for (int u = tid; u < nb * UPQ; u += NT)
+          *reinterpret_cast<u32x4*>(keyg + (kslot_t * a.W_max + beam_of(c0 + u / UPQ)) * C::QB + (u % UPQ) * 16) =
+              *reinterpret_cast<const u32x4*>(Lk + (u / UPQ) * QROW + (u % UPQ) * 16);
       if (tid < nb) a.gtr_alpha[slot_t * a.W_max + beam_of(c0 + tid)] = Lab[tid];
     }
     if (c + 1 < nch) stage_store((c + 1) & 1);
@@ -428,6 +437,7 @@ __global__ void __launch_bounds__(DV < 32 ? 256 : 2 * DV) prefill_kernel(Prefill
   constexpr int TPR = DV < 32 ? 256 / DV : 2;        // lanes per row
   constexpr int COLS = DK / TPR;
   const int rh = blockIdx.x, r = rh / a.H, h = rh % a.H;
+  const int hk = h / (a.H / a.HK);                        // key head of value head h
   const int row = threadIdx.x / TPR, cp = threadIdx.x % TPR;
   int beg = a.offsets[r], end = a.offsets[r + 1];
   beg = beg < 0 ? 0 : (beg > a.N ? int(a.N) : beg);
@@ -438,7 +448,7 @@ __global__ void __launch_bounds__(DV < 32 ? 256 : 2 * DV) prefill_kernel(Prefill
   float kc[COLS];
   float vn = 0.0f, an = 0.0f, bn = 0.0f;
   auto load = [&](int i, float* kk, float& vv, float& aa, float& bb) {
-    const float* kp = a.k + (size_t(i) * a.H + h) * DK + cp * COLS;
+    const float* kp = a.k + (size_t(i) * a.HK + hk) * DK + cp * COLS;
 #pragma unroll
     for (int c = 0; c < COLS; ++c) kk[c] = kp[c];
     vv = a.v[(size_t(i) * a.H + h) * DV + row];
@@ -485,7 +495,7 @@ static int launch_step_t(const StepArgs& a, hipStream_t s) {
   // one workgroup per (request, head): S_ctx is read once and kept in registers
   const long grid = (long(nrh) + 7) / 8 * 8;
   char* ws = static_cast<char*>(a.ws);
-  StepK k{a.H, a.W, a.W_max, a.T_max, a.t, nrh, a.q, a.k, a.v, a.alpha, a.beta, a.o,
+  StepK k{a.H, a.HK, a.W, a.W_max, a.T_max, a.t, nrh, a.q, a.k, a.v, a.alpha, a.beta, a.o,
           ws + a.L.s_frag, reinterpret_cast<float*>(ws + a.L.gtr_alpha),
           reinterpret_cast<float*>(ws + a.L.gtr_delta), ws + a.L.gtr_key,
           reinterpret_cast<const int32_t*>(ws + a.L.anc[a.t & 1]),

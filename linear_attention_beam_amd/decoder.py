@@ -14,10 +14,11 @@ _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 class BeamDecoder:
     def __init__(self, R, H, d_k, d_v, T_max, W_max, V_max, io="bf16", wout="bf16",
-                 device="cuda"):
-        self.cfg = B.make_config(R, H, d_k, d_v, T_max, W_max, V_max, io, wout)
+                 device="cuda", H_K=0):
+        self.cfg = B.make_config(R, H, d_k, d_v, T_max, W_max, V_max, io, wout, H_K)
         self.io, self.wout = io, wout
-        self.shape = dict(R=R, H=H, d_k=d_k, d_v=d_v, T_max=T_max, W_max=W_max, V_max=V_max)
+        self.shape = dict(R=R, H=H, H_K=H_K or H, d_k=d_k, d_v=d_v, T_max=T_max, W_max=W_max,
+                          V_max=V_max)
         self.ws_bytes = B.gdn_beam_workspace_bytes(self.cfg)
         self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)
         off = (-self.ws.data_ptr()) % 256            # the ABI wants a 256-byte aligned base
@@ -68,7 +69,7 @@ class BeamDecoder:
             B.GDN_EXPORT_CUM: ((R, W), torch.float32),
             B.GDN_EXPORT_GTR_ALPHA: ((R, H, T, W), torch.float32),
             B.GDN_EXPORT_GTR_DELTA: ((R, H, T, W, s["d_v"]), torch.float32),
-            B.GDN_EXPORT_GTR_KEY: ((R, H, T, W, s["d_k"]), _DT[self.io]),
+            B.GDN_EXPORT_GTR_KEY: ((R, s["H_K"], T, W, s["d_k"]), _DT[self.io]),
             B.GDN_EXPORT_STATUS: ((1,), torch.int32),
         }
         shape, dt = shapes[what]
@@ -90,8 +91,9 @@ class BeamDecoder:
 
 
 def prefill(S_out, k, v, alpha, beta, offsets, stream=None):
-    """S_out [R,H,d_v,d_k] <- eq. (3) over stacked prompt tokens (see gdn_beam_prefill)."""
+    """S_out [R,H,d_v,d_k] <- eq. (3) over stacked prompt tokens (see gdn_beam_prefill);
+    k [N,H_K,d_k] may hold fewer (key) heads than v [N,H,d_v] (grouped value heads)."""
     R, H, d_v, d_k = S_out.shape
     N = k.shape[0]
-    B.gdn_beam_prefill(R, H, d_k, d_v, N, k, v, alpha, beta, offsets, S_out,
+    B.gdn_beam_prefill(R, H, k.shape[1], d_k, d_v, N, k, v, alpha, beta, offsets, S_out,
                        torch.cuda.current_stream() if stream is None else stream)

@@ -18,7 +18,8 @@ from .beam import FullStateDecoder
 def prefill_request(wl, r):
     """S_ctx of request r: eq. (3) over its prompt in float64, then rounded to fp32."""
     p = gen.prompt_tokens(wl, r)
-    S = prefill(p["k"].astype(np.float64), p["v"].astype(np.float64),
+    # grouped value heads: value head h reads the keys of key head h // group
+    S = prefill(np.repeat(p["k"].astype(np.float64), wl.group, axis=1), p["v"].astype(np.float64),
                 p["alpha"].astype(np.float64), p["beta"].astype(np.float64))
     return S.astype(np.float32)
 
@@ -26,7 +27,10 @@ def prefill_request(wl, r):
 def step_arrays(wl, r, t):
     """float64 views of the step-t inputs of request r."""
     x = gen.step_inputs(wl, r, t)
-    return (x["q"].value.astype(np.float64), x["k"].value.astype(np.float64),
+    # grouped value heads: value head h reads q, k of key head h // group
+    g = wl.group
+    return (np.repeat(x["q"].value.astype(np.float64), g, axis=0),
+            np.repeat(x["k"].value.astype(np.float64), g, axis=0),
             x["v"].value.astype(np.float64), x["alpha"].astype(np.float64),
             x["beta"].astype(np.float64))
 

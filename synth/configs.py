@@ -30,7 +30,19 @@ class Workload:
     V: int                      # codebook size per step
     parents: str                # forced parent draw: "uniform" | "heavy"
     seed: int
+    H_K: int = 0                # key heads (0: one per value head); value head h uses
+                                # key head h // (H / H_K), grouped value heads
     summary: str = field(default="", compare=False)
+
+    @property
+    def hk(self) -> int:
+        """Key heads: q, k and the records' keys are per key head."""
+        return self.H_K or self.H
+
+    @property
+    def group(self) -> int:
+        """Value heads per key head."""
+        return self.H // self.hk
 
     @property
     def W_max(self) -> int:

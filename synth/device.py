@@ -34,8 +34,8 @@ def step_inputs(wl: Workload, t: int, device, R=None) -> dict:
     W = wl.width(t)
     g = _gen(wl, 3, t, device)
     dt = TDT[wl.io]
-    q = _unit((R, wl.H, W, wl.d_k), g, device).to(dt)
-    k = _unit((R, wl.H, W, wl.d_k), g, device).to(dt)
+    q = _unit((R, wl.hk, W, wl.d_k), g, device).to(dt)
+    k = _unit((R, wl.hk, W, wl.d_k), g, device).to(dt)
     v = torch.randn((R, wl.H, W, wl.d_v), generator=g, device=device).to(dt)
     alpha = torch.rand((R, wl.H, W), generator=g, device=device) * 0.1 + 0.9
     beta = torch.rand((R, wl.H, W), generator=g, device=device)
@@ -77,7 +77,7 @@ def prompts(wl: Workload, device, R=None, lengths=None) -> dict:
     offs[1:] = np.cumsum(lengths)
     N = int(offs[-1])
     g = _gen(wl, 2, 0, device)
-    k = _unit((N, wl.H, wl.d_k), g, device)
+    k = _unit((N, wl.hk, wl.d_k), g, device)
     v = torch.randn((N, wl.H, wl.d_v), generator=g, device=device)
     alpha = torch.rand((N, wl.H), generator=g, device=device) * 0.1 + 0.9
     beta = torch.rand((N, wl.H), generator=g, device=device)

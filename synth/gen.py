@@ -82,7 +82,7 @@ def prompt_tokens(wl: Workload, r: int) -> dict:
     """Prompt tokens of request r: k [L,H,d_k], v [L,H,d_v], alpha/beta [L,H], all fp32."""
     L = prompt_length(wl, r)
     g = _rng(wl, _PROMPT, r)
-    k = _unit(g, (L, wl.H, wl.d_k))
+    k = _unit(g, (L, wl.hk, wl.d_k))
     v = g.standard_normal((L, wl.H, wl.d_v), dtype=np.float32)
     alpha = g.uniform(0.9, 1.0, (L, wl.H)).astype(np.float32)
     beta = g.uniform(0.0, 1.0, (L, wl.H)).astype(np.float32)
@@ -93,8 +93,8 @@ def step_inputs(wl: Workload, r: int, t: int) -> dict:
     """Per-beam inputs of request r at SID step t (arrays [H, W_t, .])."""
     W = wl.width(t)
     g = _rng(wl, _STEP, r, t)
-    q = _unit(g, (wl.H, W, wl.d_k))
-    k = _unit(g, (wl.H, W, wl.d_k))
+    q = _unit(g, (wl.hk, W, wl.d_k))
+    k = _unit(g, (wl.hk, W, wl.d_k))
     v = g.standard_normal((wl.H, W, wl.d_v), dtype=np.float32)
     alpha = g.uniform(0.9, 1.0, (wl.H, W)).astype(np.float32)
     beta = g.uniform(0.0, 1.0, (wl.H, W)).astype(np.float32)

@@ -51,7 +51,8 @@ class GpuDecode:
         self.dev = dev
         say(f"workload={wl.name} R={self.R} exact={self.exact} H={wl.H} d_k={wl.d_k} d_v={wl.d_v} "
             f"io={wl.io} T={wl.T} widths={wl.widths} V={wl.V}")
-        self.dec = BeamDecoder(self.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, wl.io, wl.wout)
+        self.dec = BeamDecoder(self.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, wl.io, wl.wout,
+                               H_K=wl.H_K)
         # S_ctx: device prefill over short random prompts, exact requests from the oracle
         lengths = [short_prompt] * self.R
         p = sdev.prompts(wl, dev, R=self.R, lengths=lengths)

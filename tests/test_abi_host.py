@@ -46,15 +46,16 @@ def _a(x):
     return (x + 255) & ~255
 
 
-def expected_bytes(R, H, d_k, d_v, T, W, V, e, ew):
+def expected_bytes(R, H, d_k, d_v, T, W, V, e, ew, HK=None):
     """Workspace regions as documented in include/gdn_beam.h, each 256-aligned."""
+    HK = H if not HK else HK
     dvp = max(d_v, 32)
     nvg = -(-V // 128)
     Vt = -(-V // 32)                      # 32-code tiles
     nch = -(-W // 32)                     # 32-beam MFMA columns
     groups = nch + 1 + min(Vt, W)
     regions = [R * H * 4 * dvp * d_k, R * H * T * W * 4, R * H * T * W * d_v * 4,
-               R * H * T * W * d_k * e, R * W * T * 4, R * W * T * 4, R * W * T * 4, R * W * T * 4,
+               R * HK * T * W * d_k * e, R * W * T * 4, R * W * T * 4, R * W * T * 4, R * W * T * 4,
                R * W * 4, R * W * 4, R * W * 4, R * W * 4, R * W * 4, R * W * 4, R * W * d_v * 4, R * nch * 32 * d_v * 6, V * d_v * ew,
                R * Vt * W * 4, R * W * nvg * 16, R * W * 4, R * 16, R * Vt * W * 4, R * W * 4,
                R * groups * 4, R * groups * 32 * 4, R * W * 32 * 4, 64 * 4]
@@ -69,6 +70,10 @@ def test_workspace_formula(name):
     got = B.gdn_beam_workspace_bytes(B.make_config(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V,
                                                    wl.io, wl.wout))
     assert got == expected_bytes(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, e, ew)
+    # grouped value heads: the records' keys are per key head
+    g = B.gdn_beam_workspace_bytes(B.make_config(wl.R, 4 * wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V,
+                                                 wl.io, wl.wout, H_K=wl.H))
+    assert g == expected_bytes(wl.R, 4 * wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, e, ew, HK=wl.H)
 
 
 def test_persistent_state_is_gtr_capacity_and_beats_fullstate():
@@ -111,6 +116,8 @@ def test_workspace_does_not_grow_with_dv_dk_w():
     (dict(V_max=70000), B.GDN_ERR_CAPACITY),
     (dict(R=0), B.GDN_ERR_INVALID_ARG),
     (dict(H=-1), B.GDN_ERR_INVALID_ARG),
+    (dict(H=4, H_K=3), B.GDN_ERR_INVALID_ARG),
+    (dict(H_K=-2), B.GDN_ERR_INVALID_ARG),
 ])
 def test_config_errors(kw, status):
     cfg = _cfg(**kw)
@@ -159,12 +166,15 @@ def test_null_context_calls():
 
 def test_prefill_argument_errors():
     f = lambda *a: B.raw_status("gdn_beam_prefill", *a)
-    assert f(2, 3, 64, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_UNSUPPORTED
-    assert f(0, 3, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
-    assert f(2, 3, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == B.GDN_ERR_INVALID_ARG
-    assert f(2, 3, 128, 128, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
-    assert f(2, 3, 128, 128, 10, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
-    assert f(2, 3, 128, 128, 1 << 31, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_CAPACITY
+    assert f(2, 3, 0, 64, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_UNSUPPORTED
+    assert f(0, 3, 0, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 0, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 0, 128, 128, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 0, 128, 128, 10, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 0, 128, 128, 1 << 31, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_CAPACITY
+    # grouped value heads: H a multiple of H_K
+    assert f(2, 4, 3, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 4, -1, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
 
 
 def test_status_strings():

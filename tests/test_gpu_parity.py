@@ -31,6 +31,9 @@ DERIVED = {
     # six SID steps (five ancestor records at the last step)
     "tiny_t6": ("tiny", dict(T=6, widths=(8,) * 6)),
     "single_bf16_t6": ("single", dict(T=6, widths=(128,) * 6, io="bf16", wout="bf16")),
+    # grouped value heads: two (four) value heads per key head
+    "single_gqa": ("single", dict(H_K=2)),
+    "batch_gqa": ("batch", dict(H_K=4)),
 }
 
 
@@ -59,11 +62,11 @@ def _cmp_gdn(wl, dec, g, r, t, o, dpool, tol, heads=None):
     return o_ref
 
 
-@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2)])
+@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("single_gqa", 1)])
 def test_prefill_matches_oracle(name, R):
     from synth import device as sdev
     from linear_attention_beam_amd.decoder import prefill
-    wl = synth.get(name)
+    wl = _wl(name)
     dev = torch.device("cuda")
     p = sdev.prompts(wl, dev, R=R)
     for r in range(R):
@@ -81,7 +84,7 @@ def test_prefill_matches_oracle(name, R):
 
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_t6", 1),
-                                    ("single_bf16_t6", 1)])
+                                    ("single_bf16_t6", 1), ("single_gqa", 1), ("batch_gqa", 2)])
 def test_forced_parents_parity(name, R):
     wl = _wl(name)
     g = GpuDecode(wl, R=R, exact=range(R))
@@ -111,7 +114,7 @@ def test_forced_parents_parity(name, R):
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_v37", 1),
                                     ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("single_v300", 1),
-                                    ("single_bf16_t6", 1)])
+                                    ("single_bf16_t6", 1), ("single_gqa", 1)])
 def test_select_mode_parity(name, R):
     """Top-W drives the beams.  The oracle follows the GPU's choice (teacher forcing)
     after the selection itself has been checked against the exact top-W."""
