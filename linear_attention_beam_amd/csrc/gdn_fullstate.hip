@@ -46,17 +46,19 @@ __device__ __forceinline__ float row_sum(float x) {
   if constexpr (L >= 8) x += __uint_as_float(lane_xor<4>(__float_as_uint(x)));
   if constexpr (L >= 16) x += __uint_as_float(lane_xor<8>(__float_as_uint(x)));
   if constexpr (L >= 32) x += __uint_as_float(lane_xor<16>(__float_as_uint(x)));
+  if constexpr (L >= 64) x += __uint_as_float(lane_xor<32>(__float_as_uint(x)));
   return x;
 }
 
 // Lanes: DK / 4 per state row (one 16-byte column slice each), 256 / (DK / 4) rows
-// at a time; every row of the parent state is loaded before any arithmetic (all
-// loads in flight), rows stream out as they finish.
+// at a time; the parent state's rows are loaded up to CH row batches at once (all of
+// them in flight), then computed and streamed out.
 template <int DK, int DV, bool BF16>
 __global__ void __launch_bounds__(256) fullstate_kernel(FullK a) {
   constexpr int LPR = DK / 4;
   constexpr int RPI = 256 / LPR;
-  constexpr int IT = (DV + RPI - 1) / RPI;
+  constexpr int NB = (DV + RPI - 1) / RPI;       // row batches
+  constexpr int CH = NB > 16 ? 16 : NB;          // batches held in registers at once
   const size_t bid = blockIdx.x;                 // ((r * H + h) * W + b)
   const int b = int(bid % a.W);
   const size_t rh = bid / a.W;
@@ -77,18 +79,20 @@ __global__ void __launch_bounds__(256) fullstate_kernel(FullK a) {
   const f32x4 k4 = load4<BF16>(a.k, kbeam * DK + 4 * lr);
   const f32x4 q4 = load4<BF16>(a.q, kbeam * DK + 4 * lr);
   const float al = a.alpha[beam], be = a.beta[beam];
-  f32x4 pr[IT];
-  float vr[IT];
+  const float kq = row_sum<LPR>(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
+#pragma unroll 1
+  for (int b0 = 0; b0 < NB; b0 += CH) {
+  f32x4 pr[CH];
+  float vr[CH];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int row = row0 + it * RPI;
+  for (int it = 0; it < CH; ++it) {
+    const int row = row0 + (b0 + it) * RPI;
     pr[it] = row < DV ? *reinterpret_cast<const f32x4*>(P + size_t(row) * DK + 4 * lr) : f32x4{};
     vr[it] = row < DV ? load1<BF16>(a.v, beam * DV + row) : 0.0f;
   }
-  const float kq = row_sum<LPR>(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int row = row0 + it * RPI;
+  for (int it = 0; it < CH; ++it) {
+    const int row = row0 + (b0 + it) * RPI;
     const f32x4 x = pr[it];
     const float uk = row_sum<LPR>(x[0] * k4[0] + x[1] * k4[1] + x[2] * k4[2] + x[3] * k4[3]);
     const float uq = row_sum<LPR>(x[0] * q4[0] + x[1] * q4[1] + x[2] * q4[2] + x[3] * q4[3]);
@@ -100,6 +104,7 @@ __global__ void __launch_bounds__(256) fullstate_kernel(FullK a) {
       *reinterpret_cast<f32x4*>(S + size_t(row) * DK + 4 * lr) = s;
       if (lr == 0) a.o[beam * DV + row] = fmaf(dl, kq, al * uq);      // S q
     }
+  }
   }
 }
 
@@ -121,6 +126,7 @@ int launch_fullstate(const FullStepArgs& s, hipStream_t st) {
   if (s.d_k == 16 && s.d_v == 16) return bf ? launch_full_t<16, 16, true>(s, st) : launch_full_t<16, 16, false>(s, st);
   if (s.d_k == 128 && s.d_v == 128) return bf ? launch_full_t<128, 128, true>(s, st) : launch_full_t<128, 128, false>(s, st);
   if (s.d_k == 128 && s.d_v == 256) return bf ? launch_full_t<128, 256, true>(s, st) : launch_full_t<128, 256, false>(s, st);
+  if (s.d_k == 256 && s.d_v == 256 && bf) return launch_full_t<256, 256, true>(s, st);
   return int(hipErrorInvalidValue);
 }
 

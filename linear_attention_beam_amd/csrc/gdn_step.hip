@@ -429,16 +429,24 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
 
 // ---------------------------------------------------------------- prefill (eq. 3)
 
-// One workgroup per (request, head); thread (row, half) holds S[row][half*DK/2 ..] in
+// One workgroup per (request, head, block of up to 128 rows): rows of S evolve
+// independently given the token.  Thread (row, part) holds S[row][part*COLS ..] in
 // registers.  Each token: u = S k (row dot, reduced over the row's lanes),
 // S <- alpha S + beta (v - alpha u) k^T.
 template <int DK, int DV>
-__global__ void __launch_bounds__(DV < 32 ? 256 : 2 * DV) prefill_kernel(PrefillArgs a) {
-  constexpr int TPR = DV < 32 ? 256 / DV : 2;        // lanes per row
+struct PrefillCfg {
+  static constexpr int RB = DV < 128 ? DV : 128;                         // rows per block
+  static constexpr int TPR = DV < 32 ? 256 / DV : (DK > 128 ? 4 : 2);    // lanes per row
+  static constexpr int NT = RB * TPR;
+};
+
+template <int DK, int DV>
+__global__ void __launch_bounds__((PrefillCfg<DK, DV>::NT)) prefill_kernel(PrefillArgs a) {
+  constexpr int TPR = PrefillCfg<DK, DV>::TPR;
   constexpr int COLS = DK / TPR;
   const int rh = blockIdx.x, r = rh / a.H, h = rh % a.H;
   const int hk = h / (a.H / a.HK);                        // key head of value head h
-  const int row = threadIdx.x / TPR, cp = threadIdx.x % TPR;
+  const int row = blockIdx.y * PrefillCfg<DK, DV>::RB + threadIdx.x / TPR, cp = threadIdx.x % TPR;
   int beg = a.offsets[r], end = a.offsets[r + 1];
   beg = beg < 0 ? 0 : (beg > a.N ? int(a.N) : beg);
   end = end < beg ? beg : (end > a.N ? int(a.N) : end);
@@ -519,13 +527,14 @@ int launch_step(const StepArgs& a, hipStream_t s) {
   if (a.d_k == 16 && a.d_v == 16) return bf ? launch_step_t<16, 16, true>(a, s) : launch_step_t<16, 16, false>(a, s);
   if (a.d_k == 128 && a.d_v == 128) return bf ? launch_step_t<128, 128, true>(a, s) : launch_step_t<128, 128, false>(a, s);
   if (a.d_k == 128 && a.d_v == 256) return bf ? launch_step_t<128, 256, true>(a, s) : launch_step_t<128, 256, false>(a, s);
+  if (a.d_k == 256 && a.d_v == 256 && bf) return launch_step_t<256, 256, true>(a, s);
   return int(hipErrorInvalidValue);
 }
 
 template <int DK, int DV>
 static int launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
-  constexpr int threads = DV < 32 ? 256 : 2 * DV;
-  hipLaunchKernelGGL((prefill_kernel<DK, DV>), dim3(a.R * a.H), dim3(threads), 0, s, a);
+  using C = PrefillCfg<DK, DV>;
+  hipLaunchKernelGGL((prefill_kernel<DK, DV>), dim3(a.R * a.H, DV / C::RB), dim3(C::NT), 0, s, a);
   return last_launch_error();
 }
 
@@ -534,6 +543,7 @@ int launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.d_k == 16 && a.d_v == 16) return launch_prefill_t<16, 16>(a, s);
   if (a.d_k == 128 && a.d_v == 128) return launch_prefill_t<128, 128>(a, s);
   if (a.d_k == 128 && a.d_v == 256) return launch_prefill_t<128, 256>(a, s);
+  if (a.d_k == 256 && a.d_v == 256) return launch_prefill_t<256, 256>(a, s);
   return int(hipErrorInvalidValue);
 }
 

@@ -26,11 +26,20 @@ def _fullstate(g, states, t):
     return g.o[t]
 
 
-@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("single_gqa", 1)])
+VARIANTS = {"single_gqa": ("single", dict(H_K=2)),
+            "single_dk256": ("single", dict(d_k=256, d_v=256, io="bf16", wout="bf16"))}
+
+
+@pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("single_gqa", 1),
+                                    ("single_dk256", 1)])
 def test_fullstate_forced_parity(name, R):
     """Fixed parent maps: o_t of every step against the float64 FullState oracle;
     ancestry and SID prefixes bit-exact."""
-    wl = synth.get(name) if name != "single_gqa" else synth.get("single").scaled(name=name, H_K=2)
+    if name in VARIANTS:
+        base, kw = VARIANTS[name]
+        wl = synth.get(base).scaled(name=name, **kw)
+    else:
+        wl = synth.get(name)
     g = GpuDecode(wl, R=R, exact=range(R))
     tol = TOL[wl.io]
     states = g.dec.alloc_states()
