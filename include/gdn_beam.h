@@ -55,7 +55,9 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 typedef struct {
   int32_t R, H;        /* requests, GDN value heads per request                           */
-  int32_t d_k, d_v;    /* head dims; supported (d_k, d_v): (16,16), (128,128), (128,256)  */
+  int32_t d_k, d_v;    /* head dims; supported (d_k, d_v): (16,16), (128,128), (128,256), */
+                       /* (128,512), and with bf16 io (256,256), (256,512); d_v = 512   */
+                       /* needs a bf16 codebook                                          */
   int32_t T_max;       /* SID decode steps (1..8)                                         */
   int32_t W_max;       /* peak beam width = GTR slots per step (1..1024)                  */
   int32_t V_max;       /* largest codebook passed to select (1..65536)                    */

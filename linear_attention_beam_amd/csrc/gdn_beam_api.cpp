@@ -36,7 +36,7 @@ gdn_status hip_fail(int err, const char* where) {
 
 bool dims_supported(int d_k, int d_v) {
   return (d_k == 16 && d_v == 16) || (d_k == 128 && d_v == 128) || (d_k == 128 && d_v == 256) ||
-         (d_k == 256 && d_v == 256);
+         (d_k == 128 && d_v == 512) || (d_k == 256 && d_v == 256) || (d_k == 256 && d_v == 512);
 }
 
 gdn_status check_config(const gdn_beam_config* c) {
@@ -50,6 +50,8 @@ gdn_status check_config(const gdn_beam_config* c) {
   if (!dims_supported(c->d_k, c->d_v)) return GDN_ERR_UNSUPPORTED;
   // d_k = 256 with fp32 q, k, v would stage 200 KB per workgroup: bf16 io only
   if (c->d_k == 256 && c->io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  // an fp32 codebook keeps z in registers as fp32: d_v <= 256 with it
+  if (c->d_v > 256 && c->wout_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
   if (c->T_max > kMaxT || c->W_max > kMaxW || c->V_max > kMaxV) return GDN_ERR_CAPACITY;
   // flat candidate index b*V + c and per-request scratch sizes must fit in 31 bits
   if (int64_t(c->W_max) * c->V_max >= (int64_t(1) << 31)) return GDN_ERR_CAPACITY;

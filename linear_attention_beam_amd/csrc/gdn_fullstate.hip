@@ -127,6 +127,8 @@ int launch_fullstate(const FullStepArgs& s, hipStream_t st) {
   if (s.d_k == 128 && s.d_v == 128) return bf ? launch_full_t<128, 128, true>(s, st) : launch_full_t<128, 128, false>(s, st);
   if (s.d_k == 128 && s.d_v == 256) return bf ? launch_full_t<128, 256, true>(s, st) : launch_full_t<128, 256, false>(s, st);
   if (s.d_k == 256 && s.d_v == 256 && bf) return launch_full_t<256, 256, true>(s, st);
+  if (s.d_k == 128 && s.d_v == 512) return bf ? launch_full_t<128, 512, true>(s, st) : launch_full_t<128, 512, false>(s, st);
+  if (s.d_k == 256 && s.d_v == 512 && bf) return launch_full_t<256, 512, true>(s, st);
   return int(hipErrorInvalidValue);
 }
 

@@ -267,33 +267,64 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
         if (e < NE) tile[buf][(e / (DV / 8)) * RS + e % (DV / 8)] = stg[u];
       }
     };
-    // the first tile's loads go out before the z operand's (loads complete in order, so
-    // staging the tile then waits for those alone)
-    fetch(code_lo);
     const u32x4* zb = a.zf + zf_lane_base(r, a.nch_max, DV, (wvalid ? chunk : 0) * 32, hf) + m;
-    u32x4 zh[KS], zm[KS], zl[KS];
+    if constexpr (KS <= 16) {
+      // the first tile's loads go out before the z operand's (loads complete in order,
+      // so staging the tile then waits for those alone)
+      fetch(code_lo);
+      u32x4 zh[KS], zm[KS], zl[KS];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      zh[kk] = zb[(3 * kk) * 64];
-      zm[kk] = zb[(3 * kk + 1) * 64];
-      zl[kk] = zb[(3 * kk + 2) * 64];
-    }
-    put(0);
-    // wait for the whole z operand here, so that inside the loop only the prefetched
-    // tile is waited for, after the MFMAs
-    asm volatile("" ::"v"(zl[KS - 1][0]));
-    __syncthreads();
-    int buf = 0;
-    for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
-      const bool more = c0 + 32 < code_hi;         // block-uniform
-      if (more) fetch(c0 + 32);
-      u32x4 w[KS];
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) w[kk] = tile[buf][m * RS + (HV / 8) * hf + kk];
-      fold(block_mfma_bf16<KS>(w, zh, zm, zl), c0);
-      if (more) put(buf ^ 1);
+      for (int kk = 0; kk < KS; ++kk) {
+        zh[kk] = zb[(3 * kk) * 64];
+        zm[kk] = zb[(3 * kk + 1) * 64];
+        zl[kk] = zb[(3 * kk + 2) * 64];
+      }
+      put(0);
+      // wait for the whole z operand here, so that inside the loop only the prefetched
+      // tile is waited for, after the MFMAs
+      asm volatile("" ::"v"(zl[KS - 1][0]));
       __syncthreads();
-      buf ^= 1;
+      int buf = 0;
+      for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
+        const bool more = c0 + 32 < code_hi;         // block-uniform
+        if (more) fetch(c0 + 32);
+        u32x4 w[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) w[kk] = tile[buf][m * RS + (HV / 8) * hf + kk];
+        fold(block_mfma_bf16<KS>(w, zh, zm, zl), c0);
+        if (more) put(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+      }
+    } else {
+      // d_v > 256: the z operand does not fit in registers; each tile re-reads it in
+      // chunks of eight k-steps (same MFMA order, kk ascending)
+      constexpr int KZ = 8;
+      fetch(code_lo);
+      put(0);
+      __syncthreads();
+      int buf = 0;
+      for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
+        const bool more = c0 + 32 < code_hi;         // block-uniform
+        if (more) fetch(c0 + 32);
+        f32x16 acc = {};
+#pragma unroll 1
+        for (int k0 = 0; k0 < KS; k0 += KZ) {
+          u32x4 zh[KZ], zm[KZ], zl[KZ], w[KZ];
+#pragma unroll
+          for (int kk = 0; kk < KZ; ++kk) {
+            zh[kk] = zb[(3 * (k0 + kk)) * 64];
+            zm[kk] = zb[(3 * (k0 + kk) + 1) * 64];
+            zl[kk] = zb[(3 * (k0 + kk) + 2) * 64];
+            w[kk] = tile[buf][m * RS + (HV / 8) * hf + k0 + kk];
+          }
+          acc = block_mfma_bf16<KZ>(w, zh, zm, zl, acc);
+        }
+        fold(acc, c0);
+        if (more) put(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+      }
     }
   } else {
     const float* zr = a.z + (size_t(r) * a.W_max + (bvalid ? b : 0)) * DV + HV * hf;
@@ -1035,6 +1066,7 @@ static int launch_by_dv(const SelectArgs& a, const LogitsK& lk, const RefineK& r
   if (a.d_v == 16) return launch_dv<16>(a, lk, rk, groups, s, refine);
   if (a.d_v == 128) return launch_dv<128>(a, lk, rk, groups, s, refine);
   if (a.d_v == 256) return launch_dv<256>(a, lk, rk, groups, s, refine);
+  if (a.d_v == 512) return launch_dv<512>(a, lk, rk, groups, s, refine);
   return int(hipErrorInvalidValue);
 }
 

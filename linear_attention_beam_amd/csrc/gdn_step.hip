@@ -91,11 +91,13 @@ struct StepK {
 template <int DK, int DV, bool BF16>
 struct StepCfg {
   static constexpr int DVP = DV < 32 ? 32 : DV;
-  static constexpr int NW = DVP / 32;            // one wave per 32-row block of d_v
+  static constexpr int DVB = DVP > 256 ? 256 : DVP;   // rows of d_v per workgroup
+  static constexpr int NRB = DVP / DVB;          // workgroups per (request, head)
+  static constexpr int NW = DVB / 32;            // one wave per 32-row block of d_v
   static constexpr int NT = NW * 64;
   static constexpr int E = BF16 ? 2 : 4;         // bytes per io element
   static constexpr int QB = DK * E;              // bytes of one q / k row
-  static constexpr int VB = DV * E;              // bytes of one v row
+  static constexpr int VB = (DV < DVB ? DV : DVB) * E;   // bytes of a workgroup's v rows
   static constexpr int QROW = QB + 16;           // padded LDS rows (bank spread)
   static constexpr int VROW = VB + 16;
   static constexpr int QU = 32 * QB / 16 / NT;   // 16-byte staging units per thread
@@ -155,8 +157,11 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
   __shared__ int ord[NJ > 0 ? kMaxW : 1];
   float* sc = reinterpret_cast<float*>(lds + 2 * C::SLOT);
 
-  const int rh = xcd_work_id();
-  if (rh >= a.nrh) return;                                // whole block, before any barrier
+  const int wid = xcd_work_id();
+  if (wid >= a.nrh * C::NRB) return;                      // whole block, before any barrier
+  // d_v rows beyond 256 go to further workgroups of the same (request, head): rows of
+  // the state evolve independently; the per-beam dot products are redone by each
+  const int rh = wid / C::NRB, rb = wid % C::NRB, row_base = rb * C::DVB;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m = lane & 31, hf = lane >> 5;
   const int W = a.W, r = rh / a.H;
@@ -186,7 +191,7 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
   {
     const u32x4* fr = reinterpret_cast<const u32x4*>(a.s_frag + size_t(rh) * 4 * C::DVP * DK);
 #pragma unroll
-    for (int i = 0; i < NA; ++i) afr[i] = fr[(w * NA + i) * 64 + lane];
+    for (int i = 0; i < NA; ++i) afr[i] = fr[((rb * C::NW + w) * NA + i) * 64 + lane];
   }
 
   // ---- staging of one chunk: registers <- global (contiguous), LDS <- registers
@@ -210,7 +215,8 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     for (int i = 0; i < C::VU; ++i) {
       const int u = tid + i * NT;
       if (u / UPV < nb)
-        sv[i] = *reinterpret_cast<const u32x4*>(vg + (base + beam_of(c0 + u / UPV)) * C::VB + size_t(u % UPV) * 16);
+        sv[i] = *reinterpret_cast<const u32x4*>(vg + ((base + beam_of(c0 + u / UPV)) * DV + row_base) * C::E +
+                                                size_t(u % UPV) * 16);
     }
     if (tid < 64 && (tid & 31) < nb) {
       const size_t bi = base + beam_of(c0 + (tid & 31));
@@ -282,8 +288,9 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     }
     const bool valid = m < nb;
     const int b = valid ? beam_of(c0 + m) : 0;
-    const int row0 = 32 * w + 16 * hf;
-    const int rowl = min(row0, DV - 16);                 // in range (rows >= DV unused)
+    const int row0 = 32 * w + 16 * hf;                   // first row of this lane half (local)
+    const int grow0 = row_base + row0;                   // ... of the state
+    const int rowl = min(grow0, DV - 16);                // in range (rows >= DV unused)
     f32x4 dj[NJ1][4];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -369,7 +376,7 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
 
     {
       // accumulator register i of this lane = physical row row0 + i of beam b
-      if (row0 < DV && valid) {
+      if (grow0 < DV && valid) {
         const float* s = sc + m * SCN;
         const float kq = s[0];
         const float al = Lab[m], be = Lab[32 + m];
@@ -396,8 +403,8 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
           for (int q4 = 0; q4 < 4; ++q4)
             for (int i = 0; i < 4; ++i) vin[4 * q4 + i] = vp[q4][i];
         }
-        f32x4* dout = reinterpret_cast<f32x4*>(a.gtr_delta + (slot_t * a.W_max + b) * DV + row0);
-        f32x4* oout = reinterpret_cast<f32x4*>(a.o + (size_t(rh) * W + b) * DV + row0);
+        f32x4* dout = reinterpret_cast<f32x4*>(a.gtr_delta + (slot_t * a.W_max + b) * DV + grow0);
+        f32x4* oout = reinterpret_cast<f32x4*>(a.o + (size_t(rh) * W + b) * DV + grow0);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           f32x4 dt, ot;
@@ -416,11 +423,11 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     // ---- append: k_t rows to slots (t, b) of the chunk's beams (once per key head),
     // and alpha_t
     {
-      if (key_writer)
+      if (key_writer && rb == 0)
         for (int u = tid; u < nb * UPQ; u += NT)
           *reinterpret_cast<u32x4*>(keyg + (kslot_t * a.W_max + beam_of(c0 + u / UPQ)) * C::QB + (u % UPQ) * 16) =
               *reinterpret_cast<const u32x4*>(Lk + (u / UPQ) * QROW + (u % UPQ) * 16);
-      if (tid < nb) a.gtr_alpha[slot_t * a.W_max + beam_of(c0 + tid)] = Lab[tid];
+      if (rb == 0 && tid < nb) a.gtr_alpha[slot_t * a.W_max + beam_of(c0 + tid)] = Lab[tid];
     }
     if (c + 1 < nch) stage_store((c + 1) & 1);
     __syncthreads();
@@ -500,8 +507,9 @@ template <int DK, int DV, bool BF16>
 static int launch_step_t(const StepArgs& a, hipStream_t s) {
   constexpr int NT = StepCfg<DK, DV, BF16>::NT;
   const int nrh = a.R * a.H;
-  // one workgroup per (request, head): S_ctx is read once and kept in registers
-  const long grid = (long(nrh) + 7) / 8 * 8;
+  // one workgroup per (request, head, 256 rows of d_v): S_ctx is read once and kept in
+  // registers
+  const long grid = (long(nrh) * StepCfg<DK, DV, BF16>::NRB + 7) / 8 * 8;
   char* ws = static_cast<char*>(a.ws);
   StepK k{a.H, a.HK, a.W, a.W_max, a.T_max, a.t, nrh, a.q, a.k, a.v, a.alpha, a.beta, a.o,
           ws + a.L.s_frag, reinterpret_cast<float*>(ws + a.L.gtr_alpha),
@@ -528,6 +536,8 @@ int launch_step(const StepArgs& a, hipStream_t s) {
   if (a.d_k == 128 && a.d_v == 128) return bf ? launch_step_t<128, 128, true>(a, s) : launch_step_t<128, 128, false>(a, s);
   if (a.d_k == 128 && a.d_v == 256) return bf ? launch_step_t<128, 256, true>(a, s) : launch_step_t<128, 256, false>(a, s);
   if (a.d_k == 256 && a.d_v == 256 && bf) return launch_step_t<256, 256, true>(a, s);
+  if (a.d_k == 128 && a.d_v == 512) return bf ? launch_step_t<128, 512, true>(a, s) : launch_step_t<128, 512, false>(a, s);
+  if (a.d_k == 256 && a.d_v == 512 && bf) return launch_step_t<256, 512, true>(a, s);
   return int(hipErrorInvalidValue);
 }
 
@@ -544,6 +554,8 @@ int launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.d_k == 128 && a.d_v == 128) return launch_prefill_t<128, 128>(a, s);
   if (a.d_k == 128 && a.d_v == 256) return launch_prefill_t<128, 256>(a, s);
   if (a.d_k == 256 && a.d_v == 256) return launch_prefill_t<256, 256>(a, s);
+  if (a.d_k == 128 && a.d_v == 512) return launch_prefill_t<128, 512>(a, s);
+  if (a.d_k == 256 && a.d_v == 512) return launch_prefill_t<256, 512>(a, s);
   return int(hipErrorInvalidValue);
 }
 

@@ -119,6 +119,8 @@ def test_workspace_does_not_grow_with_dv_dk_w():
     (dict(H=4, H_K=3), B.GDN_ERR_INVALID_ARG),
     (dict(d_k=256, d_v=256, io="f32"), B.GDN_ERR_UNSUPPORTED),
     (dict(d_k=256, d_v=128), B.GDN_ERR_UNSUPPORTED),
+    (dict(d_v=512, wout="f32"), B.GDN_ERR_UNSUPPORTED),
+    (dict(d_v=384), B.GDN_ERR_UNSUPPORTED),
     (dict(H_K=-2), B.GDN_ERR_INVALID_ARG),
 ])
 def test_config_errors(kw, status):

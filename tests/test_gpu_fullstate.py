@@ -27,11 +27,12 @@ def _fullstate(g, states, t):
 
 
 VARIANTS = {"single_gqa": ("single", dict(H_K=2)),
-            "single_dk256": ("single", dict(d_k=256, d_v=256, io="bf16", wout="bf16"))}
+            "single_dk256": ("single", dict(d_k=256, d_v=256, io="bf16", wout="bf16")),
+            "single_dv512": ("single", dict(d_v=512, io="bf16", wout="bf16"))}
 
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("single_gqa", 1),
-                                    ("single_dk256", 1)])
+                                    ("single_dk256", 1), ("single_dv512", 1)])
 def test_fullstate_forced_parity(name, R):
     """Fixed parent maps: o_t of every step against the float64 FullState oracle;
     ancestry and SID prefixes bit-exact."""

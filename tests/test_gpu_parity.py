@@ -36,6 +36,10 @@ DERIVED = {
     "batch_gqa": ("batch", dict(H_K=4)),
     # wide heads: d_k = d_v = 256 (bf16 io)
     "single_dk256": ("single", dict(d_k=256, d_v=256, io="bf16", wout="bf16")),
+    # d_v = 512: two workgroups per (request, head) in the step, z re-read in chunks
+    "single_dv512": ("single", dict(d_v=512, io="bf16", wout="bf16")),
+    "single_dv512_f32io": ("single", dict(d_v=512, wout="bf16")),
+    "single_dk256_dv512": ("single", dict(d_k=256, d_v=512, io="bf16", wout="bf16")),
 }
 
 
@@ -65,7 +69,7 @@ def _cmp_gdn(wl, dec, g, r, t, o, dpool, tol, heads=None):
 
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("single_gqa", 1),
-                                    ("single_dk256", 1)])
+                                    ("single_dk256", 1), ("single_dk256_dv512", 1)])
 def test_prefill_matches_oracle(name, R):
     from synth import device as sdev
     from linear_attention_beam_amd.decoder import prefill
@@ -88,7 +92,8 @@ def test_prefill_matches_oracle(name, R):
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_t6", 1),
                                     ("single_bf16_t6", 1), ("single_gqa", 1), ("batch_gqa", 2),
-                                    ("single_dk256", 1)])
+                                    ("single_dk256", 1), ("single_dv512", 1), ("single_dv512_f32io", 1),
+                                    ("single_dk256_dv512", 1)])
 def test_forced_parents_parity(name, R):
     wl = _wl(name)
     g = GpuDecode(wl, R=R, exact=range(R))
@@ -118,7 +123,8 @@ def test_forced_parents_parity(name, R):
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_v37", 1),
                                     ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("single_v300", 1),
-                                    ("single_bf16_t6", 1), ("single_gqa", 1), ("single_dk256", 1)])
+                                    ("single_bf16_t6", 1), ("single_gqa", 1), ("single_dk256", 1),
+                                    ("single_dv512", 1), ("single_dk256_dv512", 1)])
 def test_select_mode_parity(name, R):
     """Top-W drives the beams.  The oracle follows the GPU's choice (teacher forcing)
     after the selection itself has been checked against the exact top-W."""
