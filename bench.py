@@ -61,18 +61,19 @@ def log(args, *a):
 def step_bytes(wl, t, distinct):
     """Algorithmic HBM bytes of one gdn_beam_step launch at step t.
 
-    Per (request, head): S_ctx once (4 d_v d_k); per beam: q, k, v (e each),
-    alpha, beta (8), the new record (4 + 4 d_v + e d_k) and o_t (4 d_v); per distinct
-    ancestor record referenced: 4 + 4 d_v + e d_k.  Per request: t ancestry indices
-    per beam (4 t W_t).  `distinct[r]` = distinct (step, slot) records request r's
-    beams reference at step t (identical for every head).
+    Per (request, value head): S_ctx once (4 d_v d_k); per beam: v (e d_v), alpha,
+    beta (8), the new record's alpha and delta (4 + 4 d_v) and o_t (4 d_v).  Per
+    (request, key head) and beam: q, k (e d_k each) and the new record's key (e d_k).
+    Per distinct ancestor record referenced: 4 + 4 d_v per value head, e d_k per key
+    head.  Per request: t ancestry indices per beam (4 t W_t).  `distinct[r]` =
+    distinct (step, slot) records request r's beams reference at step t.
     """
     e = 2 if wl.io == "bf16" else 4
     W = wl.width(t)
-    rec = 4 + 4 * wl.d_v + e * wl.d_k
-    per_rh = 4 * wl.d_v * wl.d_k + W * (e * (2 * wl.d_k + wl.d_v) + 8 + rec + 4 * wl.d_v)
-    total = wl.R * wl.H * per_rh + 4 * t * W * wl.R
-    total += wl.H * rec * int(np.sum(distinct))
+    per_rh = 4 * wl.d_v * wl.d_k + W * (e * wl.d_v + 8 + (4 + 4 * wl.d_v) + 4 * wl.d_v)
+    per_rk = W * 3 * e * wl.d_k
+    total = wl.R * (wl.H * per_rh + wl.hk * per_rk) + 4 * t * W * wl.R
+    total += (wl.H * (4 + 4 * wl.d_v) + wl.hk * e * wl.d_k) * int(np.sum(distinct))
     return total
 
 

@@ -88,6 +88,22 @@ WORKLOADS = {
         L_prompt=(512, 8192), T=4, widths=(64, 256, 512, 1024), V=4096,
         parents="uniform", seed=1005,
         summary="128 requests, 16 heads, d_k=128, d_v=256, bf16 io, W 64->256->512->1024, V=4096, T=4"),
+    # geometry variants of the operator sweep at the batch shape
+    "wide": Workload(
+        name="wide", R=32, H=16, d_k=256, d_v=256, io="bf16", wout="bf16",
+        L_prompt=(1024, 1024), T=4, widths=(256, 256, 256, 256), V=1024,
+        parents="uniform", seed=1006,
+        summary="32 requests, 16 heads, d_k=d_v=256, bf16 io, W=256, V=1024, T=4"),
+    "grouped": Workload(
+        name="grouped", R=32, H=32, H_K=16, d_k=128, d_v=128, io="bf16", wout="bf16",
+        L_prompt=(1024, 1024), T=4, widths=(256, 256, 256, 256), V=1024,
+        parents="uniform", seed=1007,
+        summary="32 requests, 32 value heads on 16 key heads, d=128, bf16 io, W=256, V=1024, T=4"),
+    "wide_v": Workload(
+        name="wide_v", R=32, H=16, d_k=128, d_v=512, io="bf16", wout="bf16",
+        L_prompt=(1024, 1024), T=4, widths=(256, 256, 256, 256), V=1024,
+        parents="uniform", seed=1008,
+        summary="32 requests, 16 heads, d_k=128, d_v=512, bf16 io, W=256, V=1024, T=4"),
 }
 
 
