@@ -281,20 +281,50 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
       }
       put(0);
       // wait for the whole z operand here, so that inside the loop only the prefetched
-      // tile is waited for, after the MFMAs
+      // tile is waited for
       asm volatile("" ::"v"(zl[KS - 1][0]));
       __syncthreads();
-      int buf = 0;
-      for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
-        const bool more = c0 + 32 < code_hi;         // block-uniform
-        if (more) fetch(c0 + 32);
+      if (code_lo + 32 < code_hi) fetch(code_lo + 32);
+      auto mfma_tile = [&](int buf) {
         u32x4 w[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) w[kk] = tile[buf][m * RS + (HV / 8) * hf + kk];
-        fold(block_mfma_bf16<KS>(w, zh, zm, zl), c0);
-        if (more) put(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
+        return block_mfma_bf16<KS>(w, zh, zm, zl);
+      };
+      // software pipeline: the MFMAs of tile i + 1 are issued before the epilogue of
+      // tile i, so the matrix cores and the VALU work at the same time.  Tile i + 1 is
+      // staged into the buffer tile i - 1 used (every wave finished with it before the
+      // previous barrier).
+      // (d_v = 256 holds twice the z operand: there the tiles go one after the other)
+      if constexpr (KS <= 8) {
+        f32x16 acc = mfma_tile(0);
+        int buf = 0;
+        for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
+          const bool more = c0 + 32 < code_hi;       // block-uniform
+          if (more) {
+            put(buf ^ 1);
+            __syncthreads();
+            if (c0 + 64 < code_hi) fetch(c0 + 64);
+            const f32x16 nxt = mfma_tile(buf ^ 1);
+            fold(acc, c0);
+            acc = nxt;
+          } else {
+            fold(acc, c0);
+          }
+          buf ^= 1;
+        }
+      } else {
+        int buf = 0;
+        for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
+          const bool more = c0 + 32 < code_hi;       // block-uniform
+          fold(mfma_tile(buf), c0);
+          if (more) {
+            put(buf ^ 1);
+            __syncthreads();
+            if (c0 + 64 < code_hi) fetch(c0 + 64);
+          }
+          buf ^= 1;
+        }
       }
     } else {
       // d_v > 256: the z operand does not fit in registers; each tile re-reads it in
