@@ -375,3 +375,44 @@ def test_per_step_codebooks(name):
         dec.advance(t, sel["parent"], sel["token"], s_ref[sel["parent"], sel["token"]])
         anc = g.export(B.GDN_EXPORT_ANCESTRY)
         np.testing.assert_array_equal(anc[0][:K, :t + 1], dec.anc)
+
+
+def test_decode_is_deterministic():
+    """Two decodes of the same inputs give bit-identical outputs, selections, ancestry
+    and records (every reduction runs in a fixed order; only the processing order of
+    equal-parent beams may differ, and it never changes a value)."""
+    wl = synth.get("batch")
+    g = GpuDecode(wl, R=4, exact=())
+    runs = []
+    for _ in range(2):
+        g.init()
+        rec = []
+        for t in range(wl.T):
+            rec.append(to_np(g.step(t)).copy())
+            sel = g.select(t)
+            rec += [sel["parent"].copy(), sel["token"].copy(), sel["score"].copy()]
+        for what in (B.GDN_EXPORT_ANCESTRY, B.GDN_EXPORT_TOKENS, B.GDN_EXPORT_CUM,
+                     B.GDN_EXPORT_GTR_DELTA, B.GDN_EXPORT_GTR_KEY):
+            rec.append(g.export(what).copy())
+        runs.append(rec)
+    for a, b in zip(*runs):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+
+
+def test_nan_scores_terminate():
+    """A NaN in one beam's output reaches every score of that beam through its
+    log-sum-exp.  The selection must still return (its radix passes always end), with
+    every parent and token in range and the ancestry valid for the next step."""
+    wl = synth.get("single")
+    g = GpuDecode(wl, R=1, exact=())
+    g.init()
+    g.step(0)
+    g.o[0][0, :, 3, :] = float("nan")
+    sel = g.select(0)
+    K = wl.width(1)
+    assert np.all((sel["parent"][0] >= 0) & (sel["parent"][0] < wl.width(0)))
+    assert np.all((sel["token"][0] >= 0) & (sel["token"][0] < wl.V))
+    anc = g.export(B.GDN_EXPORT_ANCESTRY)
+    assert np.all((anc[0][:K, 0] >= 0) & (anc[0][:K, 0] < wl.width(0)))
+    g.step(1)                     # the next step gathers through that ancestry
+    torch.cuda.synchronize()
