@@ -50,6 +50,15 @@ __device__ __forceinline__ float cand_score(float cum, float logit, float lse) {
   return cum + (logit - lse);
 }
 
+// Work item of block b of an n-block 1-D grid: blocks are dealt round-robin to the 8
+// XCDs, so XCD x runs blocks x, x + 8, ...; it is given the contiguous work range
+// [x q + min(x, n % 8), ...) with q = n / 8 (a bijection for any n), so work items
+// next to each other share one XCD's L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int x = b & 7, q = n >> 3, rr = n & 7;
+  return x * q + (x < rr ? x : rr) + (b >> 3);
+}
+
 __device__ __forceinline__ int xcd_work_id() {
   // consecutive blocks are dealt round-robin to the 8 XCDs; give each XCD a
   // contiguous range of work so the workgroups of one (request, head) share an L2

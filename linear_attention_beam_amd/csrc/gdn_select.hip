@@ -199,10 +199,14 @@ template <int DV, bool WBF16>
 __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   constexpr int HV = DV / 2;
   const int wave = threadIdx.x >> 6;
-  const int vg = blockIdx.x % a.nvg;
-  const int chunk = (blockIdx.x / a.nvg) * kLogitsWaves + wave;
+  // 1-D grid over (request, chunk block, code group), code group fastest; the blocks
+  // of one request (which read the same z operand) share an XCD
+  const int nx = ((a.nchunk + kLogitsWaves - 1) / kLogitsWaves) * a.nvg;
+  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int r = wid / nx, bx = wid % nx;
+  const int vg = bx % a.nvg;
+  const int chunk = (bx / a.nvg) * kLogitsWaves + wave;
   const bool wvalid = chunk < a.nchunk;
-  const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
   const int b = (wvalid ? chunk : 0) * 32 + m;
   const bool bvalid = wvalid && b < a.W;
@@ -856,54 +860,61 @@ __device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
   return (uint64_t(lane_xor<J>(uint32_t(v >> 32))) << 32) | lane_xor<J>(uint32_t(v));
 }
 
-// One compare-exchange stage of a bitonic sort, one entry per thread of the block,
-// descending within blocks of k where (tid & k) == 0: partner tid ^ J inside the wave,
-// through LDS (two barriers) across waves.
+// One compare-exchange of a bitonic sort, one entry per thread of the block: blocks of
+// k where (tid & k) == 0 are sorted descending; the partner is tid ^ J.
 template <int J>
-__device__ __forceinline__ uint64_t bitonic_stage(uint64_t v, int k, uint64_t* xs) {
+__device__ __forceinline__ uint64_t bitonic_cx(uint64_t v, uint64_t o, int k) {
   const int tid = threadIdx.x;
-  uint64_t o;
-  if constexpr (J >= 64) {
-    __syncthreads();
-    xs[tid] = v;
-    __syncthreads();
-    o = xs[tid ^ J];
-  } else {
-    o = lane_xor64<J>(v);
-  }
   const bool desc = (tid & k) == 0, lower = (tid & J) == 0;
   return (desc == lower) ? (v > o ? v : o) : (v < o ? v : o);
 }
 
+// A stage whose partner is in another wave: through LDS, two barriers that every wave
+// of the block passes; only active waves exchange.
+template <int J>
+__device__ __forceinline__ uint64_t bitonic_lds(uint64_t v, int k, uint64_t* xs, bool act) {
+  __syncthreads();
+  if (act) xs[threadIdx.x] = v;
+  __syncthreads();
+  if (act) v = bitonic_cx<J>(v, xs[threadIdx.x ^ J], k);
+  return v;
+}
+
+// Merge of bitonic blocks of k = 2^LK.  act is uniform over each wave: waves holding
+// no entry of the sorted range pass the barriers and skip the work.
 template <int LK>
-__device__ __forceinline__ uint64_t bitonic_merge(uint64_t v, uint64_t* xs) {
+__device__ __forceinline__ uint64_t bitonic_merge(uint64_t v, uint64_t* xs, bool act) {
   constexpr int k = 1 << LK;
-  if constexpr (LK >= 10) v = bitonic_stage<512>(v, k, xs);
-  if constexpr (LK >= 9) v = bitonic_stage<256>(v, k, xs);
-  if constexpr (LK >= 8) v = bitonic_stage<128>(v, k, xs);
-  if constexpr (LK >= 7) v = bitonic_stage<64>(v, k, xs);
-  if constexpr (LK >= 6) v = bitonic_stage<32>(v, k, xs);
-  if constexpr (LK >= 5) v = bitonic_stage<16>(v, k, xs);
-  if constexpr (LK >= 4) v = bitonic_stage<8>(v, k, xs);
-  if constexpr (LK >= 3) v = bitonic_stage<4>(v, k, xs);
-  if constexpr (LK >= 2) v = bitonic_stage<2>(v, k, xs);
-  v = bitonic_stage<1>(v, k, xs);
+  if constexpr (LK >= 10) v = bitonic_lds<512>(v, k, xs, act);
+  if constexpr (LK >= 9) v = bitonic_lds<256>(v, k, xs, act);
+  if constexpr (LK >= 8) v = bitonic_lds<128>(v, k, xs, act);
+  if constexpr (LK >= 7) v = bitonic_lds<64>(v, k, xs, act);
+  if (act) {
+    if constexpr (LK >= 6) v = bitonic_cx<32>(v, lane_xor64<32>(v), k);
+    if constexpr (LK >= 5) v = bitonic_cx<16>(v, lane_xor64<16>(v), k);
+    if constexpr (LK >= 4) v = bitonic_cx<8>(v, lane_xor64<8>(v), k);
+    if constexpr (LK >= 3) v = bitonic_cx<4>(v, lane_xor64<4>(v), k);
+    if constexpr (LK >= 2) v = bitonic_cx<2>(v, lane_xor64<2>(v), k);
+    v = bitonic_cx<1>(v, lane_xor64<1>(v), k);
+  }
   return v;
 }
 
 // Sort the first np (a power of two <= 1024) entries of the block descending, entry i
-// held by thread i; threads past np sort their own entries among themselves.
+// held by thread i.  Only the waves holding those entries work (every lane of wave 0
+// when np < 64: lanes past np sort their own entries among themselves).
 __device__ __forceinline__ uint64_t bitonic_sort_desc(uint64_t v, int np, uint64_t* xs) {
-  if (np >= 2) v = bitonic_merge<1>(v, xs);
-  if (np >= 4) v = bitonic_merge<2>(v, xs);
-  if (np >= 8) v = bitonic_merge<3>(v, xs);
-  if (np >= 16) v = bitonic_merge<4>(v, xs);
-  if (np >= 32) v = bitonic_merge<5>(v, xs);
-  if (np >= 64) v = bitonic_merge<6>(v, xs);
-  if (np >= 128) v = bitonic_merge<7>(v, xs);
-  if (np >= 256) v = bitonic_merge<8>(v, xs);
-  if (np >= 512) v = bitonic_merge<9>(v, xs);
-  if (np >= 1024) v = bitonic_merge<10>(v, xs);
+  const bool act = int(threadIdx.x & ~63u) < np;
+  if (np >= 2) v = bitonic_merge<1>(v, xs, act);
+  if (np >= 4) v = bitonic_merge<2>(v, xs, act);
+  if (np >= 8) v = bitonic_merge<3>(v, xs, act);
+  if (np >= 16) v = bitonic_merge<4>(v, xs, act);
+  if (np >= 32) v = bitonic_merge<5>(v, xs, act);
+  if (np >= 64) v = bitonic_merge<6>(v, xs, act);
+  if (np >= 128) v = bitonic_merge<7>(v, xs, act);
+  if (np >= 256) v = bitonic_merge<8>(v, xs, act);
+  if (np >= 512) v = bitonic_merge<9>(v, xs, act);
+  if (np >= 1024) v = bitonic_merge<10>(v, xs, act);
   return v;
 }
 
@@ -930,7 +941,7 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
   const uint32_t* rk = a.rkeys + size_t(r) * a.W_max * kTile;
   if (tid == 0) { kmax_sh = 0u; m_sh = 0u; }
   {
-    // the tile list and every key load go out together; one barrier then waits for all
+    // the tile list and every key load go out together
     for (int p = tid; p < a.Kt; p += 1024) tl[p] = a.tiles[size_t(r) * a.W_max + p];
     constexpr int IT = kMaxW * kTile / 4 / 1024;         // u32x4 loads per thread
     const u32x4* src = reinterpret_cast<const u32x4*>(rk);
@@ -940,30 +951,33 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
       const uint32_t q = uint32_t(it) * 1024 + tid;
       kv[it] = q < n / 4 ? src[q] : u32x4{0u, 0u, 0u, 0u};
     }
-    __syncthreads();
-    uint32_t lmax = 0u;
+    // compaction of the keys at or above lo in one block scan of the per-thread counts
+    // (its barriers also publish the tile list)
+    uint32_t lmax = 0u, cnt = 0u;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
+    for (int it = 0; it < IT; ++it)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t key = kv[it][e];
-        const bool keep = key >= lo;
-        lmax = keep ? max(lmax, key) : lmax;
-        const uint64_t mask = __ballot(keep);
-        if (mask) {
-          uint32_t base = 0u;
-          if (lane == 0) base = atomicAdd(&m_sh, uint32_t(__popcll(mask)));
-          base = uint32_t(__shfl(int(base), 0));
-          if (keep) {
-            const uint32_t p = base + uint32_t(__popcll(mask & ((1ull << lane) - 1ull)));
-            if (p < uint32_t(kFinCap)) { ck[p] = key; ce[p] = 4 * (uint32_t(it) * 1024 + tid) + e; }
-          }
+        cnt += key >= lo;
+        lmax = key >= lo ? max(lmax, key) : lmax;
+      }
+    uint32_t total;
+    uint32_t p = block_excl_scan(cnt, wsum, total);
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = kv[it][e];
+        if (key >= lo) {
+          if (p < uint32_t(kFinCap)) { ck[p] = key; ce[p] = 4 * (uint32_t(it) * 1024 + tid) + e; }
+          ++p;
         }
       }
-    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lmax = max(lmax, uint32_t(__shfl_xor(int(lmax), off)));
     if (lane == 0) atomicMax(&kmax_sh, lmax);
+    if (tid == 0) m_sh = total;
   }
   __syncthreads();
   const uint32_t m = m_sh, hi = kmax_sh;
@@ -1080,7 +1094,7 @@ static int launch_dv(const SelectArgs& a, const LogitsK& lk, const RefineK& rk, 
                      hipStream_t s, bool refine) {
   const bool bf = a.wout_dtype == GDN_BF16;
   if (!refine) {
-    dim3 grid(((lk.nchunk + kLogitsWaves - 1) / kLogitsWaves) * lk.nvg, a.R);
+    dim3 grid(((lk.nchunk + kLogitsWaves - 1) / kLogitsWaves) * lk.nvg * a.R);
     if (bf) hipLaunchKernelGGL((logits_kernel<DV, true>), grid, dim3(64 * kLogitsWaves), 0, s, lk);
     else hipLaunchKernelGGL((logits_kernel<DV, false>), grid, dim3(64 * kLogitsWaves), 0, s, lk);
   } else {
