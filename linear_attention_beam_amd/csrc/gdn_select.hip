@@ -378,7 +378,7 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   if (hf == 0 && bvalid) a.lse_part[(size_t(r) * a.W_max + b) * a.nvg + vg] = make_float4(mm, ss, nrun, 0.0f);
 }
 
-// ---------------------------------------------------------------- block-wide radix helpers
+// ---------------------------------------------------------------- block-wide radix and sort helpers
 
 // The range [lo, hi] is split into 2048 digits of width 2^shift.
 __device__ __forceinline__ int first_shift(uint32_t lo, uint32_t hi) {
@@ -521,6 +521,115 @@ __device__ uint32_t tie_cut(KeyAt key_at, FlatAt flat_at, uint32_t n, uint32_t t
   return pre;
 }
 
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
+  return (uint64_t(lane_xor<J>(uint32_t(v >> 32))) << 32) | lane_xor<J>(uint32_t(v));
+}
+
+// One compare-exchange of a bitonic network inside a wave: partner lane ^ J; this
+// lane keeps the larger entry iff desc == ((lane & J) == 0).
+template <int J>
+__device__ __forceinline__ uint64_t bitonic_cx(uint64_t v, bool desc) {
+  const uint64_t o = lane_xor64<J>(v);
+  const bool lower = (threadIdx.x & J) == 0;
+  return (desc == lower) ? (v > o ? v : o) : (v < o ? v : o);
+}
+
+// Merge of bitonic runs of k = 2^LK lanes: runs with (lane & k) == 0 end descending.
+template <int LK>
+__device__ __forceinline__ uint64_t wave_merge(uint64_t v) {
+  constexpr int k = 1 << LK;
+  const bool desc = LK == 6 || (threadIdx.x & k) == 0;
+  if constexpr (LK >= 6) v = bitonic_cx<32>(v, desc);
+  if constexpr (LK >= 5) v = bitonic_cx<16>(v, desc);
+  if constexpr (LK >= 4) v = bitonic_cx<8>(v, desc);
+  if constexpr (LK >= 3) v = bitonic_cx<4>(v, desc);
+  if constexpr (LK >= 2) v = bitonic_cx<2>(v, desc);
+  return bitonic_cx<1>(v, desc);
+}
+
+// The first np (a power of two <= 64) lanes of the wave sorted descending (lane 0
+// the largest); lanes past np sort their own entries among themselves.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v, int np) {
+  if (np >= 2) v = wave_merge<1>(v);
+  if (np >= 4) v = wave_merge<2>(v);
+  if (np >= 8) v = wave_merge<3>(v);
+  if (np >= 16) v = wave_merge<4>(v);
+  if (np >= 32) v = wave_merge<5>(v);
+  if (np >= 64) v = wave_merge<6>(v);
+  return v;
+}
+
+// Number of entries above v in the NW sorted runs of 64 other than run w: a binary
+// search in every run at once (run w is searched too and ignored), so that the NW
+// reads of a step issue together.
+template <int NW>
+__device__ __forceinline__ uint32_t count_above(uint64_t v, const uint64_t* runs, int w) {
+  uint32_t c[NW];
+#pragma unroll
+  for (int u = 0; u < NW; ++u) c[u] = 0u;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    uint64_t x[NW];
+#pragma unroll
+    for (int u = 0; u < NW; ++u) x[u] = runs[u * 64 + c[u] + s - 1];
+#pragma unroll
+    for (int u = 0; u < NW; ++u) c[u] += x[u] > v ? uint32_t(s) : 0u;
+  }
+  uint64_t y[NW];
+#pragma unroll
+  for (int u = 0; u < NW; ++u) y[u] = runs[u * 64 + 63];
+  uint32_t above = 0u;
+#pragma unroll
+  for (int u = 0; u < NW; ++u)
+    if (u != w) above += c[u] + (c[u] == 63u && y[u] > v);   // the search caps at 63
+  return above;
+}
+
+// Block-wide descending sort of n <= 1024 distinct nonzero entries, entry i held by
+// thread i < n (other threads hold anything).  Each wave holding entries sorts them in
+// its lanes and lays the run out in `runs`; an entry's rank is its place in its own
+// run plus the entries above it in every other run.  Returns entry i in thread i < n,
+// 0 past n.  `runs` and `out` may be arrays the entries were read from before the call.
+__device__ __forceinline__ uint64_t rank_sort_desc(uint64_t v, int n, uint64_t* runs, uint64_t* out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = (n + 63) >> 6;
+  if (tid >= n) v = 0ull;                                 // padding sorts last in every run
+  if (nw <= 1) {                                          // one run: sorted in place
+    int np = 1;
+    while (np < n) np <<= 1;
+    return w == 0 ? wave_sort_desc(v, np) : 0ull;
+  }
+  if (w < nw) v = wave_sort_desc(v, 64);
+  __syncthreads();
+  if (w < nw) runs[tid] = v;
+  __syncthreads();
+  if (w < nw) {
+    uint32_t above = 0u;
+    switch (nw) {
+      case 2: above = count_above<2>(v, runs, w); break;
+      case 3: above = count_above<3>(v, runs, w); break;
+      case 4: above = count_above<4>(v, runs, w); break;
+      case 5: above = count_above<5>(v, runs, w); break;
+      case 6: above = count_above<6>(v, runs, w); break;
+      case 7: above = count_above<7>(v, runs, w); break;
+      case 8: above = count_above<8>(v, runs, w); break;
+      case 9: above = count_above<9>(v, runs, w); break;
+      case 10: above = count_above<10>(v, runs, w); break;
+      case 11: above = count_above<11>(v, runs, w); break;
+      case 12: above = count_above<12>(v, runs, w); break;
+      case 13: above = count_above<13>(v, runs, w); break;
+      case 14: above = count_above<14>(v, runs, w); break;
+      case 15: above = count_above<15>(v, runs, w); break;
+      default: above = count_above<16>(v, runs, w); break;
+    }
+    if (v != 0ull) out[lane + above] = v;                 // lane + above < 64 nw <= 1024
+  }
+  __syncthreads();
+  return tid < n ? out[tid] : 0ull;
+}
+
 // ---------------------------------------------------------------- tile select
 
 struct TileSelK {
@@ -545,7 +654,8 @@ struct TileSelK {
 //  2. Pass over all tile keys: 2048-digit histogram over that exact range; the digit
 //     holding the K-th largest key.
 //  3. Pass: keys above the digit are chosen, keys inside it are kept.
-//  4. Radix finish inside the digit over the kept tiles, ties by flat tile index.
+//  4. The rest of the K inside the digit, ties by flat tile index: one sort of the kept
+//     tiles when at most 1024 (the usual case: a handful), else a radix finish.
 //  5. Counting sort of the K chosen tiles by code tile j, cut into groups of at most
 //     32 beams: one MFMA block of the refinement each.
 __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
@@ -554,9 +664,10 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   __shared__ uint32_t fill[kHistBins];
   __shared__ uint32_t jstart[kHistBins];
   __shared__ uint32_t chosen[kMaxW];
+  __shared__ uint64_t cs[kMaxW], xs[kMaxW];                // kept tiles as (key, ~flat); sorted
   __shared__ uint32_t wsum[16];
   __shared__ RadixSh sh;
-  __shared__ uint32_t kmin_sh, kmax_sh, nwin_sh, ncand_sh;
+  __shared__ uint32_t kmin_sh, kmax_sh, nwin_sh, ncand_sh, theta_sh;
   const int r = blockIdx.x, tid = threadIdx.x;
   const int W = a.W;
   const uint32_t Vt = uint32_t(a.Vt), K = uint32_t(a.K);
@@ -576,19 +687,27 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
     const int jj = jg + u * G;
     x0[u] = act && jj < a.Vt ? tm[size_t(jj) * W + b] : 0.0f;
   }
+  // the first eight log-sum-exp parts and the cumulative score of beam tid are loaded
+  // before the first barrier too (a barrier waits for every load in flight)
+  const float4* lp = a.lse_part + (size_t(r) * a.W_max + (tid < W ? tid : 0)) * a.nvg;
+  float4 q[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    q[u] = tid < W && u < a.nvg ? lp[u] : make_float4(-INFINITY, 0.0f, INFINITY, 0.0f);
+  const float c = tid < W ? a.cum[size_t(r) * a.W_max + tid] : 0.0f;
   if (tid == 0) { kmin_sh = 0xFFFFFFFFu; kmax_sh = 0u; nwin_sh = 0u; ncand_sh = 0u; }
   for (int i = tid; i < kHistBins; i += 1024) hist[i] = 0;
   __syncthreads();
   {
     uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
     if (tid < W) {
-      const float4* p = a.lse_part + (size_t(r) * a.W_max + tid) * a.nvg;
       float mm = -INFINITY, mn = INFINITY, s = 0.0f;
       for (int g0 = 0; g0 < a.nvg; g0 += 8) {
-        float4 q[8];
+        if (g0 > 0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          q[u] = g0 + u < a.nvg ? p[g0 + u] : make_float4(-INFINITY, 0.0f, INFINITY, 0.0f);
+          for (int u = 0; u < 8; ++u)
+            q[u] = g0 + u < a.nvg ? lp[g0 + u] : make_float4(-INFINITY, 0.0f, INFINITY, 0.0f);
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           mn = fminf(mn, q[u].z);
@@ -600,7 +719,6 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
         }
       }
       const float l = mm + logf(s);
-      const float c = a.cum[size_t(r) * a.W_max + tid];
       lse_s[tid] = l;
       cum_s[tid] = c;
       a.lse[size_t(r) * a.W_max + tid] = l;
@@ -658,32 +776,48 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
     } else {
       const uint32_t p = atomicAdd(&ncand_sh, 1u);
       if (p < cap) cand[p] = flat;
+      if (p < uint32_t(kMaxW)) cs[p] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - flat);
     }
   });
   __syncthreads();
   const uint32_t n_cand = min(ncand_sh, uint32_t(cap));
-  auto key_at = [&](uint32_t i) {
-    const uint32_t f = cand[i];
-    const uint32_t bb = f / Vt;
-    return f2key(cand_score(cum_s[bb], tm[size_t(f % Vt) * W + bb], lse_s[bb]));
-  };
-  auto flat_at = [&](uint32_t i) { return cand[i]; };
-  const uint32_t theta = radix_finish(key_at, n_cand, lo, hi, need, shift1, hist, wsum, sh);
-  const uint32_t phi = tie_cut(key_at, flat_at, n_cand, theta, need, hist, sh);
+  uint32_t theta, nwin;
+  if (n_cand <= uint32_t(kMaxW)) {
+    // sorted as (key, ~flat) descending, the first `need` kept tiles complete the K
+    const uint32_t above = nwin_sh;
+    const uint64_t v = rank_sort_desc(uint32_t(tid) < n_cand ? cs[tid] : 0ull, int(n_cand), cs, xs);
+    const uint32_t take = min(need, n_cand);
+    if (uint32_t(tid) < take && above + tid < uint32_t(kMaxW)) chosen[above + tid] = 0xFFFFFFFFu - uint32_t(v);
+    if (uint32_t(tid) + 1 == take) theta_sh = uint32_t(v >> 32);
+    __syncthreads();
+    theta = take ? theta_sh : lo;
+    nwin = above + take;
+  } else {
+    auto key_at = [&](uint32_t i) {
+      const uint32_t f = cand[i];
+      const uint32_t bb = f / Vt;
+      return f2key(cand_score(cum_s[bb], tm[size_t(f % Vt) * W + bb], lse_s[bb]));
+    };
+    auto flat_at = [&](uint32_t i) { return cand[i]; };
+    theta = radix_finish(key_at, n_cand, lo, hi, need, shift1, hist, wsum, sh);
+    const uint32_t phi = tie_cut(key_at, flat_at, n_cand, theta, need, hist, sh);
+    for (uint32_t i = tid; i < n_cand; i += 1024) {
+      const uint32_t f = cand[i];
+      const uint32_t key = key_at(i);
+      if (key > theta || (key == theta && f <= phi)) {
+        const uint32_t p = atomicAdd(&nwin_sh, 1u);
+        if (p < uint32_t(kMaxW)) chosen[p] = f;
+      }
+    }
+    __syncthreads();
+    nwin = nwin_sh;
+  }
   // the K-th tile key bounds the K-th candidate key from below when K tiles are chosen
   if (tid == 0) a.sel[r].theta = a.K == a.K_full ? theta : 0u;
-  for (uint32_t i = tid; i < n_cand; i += 1024) {
-    const uint32_t f = cand[i];
-    const uint32_t key = key_at(i);
-    if (key > theta || (key == theta && f <= phi)) {
-      const uint32_t p = atomicAdd(&nwin_sh, 1u);
-      if (p < uint32_t(kMaxW)) chosen[p] = f;
-    }
-  }
   for (int j = tid; j < kHistBins; j += 1024) hist[j] = 0;
   __syncthreads();
-  const uint32_t got = min(nwin_sh, K);
-  if (tid == 0 && nwin_sh != K) atomicOr(a.status, 2);
+  const uint32_t got = min(nwin, K);
+  if (tid == 0 && nwin != K) atomicOr(a.status, 2);
   for (uint32_t p = tid; p < got; p += 1024) atomicAdd(&hist[chosen[p] % Vt], 1u);
   __syncthreads();
   // exclusive scans over j of the counts (low 16 bits) and the group counts (high 16)
@@ -854,76 +988,19 @@ __device__ float forced_logit(const FinK& a, int r, int b, int c) {
 // Refined keys kept in LDS by the final select; more than this many keys at or above
 // the tile threshold (massive ties) are read from global memory instead.
 constexpr int kFinCap = 8192;
-
-template <int J>
-__device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
-  return (uint64_t(lane_xor<J>(uint32_t(v >> 32))) << 32) | lane_xor<J>(uint32_t(v));
-}
-
-// One compare-exchange of a bitonic sort, one entry per thread of the block: blocks of
-// k where (tid & k) == 0 are sorted descending; the partner is tid ^ J.
-template <int J>
-__device__ __forceinline__ uint64_t bitonic_cx(uint64_t v, uint64_t o, int k) {
-  const int tid = threadIdx.x;
-  const bool desc = (tid & k) == 0, lower = (tid & J) == 0;
-  return (desc == lower) ? (v > o ? v : o) : (v < o ? v : o);
-}
-
-// A stage whose partner is in another wave: through LDS, two barriers that every wave
-// of the block passes; only active waves exchange.
-template <int J>
-__device__ __forceinline__ uint64_t bitonic_lds(uint64_t v, int k, uint64_t* xs, bool act) {
-  __syncthreads();
-  if (act) xs[threadIdx.x] = v;
-  __syncthreads();
-  if (act) v = bitonic_cx<J>(v, xs[threadIdx.x ^ J], k);
-  return v;
-}
-
-// Merge of bitonic blocks of k = 2^LK.  act is uniform over each wave: waves holding
-// no entry of the sorted range pass the barriers and skip the work.
-template <int LK>
-__device__ __forceinline__ uint64_t bitonic_merge(uint64_t v, uint64_t* xs, bool act) {
-  constexpr int k = 1 << LK;
-  if constexpr (LK >= 10) v = bitonic_lds<512>(v, k, xs, act);
-  if constexpr (LK >= 9) v = bitonic_lds<256>(v, k, xs, act);
-  if constexpr (LK >= 8) v = bitonic_lds<128>(v, k, xs, act);
-  if constexpr (LK >= 7) v = bitonic_lds<64>(v, k, xs, act);
-  if (act) {
-    if constexpr (LK >= 6) v = bitonic_cx<32>(v, lane_xor64<32>(v), k);
-    if constexpr (LK >= 5) v = bitonic_cx<16>(v, lane_xor64<16>(v), k);
-    if constexpr (LK >= 4) v = bitonic_cx<8>(v, lane_xor64<8>(v), k);
-    if constexpr (LK >= 3) v = bitonic_cx<4>(v, lane_xor64<4>(v), k);
-    if constexpr (LK >= 2) v = bitonic_cx<2>(v, lane_xor64<2>(v), k);
-    v = bitonic_cx<1>(v, lane_xor64<1>(v), k);
-  }
-  return v;
-}
-
-// Sort the first np (a power of two <= 1024) entries of the block descending, entry i
-// held by thread i.  Only the waves holding those entries work (every lane of wave 0
-// when np < 64: lanes past np sort their own entries among themselves).
-__device__ __forceinline__ uint64_t bitonic_sort_desc(uint64_t v, int np, uint64_t* xs) {
-  const bool act = int(threadIdx.x & ~63u) < np;
-  if (np >= 2) v = bitonic_merge<1>(v, xs, act);
-  if (np >= 4) v = bitonic_merge<2>(v, xs, act);
-  if (np >= 8) v = bitonic_merge<3>(v, xs, act);
-  if (np >= 16) v = bitonic_merge<4>(v, xs, act);
-  if (np >= 32) v = bitonic_merge<5>(v, xs, act);
-  if (np >= 64) v = bitonic_merge<6>(v, xs, act);
-  if (np >= 128) v = bitonic_merge<7>(v, xs, act);
-  if (np >= 256) v = bitonic_merge<8>(v, xs, act);
-  if (np >= 512) v = bitonic_merge<9>(v, xs, act);
-  if (np >= 1024) v = bitonic_merge<10>(v, xs, act);
-  return v;
-}
+// Ancestry and SID prefix entries (live beams x past steps) the final select stages in
+// LDS at its start; beyond this they are read from global memory where needed.
+constexpr int kAncCap = 4096;
+static_assert(kAncCap % 1024 == 0 && kMaxW <= 1024, "final select: one block of 1024 threads");
 
 // One 1024-thread block per request.  Only refined keys at or above the K-th tile key
 // can be among the top K (when K tiles were chosen: their maxima are K candidates);
 // they are compacted into LDS.  Then the exact top-K (score descending, flat index
-// b * V + c ascending), a bitonic sort with one entry per thread (exchanges inside a
-// wave by shuffles, across waves through LDS), the top-W outputs, and the eq. (9)
-// remap of ancestry, SID prefixes and cumulative scores.
+// b * V + c ascending): when at most 1024 keys were kept, one sort of all of them;
+// otherwise a radix select of the K winners and a sort of those (one entry per thread:
+// runs of 64 sorted inside the waves, ranks by binary search across runs).  Last,
+// the top-W outputs and the eq. (9) remap of ancestry, SID prefixes and cumulative
+// scores, from the parents' rows staged in LDS at the start.
 __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
   __shared__ uint32_t ck[kFinCap], ce[kFinCap];
   __shared__ uint32_t tl[kMaxW];
@@ -934,6 +1011,10 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
   __shared__ uint32_t wsum[16];
   __shared__ RadixSh sh;
   __shared__ uint32_t kmax_sh, m_sh;
+  __shared__ int32_t pa[kAncCap], pt[kAncCap];           // [b][j < t] of the live beams
+  __shared__ float cum_s[kMaxW];
+  __shared__ int32_t opos_s[kMaxW];
+  __shared__ uint64_t runs[kMaxW];                         // sorted runs of the rank sort
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const uint32_t n = uint32_t(a.Kt) * kTile;
   const uint32_t V = uint32_t(a.V), Vt = uint32_t(a.Vt);
@@ -941,8 +1022,22 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
   const uint32_t* rk = a.rkeys + size_t(r) * a.W_max * kTile;
   if (tid == 0) { kmax_sh = 0u; m_sh = 0u; }
   {
-    // the tile list and every key load go out together
-    for (int p = tid; p < a.Kt; p += 1024) tl[p] = a.tiles[size_t(r) * a.W_max + p];
+    // every global load of the prologue is issued before the first is used: the tile
+    // list (Kt <= 1024), the live beams' cumulative scores and order positions, their
+    // ancestry and SID prefix rows (up to 4 x 1024 entries each) and the refined keys
+    const size_t rw = size_t(r) * a.W_max;
+    const uint32_t tlv = tid < a.Kt ? a.tiles[rw + tid] : 0u;
+    const float cumv = tid < a.W ? a.cum[rw + tid] : 0.0f;
+    const int32_t oposv = tid < a.W && a.t > 0 ? a.opos[rw + tid] : tid;
+    const int nanc = a.W * a.t <= kAncCap ? a.W * a.t : 0;
+    int32_t pav[kAncCap / 1024], ptv[kAncCap / 1024];
+#pragma unroll
+    for (int q = 0; q < kAncCap / 1024; ++q) {
+      const int e = q * 1024 + tid;
+      const size_t g = e < nanc ? (rw + e / a.t) * a.T_max + e % a.t : 0;
+      pav[q] = e < nanc ? a.anc[g] : 0;
+      ptv[q] = e < nanc ? a.tok[g] : 0;
+    }
     constexpr int IT = kMaxW * kTile / 4 / 1024;         // u32x4 loads per thread
     const u32x4* src = reinterpret_cast<const u32x4*>(rk);
     u32x4 kv[IT];
@@ -951,6 +1046,11 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
       const uint32_t q = uint32_t(it) * 1024 + tid;
       kv[it] = q < n / 4 ? src[q] : u32x4{0u, 0u, 0u, 0u};
     }
+    if (tid < a.Kt) tl[tid] = tlv;
+    if (tid < a.W) { cum_s[tid] = cumv; opos_s[tid] = oposv; }
+#pragma unroll
+    for (int q = 0; q < kAncCap / 1024; ++q)
+      if (q * 1024 + tid < nanc) { pa[q * 1024 + tid] = pav[q]; pt[q * 1024 + tid] = ptv[q]; }
     // compaction of the keys at or above lo in one block scan of the per-thread counts
     // (its barriers also publish the tile list)
     uint32_t lmax = 0u, cnt = 0u;
@@ -989,47 +1089,55 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
     const uint32_t f = tl[e >> 5];
     return (f / Vt) * V + (f % Vt) * kTile + (e & 31u);
   };
-  uint32_t need = uint32_t(a.K);
-  const uint32_t theta = radix_finish(key_at, ns, lo, hi, need, first_shift(lo, hi), u.hist, wsum, sh);
-  const uint32_t phi = tie_cut(key_at, flat_at, ns, theta, need, u.hist, sh);
-
-  // gather the K winners as (key, ~flat): sorting these descending ranks by score
-  // descending, then flat index ascending
-  if (tid == 0) sh.cnt = 0;
-  __syncthreads();
-  for (uint32_t i0 = 0; i0 < ns; i0 += 1024) {
-    const uint32_t i = i0 + tid;
-    bool win = false;
-    uint64_t ent = 0;
-    if (i < ns) {
-      const uint32_t key = key_at(i);
-      if (key >= theta) {
-        const uint32_t f = flat_at(i);
-        win = key > theta || f <= phi;
-        ent = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - f);
+  uint64_t v;
+  uint32_t got, nsort;
+  if (inl && m <= uint32_t(kMaxW)) {
+    // few keys at or above the tile threshold (the usual case: a little over K):
+    // sorting all of them as (key, ~flat) ranks the top K directly
+    v = uint32_t(tid) < m ? (uint64_t(ck[tid]) << 32) | uint64_t(0xFFFFFFFFu - flat_at(tid)) : 0ull;
+    got = min(m, uint32_t(a.K));
+    if (tid == 0 && m < uint32_t(a.K)) atomicOr(a.status, 2);
+    nsort = m;
+  } else {
+    uint32_t need = uint32_t(a.K);
+    const uint32_t theta = radix_finish(key_at, ns, lo, hi, need, first_shift(lo, hi), u.hist, wsum, sh);
+    const uint32_t phi = tie_cut(key_at, flat_at, ns, theta, need, u.hist, sh);
+    // gather the K winners as (key, ~flat): sorting these descending ranks by score
+    // descending, then flat index ascending
+    if (tid == 0) sh.cnt = 0;
+    __syncthreads();
+    for (uint32_t i0 = 0; i0 < ns; i0 += 1024) {
+      const uint32_t i = i0 + tid;
+      bool win = false;
+      uint64_t ent = 0;
+      if (i < ns) {
+        const uint32_t key = key_at(i);
+        if (key >= theta) {
+          const uint32_t f = flat_at(i);
+          win = key > theta || f <= phi;
+          ent = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - f);
+        }
+      }
+      const uint64_t mask = __ballot(win);
+      if (mask) {
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&sh.cnt, uint32_t(__popcll(mask)));
+        base = uint32_t(__shfl(int(base), 0));
+        if (win) {
+          const uint32_t p = base + uint32_t(__popcll(mask & ((1ull << lane) - 1ull)));
+          if (p < uint32_t(kMaxW)) u.s[p] = ent;
+        }
       }
     }
-    const uint64_t mask = __ballot(win);
-    if (mask) {
-      uint32_t base = 0u;
-      if (lane == 0) base = atomicAdd(&sh.cnt, uint32_t(__popcll(mask)));
-      base = uint32_t(__shfl(int(base), 0));
-      if (win) {
-        const uint32_t p = base + uint32_t(__popcll(mask & ((1ull << lane) - 1ull)));
-        if (p < uint32_t(kMaxW)) u.s[p] = ent;
-      }
-    }
+    __syncthreads();
+    got = min(sh.cnt, uint32_t(kMaxW));
+    if (tid == 0 && sh.cnt != uint32_t(a.K)) atomicOr(a.status, 2);
+    v = uint32_t(tid) < got ? u.s[tid] : 0ull;
+    nsort = got;
   }
-  __syncthreads();
-  const uint32_t got = min(sh.cnt, uint32_t(kMaxW));
-  if (tid == 0 && sh.cnt != uint32_t(a.K)) atomicOr(a.status, 2);
-  uint64_t v = uint32_t(tid) < got ? u.s[tid] : 0ull;    // padding sorts last
-  int np = 1;
-  while (np < a.K) np <<= 1;
-  v = bitonic_sort_desc(v, np, u.s);
+  v = rank_sort_desc(v, int(nsort), runs, u.s);
   // thread i holds rank i
   const float* lse = a.lse + size_t(r) * a.W_max;
-  const float* cum = a.cum + size_t(r) * a.W_max;
   int okey = 0;                                           // parent's position (order below)
   if (tid < a.K) {
     const int i = tid;
@@ -1054,11 +1162,12 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
         fp = fp < 0 ? 0 : (fp >= a.W ? a.W - 1 : fp);
         fc = fc < 0 ? 0 : (fc >= a.V ? a.V - 1 : fc);
       }
-      fs = cand_score(cum[fp], forced_logit(a, r, fp, fc), lse[fp]) + 0.0f;
+      fs = cand_score(cum_s[fp], forced_logit(a, r, fp, fc), lse[fp]) + 0.0f;
     }
     // eq. (9): the child copies its parent's ancestry and appends the parent's slot
-    const int32_t* ap = a.anc + (size_t(r) * a.W_max + fp) * a.T_max;
-    const int32_t* tp = a.tok + (size_t(r) * a.W_max + fp) * a.T_max;
+    const bool lds = a.W * a.t <= kAncCap;                 // block-uniform
+    const int32_t* ap = lds ? pa + fp * a.t : a.anc + (size_t(r) * a.W_max + fp) * a.T_max;
+    const int32_t* tp = lds ? pt + fp * a.t : a.tok + (size_t(r) * a.W_max + fp) * a.T_max;
     int32_t* an = a.anc_next + (size_t(r) * a.W_max + i) * a.T_max;
     int32_t* tn = a.tok_next + (size_t(r) * a.W_max + i) * a.T_max;
     for (int j = 0; j < a.T_max; ++j) {
@@ -1066,7 +1175,7 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
       tn[j] = j < a.t ? tp[j] : (j == a.t ? fc : 0);
     }
     a.cum_next[size_t(r) * a.W_max + i] = fs;
-    okey = a.t == 0 ? fp : a.opos[size_t(r) * a.W_max + fp];
+    okey = opos_s[fp];
   }
   // processing order of step t + 1: a counting sort of the beams by their parent's
   // position in step t's order, so children of one parent are adjacent and subtrees
