@@ -872,7 +872,7 @@ struct RefineK {
 // One wave per group: code tile j against up to 32 beams that chose it.  Columns are
 // independent in the MFMA, so every logit equals the first pass's bit for bit.
 template <int DV, bool WBF16>
-__global__ void __launch_bounds__(256, 2) refine_kernel(RefineK a) {
+__global__ void __launch_bounds__(256, 3) refine_kernel(RefineK a) {
   constexpr int HV = DV / 2;
   const int r = blockIdx.y;
   const int g = blockIdx.x * 4 + (threadIdx.x >> 6);      // < G_max by the launch
@@ -886,6 +886,8 @@ __global__ void __launch_bounds__(256, 2) refine_kernel(RefineK a) {
   const bool valid = g < int(ng) && m < cnt;
   const int b = valid ? int(f / uint32_t(a.Vt)) : 0;
   const int c0 = 32 * j;
+  // the beam's cumulative score and log-sum-exp go out with the operands
+  const float cb = a.cum[size_t(r) * a.W_max + b], lb = a.lse[size_t(r) * a.W_max + b];
   f32x16 acc;
   if constexpr (WBF16) {
     // the same MFMA sequence as the first pass (kk ascending), operands held for at
@@ -918,7 +920,6 @@ __global__ void __launch_bounds__(256, 2) refine_kernel(RefineK a) {
   }
   if (valid) {
     // lane half hf holds codes 8 q + 4 hf + (0..3): four 16-byte runs of the row
-    const float cb = a.cum[size_t(r) * a.W_max + b], lb = a.lse[size_t(r) * a.W_max + b];
     u32x4* out = reinterpret_cast<u32x4*>(a.rkeys + (size_t(r) * a.W_max + start + m) * kTile);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

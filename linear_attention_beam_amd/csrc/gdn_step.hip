@@ -301,77 +301,92 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     }
     if (c + 1 < nch) stage_load(c + 1);                  // in flight until the end of the chunk
 
-    // ---- dots: TPB threads per beam, SEGB bytes of d_k each
-    {
-      u32x4 xq[SV], xk[SV];
-#pragma unroll
-      for (int i = 0; i < SV; ++i) {
-        xq[i] = *reinterpret_cast<const u32x4*>(Lq + bm * QROW + sg * C::SEGB + 16 * i);
-        xk[i] = *reinterpret_cast<const u32x4*>(Lk + bm * QROW + sg * C::SEGB + 16 * i);
-      }
-      float kq = 0.0f;
-#pragma unroll
-      for (int i = 0; i < SV; ++i) kq = dot16<BF16>(xk[i], xq[i], kq);
-      float cq[NJ1], ck[NJ1];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        cq[j] = 0.0f;
-        ck[j] = 0.0f;
+    // ---- dots: TPB threads per beam, SEGB bytes of d_k each; then a barrier (the
+    // epilogue reads them per beam)
+    auto dots = [&]() {
+      {
+        u32x4 xq[SV], xk[SV];
 #pragma unroll
         for (int i = 0; i < SV; ++i) {
-          cq[j] = dot16<BF16>(kj[j][i], xq[i], cq[j]);
-          ck[j] = dot16<BF16>(kj[j][i], xk[i], ck[j]);
+          xq[i] = *reinterpret_cast<const u32x4*>(Lq + bm * QROW + sg * C::SEGB + 16 * i);
+          xk[i] = *reinterpret_cast<const u32x4*>(Lk + bm * QROW + sg * C::SEGB + 16 * i);
         }
-      }
+        float kq = 0.0f;
 #pragma unroll
-      for (int off = 1; off < TPB; off <<= 1) {
-        kq += __shfl_xor(kq, off);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          cq[j] += __shfl_xor(cq[j], off);
-          ck[j] += __shfl_xor(ck[j], off);
-        }
-      }
-      if (sg == 0) {
-        sc[bm * SCN] = kq;
+        for (int i = 0; i < SV; ++i) kq = dot16<BF16>(xk[i], xq[i], kq);
+        float cq[NJ1], ck[NJ1];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          sc[bm * SCN + 1 + j] = aj[j];
-          sc[bm * SCN + 1 + NJ + j] = cq[j];
-          sc[bm * SCN + 1 + 2 * NJ + j] = ck[j];
+          cq[j] = 0.0f;
+          ck[j] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < SV; ++i) {
+            cq[j] = dot16<BF16>(kj[j][i], xq[i], cq[j]);
+            ck[j] = dot16<BF16>(kj[j][i], xk[i], ck[j]);
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < TPB; off <<= 1) {
+          kq += __shfl_xor(kq, off);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            cq[j] += __shfl_xor(cq[j], off);
+            ck[j] += __shfl_xor(ck[j], off);
+          }
+        }
+        if (sg == 0) {
+          sc[bm * SCN] = kq;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            sc[bm * SCN + 1 + j] = aj[j];
+            sc[bm * SCN + 1 + NJ + j] = cq[j];
+            sc[bm * SCN + 1 + 2 * NJ + j] = ck[j];
+          }
         }
       }
-    }
-    __syncthreads();
+      __syncthreads();
+    };
 
     // ---- this wave's row block for the chunk's 32 beams (lane: beam m, rows half hf)
     f32x16 accq = {}, acck = {};
-    if constexpr (BF16) {
+    auto project = [&]() {
+      if constexpr (BF16) {
 #pragma unroll
-      for (int kk = 0; kk < DK / 16; ++kk) {
-        const int off = m * QROW + (HK * hf + 8 * kk) * 2;
-        const bf16x8 bq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lq + off));
-        const bf16x8 bk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lk + off));
-        const bf16x8 ahi = __builtin_bit_cast(bf16x8, afr[2 * kk]);
-        const bf16x8 alo = __builtin_bit_cast(bf16x8, afr[2 * kk + 1]);
-        accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bq, accq, 0, 0, 0);
-        acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bk, acck, 0, 0, 0);
-        accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bq, accq, 0, 0, 0);
-        acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bk, acck, 0, 0, 0);
-      }
-    } else {
+        for (int kk = 0; kk < DK / 16; ++kk) {
+          const int off = m * QROW + (HK * hf + 8 * kk) * 2;
+          const bf16x8 bq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lq + off));
+          const bf16x8 bk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Lk + off));
+          const bf16x8 ahi = __builtin_bit_cast(bf16x8, afr[2 * kk]);
+          const bf16x8 alo = __builtin_bit_cast(bf16x8, afr[2 * kk + 1]);
+          accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bq, accq, 0, 0, 0);
+          acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bk, acck, 0, 0, 0);
+          accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bq, accq, 0, 0, 0);
+          acck = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bk, acck, 0, 0, 0);
+        }
+      } else {
 #pragma unroll
-      for (int kk4 = 0; kk4 < DK / 8; ++kk4) {
-        const int off = m * QROW + (HK * hf + 4 * kk4) * 4;
-        const f32x4 bq = *reinterpret_cast<const f32x4*>(Lq + off);
-        const f32x4 bk = *reinterpret_cast<const f32x4*>(Lk + off);
-        const f32x4 af = __builtin_bit_cast(f32x4, afr[kk4]);
+        for (int kk4 = 0; kk4 < DK / 8; ++kk4) {
+          const int off = m * QROW + (HK * hf + 4 * kk4) * 4;
+          const f32x4 bq = *reinterpret_cast<const f32x4*>(Lq + off);
+          const f32x4 bk = *reinterpret_cast<const f32x4*>(Lk + off);
+          const f32x4 af = __builtin_bit_cast(f32x4, afr[kk4]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          accq = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bq[i], accq, 0, 0, 0);
-          acck = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bk[i], acck, 0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            accq = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bq[i], accq, 0, 0, 0);
+            acck = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bk[i], acck, 0, 0, 0);
+          }
         }
       }
+    };
+    // with at most two records to replay (d_k <= 128) the projection goes first, on the
+    // matrix cores while the records' keys are still on their way; deeper replays and
+    // wider keys keep the order that fits their registers
+    if constexpr (NJ <= 2 && DK <= 128) {
+      project();
+      dots();
+    } else {
+      dots();
+      project();
     }
 
     {
