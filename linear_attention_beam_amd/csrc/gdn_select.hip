@@ -744,15 +744,17 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
       const int jj = jg + u * G;
       if (jj < a.Vt) f(f2key(cand_score(cb, x0[u], lb)), jj);
     }
-    for (int j = jg + U * G; j < a.Vt; j += U * G) {
-      float x[U];
+    // the rest in batches of UB loads in flight (large codebooks: up to 256 per thread)
+    constexpr int UB = 32;
+    for (int j = jg + U * G; j < a.Vt; j += UB * G) {
+      float x[UB];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < UB; ++u) {
         const int jj = j + u * G;
         x[u] = jj < a.Vt ? tm[size_t(jj) * W + b] : 0.0f;
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < UB; ++u) {
         const int jj = j + u * G;
         if (jj < a.Vt) f(f2key(cand_score(cb, x[u], lb)), jj);
       }
