@@ -30,6 +30,8 @@ DERIVED = {
     "ties_w512": ("tiny", dict(widths=(512, 512, 512), V=64)),
     # 1536 tied tiles: more than one sort of the kept tiles holds (radix finish instead)
     "ties_w512_v96": ("tiny", dict(widths=(512, 512, 512), V=96)),
+    # bf16 codebook: 512 x 32 tied refined keys, more than the final select keeps in LDS
+    "ties_bf16_w512": ("single", dict(widths=(512, 512, 512), V=64, io="bf16", wout="bf16")),
     # 1024 beams over six steps: the parents' rows exceed what the final select stages
     # in LDS (1024 x 5 entries at the last step) and are read from global memory
     "tiny_w1024_t6": ("tiny", dict(T=6, widths=(1024,) * 6, V=64)),
@@ -251,7 +253,7 @@ def test_full_size_select_properties(name):
             assert np.array_equal(anc[r][:K, :t + 1], anc_ref[r]), f"ancestry r={r} t={t}"
 
 
-@pytest.mark.parametrize("name", ["tiny", "single", "ties_w512", "ties_w512_v96"])
+@pytest.mark.parametrize("name", ["tiny", "single", "ties_w512", "ties_w512_v96", "ties_bf16_w512"])
 def test_all_scores_tied(name):
     """Wout = 0: every candidate of a request scores cum - log V; the top-W is then the
     W smallest flat indices, in order (the tie-break), at every step."""
