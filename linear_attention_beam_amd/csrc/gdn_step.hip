@@ -155,6 +155,11 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
   constexpr int SCN = 1 + 3 * NJ;                        // kq, alpha_j, cq_j, ck_j
   __shared__ __align__(16) unsigned char lds[2 * C::SLOT + 32 * SCN * 4];
   __shared__ int ord[NJ > 0 ? kMaxW : 1];
+  // per wave: its 32 x 32 block of delta_t (then o_t) as [beam][row], rows padded to 36
+  // (where the LDS allows; else each lane stores its own 16 rows)
+  constexpr int XT = 36;
+  constexpr bool TURN = 2 * C::SLOT + 32 * (1 + 3 * 7) * 4 + 4 * kMaxW + C::NW * 32 * XT * 4 <= 160 * 1024;
+  __shared__ __align__(16) float xt[TURN ? C::NW * 32 * XT : 1];
   float* sc = reinterpret_cast<float*>(lds + 2 * C::SLOT);
 
   const int wid = xcd_work_id();
@@ -391,6 +396,7 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
 
     {
       // accumulator register i of this lane = physical row row0 + i of beam b
+      f32x4 dt[4] = {}, ot[4] = {};
       if (grow0 < DV && valid) {
         const float* s = sc + m * SCN;
         const float kq = s[0];
@@ -418,19 +424,44 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
           for (int q4 = 0; q4 < 4; ++q4)
             for (int i = 0; i < 4; ++i) vin[4 * q4 + i] = vp[q4][i];
         }
-        f32x4* dout = reinterpret_cast<f32x4*>(a.gtr_delta + (slot_t * a.W_max + b) * DV + grow0);
-        f32x4* oout = reinterpret_cast<f32x4*>(a.o + (size_t(rh) * W + b) * DV + grow0);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          f32x4 dt, ot;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = 4 * q4 + i;
-            dt[i] = be * (vin[e] - al * acck[e]);              // eq. (8) delta_t
-            ot[i] = fmaf(dt[i], kq, al * accq[e]);             // eq. (8) o_t
+            dt[q4][i] = be * (vin[e] - al * acck[e]);          // eq. (8) delta_t
+            ot[q4][i] = fmaf(dt[q4][i], kq, al * accq[e]);     // eq. (8) o_t
           }
-          dout[q4] = dt;
-          oout[q4] = ot;
+        }
+      }
+      // delta_t and o_t leave through this wave's LDS block, turned so that eight lanes
+      // store one beam's 32 rows (128 contiguous bytes) per instruction: lane l stores
+      // rows 4 (l % 8) .. + 3 of beam 8 s + l / 8 (s < 4).  The wave alone uses its
+      // block, and a wave's LDS operations complete in order.
+      float* dbase = a.gtr_delta + slot_t * a.W_max * DV;
+      float* obase = a.o + size_t(rh) * W * DV;
+      if constexpr (TURN) {
+        float* tw = xt + w * (32 * XT);
+        const int sb = lane >> 3, sr = 4 * (lane & 7);
+        const int gr = grow0 - 16 * hf + sr;                  // first row of the state stored
+        auto out_tile = [&](const f32x4* x, float* base) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<f32x4*>(tw + m * XT + 16 * hf + 4 * q4) = x[q4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 y = *reinterpret_cast<const f32x4*>(tw + (8 * q + sb) * XT + sr);
+            if (8 * q + sb < nb && gr < DV)
+              *reinterpret_cast<f32x4*>(base + size_t(beam_of(c0 + 8 * q + sb)) * DV + gr) = y;
+          }
+          asm volatile("" ::: "memory");                     // the block's reads before its reuse
+        };
+        out_tile(dt, dbase);
+        out_tile(ot, obase);
+      } else if (grow0 < DV && valid) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          reinterpret_cast<f32x4*>(dbase + size_t(b) * DV + grow0)[q4] = dt[q4];
+          reinterpret_cast<f32x4*>(obase + size_t(b) * DV + grow0)[q4] = ot[q4];
         }
       }
     }
