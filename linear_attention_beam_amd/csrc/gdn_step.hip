@@ -277,8 +277,11 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     // Issue order for the chunk (loads complete in issue order): the ancestor keys for
     // the dot products, the ancestors' delta rows for this wave's replay, the next
     // chunk's inputs.  The dots wait only for the keys.
-    const int bm = tid / TPB, sg = tid % TPB;             // dot-phase role
+    // dot-phase role: TPB threads per beam; thread sg takes the 16-byte pieces sg,
+    // sg + TPB, ... of a row, so TPB neighbours read 16 TPB contiguous bytes at a time
+    const int bm = tid / TPB, sg = tid % TPB;
     constexpr int SV = C::SEGB / 16;
+    auto piece = [&](int i) { return 16 * sg + 16 * TPB * i; };
     u32x4 kj[NJ1][SV];
     float aj[NJ1];
 #pragma unroll
@@ -289,7 +292,7 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
       aj[j] = a.gtr_alpha[rec];
 #pragma unroll
       for (int i = 0; i < SV; ++i)
-        kj[j][i] = *reinterpret_cast<const u32x4*>(keyg + krec * C::QB + sg * C::SEGB + 16 * i);
+        kj[j][i] = *reinterpret_cast<const u32x4*>(keyg + krec * C::QB + piece(i));
     }
     const bool valid = m < nb;
     const int b = valid ? beam_of(c0 + m) : 0;
@@ -313,8 +316,8 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
         u32x4 xq[SV], xk[SV];
 #pragma unroll
         for (int i = 0; i < SV; ++i) {
-          xq[i] = *reinterpret_cast<const u32x4*>(Lq + bm * QROW + sg * C::SEGB + 16 * i);
-          xk[i] = *reinterpret_cast<const u32x4*>(Lk + bm * QROW + sg * C::SEGB + 16 * i);
+          xq[i] = *reinterpret_cast<const u32x4*>(Lq + bm * QROW + piece(i));
+          xk[i] = *reinterpret_cast<const u32x4*>(Lk + bm * QROW + piece(i));
         }
         float kq = 0.0f;
 #pragma unroll
