@@ -298,14 +298,30 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     const int b = valid ? beam_of(c0 + m) : 0;
     const int row0 = 32 * w + 16 * hf;                   // first row of this lane half (local)
     const int grow0 = row_base + row0;                   // ... of the state
-    const int rowl = min(grow0, DV - 16);                // in range (rows >= DV unused)
+    // turned layout of the epilogue (where the wave's LDS block exists): lane l holds
+    // rows sr .. sr + 3 of this wave's 32 rows for beams 8 q + sb (q < 4), so that eight
+    // lanes cover one beam's 128 contiguous bytes of a record, of delta_t and of o_t
+    const int sb = lane >> 3, sr = 4 * (lane & 7);
     f32x4 dj[NJ1][4];
+    if constexpr (TURN) {
+      const int rt = min(row_base + 32 * w + sr, DV - 4);    // in range (rows >= DV unused)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (valid ? Lan[m * kMaxT + j] : 0);
-      const f32x4* dp = reinterpret_cast<const f32x4*>(a.gtr_delta + rec * DV + rowl);
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) dj[j][q4] = dp[q4];
+        for (int q = 0; q < 4; ++q) {
+          const int bb = 8 * q + sb;
+          const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (bb < nb ? Lan[bb * kMaxT + j] : 0);
+          dj[j][q] = *reinterpret_cast<const f32x4*>(a.gtr_delta + rec * DV + rt);
+        }
+    } else {
+      const int rowl = min(grow0, DV - 16);                // in range (rows >= DV unused)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const size_t rec = (size_t(rh) * a.T_max + j) * a.W_max + (valid ? Lan[m * kMaxT + j] : 0);
+        const f32x4* dp = reinterpret_cast<const f32x4*>(a.gtr_delta + rec * DV + rowl);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) dj[j][q4] = dp[q4];
+      }
     }
     if (c + 1 < nch) stage_load(c + 1);                  // in flight until the end of the chunk
 
@@ -398,9 +414,68 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
     }
 
     {
-      // accumulator register i of this lane = physical row row0 + i of beam b
-      f32x4 dt[4] = {}, ot[4] = {};
-      if (grow0 < DV && valid) {
+      float* dbase = a.gtr_delta + slot_t * a.W_max * DV;
+      float* obase = a.o + size_t(rh) * W * DV;
+      if constexpr (TURN) {
+        // the accumulators turn through the wave's LDS block (the wave alone uses it;
+        // its LDS operations complete in order), then eqs. (6)-(8) run per beam of the
+        // turned layout and delta_t, o_t go straight out
+        float* tw = xt + w * (32 * XT);
+        const int rl = 32 * w + sr;                          // row among this workgroup's rows
+        const int gr = row_base + rl;                        // row of the state
+        constexpr int RV = (DV < C::DVB ? DV : C::DVB) - 4;  // last row group staged in Lv
+        f32x4 uq[4], uk[4];
+        auto turn = [&](const f32x16& x, f32x4* y) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4*>(tw + m * XT + 16 * hf + 4 * q4) =
+                f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) y[q] = *reinterpret_cast<const f32x4*>(tw + (8 * q + sb) * XT + sr);
+          asm volatile("" ::: "memory");                     // the block's reads before its reuse
+        };
+        turn(accq, uq);
+        turn(acck, uk);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int bb = 8 * q + sb;                         // beam slot of the chunk
+          const float* sp = sc + bb * SCN;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const float ajj = sp[1 + j], cqj = sp[1 + NJ + j], ckj = sp[1 + 2 * NJ + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              uq[q][i] = fmaf(dj[j][q][i], cqj, ajj * uq[q][i]);   // eq. (6)
+              uk[q][i] = fmaf(dj[j][q][i], ckj, ajj * uk[q][i]);   // eq. (7)
+            }
+          }
+          const float kq = sp[0], al = Lab[bb], be = Lab[32 + bb];
+          float vv[4];
+          const int rv = rl < RV ? rl : RV;
+          if constexpr (BF16) {
+            const uint32_t* vp = reinterpret_cast<const uint32_t*>(Lv + bb * VROW + rv * 2);
+            const uint32_t v01 = vp[0], v23 = vp[1];
+            vv[0] = bf2f(v01 & 0xFFFFu); vv[1] = bf2f(v01 >> 16);
+            vv[2] = bf2f(v23 & 0xFFFFu); vv[3] = bf2f(v23 >> 16);
+          } else {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(Lv + bb * VROW + rv * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vv[i] = x[i];
+          }
+          f32x4 dt, ot;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dt[i] = be * (vv[i] - al * uk[q][i]);            // eq. (8) delta_t
+            ot[i] = fmaf(dt[i], kq, al * uq[q][i]);          // eq. (8) o_t
+          }
+          if (bb < nb && gr < DV) {
+            const size_t bo = size_t(beam_of(c0 + bb)) * DV + gr;
+            *reinterpret_cast<f32x4*>(dbase + bo) = dt;
+            *reinterpret_cast<f32x4*>(obase + bo) = ot;
+          }
+        }
+      } else if (grow0 < DV && valid) {
+        // accumulator register i of this lane = physical row row0 + i of beam b
         const float* s = sc + m * SCN;
         const float kq = s[0];
         const float al = Lab[m], be = Lab[32 + m];
@@ -429,42 +504,15 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
         }
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 dt, ot;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = 4 * q4 + i;
-            dt[q4][i] = be * (vin[e] - al * acck[e]);          // eq. (8) delta_t
-            ot[q4][i] = fmaf(dt[q4][i], kq, al * accq[e]);     // eq. (8) o_t
+            dt[i] = be * (vin[e] - al * acck[e]);              // eq. (8) delta_t
+            ot[i] = fmaf(dt[i], kq, al * accq[e]);             // eq. (8) o_t
           }
-        }
-      }
-      // delta_t and o_t leave through this wave's LDS block, turned so that eight lanes
-      // store one beam's 32 rows (128 contiguous bytes) per instruction: lane l stores
-      // rows 4 (l % 8) .. + 3 of beam 8 s + l / 8 (s < 4).  The wave alone uses its
-      // block, and a wave's LDS operations complete in order.
-      float* dbase = a.gtr_delta + slot_t * a.W_max * DV;
-      float* obase = a.o + size_t(rh) * W * DV;
-      if constexpr (TURN) {
-        float* tw = xt + w * (32 * XT);
-        const int sb = lane >> 3, sr = 4 * (lane & 7);
-        const int gr = grow0 - 16 * hf + sr;                  // first row of the state stored
-        auto out_tile = [&](const f32x4* x, float* base) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<f32x4*>(tw + m * XT + 16 * hf + 4 * q4) = x[q4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 y = *reinterpret_cast<const f32x4*>(tw + (8 * q + sb) * XT + sr);
-            if (8 * q + sb < nb && gr < DV)
-              *reinterpret_cast<f32x4*>(base + size_t(beam_of(c0 + 8 * q + sb)) * DV + gr) = y;
-          }
-          asm volatile("" ::: "memory");                     // the block's reads before its reuse
-        };
-        out_tile(dt, dbase);
-        out_tile(ot, obase);
-      } else if (grow0 < DV && valid) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          reinterpret_cast<f32x4*>(dbase + size_t(b) * DV + grow0)[q4] = dt[q4];
-          reinterpret_cast<f32x4*>(obase + size_t(b) * DV + grow0)[q4] = ot[q4];
+          reinterpret_cast<f32x4*>(dbase + size_t(b) * DV + grow0)[q4] = dt;
+          reinterpret_cast<f32x4*>(obase + size_t(b) * DV + grow0)[q4] = ot;
         }
       }
     }
