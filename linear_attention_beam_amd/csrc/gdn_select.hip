@@ -247,9 +247,11 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   if constexpr (WBF16) {
     constexpr int KS = DV / 16;
     constexpr int RS = DV / 8 + 1;                 // LDS row stride in u32x4 (16 B pad)
-    constexpr int NE = 32 * DV / 8;                // u32x4 per codebook tile
+    // codebook tiles staged per barrier: two where the z operand leaves the registers
+    constexpr int TPS = KS <= 8 ? 2 : 1;
+    constexpr int NE = TPS * 32 * DV / 8;          // u32x4 per stage
     constexpr int PT = (NE + 64 * kLogitsWaves - 1) / (64 * kLogitsWaves);
-    __shared__ u32x4 tile[2][32 * RS];
+    __shared__ u32x4 tile[2][TPS * 32 * RS];
     const u32x4* wt = static_cast<const u32x4*>(a.woutT);
     // thread e-th entry of a tile: row e / (DV / 8), column e % (DV / 8); rows past the
     // codebook load code 0 (never used)
@@ -288,32 +290,36 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
       // tile is waited for
       asm volatile("" ::"v"(zl[KS - 1][0]));
       __syncthreads();
-      if (code_lo + 32 < code_hi) fetch(code_lo + 32);
-      auto mfma_tile = [&](int buf) {
+      if (code_lo + 32 * TPS < code_hi) fetch(code_lo + 32 * TPS);
+      auto mfma_tile = [&](int buf, int sub) {
         u32x4 w[KS];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) w[kk] = tile[buf][m * RS + (HV / 8) * hf + kk];
+        for (int kk = 0; kk < KS; ++kk) w[kk] = tile[buf][(32 * sub + m) * RS + (HV / 8) * hf + kk];
         return block_mfma_bf16<KS>(w, zh, zm, zl);
       };
-      // software pipeline: the MFMAs of tile i + 1 are issued before the epilogue of
-      // tile i, so the matrix cores and the VALU work at the same time.  Tile i + 1 is
-      // staged into the buffer tile i - 1 used (every wave finished with it before the
-      // previous barrier).
+      // software pipeline over stages of two tiles (64 codes, one barrier): the MFMAs of
+      // stage i + 1 are issued before the epilogue of stage i, so the matrix cores and
+      // the VALU work at the same time.  Stage i + 1 is staged into the buffer stage
+      // i - 1 used (every wave finished with it before the previous barrier).  A group
+      // with an odd number of tiles computes one unused tile at its end.
       // (d_v = 256 holds twice the z operand: there the tiles go one after the other)
       if constexpr (KS <= 8) {
-        f32x16 acc = mfma_tile(0);
+        f32x16 a0 = mfma_tile(0, 0), a1 = mfma_tile(0, 1);
         int buf = 0;
-        for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
-          const bool more = c0 + 32 < code_hi;       // block-uniform
+        for (int c0 = code_lo; c0 < code_hi; c0 += 64) {
+          const bool more = c0 + 64 < code_hi;       // block-uniform
           if (more) {
             put(buf ^ 1);
             __syncthreads();
-            if (c0 + 64 < code_hi) fetch(c0 + 64);
-            const f32x16 nxt = mfma_tile(buf ^ 1);
-            fold(acc, c0);
-            acc = nxt;
+            if (c0 + 128 < code_hi) fetch(c0 + 128);
+            const f32x16 n0 = mfma_tile(buf ^ 1, 0), n1 = mfma_tile(buf ^ 1, 1);
+            fold(a0, c0);
+            if (c0 + 32 < code_hi) fold(a1, c0 + 32);
+            a0 = n0;
+            a1 = n1;
           } else {
-            fold(acc, c0);
+            fold(a0, c0);
+            if (c0 + 32 < code_hi) fold(a1, c0 + 32);
           }
           buf ^= 1;
         }
@@ -321,7 +327,7 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
         int buf = 0;
         for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
           const bool more = c0 + 32 < code_hi;       // block-uniform
-          fold(mfma_tile(buf), c0);
+          fold(mfma_tile(buf, 0), c0);
           if (more) {
             put(buf ^ 1);
             __syncthreads();
