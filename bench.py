@@ -52,6 +52,11 @@ def parse():
     p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                    help="first copy MIB MiB device-to-device 3 times (a plain copy of known size "
                         "for scaling hardware byte counters)")
+    p.add_argument("--flush-mall", choices=["read", "write"], default=None,
+                   help="cold-cache timing: read (or write) 1 GiB of scratch before every step "
+                        "launch, so neither L2 nor the 256 MiB last-level cache holds its inputs; "
+                        "every launch is timed alone between events, and value counts only the "
+                        "event-timed init, step and select work")
     return p.parse_args()
 
 
@@ -267,44 +272,62 @@ def main():
         decode()
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole decodes back to back on the stream, nothing else on it
-    # (a timing event between kernels costs the stream a few microseconds)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        decode()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
     # ---- per-launch kernel times: an instrumented pass of the same decodes, HIP events
-    # recorded on the launch stream.  Each step(t) is issued REP times back to back
+    # recorded on the launch stream.  Each step(t) is issued rep times back to back
     # between one pair of events (re-issuing step(t) rewrites the same values), so the
-    # events' own cost is spread over REP launches; select(t) runs once between its pair.
-    REP = 4
-    n_ins = max(3, min(args.steps, 10))
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(wl.T)]
-           for _ in range(n_ins)]
-    for i in range(n_ins):
-        dec.init(S_ctx, wl.width(0), stream)
-        for t in range(wl.T):
-            x = inputs[t]
-            evs[i][t][0].record(stream)
-            for _ in range(REP):
-                gdn_step(t, x)
-            evs[i][t][1].record(stream)
-            s = sels[t]
-            dec.select(t, outs[t], Wout, wl.V, wl.width(t + 1), s["parent"], s["token"],
-                       s["score"], forced[t][0], forced[t][1], stream)
-            evs[i][t][2].record(stream)
-    torch.cuda.synchronize()
-    step_ms = np.zeros(wl.T)
-    sel_ms = np.zeros(wl.T)
-    for i in range(n_ins):
-        for t in range(wl.T):
-            step_ms[t] += evs[i][t][0].elapsed_time(evs[i][t][1]) / REP
-            sel_ms[t] += evs[i][t][1].elapsed_time(evs[i][t][2])
-    step_ms /= n_ins
-    sel_ms /= n_ins
+    # events' own cost is spread over rep launches; select(t) runs once between its pair.
+    # With a flush buffer, 1 GiB of it is read or written before every step launch
+    # (outside the events), so the launch finds none of its inputs in any cache.
+    def instrumented(n, rep, flush_buf=None):
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(wl.T)]
+               for _ in range(n)]
+        evi = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for i in range(n):
+            evi[i][0].record(stream)
+            dec.init(S_ctx, wl.width(0), stream)
+            evi[i][1].record(stream)
+            for t in range(wl.T):
+                x = inputs[t]
+                if flush_buf is not None:
+                    if args.flush_mall == "write":
+                        flush_buf.zero_()
+                    else:
+                        flush_buf.sum()
+                evs[i][t][0].record(stream)
+                for _ in range(rep):
+                    gdn_step(t, x)
+                evs[i][t][1].record(stream)
+                s = sels[t]
+                dec.select(t, outs[t], Wout, wl.V, wl.width(t + 1), s["parent"], s["token"],
+                           s["score"], forced[t][0], forced[t][1], stream)
+                evs[i][t][2].record(stream)
+        torch.cuda.synchronize()
+        st, se, it = np.zeros(wl.T), np.zeros(wl.T), 0.0
+        for i in range(n):
+            it += evi[i][0].elapsed_time(evi[i][1])
+            for t in range(wl.T):
+                st[t] += evs[i][t][0].elapsed_time(evs[i][t][1]) / rep
+                se[t] += evs[i][t][1].elapsed_time(evs[i][t][2])
+        return st / n, se / n, it / n
+
     trans = wl.transitions()
+    if not args.flush_mall:
+        # ---- timed region: K whole decodes back to back on the stream, nothing else on
+        # it (a timing event between kernels costs the stream a few microseconds)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            decode()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        step_ms, sel_ms, _ = instrumented(max(3, min(args.steps, 10)), 4)
+    else:
+        # ---- cold caches: K decodes whose every step launch follows a 1 GiB read or
+        # write; the decode time is the sum of its event-timed init, step and select
+        # intervals
+        flush_buf = torch.zeros(256 << 20, dtype=torch.float32, device=dev)
+        step_ms, sel_ms, init_ms = instrumented(args.steps, 1, flush_buf)
+        elapsed = (init_ms + step_ms.sum() + sel_ms.sum()) * 1e-3 * args.steps
+        del flush_buf
     value = trans * args.steps / elapsed
     if states is None:
         bytes_t = [step_bytes(wl, t, distinct[t]) for t in range(wl.T)]
@@ -330,7 +353,7 @@ def main():
         "config": {"workload": wl.name, "R": wl.R, "H": wl.H, "d_k": wl.d_k, "d_v": wl.d_v,
                    "T": wl.T, "W_t": list(wl.widths), "V": wl.V, "io_dtype": wl.io,
                    "state_dtype": "f32", "mode": args.mode, "path": args.path,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "cache": f"cold ({args.flush_mall} flush)" if args.flush_mall else "pipeline"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gdn step_kernel" if states is None else "gdn fullstate_kernel",
