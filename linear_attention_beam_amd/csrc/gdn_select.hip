@@ -189,6 +189,8 @@ struct LogitsK {
 
 // Beam chunks (waves) per first-pass block; the block shares one code group.
 constexpr int kLogitsWaves = 8;
+// Codes per group are at most 1024 (the launcher's choice): 32 tiles.
+constexpr int kMaxGroupTiles = 32;
 
 // Block: kLogitsWaves chunks of 32 beams x one group of cpw codes.  Each 32-code tile of
 // the codebook is staged once per block in LDS (double-buffered, one barrier per tile)
@@ -215,6 +217,30 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   const int code_hi = min(a.V, code_lo + a.cpw);
 
   float mrun = -INFINITY, srun = 0.0f, nrun = INFINITY;
+  // tile maxima of the block, staged in LDS where the pair loop below runs (its folds
+  // then hold no branch) and written out, coalesced, at the end
+  constexpr bool STAGE_TM = WBF16 && DV <= 128;
+  __shared__ float tms[STAGE_TM ? kMaxGroupTiles * kLogitsWaves * 32 : 1];
+  auto put_tm = [&](float tm, int c0) {
+    if constexpr (STAGE_TM) tms[((c0 - code_lo) >> 5) * (kLogitsWaves * 32) + wave * 32 + m] = tm;
+    else if (hf == 0 && bvalid) tm_r[size_t(c0 >> 5) * a.W + b] = tm;
+  };
+  // fold of a tile whose 32 codes all exist: the same arithmetic as fold below, as
+  // straight-line code (selects in place of its branches)
+  auto fold_full = [&](const f32x16& acc, int c0) {
+    float tm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tm = fmaxf(tm, acc[i]);
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    put_tm(tm, c0);
+    nrun = fminf(nrun, tm);
+    const bool up = tm > mrun;
+    const float sc = mrun == -INFINITY ? 0.0f : srun * __builtin_amdgcn_exp2f((mrun - tm) * kLog2e);
+    srun = up ? sc : srun;
+    mrun = up ? tm : mrun;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) srun += __builtin_amdgcn_exp2f((acc[i] - mrun) * kLog2e);
+  };
   auto fold = [&](const f32x16& acc, int c0) {
     const bool full = c0 + 32 <= a.V;              // block-uniform
     float tm = -INFINITY;
@@ -227,7 +253,7 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
         if (c0 + 8 * (i >> 2) + 4 * hf + (i & 3) < a.V) tm = fmaxf(tm, acc[i]);
     }
     tm = fmaxf(tm, __shfl_xor(tm, 32));            // code c0 is valid: tm is finite
-    if (hf == 0 && bvalid) tm_r[size_t(c0 >> 5) * a.W + b] = tm;
+    put_tm(tm, c0);
     nrun = fminf(nrun, tm);
     if (tm > mrun) {
       srun = mrun == -INFINITY ? 0.0f : srun * __builtin_amdgcn_exp2f((mrun - tm) * kLog2e);
@@ -305,24 +331,29 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
       // (d_v = 256 holds twice the z operand: there the tiles go one after the other)
       if constexpr (KS <= 8) {
         f32x16 a0 = mfma_tile(0, 0), a1 = mfma_tile(0, 1);
-        int buf = 0;
-        for (int c0 = code_lo; c0 < code_hi; c0 += 64) {
-          const bool more = c0 + 64 < code_hi;       // block-uniform
-          if (more) {
-            put(buf ^ 1);
-            __syncthreads();
-            if (c0 + 128 < code_hi) fetch(c0 + 128);
-            const f32x16 n0 = mfma_tile(buf ^ 1, 0), n1 = mfma_tile(buf ^ 1, 1);
-            fold(a0, c0);
-            if (c0 + 32 < code_hi) fold(a1, c0 + 32);
-            a0 = n0;
-            a1 = n1;
-          } else {
-            fold(a0, c0);
-            if (c0 + 32 < code_hi) fold(a1, c0 + 32);
+        int buf = 0, c0 = code_lo;
+        // stages with a successor: both of their tiles are whole, and the body is one
+        // basic block in which the 48 MFMAs of the next stage interleave with the folds
+        // of this one (the next fetch is issued unconditionally on clamped rows; past
+        // the group it is never staged)
+        for (; c0 + 64 < code_hi; c0 += 64) {
+          put(buf ^ 1);
+          __syncthreads();
+          fetch(c0 + 128);
+          const f32x16 n0 = mfma_tile(buf ^ 1, 0), n1 = mfma_tile(buf ^ 1, 1);
+          fold_full(a0, c0);
+          fold_full(a1, c0 + 32);
+#pragma unroll
+          for (int i = 0; i < 6 * KS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
           }
+          a0 = n0;
+          a1 = n1;
           buf ^= 1;
         }
+        fold(a0, c0);
+        if (c0 + 32 < code_hi) fold(a1, c0 + 32);
       } else {
         int buf = 0;
         for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
@@ -374,6 +405,15 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     const float* wt = static_cast<const float*>(a.woutT);
     for (int c0 = code_lo; c0 < code_hi; c0 += 32)
       fold(block_mfma_f32<DV>(wt, c0 + m, a.V, hf, zv), c0);
+  }
+  if constexpr (STAGE_TM) {
+    __syncthreads();
+    const int nt = (code_hi - code_lo + 31) >> 5;
+    const int b0 = (bx / a.nvg) * kLogitsWaves * 32;
+    for (int e = threadIdx.x; e < nt * kLogitsWaves * 32; e += 64 * kLogitsWaves) {
+      const int bb = b0 + e % (kLogitsWaves * 32);
+      if (bb < a.W) tm_r[size_t((code_lo >> 5) + e / (kLogitsWaves * 32)) * a.W + bb] = tms[e];
+    }
   }
   // merge the two lane halves of beam b
   const float mo = __shfl_xor(mrun, 32), so = __shfl_xor(srun, 32);
