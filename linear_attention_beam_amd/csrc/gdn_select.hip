@@ -191,6 +191,8 @@ struct LogitsK {
 constexpr int kLogitsWaves = 8;
 // Codes per group are at most 1024 (the launcher's choice): 32 tiles.
 constexpr int kMaxGroupTiles = 32;
+// Tiles the selection keeps in LDS between its bound and the exact K-th key.
+constexpr int kSelList = 8192;
 
 // Block: kLogitsWaves chunks of 32 beams x one group of cpw codes.  Each 32-code tile of
 // the codebook is staged once per block in LDS (double-buffered, one barrier per tile)
@@ -697,12 +699,19 @@ struct TileSelK {
 //  1. log-sum-exp of every beam from its parts; the request's tile-key range (the
 //     score is monotone in the logit: the largest logit and the smallest tile maximum
 //     of each row bound its tile keys).
-//  2. Pass over all tile keys: 2048-digit histogram over that exact range; the digit
-//     holding the K-th largest key.
-//  3. Pass: keys above the digit are chosen, keys inside it are kept.
-//  4. The rest of the K inside the digit, ties by flat tile index: one sort of the kept
+//  2. A lower bound theta0 on the K-th largest tile key: each code group's largest
+//     logit is one of its tile maxima, so the W * nvg group keys are keys of distinct
+//     tiles, and the low edge of the histogram digit holding the K-th largest of them
+//     has at least K tile keys at or above it.  Per beam, the smallest tile-maximum key
+//     whose tile key reaches theta0 (the key is monotone in the logit).
+//  3. One pass over all tile maxima: those at or above their beam's threshold (a few
+//     more than K) go to an LDS list with their keys; when the list overflows, the
+//     passes below read every tile instead.
+//  4. Over the list: 2048-digit histogram, the digit holding the K-th largest key;
+//     keys above the digit are chosen, keys inside it are kept.
+//  5. The rest of the K inside the digit, ties by flat tile index: one sort of the kept
 //     tiles when at most 1024 (the usual case: a handful), else a radix finish.
-//  5. Counting sort of the K chosen tiles by code tile j, cut into groups of at most
+//  6. Counting sort of the K chosen tiles by code tile j, cut into groups of at most
 //     32 beams: one MFMA block of the refinement each.
 __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   __shared__ float lse_s[kMaxW], cum_s[kMaxW];
@@ -713,7 +722,9 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   __shared__ uint64_t cs[kMaxW], xs[kMaxW];                // kept tiles as (key, ~flat); sorted
   __shared__ uint32_t wsum[16];
   __shared__ RadixSh sh;
-  __shared__ uint32_t kmin_sh, kmax_sh, nwin_sh, ncand_sh, theta_sh;
+  __shared__ uint32_t kmin_sh, kmax_sh, nwin_sh, ncand_sh, theta_sh, nlist_sh;
+  __shared__ uint32_t kthr_s[kMaxW];                       // per beam: least passing tile-max key
+  __shared__ uint64_t list[kSelList];                      // (key, ~flat) at or above theta0
   const int r = blockIdx.x, tid = threadIdx.x;
   const int W = a.W;
   const uint32_t Vt = uint32_t(a.Vt), K = uint32_t(a.K);
@@ -721,8 +732,11 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   uint32_t* cand = a.cand + size_t(r) * a.stride;
   const size_t cap = size_t(Vt) * W;
 
+  // Where the request's tiles outnumber the list, the tile maxima are read once, by
+  // the bounded pass below, else twice, by the passes over every tile.
+  const bool bounded = size_t(W) * Vt > size_t(kSelList) && uint32_t(W) * uint32_t(a.nvg) >= K;
   // thread -> one beam b and every G-th tile from jg; its first U tiles are loaded now,
-  // under the log-sum-exp phase, and kept for both passes
+  // under the log-sum-exp phase, and kept for the passes
   constexpr int U = 16;
   const int G = 1024 / W;
   const bool act = tid < G * W;
@@ -741,9 +755,10 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   for (int u = 0; u < 8; ++u)
     q[u] = tid < W && u < a.nvg ? lp[u] : make_float4(-INFINITY, 0.0f, INFINITY, 0.0f);
   const float c = tid < W ? a.cum[size_t(r) * a.W_max + tid] : 0.0f;
-  if (tid == 0) { kmin_sh = 0xFFFFFFFFu; kmax_sh = 0u; nwin_sh = 0u; ncand_sh = 0u; }
+  if (tid == 0) { kmin_sh = 0xFFFFFFFFu; kmax_sh = 0u; nwin_sh = 0u; ncand_sh = 0u; nlist_sh = 0u; }
   for (int i = tid; i < kHistBins; i += 1024) hist[i] = 0;
   __syncthreads();
+  float lt = 0.0f;                                        // log-sum-exp of beam tid
   {
     uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
     if (tid < W) {
@@ -765,6 +780,7 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
         }
       }
       const float l = mm + logf(s);
+      lt = l;
       lse_s[tid] = l;
       cum_s[tid] = c;
       a.lse[size_t(r) * a.W_max + tid] = l;
@@ -782,13 +798,62 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   const uint32_t kmin = kmin_sh, kmax = kmax_sh;
   const int shift0 = first_shift(kmin, kmax);
 
+  // ---- theta0 from the code groups' largest logits (hist is clear)
+  uint32_t theta0 = kmin;
+  if (bounded) {                                          // block-uniform
+    if (tid < W) {
+      const float c = cum_s[tid];
+      auto add = [&](float gx) {
+        const uint32_t key = f2key(cand_score(c, gx, lt));
+        if (key >= kmin && key <= kmax) atomicAdd(&hist[(key - kmin) >> shift0], 1u);
+      };
+      if (a.nvg <= 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (u < a.nvg) add(q[u].x);
+      } else {
+        for (int u = 0; u < a.nvg; ++u) add(lp[u].x);
+      }
+    }
+    __syncthreads();
+    pick_digit(hist, wsum, kmin, kmax, shift0, K, sh);
+    theta0 = sh.lo;                                       // kmin when the counts fall short
+    for (int i = tid; i < kHistBins; i += 1024) hist[i] = 0;
+  }
+  if (bounded && tid < W) {
+    // the least tile-maximum key x whose tile key reaches theta0, by bisection over the
+    // keys of -inf .. +inf (tile maxima are never NaN); 0 (every tile tested by its key)
+    // for a beam whose cumulative score or log-sum-exp is not finite
+    const float c = cum_s[tid];
+    uint32_t kt = 0u;
+    if (theta0 > kmin && __builtin_isfinite(c) && __builtin_isfinite(lt)) {
+      auto reach = [&](uint32_t kx) { return f2key(cand_score(c, key2f(kx), lt)) >= theta0; };
+      uint32_t lo = 0x007FFFFFu, hi = 0xFF800000u;        // keys of -inf and +inf
+      if (!reach(lo)) {
+        if (!reach(hi)) {
+          kt = 0xFFFFFFFFu;
+        } else {
+          while (hi - lo > 1u) {
+            const uint32_t mid = lo + ((hi - lo) >> 1);
+            if (reach(mid)) hi = mid;
+            else lo = mid;
+          }
+          kt = hi;
+        }
+      }
+    }
+    kthr_s[tid] = kt;
+  }
+  __syncthreads();
+
   const float cb = cum_s[b], lb = lse_s[b];
-  auto stream = [&](auto&& f) {
+  // every tile of this thread's beam b: f(tile maximum, j)
+  auto stream_tiles = [&](auto&& f) {
     if (!act) return;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int jj = jg + u * G;
-      if (jj < a.Vt) f(f2key(cand_score(cb, x0[u], lb)), jj);
+      if (jj < a.Vt) f(x0[u], jj);
     }
     // the rest in batches of UB loads in flight (large codebooks: up to 256 per thread)
     constexpr int UB = 32;
@@ -802,22 +867,49 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int jj = j + u * G;
-        if (jj < a.Vt) f(f2key(cand_score(cb, x[u], lb)), jj);
+        if (jj < a.Vt) f(x[u], jj);
       }
     }
   };
-  stream([&](uint32_t key, int) {
-    if (key >= kmin && key <= kmax) atomicAdd(&hist[(key - kmin) >> shift0], 1u);
+  // ---- the list: tiles whose key reaches theta0
+  if (bounded) {
+    const uint32_t kb = act ? kthr_s[b] : 0xFFFFFFFFu;
+    stream_tiles([&](float x, int j) {
+      if (f2key(x) < kb) return;
+      const uint32_t key = f2key(cand_score(cb, x, lb));
+      if (key < theta0) return;
+      const uint32_t p = atomicAdd(&nlist_sh, 1u);
+      if (p < uint32_t(kSelList))
+        list[p] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - (uint32_t(b) * Vt + uint32_t(j)));
+    });
+  }
+  __syncthreads();
+  const uint32_t nlist = nlist_sh;
+  const bool use_list = bounded && nlist <= uint32_t(kSelList);   // block-uniform
+  const uint32_t rlo = use_list ? theta0 : kmin;
+  const int shiftA = first_shift(rlo, kmax);
+  // the keys the passes below read: the list, or every tile: f(key, flat)
+  auto stream = [&](auto&& f) {
+    if (use_list) {
+      for (uint32_t p = tid; p < nlist; p += 1024) {
+        const uint64_t e = list[p];
+        f(uint32_t(e >> 32), 0xFFFFFFFFu - uint32_t(e));
+      }
+    } else {
+      stream_tiles([&](float x, int j) { f(f2key(cand_score(cb, x, lb)), uint32_t(b) * Vt + uint32_t(j)); });
+    }
+  };
+  stream([&](uint32_t key, uint32_t) {
+    if (key >= rlo && key <= kmax) atomicAdd(&hist[(key - rlo) >> shiftA], 1u);
   });
   __syncthreads();
-  pick_digit(hist, wsum, kmin, kmax, shift0, K, sh);
+  pick_digit(hist, wsum, rlo, kmax, shiftA, K, sh);
   const uint32_t lo = sh.lo, hi = sh.hi;
   uint32_t need = sh.need;
   const int shift1 = sh.shift;
   __syncthreads();
-  stream([&](uint32_t key, int j) {
+  stream([&](uint32_t key, uint32_t flat) {
     if (key < lo) return;
-    const uint32_t flat = uint32_t(b) * Vt + uint32_t(j);
     if (key > hi) {
       const uint32_t p = atomicAdd(&nwin_sh, 1u);
       if (p < uint32_t(kMaxW)) chosen[p] = flat;
