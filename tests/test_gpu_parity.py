@@ -35,6 +35,9 @@ DERIVED = {
     # 1024 beams over six steps: the parents' rows exceed what the final select stages
     # in LDS (1024 x 5 entries at the last step) and are read from global memory
     "tiny_w1024_t6": ("tiny", dict(T=6, widths=(1024,) * 6, V=64)),
+    # 512 x 32 tiles, more than the tile selection's list holds: the bounded pass (and,
+    # with every score tied, its overflow back to the passes over every tile)
+    "tiny_bounded": ("tiny", dict(widths=(512, 512, 512), V=1024)),
     # six SID steps (five ancestor records at the last step)
     "tiny_t6": ("tiny", dict(T=6, widths=(8,) * 6)),
     "single_bf16_t6": ("single", dict(T=6, widths=(128,) * 6, io="bf16", wout="bf16")),
@@ -131,8 +134,9 @@ def test_forced_parents_parity(name, R):
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_v37", 1),
                                     ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("single_v300", 1),
-                                    ("single_bf16_t6", 1), ("tiny_w1024_t6", 1), ("single_gqa", 1),
-                                    ("single_dk256", 1), ("single_dv512", 1), ("single_dk256_dv512", 1)])
+                                    ("single_bf16_t6", 1), ("tiny_w1024_t6", 1), ("tiny_bounded", 2),
+                                    ("single_gqa", 1), ("single_dk256", 1), ("single_dv512", 1),
+                                    ("single_dk256_dv512", 1)])
 def test_select_mode_parity(name, R):
     """Top-W drives the beams.  The oracle follows the GPU's choice (teacher forcing)
     after the selection itself has been checked against the exact top-W."""
@@ -253,7 +257,8 @@ def test_full_size_select_properties(name):
             assert np.array_equal(anc[r][:K, :t + 1], anc_ref[r]), f"ancestry r={r} t={t}"
 
 
-@pytest.mark.parametrize("name", ["tiny", "single", "ties_w512", "ties_w512_v96", "ties_bf16_w512"])
+@pytest.mark.parametrize("name", ["tiny", "single", "ties_w512", "ties_w512_v96", "ties_bf16_w512",
+                                  "tiny_bounded"])
 def test_all_scores_tied(name):
     """Wout = 0: every candidate of a request scores cum - log V; the top-W is then the
     W smallest flat indices, in order (the tie-break), at every step."""
