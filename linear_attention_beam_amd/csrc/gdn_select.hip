@@ -713,6 +713,7 @@ struct TileSelK {
 //     tiles when at most 1024 (the usual case: a handful), else a radix finish.
 //  6. Counting sort of the K chosen tiles by code tile j, cut into groups of at most
 //     32 beams: one MFMA block of the refinement each.
+template <bool BOUNDED>
 __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   __shared__ float lse_s[kMaxW], cum_s[kMaxW];
   __shared__ uint32_t hist[kHistBins];
@@ -723,8 +724,8 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   __shared__ uint32_t wsum[16];
   __shared__ RadixSh sh;
   __shared__ uint32_t kmin_sh, kmax_sh, nwin_sh, ncand_sh, theta_sh, nlist_sh;
-  __shared__ uint32_t kthr_s[kMaxW];                       // per beam: least passing tile-max key
-  __shared__ uint64_t list[kSelList];                      // (key, ~flat) at or above theta0
+  __shared__ uint32_t kthr_s[BOUNDED ? kMaxW : 1];         // per beam: least passing tile-max key
+  __shared__ uint64_t list[BOUNDED ? kSelList : 1];        // (key, ~flat) at or above theta0
   const int r = blockIdx.x, tid = threadIdx.x;
   const int W = a.W;
   const uint32_t Vt = uint32_t(a.Vt), K = uint32_t(a.K);
@@ -732,9 +733,10 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   uint32_t* cand = a.cand + size_t(r) * a.stride;
   const size_t cap = size_t(Vt) * W;
 
-  // Where the request's tiles outnumber the list, the tile maxima are read once, by
-  // the bounded pass below, else twice, by the passes over every tile.
-  const bool bounded = size_t(W) * Vt > size_t(kSelList) && uint32_t(W) * uint32_t(a.nvg) >= K;
+  // Bounded (the launcher's choice where a request's tiles outnumber the list): the
+  // tile maxima are read once, by the bounded pass below; else twice, by the passes
+  // over every tile.
+  constexpr bool bounded = BOUNDED;
   // thread -> one beam b and every G-th tile from jg; its first U tiles are loaded now,
   // under the log-sum-exp phase, and kept for the passes
   constexpr int U = 16;
@@ -798,9 +800,10 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   const uint32_t kmin = kmin_sh, kmax = kmax_sh;
   const int shift0 = first_shift(kmin, kmax);
 
-  // ---- theta0 from the code groups' largest logits (hist is clear)
+  // ---- bounded mode: theta0 from the code groups' largest logits (hist is clear), then
+  // each beam's threshold on its tile maxima
   uint32_t theta0 = kmin;
-  if (bounded) {                                          // block-uniform
+  if constexpr (bounded) {
     if (tid < W) {
       const float c = cum_s[tid];
       auto add = [&](float gx) {
@@ -819,32 +822,32 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
     pick_digit(hist, wsum, kmin, kmax, shift0, K, sh);
     theta0 = sh.lo;                                       // kmin when the counts fall short
     for (int i = tid; i < kHistBins; i += 1024) hist[i] = 0;
-  }
-  if (bounded && tid < W) {
-    // the least tile-maximum key x whose tile key reaches theta0, by bisection over the
-    // keys of -inf .. +inf (tile maxima are never NaN); 0 (every tile tested by its key)
-    // for a beam whose cumulative score or log-sum-exp is not finite
-    const float c = cum_s[tid];
-    uint32_t kt = 0u;
-    if (theta0 > kmin && __builtin_isfinite(c) && __builtin_isfinite(lt)) {
-      auto reach = [&](uint32_t kx) { return f2key(cand_score(c, key2f(kx), lt)) >= theta0; };
-      uint32_t lo = 0x007FFFFFu, hi = 0xFF800000u;        // keys of -inf and +inf
-      if (!reach(lo)) {
-        if (!reach(hi)) {
-          kt = 0xFFFFFFFFu;
-        } else {
-          while (hi - lo > 1u) {
-            const uint32_t mid = lo + ((hi - lo) >> 1);
-            if (reach(mid)) hi = mid;
-            else lo = mid;
+    if (tid < W) {
+      // the least tile-maximum key x whose tile key reaches theta0, by bisection over
+      // the keys of -inf .. +inf (tile maxima are never NaN); 0 (every tile tested by
+      // its key) for a beam whose cumulative score or log-sum-exp is not finite
+      const float c = cum_s[tid];
+      uint32_t kt = 0u;
+      if (theta0 > kmin && __builtin_isfinite(c) && __builtin_isfinite(lt)) {
+        auto reach = [&](uint32_t kx) { return f2key(cand_score(c, key2f(kx), lt)) >= theta0; };
+        uint32_t lo = 0x007FFFFFu, hi = 0xFF800000u;      // keys of -inf and +inf
+        if (!reach(lo)) {
+          if (!reach(hi)) {
+            kt = 0xFFFFFFFFu;
+          } else {
+            while (hi - lo > 1u) {
+              const uint32_t mid = lo + ((hi - lo) >> 1);
+              if (reach(mid)) hi = mid;
+              else lo = mid;
+            }
+            kt = hi;
           }
-          kt = hi;
         }
       }
+      kthr_s[tid] = kt;
     }
-    kthr_s[tid] = kt;
+    __syncthreads();
   }
-  __syncthreads();
 
   const float cb = cum_s[b], lb = lse_s[b];
   // every tile of this thread's beam b: f(tile maximum, j)
@@ -872,7 +875,9 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
     }
   };
   // ---- the list: tiles whose key reaches theta0
-  if (bounded) {
+  uint32_t nlist = 0u;
+  bool use_list = false;
+  if constexpr (bounded) {
     const uint32_t kb = act ? kthr_s[b] : 0xFFFFFFFFu;
     stream_tiles([&](float x, int j) {
       if (f2key(x) < kb) return;
@@ -883,9 +888,11 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
         list[p] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - (uint32_t(b) * Vt + uint32_t(j)));
     });
   }
-  __syncthreads();
-  const uint32_t nlist = nlist_sh;
-  const bool use_list = bounded && nlist <= uint32_t(kSelList);   // block-uniform
+  if constexpr (bounded) {
+    __syncthreads();
+    nlist = nlist_sh;
+    use_list = nlist <= uint32_t(kSelList);               // block-uniform
+  }
   const uint32_t rlo = use_list ? theta0 : kmin;
   const int shiftA = first_shift(rlo, kmax);
   // the keys the passes below read: the list, or every tile: f(key, flat)
@@ -1420,7 +1427,11 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   {
     TileSelK k{a.W, a.W_max, Vt, Kt, a.W_next, G_max, nvg, tstride, tmax, lse_part, cum, lse, sel,
                cand, tiles, groups, gtiles, status};
-    hipLaunchKernelGGL(tile_select_kernel, dim3(a.R), dim3(1024), 0, s, k);
+    // the bounded pass where a request's tiles outnumber the list (and the code groups'
+    // maxima number at least K)
+    const bool bounded = int64_t(a.W) * Vt > kSelList && int64_t(a.W) * nvg >= Kt;
+    if (bounded) hipLaunchKernelGGL(tile_select_kernel<true>, dim3(a.R), dim3(1024), 0, s, k);
+    else hipLaunchKernelGGL(tile_select_kernel<false>, dim3(a.R), dim3(1024), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
   {  // groups <= ceil(Kt / 32) + min(Vt, Kt) <= G_max
