@@ -850,13 +850,13 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   }
 
   const float cb = cum_s[b], lb = lse_s[b];
-  // every tile of this thread's beam b: f(tile maximum, j)
-  auto stream_tiles = [&](auto&& f) {
+  // every tile of this thread's beam b: f(key, j)
+  auto stream = [&](auto&& f) {
     if (!act) return;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int jj = jg + u * G;
-      if (jj < a.Vt) f(x0[u], jj);
+      if (jj < a.Vt) f(f2key(cand_score(cb, x0[u], lb)), jj);
     }
     // the rest in batches of UB loads in flight (large codebooks: up to 256 per thread)
     constexpr int UB = 32;
@@ -870,52 +870,14 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int jj = j + u * G;
-        if (jj < a.Vt) f(x[u], jj);
+        if (jj < a.Vt) f(f2key(cand_score(cb, x[u], lb)), jj);
       }
     }
   };
-  // ---- the list: tiles whose key reaches theta0
-  uint32_t nlist = 0u;
-  bool use_list = false;
-  if constexpr (bounded) {
-    const uint32_t kb = act ? kthr_s[b] : 0xFFFFFFFFu;
-    stream_tiles([&](float x, int j) {
-      if (f2key(x) < kb) return;
-      const uint32_t key = f2key(cand_score(cb, x, lb));
-      if (key < theta0) return;
-      const uint32_t p = atomicAdd(&nlist_sh, 1u);
-      if (p < uint32_t(kSelList))
-        list[p] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - (uint32_t(b) * Vt + uint32_t(j)));
-    });
-  }
-  if constexpr (bounded) {
-    __syncthreads();
-    nlist = nlist_sh;
-    use_list = nlist <= uint32_t(kSelList);               // block-uniform
-  }
-  const uint32_t rlo = use_list ? theta0 : kmin;
-  const int shiftA = first_shift(rlo, kmax);
-  // the keys the passes below read: the list, or every tile: f(key, flat)
-  auto stream = [&](auto&& f) {
-    if (use_list) {
-      for (uint32_t p = tid; p < nlist; p += 1024) {
-        const uint64_t e = list[p];
-        f(uint32_t(e >> 32), 0xFFFFFFFFu - uint32_t(e));
-      }
-    } else {
-      stream_tiles([&](float x, int j) { f(f2key(cand_score(cb, x, lb)), uint32_t(b) * Vt + uint32_t(j)); });
-    }
-  };
-  stream([&](uint32_t key, uint32_t) {
-    if (key >= rlo && key <= kmax) atomicAdd(&hist[(key - rlo) >> shiftA], 1u);
-  });
-  __syncthreads();
-  pick_digit(hist, wsum, rlo, kmax, shiftA, K, sh);
-  const uint32_t lo = sh.lo, hi = sh.hi;
-  uint32_t need = sh.need;
-  const int shift1 = sh.shift;
-  __syncthreads();
-  stream([&](uint32_t key, uint32_t flat) {
+  // the split of one key: above the boundary digit chosen, inside it kept
+  uint32_t lo, hi, need;
+  int shift1;
+  auto split = [&](uint32_t key, uint32_t flat) {
     if (key < lo) return;
     if (key > hi) {
       const uint32_t p = atomicAdd(&nwin_sh, 1u);
@@ -925,7 +887,74 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
       if (p < cap) cand[p] = flat;
       if (p < uint32_t(kMaxW)) cs[p] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - flat);
     }
-  });
+  };
+  bool use_list = false;
+  if constexpr (bounded) {
+    // ---- the list: tiles whose tile-maximum key reaches their beam's threshold (and
+    // whose key then reaches theta0); the passes below read it, or every tile when it
+    // overflowed
+    {
+      const uint32_t kb = act ? kthr_s[b] : 0xFFFFFFFFu;
+      if (act) {
+        auto test = [&](float x, int j) {
+          if (f2key(x) < kb) return;
+          const uint32_t key = f2key(cand_score(cb, x, lb));
+          if (key < theta0) return;
+          const uint32_t p = atomicAdd(&nlist_sh, 1u);
+          if (p < uint32_t(kSelList))
+            list[p] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - (uint32_t(b) * Vt + uint32_t(j)));
+        };
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int jj = jg + u * G;
+          if (jj < a.Vt) test(x0[u], jj);
+        }
+        constexpr int UB = 32;
+        for (int j = jg + U * G; j < a.Vt; j += UB * G) {
+          float x[UB];
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            const int jj = j + u * G;
+            x[u] = jj < a.Vt ? tm[size_t(jj) * W + b] : 0.0f;
+          }
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            const int jj = j + u * G;
+            if (jj < a.Vt) test(x[u], jj);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t nlist = nlist_sh;
+    use_list = nlist <= uint32_t(kSelList);               // block-uniform
+    if (use_list) {
+      const int sh0 = first_shift(theta0, kmax);
+      for (uint32_t p = tid; p < nlist; p += 1024) {
+        const uint32_t key = uint32_t(list[p] >> 32);
+        if (key <= kmax) atomicAdd(&hist[(key - theta0) >> sh0], 1u);
+      }
+      __syncthreads();
+      pick_digit(hist, wsum, theta0, kmax, sh0, K, sh);
+      lo = sh.lo; hi = sh.hi; need = sh.need; shift1 = sh.shift;
+      __syncthreads();
+      for (uint32_t p = tid; p < nlist; p += 1024) {
+        const uint64_t e = list[p];
+        split(uint32_t(e >> 32), 0xFFFFFFFFu - uint32_t(e));
+      }
+    }
+  }
+  if (!use_list) {
+    // ---- every tile: 2048-digit histogram over the key range, then the split
+    stream([&](uint32_t key, int) {
+      if (key >= kmin && key <= kmax) atomicAdd(&hist[(key - kmin) >> shift0], 1u);
+    });
+    __syncthreads();
+    pick_digit(hist, wsum, kmin, kmax, shift0, K, sh);
+    lo = sh.lo; hi = sh.hi; need = sh.need; shift1 = sh.shift;
+    __syncthreads();
+    stream([&](uint32_t key, int j) { split(key, uint32_t(b) * Vt + uint32_t(j)); });
+  }
   __syncthreads();
   const uint32_t n_cand = min(ncand_sh, uint32_t(cap));
   uint32_t theta, nwin;
