@@ -20,8 +20,10 @@
 //   logits_kernel    first pass on MFMA: per (beam, tile) largest logit, online
 //                    log-sum-exp parts per code group.
 //   tile_select_kernel  one block per request: log-sum-exp per beam, then the exact
-//                    top-K tiles by two streaming radix passes over the tile maxima and a
-//                    finish inside the boundary digit; groups the chosen tiles by code tile.
+//                    top-K tiles by radix passes over the tile maxima (or, for requests
+//                    with many tiles, over the few that reach a lower bound taken from the
+//                    code groups' maxima) and a finish inside the boundary digit; groups
+//                    the chosen tiles by code tile.
 //   refine_kernel    recomputes the chosen tiles' logits (one MFMA block per group) and
 //                    writes their 32 candidate keys each.
 //   final_kernel     exact top-K over the refined keys in LDS, ties by flat index,
@@ -195,8 +197,9 @@ constexpr int kMaxGroupTiles = 32;
 constexpr int kSelList = 8192;
 
 // Block: kLogitsWaves chunks of 32 beams x one group of cpw codes.  Each 32-code tile of
-// the codebook is staged once per block in LDS (double-buffered, one barrier per tile)
-// and read by every wave as its A operand.  Lane l keeps beam l % 32 and folds its 16
+// the codebook is staged once per block in LDS (double-buffered; one barrier per stage
+// of two tiles for d_v <= 128, of one tile above) and read by every wave as its A
+// operand.  Lane l keeps beam l % 32 and folds its 16
 // codes of every tile into the tile maximum (with its partner half) and a running
 // log-sum-exp.  Waves past the last chunk follow the barriers and store nothing.
 template <int DV, bool WBF16>
