@@ -181,10 +181,11 @@ __device__ __forceinline__ f32x16 block_mfma_f32(const float* wt, int code, int 
 
 struct LogitsK {
   int W, W_max, V, nchunk, nvg, cpw, nch_max;
+  int beam_major;        // tile maxima per request [W][n_tiles(V)] (else [n_tiles(V)][W])
   const float* z;        // [R,W_max,DV]      fp32 codebook
   const u32x4* zf;       // operand fragments bf16 codebook
   const void* woutT;     // [V,DV]
-  float* tmax;           // per request [n_tiles(V)][W]: largest logit of each tile
+  float* tmax;           // per request: largest logit of each (beam, tile)
   size_t tmax_stride;    // elements per request
   float4* lse_part;      // [R,W_max,nvg]: max, sum of exp(x - max), min tile max
 };
@@ -193,8 +194,15 @@ struct LogitsK {
 constexpr int kLogitsWaves = 8;
 // Codes per group are at most 1024 (the launcher's choice): 32 tiles.
 constexpr int kMaxGroupTiles = 32;
-// Tiles the selection keeps in LDS between its bound and the exact K-th key.
+// LDS row of the staged tile maxima: one tile for the block's 256 beams, padded so
+// that a beam-major read of 32 tiles of one beam spreads over the banks.
+constexpr int kTmRow = kLogitsWaves * 32 + 1;
+// Tiles the selection keeps in LDS between its bound and the exact K-th key, the
+// (beam, code group) pairs whose tiles it reads to find them, and the code groups per
+// beam its masks cover.
 constexpr int kSelList = 8192;
+constexpr int kSelPairs = 4096;
+constexpr int kMaxGroupsMask = 128;
 
 // Block: kLogitsWaves chunks of 32 beams x one group of cpw codes.  Each 32-code tile of
 // the codebook is staged once per block in LDS (double-buffered; one barrier per stage
@@ -222,13 +230,18 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   const int code_hi = min(a.V, code_lo + a.cpw);
 
   float mrun = -INFINITY, srun = 0.0f, nrun = INFINITY;
-  // tile maxima of the block, staged in LDS where the pair loop below runs (its folds
-  // then hold no branch) and written out, coalesced, at the end
-  constexpr bool STAGE_TM = WBF16 && DV <= 128;
-  __shared__ float tms[STAGE_TM ? kMaxGroupTiles * kLogitsWaves * 32 : 1];
+  // tile maxima of the block, staged in LDS on the bf16 paths with z in registers (the
+  // folds of the pair loop below then hold no branch) and written out, coalesced in
+  // either layout, at the end
+  constexpr bool STAGE_TM = WBF16 && DV <= 256;
+  const int vt = (a.V + 31) >> 5;
+  __shared__ float tms[STAGE_TM ? kMaxGroupTiles * kTmRow : 1];
   auto put_tm = [&](float tm, int c0) {
-    if constexpr (STAGE_TM) tms[((c0 - code_lo) >> 5) * (kLogitsWaves * 32) + wave * 32 + m] = tm;
-    else if (hf == 0 && bvalid) tm_r[size_t(c0 >> 5) * a.W + b] = tm;
+    if constexpr (STAGE_TM) {
+      tms[((c0 - code_lo) >> 5) * kTmRow + wave * 32 + m] = tm;
+    } else if (hf == 0 && bvalid) {
+      tm_r[a.beam_major ? size_t(b) * vt + (c0 >> 5) : size_t(c0 >> 5) * a.W + b] = tm;
+    }
   };
   // fold of a tile whose 32 codes all exist: the same arithmetic as fold below, as
   // straight-line code (selects in place of its branches)
@@ -415,9 +428,16 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     __syncthreads();
     const int nt = (code_hi - code_lo + 31) >> 5;
     const int b0 = (bx / a.nvg) * kLogitsWaves * 32;
-    for (int e = threadIdx.x; e < nt * kLogitsWaves * 32; e += 64 * kLogitsWaves) {
-      const int bb = b0 + e % (kLogitsWaves * 32);
-      if (bb < a.W) tm_r[size_t((code_lo >> 5) + e / (kLogitsWaves * 32)) * a.W + bb] = tms[e];
+    if (a.beam_major) {
+      // 32 lanes per beam: one contiguous row of the group's tiles
+      const int ti = threadIdx.x & 31;
+      for (int bb = threadIdx.x >> 5; bb < kLogitsWaves * 32; bb += 2 * kLogitsWaves)
+        if (ti < nt && b0 + bb < a.W) tm_r[size_t(b0 + bb) * vt + (code_lo >> 5) + ti] = tms[ti * kTmRow + bb];
+    } else {
+      for (int e = threadIdx.x; e < nt * kLogitsWaves * 32; e += 64 * kLogitsWaves) {
+        const int bb = e % (kLogitsWaves * 32), ti = e / (kLogitsWaves * 32);
+        if (b0 + bb < a.W) tm_r[size_t((code_lo >> 5) + ti) * a.W + b0 + bb] = tms[ti * kTmRow + bb];
+      }
     }
   }
   // merge the two lane halves of beam b
@@ -685,8 +705,9 @@ __device__ __forceinline__ uint64_t rank_sort_desc(uint64_t v, int n, uint64_t* 
 
 struct TileSelK {
   int W, W_max, Vt, K, K_full, G_max, nvg;
+  int tg_shift;            // log2 of the tiles in one code group of the first pass
   size_t stride;           // tile maxima / kept tiles per request (n_tiles(V_max) * W_max)
-  const float* tmax;       // per request [Vt][W]
+  const float* tmax;       // per request [Vt][W], beam-major [W][Vt] when bounded
   const float4* lse_part;  // [R,W_max,nvg]
   const float* cum;        // [R,W_max] of step t
   float* lse;              // [R,W_max] out
@@ -729,6 +750,7 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   __shared__ uint32_t kmin_sh, kmax_sh, nwin_sh, ncand_sh, theta_sh, nlist_sh;
   __shared__ uint32_t kthr_s[BOUNDED ? kMaxW : 1];         // per beam: least passing tile-max key
   __shared__ uint64_t list[BOUNDED ? kSelList : 1];        // (key, ~flat) at or above theta0
+  __shared__ uint32_t pairs[BOUNDED ? kSelPairs : 1];      // (beam << 16 | group) that can pass
   const int r = blockIdx.x, tid = threadIdx.x;
   const int W = a.W;
   const uint32_t Vt = uint32_t(a.Vt), K = uint32_t(a.K);
@@ -737,11 +759,13 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   const size_t cap = size_t(Vt) * W;
 
   // Bounded (the launcher's choice where a request's tiles outnumber the list): the
-  // tile maxima are read once, by the bounded pass below; else twice, by the passes
-  // over every tile.
+  // tile maxima are beam-major, and the bounded pass below reads only the code groups
+  // that can hold a tile above the bound; else they are tile-major and read twice, by
+  // the passes over every tile.
   constexpr bool bounded = BOUNDED;
+  auto tm_at = [&](int bb, int jj) { return bounded ? size_t(bb) * Vt + jj : size_t(jj) * W + bb; };
   // thread -> one beam b and every G-th tile from jg; its first U tiles are loaded now,
-  // under the log-sum-exp phase, and kept for the passes
+  // under the log-sum-exp phase, and kept for the passes (not in the bounded mode)
   constexpr int U = 16;
   const int G = 1024 / W;
   const bool act = tid < G * W;
@@ -750,7 +774,7 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int jj = jg + u * G;
-    x0[u] = act && jj < a.Vt ? tm[size_t(jj) * W + b] : 0.0f;
+    x0[u] = !bounded && act && jj < a.Vt ? tm[tm_at(b, jj)] : 0.0f;
   }
   // the first eight log-sum-exp parts and the cumulative score of beam tid are loaded
   // before the first barrier too (a barrier waits for every load in flight)
@@ -859,7 +883,7 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int jj = jg + u * G;
-      if (jj < a.Vt) f(f2key(cand_score(cb, x0[u], lb)), jj);
+      if (jj < a.Vt) f(f2key(cand_score(cb, bounded ? tm[tm_at(b, jj)] : x0[u], lb)), jj);
     }
     // the rest in batches of UB loads in flight (large codebooks: up to 256 per thread)
     constexpr int UB = 32;
@@ -868,7 +892,7 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int jj = j + u * G;
-        x[u] = jj < a.Vt ? tm[size_t(jj) * W + b] : 0.0f;
+        x[u] = jj < a.Vt ? tm[tm_at(b, jj)] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
@@ -893,38 +917,78 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   };
   bool use_list = false;
   if constexpr (bounded) {
-    // ---- the list: tiles whose tile-maximum key reaches their beam's threshold (and
-    // whose key then reaches theta0); the passes below read it, or every tile when it
-    // overflowed
+    // ---- the list: the (beam, group) pairs whose group maximum reaches the beam's
+    // threshold, compacted by one block scan; then their tiles, 32 lanes to a group
+    // row, whose tile-maximum key reaches the threshold and whose key reaches theta0.
+    // Too many pairs (ties): every tile is tested, in the same order.
+    uint32_t npairs;
     {
-      const uint32_t kb = act ? kthr_s[b] : 0xFFFFFFFFu;
-      if (act) {
-        auto test = [&](float x, int j) {
-          if (f2key(x) < kb) return;
-          const uint32_t key = f2key(cand_score(cb, x, lb));
-          if (key < theta0) return;
-          const uint32_t p = atomicAdd(&nlist_sh, 1u);
-          if (p < uint32_t(kSelList))
-            list[p] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - (uint32_t(b) * Vt + uint32_t(j)));
+      uint32_t gw[kMaxGroupsMask / 32] = {};
+      uint32_t cnt = 0u;
+      if (tid < W) {
+        const uint32_t kt = kthr_s[tid];
+        auto mark = [&](int u, float gx) {
+          if (f2key(gx) >= kt) { gw[u >> 5] |= 1u << (u & 31); ++cnt; }
         };
+        if (a.nvg <= 8) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int jj = jg + u * G;
-          if (jj < a.Vt) test(x0[u], jj);
+          for (int u = 0; u < 8; ++u)
+            if (u < a.nvg) mark(u, q[u].x);
+        } else if (a.nvg <= kMaxGroupsMask) {
+          for (int u = 0; u < a.nvg; ++u) mark(u, lp[u].x);
+        } else {
+          cnt = uint32_t(kSelPairs) + 1u;                 // no mask: every tile
         }
-        constexpr int UB = 32;
-        for (int j = jg + U * G; j < a.Vt; j += UB * G) {
-          float x[UB];
+      }
+      uint32_t off = block_excl_scan(cnt, wsum, npairs);
+      if (npairs <= uint32_t(kSelPairs) && tid < W) {
+        for (int u = 0; u < a.nvg; ++u)
+          if ((gw[u >> 5] >> (u & 31)) & 1u) pairs[off++] = (uint32_t(tid) << 16) | uint32_t(u);
+      }
+      __syncthreads();
+    }
+    auto test = [&](float x, int bb, int jj) {
+      if (f2key(x) < kthr_s[bb]) return;
+      const uint32_t key = f2key(cand_score(cum_s[bb], x, lse_s[bb]));
+      if (key < theta0) return;
+      const uint32_t p = atomicAdd(&nlist_sh, 1u);
+      if (p < uint32_t(kSelList))
+        list[p] = (uint64_t(key) << 32) | uint64_t(0xFFFFFFFFu - (uint32_t(bb) * Vt + uint32_t(jj)));
+    };
+    if (npairs <= uint32_t(kSelPairs)) {
+      const int ts = a.tg_shift, tpg = 1 << ts;
+      const int nitem = int(npairs) << ts;
+      constexpr int UB = 16;
+      for (int i0 = 0; i0 < nitem; i0 += UB * 1024) {
+        float x[UB];
+        int ib[UB], ij[UB];
 #pragma unroll
-          for (int u = 0; u < UB; ++u) {
-            const int jj = j + u * G;
-            x[u] = jj < a.Vt ? tm[size_t(jj) * W + b] : 0.0f;
-          }
+        for (int u = 0; u < UB; ++u) {
+          const int it = i0 + u * 1024 + tid;
+          const uint32_t pr = pairs[it < nitem ? it >> ts : 0];
+          ib[u] = int(pr >> 16);
+          ij[u] = (int(pr & 0xFFFFu) << ts) + (it & (tpg - 1));
+          const bool live = it < nitem && ij[u] < a.Vt;
+          x[u] = tm[live ? tm_at(ib[u], ij[u]) : 0];
+          ib[u] = live ? ib[u] : -1;
+        }
 #pragma unroll
-          for (int u = 0; u < UB; ++u) {
-            const int jj = j + u * G;
-            if (jj < a.Vt) test(x[u], jj);
-          }
+        for (int u = 0; u < UB; ++u)
+          if (ib[u] >= 0) test(x[u], ib[u], ij[u]);
+      }
+    } else if (act) {
+      // every tile of this thread's beam
+      for (int j0 = jg; j0 < a.Vt; j0 += 32 * G) {
+        float x[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          const int jj = j0 + u * G;
+          x[u] = jj < a.Vt ? tm[tm_at(b, jj)] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          const int jj = j0 + u * G;
+          if (jj < a.Vt) test(x[u], b, jj);
         }
       }
     }
@@ -975,7 +1039,7 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
     auto key_at = [&](uint32_t i) {
       const uint32_t f = cand[i];
       const uint32_t bb = f / Vt;
-      return f2key(cand_score(cum_s[bb], tm[size_t(f % Vt) * W + bb], lse_s[bb]));
+      return f2key(cand_score(cum_s[bb], tm[tm_at(int(bb), int(f % Vt))], lse_s[bb]));
     };
     auto flat_at = [&](uint32_t i) { return cand[i]; };
     theta = radix_finish(key_at, n_cand, lo, hi, need, shift1, hist, wsum, sh);
@@ -1453,15 +1517,18 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   int cpw = 128;
   while (cpw < 1024 && cpw < a.V && int64_t(a.R) * nch * ((a.V + 2 * cpw - 1) / (2 * cpw)) >= 16384) cpw *= 2;
   const int nvg = (a.V + cpw - 1) / cpw;
-  LogitsK lk{a.W, a.W_max, a.V, nch, nvg, cpw, nch_max, z, zf, woutT, tmax, tstride, lse_part};
+  // the bounded tile selection where a request's tiles outnumber its list (and the code
+  // groups' maxima number at least K); it reads the tile maxima beam-major
+  const bool bounded = int64_t(a.W) * Vt > kSelList && int64_t(a.W) * nvg >= Kt;
+  LogitsK lk{a.W, a.W_max, a.V, nch, nvg, cpw, nch_max, bounded ? 1 : 0, z, zf, woutT, tmax, tstride,
+             lse_part};
   RefineK rk{a.W, a.W_max, a.V, Vt, G_max, nch_max, z, zf, woutT, lse, cum, sel, groups, gtiles, rkeys};
   if ((err = launch_by_dv(a, lk, rk, 0, s, false))) return err;
   {
-    TileSelK k{a.W, a.W_max, Vt, Kt, a.W_next, G_max, nvg, tstride, tmax, lse_part, cum, lse, sel,
-               cand, tiles, groups, gtiles, status};
-    // the bounded pass where a request's tiles outnumber the list (and the code groups'
-    // maxima number at least K)
-    const bool bounded = int64_t(a.W) * Vt > kSelList && int64_t(a.W) * nvg >= Kt;
+    int tg_shift = 0;
+    while ((kTile << (tg_shift + 1)) <= cpw) ++tg_shift;    // cpw / 32 tiles, a power of two
+    TileSelK k{a.W, a.W_max, Vt, Kt, a.W_next, G_max, nvg, tg_shift, tstride, tmax, lse_part, cum, lse,
+               sel, cand, tiles, groups, gtiles, status};
     if (bounded) hipLaunchKernelGGL(tile_select_kernel<true>, dim3(a.R), dim3(1024), 0, s, k);
     else hipLaunchKernelGGL(tile_select_kernel<false>, dim3(a.R), dim3(1024), 0, s, k);
     if ((err = last_launch_error())) return err;
