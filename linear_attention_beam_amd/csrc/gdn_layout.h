@@ -40,7 +40,8 @@ struct Layout {
   size_t z;           // [R,W_max,d_v] f32  head-summed outputs (fp32 codebook)
   size_t zf;          // [R,n_chunks(W_max),d_v/16,3,64] u32x4: z as bf16 hi/mid/lo MFMA operand
   size_t woutT;       // [V_max,d_v] wout dtype, codebook transposed
-  size_t tmax;        // [R, n_tiles(V_max)*W_max] f32, per request [n_tiles(V)][W_t]
+  size_t tmax;        // [R, n_tiles(V_max)*W_max] f32, per request [n_tiles(V)][W_t] ([W_t][n_tiles(V)]
+                      // where the selection is bounded)
   size_t lse_part;    // [R,W_max,n_vgroups(V_max)] float4 (max, sum of exp, min tile max, 0)
   size_t lse;         // [R,W_max] f32
   size_t sel;         // [R] SelState
