@@ -918,9 +918,10 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   bool use_list = false;
   if constexpr (bounded) {
     // ---- the list: the (beam, group) pairs whose group maximum reaches the beam's
-    // threshold, compacted by one block scan; then their tiles, 32 lanes to a group
-    // row, whose tile-maximum key reaches the threshold and whose key reaches theta0.
-    // Too many pairs (ties): every tile is tested, in the same order.
+    // threshold, compacted by one block scan; then the tiles of those group rows
+    // (consecutive lanes on consecutive tiles of a row) whose tile-maximum key
+    // reaches the threshold and whose key reaches theta0.  Too many pairs (ties):
+    // every tile of every beam is tested.
     uint32_t npairs;
     {
       uint32_t gw[kMaxGroupsMask / 32] = {};
