@@ -38,6 +38,8 @@ DERIVED = {
     # 512 x 32 tiles, more than the tile selection's list holds: the bounded pass (and,
     # with every score tied, its overflow back to the passes over every tile)
     "tiny_bounded": ("tiny", dict(widths=(512, 512, 512), V=1024)),
+    # the same with a partial last tile and a partial last code group
+    "tiny_bounded_v1000": ("tiny", dict(widths=(512, 512, 512), V=1000)),
     # six SID steps (five ancestor records at the last step)
     "tiny_t6": ("tiny", dict(T=6, widths=(8,) * 6)),
     "single_bf16_t6": ("single", dict(T=6, widths=(128,) * 6, io="bf16", wout="bf16")),
@@ -135,6 +137,7 @@ def test_forced_parents_parity(name, R):
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_v37", 1),
                                     ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("single_v300", 1),
                                     ("single_bf16_t6", 1), ("tiny_w1024_t6", 1), ("tiny_bounded", 2),
+                                    ("tiny_bounded_v1000", 1),
                                     ("single_gqa", 1), ("single_dk256", 1), ("single_dv512", 1),
                                     ("single_dk256_dv512", 1)])
 def test_select_mode_parity(name, R):
@@ -258,7 +261,7 @@ def test_full_size_select_properties(name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "single", "ties_w512", "ties_w512_v96", "ties_bf16_w512",
-                                  "tiny_bounded"])
+                                  "tiny_bounded", "tiny_bounded_v1000"])
 def test_all_scores_tied(name):
     """Wout = 0: every candidate of a request scores cum - log V; the top-W is then the
     W smallest flat indices, in order (the tie-break), at every step."""
