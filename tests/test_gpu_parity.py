@@ -40,6 +40,9 @@ DERIVED = {
     "tiny_bounded": ("tiny", dict(widths=(512, 512, 512), V=1024)),
     # the same with a partial last tile and a partial last code group
     "tiny_bounded_v1000": ("tiny", dict(widths=(512, 512, 512), V=1000)),
+    # d_v = 512 with a bf16 codebook (tile maxima written beam-major without staging)
+    "single_dv512_bounded": ("single", dict(d_v=512, io="bf16", wout="bf16", widths=(512, 512, 512),
+                                            V=1024)),
     # six SID steps (five ancestor records at the last step)
     "tiny_t6": ("tiny", dict(T=6, widths=(8,) * 6)),
     "single_bf16_t6": ("single", dict(T=6, widths=(128,) * 6, io="bf16", wout="bf16")),
@@ -236,11 +239,11 @@ def test_full_size_select_teacher_forced(name):
         np.testing.assert_array_equal(anc[0][:K, :t + 1], dec.anc)
 
 
-@pytest.mark.parametrize("name", ["stress", "growing"])
+@pytest.mark.parametrize("name", ["stress", "growing", "single_dv512_bounded"])
 def test_full_size_select_properties(name):
     """Full-size select mode: exact selection on sampled requests (float64 rescoring of
     the GPU's own outputs) and eq. (9) ancestry for every request."""
-    wl = synth.get(name)
+    wl = _wl(name)
     R = wl.R
     g = GpuDecode(wl, exact=())
     anc_ref = [np.zeros((wl.width(0), 0), np.int32) for _ in range(R)]
