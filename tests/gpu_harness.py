@@ -143,3 +143,26 @@ def check_selection(o_r, cum_r, Wout64, K, sel_r, where=""):
     ok = (sc[:-1] > sc[1:]) | ((sc[:-1] == sc[1:]) & (gflat[:-1] < gflat[1:]))
     assert np.all(ok), f"{where}: order is not score-descending / flat-ascending"
     return len(diff)
+
+
+def decode_record(name="batch", R=4):
+    """One select-mode decode of workload `name` on its first R requests: every step's
+    o_t and selection, then the ancestry, SID prefixes, cumulative scores and record
+    pool.  Inputs are seeded, so another process records the same decode."""
+    import synth
+    wl = synth.get(name)
+    g = GpuDecode(wl, R=R, exact=())
+    g.init()
+    rec = []
+    for t in range(wl.T):
+        rec.append(to_np(g.step(t)).copy())
+        sel = g.select(t)
+        rec += [sel["parent"].copy(), sel["token"].copy(), sel["score"].copy()]
+    for what in (B.GDN_EXPORT_ANCESTRY, B.GDN_EXPORT_TOKENS, B.GDN_EXPORT_CUM,
+                 B.GDN_EXPORT_GTR_DELTA, B.GDN_EXPORT_GTR_KEY):
+        rec.append(g.export(what).copy())
+    return rec
+
+
+def same_bits(a, b):
+    return np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))

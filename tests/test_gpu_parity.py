@@ -6,6 +6,10 @@ and slot contents bit-exact whenever parent maps are fixed; selected sets equal
 except for candidates within 1e-6 (relative to max(1, |threshold|)) of the
 threshold score.
 """
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -14,7 +18,7 @@ import oracle
 import synth
 from synth import gen
 from linear_attention_beam_amd import binding as B
-from gpu_harness import GpuDecode, TOL, check_selection, rel_err, say, to_np
+from gpu_harness import GpuDecode, TOL, check_selection, decode_record, rel_err, same_bits, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -400,22 +404,37 @@ def test_decode_is_deterministic():
     """Two decodes of the same inputs give bit-identical outputs, selections, ancestry
     and records (every reduction runs in a fixed order; only the processing order of
     equal-parent beams may differ, and it never changes a value)."""
-    wl = synth.get("batch")
-    g = GpuDecode(wl, R=4, exact=())
-    runs = []
-    for _ in range(2):
-        g.init()
-        rec = []
-        for t in range(wl.T):
-            rec.append(to_np(g.step(t)).copy())
-            sel = g.select(t)
-            rec += [sel["parent"].copy(), sel["token"].copy(), sel["score"].copy()]
-        for what in (B.GDN_EXPORT_ANCESTRY, B.GDN_EXPORT_TOKENS, B.GDN_EXPORT_CUM,
-                     B.GDN_EXPORT_GTR_DELTA, B.GDN_EXPORT_GTR_KEY):
-            rec.append(g.export(what).copy())
-        runs.append(rec)
-    for a, b in zip(*runs):
-        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+    a, b = decode_record(), decode_record()
+    assert len(a) == len(b)
+    for x, y in zip(a, b):
+        assert same_bits(x, y)
+
+
+_SERIAL_CHILD = """
+import sys
+import numpy as np
+sys.path[:0] = [{root!r}, {tests!r}]
+from gpu_harness import decode_record
+np.savez({out!r}, *decode_record())
+"""
+
+
+def test_serialized_launches_match(tmp_path):
+    """The same decode in a child process whose kernel launches the runtime serialises
+    and waits for one by one (AMD_SERIALIZE_KERNEL=3) gives the same bits: no result
+    depends on how launches overlap."""
+    ref = decode_record()
+    out = str(tmp_path / "serial.npz")
+    tests = os.path.dirname(os.path.abspath(__file__))
+    code = _SERIAL_CHILD.format(root=os.path.dirname(tests), tests=tests, out=out)
+    say("child process: the same decode with AMD_SERIALIZE_KERNEL=3")
+    r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, AMD_SERIALIZE_KERNEL="3"),
+                       capture_output=True, text=True, timeout=100)
+    assert r.returncode == 0, r.stderr[-3000:]
+    got = np.load(out)
+    assert len(got.files) == len(ref)
+    for i, x in enumerate(ref):
+        assert same_bits(x, got[f"arr_{i}"]), f"record {i} differs"
 
 
 def test_nan_scores_terminate():
