@@ -30,6 +30,8 @@ DERIVED = {
     "tiny_v37": ("tiny", dict(V=37)),
     "tiny_odd_w": ("tiny", dict(widths=(5, 13, 7), V=37)),
     "tiny_few_tiles": ("tiny", dict(widths=(4, 8, 16), V=32)),
+    # shrinking beam widths: each selection keeps fewer beams than the step had
+    "tiny_shrink": ("tiny", dict(widths=(96, 40, 9), V=37)),
     "single_v300": ("single", dict(V=300)),
     "ties_w512": ("tiny", dict(widths=(512, 512, 512), V=64)),
     # 1536 tied tiles: more than one sort of the kept tiles holds (radix finish instead)
@@ -142,7 +144,7 @@ def test_forced_parents_parity(name, R):
 
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_v37", 1),
-                                    ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("single_v300", 1),
+                                    ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("tiny_shrink", 2), ("single_v300", 1),
                                     ("single_bf16_t6", 1), ("tiny_w1024_t6", 1), ("tiny_bounded", 2),
                                     ("tiny_bounded_v1000", 1),
                                     ("single_gqa", 1), ("single_dk256", 1), ("single_dv512", 1),
