@@ -101,6 +101,39 @@ def step_flops(wl, t):
     return wl.R * wl.H * W * (4 * wl.d_v * wl.d_k + t * (4 * wl.d_k + 4 * wl.d_v) + 8 * wl.d_v)
 
 
+MFMA_BF16_PEAK = 2.5e15                  # dense bf16 MFMA, flop/s
+MFMA_F32_PEAK = 157.3e12                 # dense fp32 MFMA, flop/s
+
+
+def decode_floor_s(wl, bytes_t):
+    """Lower bound on one decode: each launch at max(algorithmic bytes / 8 TB/s, its
+    MFMA flops / the dense peak of their dtype), summed over init, the T step launches
+    and the T selections.
+
+    init: S_ctx read and its fragments written (4 d_v d_k + 4 max(d_v, 32) d_k per
+    (request, head)).  step: bytes_t (the step kernel is HBM-bound: its intensity is far
+    below the MFMA ridge).  select(t): o_t read (4 H W_t d_v per request), cumulative
+    scores, the codebook (once), the top-W outputs (12 W_next) and the new ancestry and
+    SID prefixes (8 (t + 1) W_next); flops: the logits W_t x d_v x V, 2 per element,
+    three times with z split into three bf16 terms for a bf16 codebook (fp32 MFMA
+    otherwise), which the selection needs to stay exact at fp32 precision.
+    """
+    bw = HBM_PEAK_GBS * 1e9
+    ew = 2 if wl.wout == "bf16" else 4
+    dvp = max(wl.d_v, 32)
+    total = wl.R * wl.H * (4 * wl.d_v * wl.d_k + 4 * dvp * wl.d_k) / bw
+    for t in range(wl.T):
+        W, Wn = wl.width(t), wl.width(t + 1)
+        total += bytes_t[t] / bw
+        sel_bytes = wl.R * (4 * wl.H * W * wl.d_v + 4 * W + 12 * Wn + 8 * (t + 1) * Wn) + wl.d_v * wl.V * ew
+        if wl.wout == "bf16":
+            sel_flops, peak = 3 * 2 * wl.R * W * wl.d_v * wl.V, MFMA_BF16_PEAK
+        else:
+            sel_flops, peak = 2 * wl.R * W * wl.d_v * wl.V, MFMA_F32_PEAK
+        total += max(sel_bytes / bw, sel_flops / peak)
+    return total
+
+
 def copy_bandwidth(torch, dev, mib=1024, reps=10):
     """Read+write GB/s of a plain device-to-device copy: the bandwidth a kernel with
     mixed reads and writes can reach on this GPU (context for the 8 TB/s peak)."""
@@ -364,6 +397,11 @@ def main():
         "gdn_step_ms": float(step_ms.sum()),
         "select_ms": float(sel_ms.sum()),
         "step_tflops": flops / (step_ms.sum() * 1e-3) / 1e12,
+        "decode_roofline": (None if states is not None else
+                            {"floor_ms": decode_floor_s(wl, bytes_t) * 1e3,
+                             "frac": decode_floor_s(wl, bytes_t) / (elapsed / args.steps),
+                             "basis": "sum over init, step and select launches of max(algorithmic "
+                                      "bytes / 8 TB/s, MFMA flops / dense peak)"}),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, wl)

@@ -96,3 +96,30 @@ def test_cpu_baseline_on_tiny():
     assert res["kind"] == "oracle" and res["unit"] == "beam-transitions/s"
     assert res["value"] > 0 and res["cores"] >= 1
     assert "1 of 1 requests" in res["sample"]
+
+
+@pytest.mark.parametrize("name", ["batch", "tiny"])
+def test_decode_floor_term_by_term(name):
+    """The full-decode floor: init, every step launch and every selection, each at the
+    larger of its bytes over 8 TB/s and its MFMA flops over the dense peak."""
+    b = _bench()
+    wl = synth.get(name)
+    bytes_t = [b.step_bytes(wl, t, np.zeros(wl.R, np.int64)) for t in range(wl.T)]
+    bw = 8000e9
+    ew = 2 if wl.wout == "bf16" else 4
+    init = wl.R * wl.H * (4 * wl.d_v * wl.d_k + 4 * max(wl.d_v, 32) * wl.d_k) / bw
+    steps = sum(bytes_t) / bw
+    sel = 0.0
+    for t in range(wl.T):
+        W, Wn = wl.width(t), wl.width(t + 1)
+        moved = (wl.R * wl.H * W * wl.d_v * 4           # o_t
+                 + wl.R * W * 4                          # cumulative scores
+                 + wl.d_v * wl.V * ew                    # codebook
+                 + wl.R * Wn * (4 + 4 + 4)               # parent, token, score
+                 + wl.R * Wn * (t + 1) * (4 + 4))        # ancestry, SID prefixes
+        flops = 2 * wl.R * W * wl.d_v * wl.V
+        peak = 2.5e15 if wl.wout == "bf16" else 157.3e12
+        if wl.wout == "bf16":
+            flops *= 3
+        sel += max(moved / bw, flops / peak)
+    assert b.decode_floor_s(wl, bytes_t) == pytest.approx(init + steps + sel, rel=1e-12)
