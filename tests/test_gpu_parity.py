@@ -46,6 +46,11 @@ DERIVED = {
     "tiny_bounded": ("tiny", dict(widths=(512, 512, 512), V=1024)),
     # the same with a partial last tile and a partial last code group
     "tiny_bounded_v1000": ("tiny", dict(widths=(512, 512, 512), V=1000)),
+    # irregular shapes whose steps switch between the bounded and the every-tile
+    # selection (W x ceil(V/32) above or below 8192), fp32 and bf16
+    "mixed_a": ("tiny", dict(widths=(300, 600, 257), V=911)),
+    "mixed_b": ("single", dict(widths=(200, 150, 100), V=1500)),
+    "mixed_c": ("single", dict(widths=(64, 700, 700), V=777, io="bf16", wout="bf16")),
     # d_v = 512 with a bf16 codebook (tile maxima written beam-major without staging)
     "single_dv512_bounded": ("single", dict(d_v=512, io="bf16", wout="bf16", widths=(512, 512, 512),
                                             V=1024)),
@@ -146,7 +151,7 @@ def test_forced_parents_parity(name, R):
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_v37", 1),
                                     ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("tiny_shrink", 2), ("single_v300", 1),
                                     ("single_bf16_t6", 1), ("tiny_w1024_t6", 1), ("tiny_bounded", 2),
-                                    ("tiny_bounded_v1000", 1),
+                                    ("tiny_bounded_v1000", 1), ("mixed_a", 1), ("mixed_b", 1), ("mixed_c", 1),
                                     ("single_gqa", 1), ("single_dk256", 1), ("single_dv512", 1),
                                     ("single_dk256_dv512", 1)])
 def test_select_mode_parity(name, R):
