@@ -80,7 +80,9 @@ __device__ void transpose_codebook(const WT* __restrict__ w, WT* __restrict__ wt
 // Blocks [0, zblocks): one thread per 8 consecutive elements of one beam of one
 // request (beams padded to a multiple of 32 with zeros); all heads' loads are in
 // flight at once (up to 16), the sum runs in head order.  Later blocks: codebook
-// transpose.
+// transpose.  STREAM: o is far larger than the last-level cache, and its loads are
+// non-temporal (streamed past that cache rather than evicting the step's records).
+template <bool STREAM>
 __global__ void __launch_bounds__(256) zsum_kernel(ZsumK a) {
   if (int(blockIdx.x) >= a.zblocks) {
     const int t0 = blockIdx.x - a.zblocks, nb = gridDim.x - a.zblocks;
@@ -105,8 +107,13 @@ __global__ void __launch_bounds__(256) zsum_kernel(ZsumK a) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const float* p = p0 + size_t(h0 + u < a.H ? h0 + u : h0) * hstride;
-          x0[u] = *reinterpret_cast<const f32x4*>(p);
-          x1[u] = *reinterpret_cast<const f32x4*>(p + 4);
+          if constexpr (STREAM) {
+            x0[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+            x1[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+          } else {
+            x0[u] = *reinterpret_cast<const f32x4*>(p);
+            x1[u] = *reinterpret_cast<const f32x4*>(p + 4);
+          }
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u)
@@ -1510,7 +1517,11 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
     zb = zb < 1 ? 1 : (zb > 8192 ? 8192 : zb);
     const int tb = ntr < 256 ? ntr : 256;
     ZsumK k{a.R, a.H, a.W, a.W_max, a.d_v, a.V, nch_max, int(zb), split, a.o, z, zf, a.Wout, woutT};
-    hipLaunchKernelGGL(zsum_kernel, dim3(unsigned(zb + tb)), dim3(256), 0, s, k);
+    // o above half of the 256 MiB last-level cache: streamed (512 MiB of o: 144 -> 120
+    // us per launch; 64 MiB of o is still in that cache, and plain loads hit it)
+    const bool stream = size_t(a.R) * a.H * a.W * a.d_v * 4 > (size_t(128) << 20);
+    if (stream) hipLaunchKernelGGL(zsum_kernel<true>, dim3(unsigned(zb + tb)), dim3(256), 0, s, k);
+    else hipLaunchKernelGGL(zsum_kernel<false>, dim3(unsigned(zb + tb)), dim3(256), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
   // codes per wave: 128 .. 1024, larger while the grid keeps >= 16384 waves, so that
