@@ -6,12 +6,12 @@ every SID step t: gdn_beam_step (fused projection + replay + update + record
 append) and gdn_beam_select (scoring, exact global top-W, ancestry remap).
 value = beam transitions (sum over steps of R*H*W_t) per second of wall time.
 
-The timed decodes run back to back with nothing else on the stream.  A separate
-instrumented pass of the same decodes times each kernel launch with HIP events on
-its stream (each step(t) issued several times between one pair of events); the
-step kernel's achieved algorithmic bandwidth is reported against the 8 TB/s HBM
-peak.  The CPU oracle (float64 FullState) is timed on a bounded sample of the
-same workload.
+The timed decodes run back to back with nothing else on the stream.  A second run
+of the same decodes has every step launch record its own start and end (HIP events
+stamped by the dispatch, gdn_beam_time_steps); the step kernel's achieved
+algorithmic bandwidth over those launches is reported against the 8 TB/s HBM peak.
+A third pass times the select calls between HIP events.  The CPU oracle (float64 FullState) is timed on a
+bounded sample of the same workload.
 
     python bench.py [--workload batch|stress|growing|single|tiny] [--steps K] [--warmup W]
 """
@@ -305,10 +305,11 @@ def main():
         decode()
     torch.cuda.synchronize()
 
-    # ---- per-launch kernel times: an instrumented pass of the same decodes, HIP events
-    # recorded on the launch stream.  Each step(t) is issued rep times back to back
-    # between one pair of events (re-issuing step(t) rewrites the same values), so the
-    # events' own cost is spread over rep launches; select(t) runs once between its pair.
+    # ---- per-call times: an instrumented pass of the same decodes, HIP events recorded
+    # on the launch stream.  Each step(t) is issued rep times back to back between one
+    # pair of events (re-issuing step(t) rewrites the same values); select(t) runs once
+    # between its pair.  The select and init times come from here; the step times
+    # reported come from the timed decodes, except with a flush buffer.
     # With a flush buffer, 1 GiB of it is read or written before every step launch
     # (outside the events), so the launch finds none of its inputs in any cache.
     def instrumented(n, rep, flush_buf=None):
@@ -346,13 +347,27 @@ def main():
     trans = wl.transitions()
     if not args.flush_mall:
         # ---- timed region: K whole decodes back to back on the stream, nothing else on
-        # it (a timing event between kernels costs the stream a few microseconds)
+        # it (a timing event between kernels costs the stream a few microseconds, and the
+        # idle gap changes what the next launch finds in the caches)
+        # it)
         t0 = time.perf_counter()
         for i in range(args.steps):
             decode()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        step_ms, sel_ms, _ = instrumented(max(3, min(args.steps, 10)), 4)
+        # ---- step kernel times: the same decodes back to back again, every step launch
+        # stamping its own start and end (the stamps cost the stream a few microseconds
+        # per launch, so this pass is not the one `value` comes from)
+        n_flow = max(3, min(args.steps, 10))
+        dec.time_steps(n_flow * wl.T)
+        for i in range(n_flow):
+            decode()
+        times, n_timed = dec.step_times(n_flow * wl.T)
+        dec.time_steps(0)
+        assert n_timed == n_flow * wl.T, n_timed
+        step_ms = np.asarray(times, dtype=np.float64).reshape(n_flow, wl.T).mean(0)
+        alone_ms, sel_ms, _ = instrumented(n_flow, 1)
+        log(args, f"step kernel ms per SID step alone between events: {np.round(alone_ms, 4).tolist()}")
     else:
         # ---- cold caches: K decodes whose every step launch follows a 1 GiB read or
         # write; the decode time is the sum of its event-timed init, step and select
@@ -373,7 +388,8 @@ def main():
         flops = sum(step_flops(wl, t) for t in range(wl.T))
     else:   # P k and P q, alpha P + delta k^T per state element
         flops = sum(wl.R * wl.H * wl.width(t) * 6 * wl.d_v * wl.d_k for t in range(wl.T))
-    log(args, f"step kernel ms per SID step: {np.round(step_ms, 4).tolist()}  select ms: "
+    where = "each after a 1 GiB flush, between HIP events" if args.flush_mall else "in back-to-back decodes"
+    log(args, f"step kernel ms per SID step ({where}): {np.round(step_ms, 4).tolist()}  select ms: "
               f"{np.round(sel_ms, 4).tolist()}")
     log(args, f"algorithmic bytes per step launch: {bytes_t}; distinct ancestors per request "
               f"(mean) {[float(d.mean()) for d in distinct]}")
@@ -395,6 +411,7 @@ def main():
                      "launches_per_decode": wl.T},
         "gdn_step_rate": gdn_rate,
         "gdn_step_ms": float(step_ms.sum()),
+        "step_ms_per_t": [float(x) for x in step_ms],
         "select_ms": float(sel_ms.sum()),
         "step_tflops": flops / (step_ms.sum() * 1e-3) / 1e12,
         "decode_roofline": (None if states is not None else

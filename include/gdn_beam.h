@@ -168,6 +168,22 @@ gdn_status gdn_beam_query(const gdn_beam_ctx* ctx, int32_t* t_next, int32_t* W_c
 /* Free a context (host memory only; the workspace stays the caller's). NULL is a no-op. */
 void gdn_beam_destroy(gdn_beam_ctx* ctx);
 
+/* Measurement, not an operation of the method: kernel time of the step launches as
+ * they run in a stream of decodes.  gdn_beam_time_steps(capacity) creates 2 * capacity
+ * HIP events on the current device (host call, no device memory) and makes each of
+ * the next `capacity` gdn_beam_step / gdn_fullstate_step launches of the process, on
+ * that device and whatever their context, record its own start and end on a pair of
+ * them: the dispatch stamps them itself, so nothing is added to the stream between
+ * launches.  capacity = 0 releases the events; calling it again restarts the count.
+ * Errors: capacity outside 0..65536 (INVALID_ARG), event creation failing (HIP). */
+gdn_status gdn_beam_time_steps(int32_t capacity);
+
+/* Waits for the timed launches recorded since the last call and writes the first
+ * min(recorded, cap) durations in milliseconds, in launch order, to ms (host); *n
+ * (host) receives the number recorded.  The count then starts over (the events are
+ * reused for the next launches). */
+gdn_status gdn_beam_step_times(float* ms /* host */, int32_t cap, int32_t* n /* host */);
+
 /* Static description of a status code. */
 const char* gdn_beam_status_str(gdn_status s);
 

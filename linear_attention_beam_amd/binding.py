@@ -25,7 +25,7 @@ GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_beam_workspace_bytes", "gdn_beam_init", "gdn_beam_step", "gdn_beam_select",
            "gdn_beam_export", "gdn_beam_export_bytes", "gdn_beam_query", "gdn_beam_destroy",
            "gdn_beam_status_str", "gdn_beam_last_error", "gdn_beam_prefill",
-           "gdn_fullstate_bytes", "gdn_fullstate_step")
+           "gdn_fullstate_bytes", "gdn_fullstate_step", "gdn_beam_time_steps", "gdn_beam_step_times")
 
 
 class gdn_beam_config(ctypes.Structure):
@@ -76,6 +76,8 @@ def _load():
         "gdn_beam_export_bytes": (st, [vp, i32, POINTER(c_size_t)]),
         "gdn_beam_query": (st, [vp, POINTER(i32), POINTER(i32)]),
         "gdn_beam_destroy": (None, [vp]),
+        "gdn_beam_time_steps": (st, [i32]),
+        "gdn_beam_step_times": (st, [POINTER(ctypes.c_float), i32, POINTER(i32)]),
         "gdn_beam_status_str": (c_char_p, [st]),
         "gdn_beam_last_error": (c_char_p, []),
         "gdn_beam_prefill": (st, [i32, i32, i32, i32, i32, c_int64, vp, vp, vp, vp, vp, vp, vp]),
@@ -161,6 +163,19 @@ def gdn_beam_query(ctx):
 
 def gdn_beam_destroy(ctx):
     _lib.gdn_beam_destroy(ctx)
+
+
+def gdn_beam_time_steps(capacity):
+    _check(_lib.gdn_beam_time_steps(capacity), "gdn_beam_time_steps")
+
+
+def gdn_beam_step_times(cap):
+    """Durations (ms) of the step launches timed since the last call, in launch order,
+    and the number recorded."""
+    buf = (ctypes.c_float * max(cap, 1))()
+    n = c_int32(0)
+    _check(_lib.gdn_beam_step_times(buf, cap, byref(n)), "gdn_beam_step_times")
+    return [buf[i] for i in range(min(n.value, cap))], n.value
 
 
 def gdn_beam_status_str(status: int) -> str:

@@ -4,8 +4,10 @@
 // runs before any launch, so a rejected call leaves the context unchanged.
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "gdn_layout.h"
 
@@ -26,6 +28,23 @@ struct gdn_beam_ctx {
 namespace {
 
 thread_local std::string g_last_error;
+
+// Step-launch timing, process-wide (a decode makes a new context per init): the next
+// `cap` step launches stamp their start and end on event pairs 2i, 2i + 1.
+struct StepTimer {
+  std::mutex m;
+  int cap = 0, n = 0;
+  std::vector<hipEvent_t> ev;
+  // the pair for a launch about to be issued, or none past the capacity
+  bool take(hipEvent_t& e0, hipEvent_t& e1) {
+    std::lock_guard<std::mutex> g(m);
+    if (n >= cap) return false;
+    e0 = ev[2 * n];
+    e1 = ev[2 * n + 1];
+    ++n;
+    return true;
+  }
+} g_timer;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -134,7 +153,8 @@ gdn_status gdn_beam_step(gdn_beam_ctx* ctx, int32_t t, const void* q, const void
   if (t >= c.T_max) return GDN_ERR_CAPACITY;
   if (t != ctx->t || ctx->mode == 2) return GDN_ERR_BAD_STATE;
   StepArgs a{c.R, c.H, key_heads(c), c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype,
-             q, k, v, alpha, beta, o, ctx->ws, ctx->L};
+             q, k, v, alpha, beta, o, ctx->ws, ctx->L, nullptr, nullptr};
+  g_timer.take(a.ev0, a.ev1);
   int err = launch_step(a, stream);
   if (err) return hip_fail(err, "gdn_beam_step");
   ctx->stepped = 1;
@@ -169,7 +189,9 @@ gdn_status gdn_fullstate_step(gdn_beam_ctx* ctx, int32_t t, const float* S_ctx, 
   if (t > 0 && states != ctx->states) return GDN_ERR_BAD_STATE;   // parents live in it
   FullStepArgs a{c.R, c.H, key_heads(c), c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype, S_ctx,
                  q, k, v, alpha, beta, o, states, half,
-                 reinterpret_cast<const int32_t*>(static_cast<char*>(ctx->ws) + ctx->L.anc[t & 1])};
+                 reinterpret_cast<const int32_t*>(static_cast<char*>(ctx->ws) + ctx->L.anc[t & 1]),
+                 nullptr, nullptr};
+  g_timer.take(a.ev0, a.ev1);
   int err = launch_fullstate(a, stream);
   if (err) return hip_fail(err, "gdn_fullstate_step");
   ctx->stepped = 1;
@@ -255,6 +277,39 @@ gdn_status gdn_beam_query(const gdn_beam_ctx* ctx, int32_t* t_next, int32_t* W_c
 }
 
 void gdn_beam_destroy(gdn_beam_ctx* ctx) { delete ctx; }
+
+gdn_status gdn_beam_time_steps(int32_t capacity) {
+  if (capacity < 0 || capacity > 65536) return GDN_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_timer.m);
+  for (hipEvent_t e : g_timer.ev) (void)hipEventDestroy(e);
+  g_timer.ev.clear();
+  g_timer.cap = g_timer.n = 0;
+  std::vector<hipEvent_t> ev(2 * size_t(capacity), nullptr);
+  for (size_t i = 0; i < ev.size(); ++i) {
+    const hipError_t e = hipEventCreate(&ev[i]);
+    if (e != hipSuccess) {
+      for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+      return hip_fail(int(e), "gdn_beam_time_steps");
+    }
+  }
+  g_timer.ev.swap(ev);
+  g_timer.cap = capacity;
+  return GDN_OK;
+}
+
+gdn_status gdn_beam_step_times(float* ms, int32_t cap, int32_t* n) {
+  if (!n || cap < 0 || (cap > 0 && !ms)) return GDN_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_timer.m);
+  const int m = g_timer.n < cap ? g_timer.n : cap;
+  for (int i = 0; i < m; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer.ev[2 * i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], g_timer.ev[2 * i], g_timer.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(int(e), "gdn_beam_step_times");
+  }
+  *n = g_timer.n;
+  g_timer.n = 0;
+  return GDN_OK;
+}
 
 gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t H_K, int32_t d_k, int32_t d_v, int64_t N,
                             const float* k, const float* v, const float* alpha,

@@ -6,6 +6,8 @@
 //                     state (S_ctx at t = 0), computes P k and P q, then
 //                     delta = beta (v - alpha P k), S = alpha P + delta k^T (written
 //                     whole) and o = S q = alpha P q + delta (k . q).
+#include <hip/hip_ext.h>
+
 #include "gdn_device.h"
 
 namespace gdn {
@@ -116,7 +118,11 @@ static int launch_full_t(const FullStepArgs& s, hipStream_t st) {
   FullK k{s.H, s.HK, s.W, s.W_max, s.T_max, s.t, s.S_ctx, s.q, s.k, s.v, s.alpha, s.beta, s.o, prev,
           next, s.anc};
   const size_t blocks = size_t(s.R) * s.H * s.W;
-  hipLaunchKernelGGL((fullstate_kernel<DK, DV, BF16>), dim3(unsigned(blocks)), dim3(256), 0, st, k);
+  if (s.ev0)   // the dispatch itself stamps its start and end
+    hipExtLaunchKernelGGL((fullstate_kernel<DK, DV, BF16>), dim3(unsigned(blocks)), dim3(256), 0, st, s.ev0,
+                          s.ev1, 0, k);
+  else
+    hipLaunchKernelGGL((fullstate_kernel<DK, DV, BF16>), dim3(unsigned(blocks)), dim3(256), 0, st, k);
   return last_launch_error();
 }
 

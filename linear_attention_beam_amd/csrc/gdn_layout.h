@@ -124,6 +124,7 @@ struct StepArgs {
   float* o;
   void* ws;
   Layout L;
+  hipEvent_t ev0, ev1;    // non-null: the launch records its own start and end on them
 };
 
 struct SelectArgs {
@@ -156,6 +157,7 @@ struct FullStepArgs {
   void* states;           // two generations of R*H*W_max*d_v*d_k fp32 states
   size_t half_bytes;      // bytes of one generation
   const int32_t* anc;     // ancestry of step t in the workspace
+  hipEvent_t ev0, ev1;    // non-null: the launch records its own start and end on them
 };
 
 inline size_t fullstate_half_bytes(const gdn_beam_config& c) {

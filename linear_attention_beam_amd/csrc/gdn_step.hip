@@ -9,6 +9,8 @@
 //   step_kernel      fused step: S_ctx [q|k] on MFMA (eqs. 6-7 initial terms), replay
 //                    along the ancestor records (eqs. 6-7), eq. (8), record append.
 //   prefill_kernel   eq. (3) over each request's prompt (the state S_ctx).
+#include <hip/hip_ext.h>
+
 #include "gdn_device.h"
 
 namespace gdn {
@@ -212,16 +214,16 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
       const int u = tid + i * NT;
       if (u / UPQ < nb) {
         const size_t row = kbase + beam_of(c0 + u / UPQ);
-        sq[i] = *reinterpret_cast<const u32x4*>(qg + row * C::QB + size_t(u % UPQ) * 16);
-        sk[i] = *reinterpret_cast<const u32x4*>(kg + row * C::QB + size_t(u % UPQ) * 16);
+        sq[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qg + row * C::QB + size_t(u % UPQ) * 16));
+        sk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kg + row * C::QB + size_t(u % UPQ) * 16));
       }
     }
 #pragma unroll
     for (int i = 0; i < C::VU; ++i) {
       const int u = tid + i * NT;
       if (u / UPV < nb)
-        sv[i] = *reinterpret_cast<const u32x4*>(vg + ((base + beam_of(c0 + u / UPV)) * DV + row_base) * C::E +
-                                                size_t(u % UPV) * 16);
+        sv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + ((base + beam_of(c0 + u / UPV)) * DV + row_base) * C::E +
+                                                size_t(u % UPV) * 16));
     }
     if (tid < 64 && (tid & 31) < nb) {
       const size_t bi = base + beam_of(c0 + (tid & 31));
@@ -613,15 +615,21 @@ static int launch_step_t(const StepArgs& a, hipStream_t s) {
           reinterpret_cast<float*>(ws + a.L.gtr_delta), ws + a.L.gtr_key,
           reinterpret_cast<const int32_t*>(ws + a.L.anc[a.t & 1]),
           reinterpret_cast<const int32_t*>(ws + a.L.order[a.t & 1])};
+  // with timing events, the dispatch itself stamps its start and end (nothing more is
+  // put on the stream)
+  auto go = [&](auto kern) {
+    if (a.ev0) hipExtLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, s, a.ev0, a.ev1, 0, k);
+    else hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, s, k);
+  };
   switch (a.t) {
-    case 0: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 0>), dim3(grid), dim3(NT), 0, s, k); break;
-    case 1: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 1>), dim3(grid), dim3(NT), 0, s, k); break;
-    case 2: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 2>), dim3(grid), dim3(NT), 0, s, k); break;
-    case 3: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 3>), dim3(grid), dim3(NT), 0, s, k); break;
-    case 4: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 4>), dim3(grid), dim3(NT), 0, s, k); break;
-    case 5: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 5>), dim3(grid), dim3(NT), 0, s, k); break;
-    case 6: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 6>), dim3(grid), dim3(NT), 0, s, k); break;
-    default: hipLaunchKernelGGL((step_kernel<DK, DV, BF16, 7>), dim3(grid), dim3(NT), 0, s, k); break;
+    case 0: go(step_kernel<DK, DV, BF16, 0>); break;
+    case 1: go(step_kernel<DK, DV, BF16, 1>); break;
+    case 2: go(step_kernel<DK, DV, BF16, 2>); break;
+    case 3: go(step_kernel<DK, DV, BF16, 3>); break;
+    case 4: go(step_kernel<DK, DV, BF16, 4>); break;
+    case 5: go(step_kernel<DK, DV, BF16, 5>); break;
+    case 6: go(step_kernel<DK, DV, BF16, 6>); break;
+    default: go(step_kernel<DK, DV, BF16, 7>); break;
   }
   return last_launch_error();
 }

@@ -78,6 +78,17 @@ class BeamDecoder:
         B.gdn_beam_export(self.ctx, what, out, n, self._stream(stream))
         return out
 
+    @staticmethod
+    def time_steps(capacity):
+        """Make the next `capacity` step launches (of any decoder: a process-wide count)
+        record their own kernel time."""
+        B.gdn_beam_time_steps(capacity)
+
+    @staticmethod
+    def step_times(cap):
+        """(durations in ms of the timed step launches, in launch order; number recorded)."""
+        return B.gdn_beam_step_times(cap)
+
     def close(self):
         if self.ctx is not None:
             B.gdn_beam_destroy(self.ctx)

@@ -145,14 +145,18 @@ def check_selection(o_r, cum_r, Wout64, K, sel_r, where=""):
     return len(diff)
 
 
-def decode_record(name="batch", R=4):
+def decode_record(name="batch", R=4, time_cap=None):
     """One select-mode decode of workload `name` on its first R requests: every step's
     o_t and selection, then the ancestry, SID prefixes, cumulative scores and record
-    pool.  Inputs are seeded, so another process records the same decode."""
+    pool.  Inputs are seeded, so another process records the same decode.  With
+    time_cap, the first time_cap step launches stamp their own start and end
+    (gdn_beam_time_steps) and the last entry is (durations, number recorded)."""
     import synth
     wl = synth.get(name)
     g = GpuDecode(wl, R=R, exact=())
     g.init()
+    if time_cap is not None:
+        g.dec.time_steps(time_cap)
     rec = []
     for t in range(wl.T):
         rec.append(to_np(g.step(t)).copy())
@@ -161,6 +165,9 @@ def decode_record(name="batch", R=4):
     for what in (B.GDN_EXPORT_ANCESTRY, B.GDN_EXPORT_TOKENS, B.GDN_EXPORT_CUM,
                  B.GDN_EXPORT_GTR_DELTA, B.GDN_EXPORT_GTR_KEY):
         rec.append(g.export(what).copy())
+    if time_cap is not None:
+        rec.append(g.dec.step_times(wl.T))
+        g.dec.time_steps(0)
     return rec
 
 

@@ -417,6 +417,36 @@ def test_decode_is_deterministic():
         assert same_bits(x, y)
 
 
+def test_timed_step_launches():
+    """Step launches that stamp their own start and end on HIP events give the same bits
+    as untimed ones; launches past the capacity are not timed; reading the times starts
+    the count over; a capacity out of range is refused."""
+    plain = decode_record()
+    timed = decode_record(time_cap=2)
+    (ms, n) = timed.pop()
+    assert len(plain) == len(timed)
+    for x, y in zip(plain, timed):
+        assert same_bits(x, y)
+    assert n == 2 and len(ms) == 2
+    assert all(0.0 < m < 1000.0 for m in ms), ms
+    wl = synth.get("tiny")
+    g = GpuDecode(wl, exact=())
+    g.init()
+    g.dec.time_steps(8)
+    g.step(0)
+    g.select(0)
+    g.step(1)
+    ms, n = g.dec.step_times(1)            # two recorded, one asked for
+    assert n == 2 and len(ms) == 1 and ms[0] > 0.0
+    assert g.dec.step_times(4) == ([], 0)  # the count started over
+    g.dec.time_steps(0)                    # events released: nothing more is timed
+    g.select(1)
+    g.step(2)
+    assert g.dec.step_times(4) == ([], 0)
+    with pytest.raises(B.GdnBeamError):
+        g.dec.time_steps(-1)
+
+
 _SERIAL_CHILD = """
 import sys
 import numpy as np
