@@ -187,7 +187,7 @@ __device__ __forceinline__ f32x16 block_mfma_f32(const float* wt, int code, int 
 // ---------------------------------------------------------------- first pass
 
 struct LogitsK {
-  int W, W_max, V, nchunk, nvg, cpw, nch_max;
+  int R, W, W_max, V, nchunk, nvg, cpw, nch_max;
   int beam_major;        // tile maxima per request [W][n_tiles(V)] (else [n_tiles(V)][W])
   const float* z;        // [R,W_max,DV]      fp32 codebook
   const u32x4* zf;       // operand fragments bf16 codebook
@@ -211,7 +211,10 @@ constexpr int kSelList = 8192;
 constexpr int kSelPairs = 4096;
 constexpr int kMaxGroupsMask = 128;
 
-// Block: kLogitsWaves chunks of 32 beams x one group of cpw codes.  Each 32-code tile of
+// Block: kLogitsWaves chunks of 32 beams x one group of cpw codes.  Chunks are numbered
+// over all requests, request-major, so that every wave has one wherever a request has
+// fewer chunks than a block has waves (the codebook is the same for all requests).
+// Each 32-code tile of
 // the codebook is staged once per block in LDS (double-buffered; one barrier per stage
 // of two tiles for d_v <= 128, of one tile above) and read by every wave as its A
 // operand.  Lane l keeps beam l % 32 and folds its 16
@@ -221,16 +224,15 @@ template <int DV, bool WBF16>
 __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   constexpr int HV = DV / 2;
   const int wave = threadIdx.x >> 6;
-  // 1-D grid over (request, chunk block, code group), code group fastest; the blocks
-  // of one request (which read the same z operand) share an XCD
-  const int nx = ((a.nchunk + kLogitsWaves - 1) / kLogitsWaves) * a.nvg;
+  // 1-D grid over (chunk group, code group), code group fastest; the blocks of one
+  // chunk group (which read the same z operand) share an XCD
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
-  const int r = wid / nx, bx = wid % nx;
-  const int vg = bx % a.nvg;
-  const int chunk = (bx / a.nvg) * kLogitsWaves + wave;
-  const bool wvalid = chunk < a.nchunk;
+  const int vg = wid % a.nvg, cg = wid / a.nvg;
+  const int gc = cg * kLogitsWaves + wave;          // chunk over all requests
+  const bool wvalid = gc < a.R * a.nchunk;
+  const int r = wvalid ? gc / a.nchunk : 0, chunk = wvalid ? gc % a.nchunk : 0;
   const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
-  const int b = (wvalid ? chunk : 0) * 32 + m;
+  const int b = chunk * 32 + m;
   const bool bvalid = wvalid && b < a.W;
   float* tm_r = a.tmax + size_t(r) * a.tmax_stride;
   const int code_lo = vg * a.cpw;
@@ -243,6 +245,14 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   constexpr bool STAGE_TM = WBF16 && DV <= 256;
   const int vt = (a.V + 31) >> 5;
   __shared__ float tms[STAGE_TM ? kMaxGroupTiles * kTmRow : 1];
+  // request and first beam of each wave's chunk (request -1: no chunk), for the flush
+  __shared__ int slot_r[STAGE_TM ? kLogitsWaves : 1], slot_b[STAGE_TM ? kLogitsWaves : 1];
+  if constexpr (STAGE_TM) {
+    if (lane == 0) {
+      slot_r[wave] = wvalid ? r : -1;
+      slot_b[wave] = chunk * 32;
+    }
+  }
   auto put_tm = [&](float tm, int c0) {
     if constexpr (STAGE_TM) {
       tms[((c0 - code_lo) >> 5) * kTmRow + wave * 32 + m] = tm;
@@ -324,7 +334,7 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
         if (e < NE) tile[buf][(e / (DV / 8)) * RS + e % (DV / 8)] = stg[u];
       }
     };
-    const u32x4* zb = a.zf + zf_lane_base(r, a.nch_max, DV, (wvalid ? chunk : 0) * 32, hf) + m;
+    const u32x4* zb = a.zf + zf_lane_base(r, a.nch_max, DV, chunk * 32, hf) + m;
     if constexpr (KS <= 16) {
       // the first tile's loads go out before the z operand's (loads complete in order,
       // so staging the tile then waits for those alone)
@@ -434,16 +444,20 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   if constexpr (STAGE_TM) {
     __syncthreads();
     const int nt = (code_hi - code_lo + 31) >> 5;
-    const int b0 = (bx / a.nvg) * kLogitsWaves * 32;
     if (a.beam_major) {
       // 32 lanes per beam: one contiguous row of the group's tiles
       const int ti = threadIdx.x & 31;
-      for (int bb = threadIdx.x >> 5; bb < kLogitsWaves * 32; bb += 2 * kLogitsWaves)
-        if (ti < nt && b0 + bb < a.W) tm_r[size_t(b0 + bb) * vt + (code_lo >> 5) + ti] = tms[ti * kTmRow + bb];
+      for (int bb = threadIdx.x >> 5; bb < kLogitsWaves * 32; bb += 2 * kLogitsWaves) {
+        const int rs = slot_r[bb >> 5], bs = slot_b[bb >> 5] + (bb & 31);
+        if (ti < nt && rs >= 0 && bs < a.W)
+          a.tmax[size_t(rs) * a.tmax_stride + size_t(bs) * vt + (code_lo >> 5) + ti] = tms[ti * kTmRow + bb];
+      }
     } else {
       for (int e = threadIdx.x; e < nt * kLogitsWaves * 32; e += 64 * kLogitsWaves) {
         const int bb = e % (kLogitsWaves * 32), ti = e / (kLogitsWaves * 32);
-        if (b0 + bb < a.W) tm_r[size_t((code_lo >> 5) + ti) * a.W + b0 + bb] = tms[ti * kTmRow + bb];
+        const int rs = slot_r[bb >> 5], bs = slot_b[bb >> 5] + (bb & 31);
+        if (rs >= 0 && bs < a.W)
+          a.tmax[size_t(rs) * a.tmax_stride + size_t((code_lo >> 5) + ti) * a.W + bs] = tms[ti * kTmRow + bb];
       }
     }
   }
@@ -1455,7 +1469,7 @@ static int launch_dv(const SelectArgs& a, const LogitsK& lk, const RefineK& rk, 
                      hipStream_t s, bool refine) {
   const bool bf = a.wout_dtype == GDN_BF16;
   if (!refine) {
-    dim3 grid(((lk.nchunk + kLogitsWaves - 1) / kLogitsWaves) * lk.nvg * a.R);
+    dim3 grid(((a.R * lk.nchunk + kLogitsWaves - 1) / kLogitsWaves) * lk.nvg);
     if (bf) hipLaunchKernelGGL((logits_kernel<DV, true>), grid, dim3(64 * kLogitsWaves), 0, s, lk);
     else hipLaunchKernelGGL((logits_kernel<DV, false>), grid, dim3(64 * kLogitsWaves), 0, s, lk);
   } else {
@@ -1532,7 +1546,7 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   // the bounded tile selection where a request's tiles outnumber its list (and the code
   // groups' maxima number at least K); it reads the tile maxima beam-major
   const bool bounded = int64_t(a.W) * Vt > kSelList && int64_t(a.W) * nvg >= Kt;
-  LogitsK lk{a.W, a.W_max, a.V, nch, nvg, cpw, nch_max, bounded ? 1 : 0, z, zf, woutT, tmax, tstride,
+  LogitsK lk{a.R, a.W, a.W_max, a.V, nch, nvg, cpw, nch_max, bounded ? 1 : 0, z, zf, woutT, tmax, tstride,
              lse_part};
   RefineK rk{a.W, a.W_max, a.V, Vt, G_max, nch_max, z, zf, woutT, lse, cum, sel, groups, gtiles, rkeys};
   if ((err = launch_by_dv(a, lk, rk, 0, s, false))) return err;
