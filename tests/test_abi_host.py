@@ -168,6 +168,21 @@ def test_null_context_calls():
     B.gdn_beam_destroy(None)   # no-op
 
 
+def test_step_timing_argument_errors():
+    """The step-launch timer refuses a capacity out of range and missing outputs before
+    any HIP call; with no timer set, reading gives nothing and releasing is a no-op."""
+    f = B.raw_status
+    assert f("gdn_beam_time_steps", -1) == B.GDN_ERR_INVALID_ARG
+    assert f("gdn_beam_time_steps", 65537) == B.GDN_ERR_INVALID_ARG
+    n = ctypes.c_int32(7)
+    ms = (ctypes.c_float * 4)()
+    assert f("gdn_beam_step_times", None, 4, ctypes.byref(n)) == B.GDN_ERR_INVALID_ARG   # no ms
+    assert f("gdn_beam_step_times", ms, -1, ctypes.byref(n)) == B.GDN_ERR_INVALID_ARG    # cap < 0
+    assert f("gdn_beam_step_times", ms, 4, None) == B.GDN_ERR_INVALID_ARG                # no n
+    assert f("gdn_beam_time_steps", 0) == B.GDN_OK
+    assert f("gdn_beam_step_times", None, 0, ctypes.byref(n)) == B.GDN_OK and n.value == 0
+
+
 def test_prefill_argument_errors():
     f = lambda *a: B.raw_status("gdn_beam_prefill", *a)
     assert f(2, 3, 0, 64, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_UNSUPPORTED
