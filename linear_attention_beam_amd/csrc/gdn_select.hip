@@ -1142,13 +1142,14 @@ __global__ void __launch_bounds__(256, 3) refine_kernel(RefineK a) {
   const int r = blockIdx.y;
   const int g = blockIdx.x * 4 + (threadIdx.x >> 6);      // < G_max by the launch
   const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
-  // no early exit: the three loads issue together; a wave past the last group works
-  // on clamped operands and stores nothing
+  // the group count and the group's descriptor and tiles are loaded together; a wave
+  // past the last group leaves once they are in (the operand loads below need them)
   const uint32_t ng = a.sel[r].n_groups;
   const uint32_t desc = a.groups[size_t(r) * a.G_max + g];
   const uint32_t f = a.gtiles[(size_t(r) * a.G_max + g) * 32 + m];
+  if (g >= int(ng)) return;                                 // wave-uniform, no barrier follows
   const int start = int(desc & 1023u), cnt = int((desc >> 10) & 63u), j = int(desc >> 16);
-  const bool valid = g < int(ng) && m < cnt;
+  const bool valid = m < cnt;
   const int b = valid ? int(f / uint32_t(a.Vt)) : 0;
   const int c0 = 32 * j;
   // the beam's cumulative score and log-sum-exp go out with the operands
