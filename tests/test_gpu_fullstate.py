@@ -145,3 +145,30 @@ def test_fullstate_state_machine():
     g.step(0)
     assert full(0, g.S_ctx.data_ptr(), states.data_ptr(), nbytes) == B.GDN_ERR_BAD_STATE
     torch.cuda.synchronize()
+
+
+def test_fullstate_timed_launches_same_bits():
+    """FullState launches that stamp their own start and end (gdn_beam_time_steps) give
+    the same outputs and selections, bit for bit, as untimed ones."""
+    wl = synth.get("single")
+
+    def run(timed):
+        g = GpuDecode(wl, R=1, exact=())
+        states = g.dec.alloc_states()
+        g.init()
+        if timed:
+            g.dec.time_steps(wl.T)
+        rec = []
+        for t in range(wl.T):
+            rec.append(to_np(_fullstate(g, states, t)).copy())
+            sel = g.select(t)
+            rec += [sel["parent"].copy(), sel["token"].copy(), sel["score"].copy()]
+        times = g.dec.step_times(wl.T) if timed else None
+        g.dec.time_steps(0)
+        return rec, times
+
+    plain, _ = run(False)
+    timed, (ms, n) = run(True)
+    assert n == wl.T and len(ms) == wl.T and all(m > 0.0 for m in ms), (ms, n)
+    for x, y in zip(plain, timed):
+        assert np.array_equal(np.ascontiguousarray(x).view(np.uint8), np.ascontiguousarray(y).view(np.uint8))
