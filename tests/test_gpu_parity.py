@@ -51,6 +51,11 @@ DERIVED = {
     "mixed_a": ("tiny", dict(widths=(300, 600, 257), V=911)),
     "mixed_b": ("single", dict(widths=(200, 150, 100), V=1500)),
     "mixed_c": ("single", dict(widths=(64, 700, 700), V=777, io="bf16", wout="bf16")),
+    # several requests whose chunk count is not a multiple of the logits block's eight
+    # waves, so blocks hold chunks of two or more requests (bf16 codebook: tile maxima
+    # staged and flushed per request), with the bounded and the every-tile selection
+    "multi_bounded": ("tiny", dict(R=3, widths=(300, 300, 300), V=1024, io="bf16", wout="bf16")),
+    "multi_small": ("tiny", dict(R=3, widths=(40, 72, 40), V=200, io="bf16", wout="bf16")),
     # d_v = 512 with a bf16 codebook (tile maxima written beam-major without staging)
     "single_dv512_bounded": ("single", dict(d_v=512, io="bf16", wout="bf16", widths=(512, 512, 512),
                                             V=1024)),
@@ -152,6 +157,7 @@ def test_forced_parents_parity(name, R):
                                     ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("tiny_shrink", 2), ("single_v300", 1),
                                     ("single_bf16_t6", 1), ("tiny_w1024_t6", 1), ("tiny_bounded", 2),
                                     ("tiny_bounded_v1000", 1), ("mixed_a", 1), ("mixed_b", 1), ("mixed_c", 1),
+                                    ("multi_bounded", 3), ("multi_small", 3),
                                     ("single_gqa", 1), ("single_dk256", 1), ("single_dv512", 1),
                                     ("single_dk256_dv512", 1)])
 def test_select_mode_parity(name, R):
