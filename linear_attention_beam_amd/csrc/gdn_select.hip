@@ -1529,7 +1529,7 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
     const long n = long(a.R) * nch * 32 * (a.d_v / 8);
     const int ntr = ((a.V + 31) / 32) * ((a.d_v + 31) / 32);   // transpose tiles
     long zb = (n + 255) / 256;
-    zb = zb < 1 ? 1 : (zb > 8192 ? 8192 : zb);
+    zb = zb < 1 ? 1 : (zb > 65536 ? 65536 : zb);
     const int tb = ntr < 256 ? ntr : 256;
     ZsumK k{a.R, a.H, a.W, a.W_max, a.d_v, a.V, nch_max, int(zb), split, a.o, z, zf, a.Wout, woutT};
     // o above half of the 256 MiB last-level cache: streamed (512 MiB of o: 144 -> 120
