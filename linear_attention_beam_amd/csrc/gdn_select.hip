@@ -592,18 +592,33 @@ __device__ uint32_t tie_cut(KeyAt key_at, FlatAt flat_at, uint32_t n, uint32_t t
       if ((f & himask) == (pre & himask)) atomicAdd(&hist[(f >> s) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t below = 0;
-      for (int d = 0; d < 256; ++d) {
-        if (below < nd && nd <= below + hist[d]) {
-          pre |= uint32_t(d) << s;
-          nd -= below;
-          break;
-        }
-        below += hist[d];
+    if (tid < 64) {
+      // the digit holding the nd-th entry: lane l sums digits 4l .. 4l + 3, an inclusive
+      // scan over the lanes, and the lane whose range holds nd resolves its four
+      const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2],
+                     h3 = hist[4 * tid + 3];
+      const uint32_t own = h0 + h1 + h2 + h3;
+      uint32_t incl = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = uint32_t(__shfl_up(int(incl), off));
+        if (tid >= off) incl += y;
       }
-      sh.lo = pre;
-      sh.need = nd;
+      const uint32_t excl = incl - own;
+      const uint64_t hit = __ballot(excl < nd && nd <= incl);
+      if (tid == 0 && !hit) { sh.lo = pre; sh.need = nd; }     // no digit: nothing changes
+      if (hit && tid == __ffsll((long long)hit) - 1) {
+        uint32_t below = excl, d = 4 * tid;
+        if (nd > below + h0) {
+          below += h0; ++d;
+          if (nd > below + h1) {
+            below += h1; ++d;
+            if (nd > below + h2) { below += h2; ++d; }
+          }
+        }
+        sh.lo = pre | (d << s);
+        sh.need = nd - below;
+      }
     }
     __syncthreads();
     pre = sh.lo;
