@@ -17,7 +17,7 @@ Sources:
   RecoGEM (conceptio mirror), section 4.3: the selection is an exact top-K
         over the W x C candidate matrix of a request.
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
   * Scoring: z_b = sum over heads of o_b; logits = z_b^T Wout; the step score of
     candidate (b, c) is cum_b + (logit_bc - logsumexp_c(logit_b)), natural log
     (the log of eq. 1's product, one log-softmax per step).
