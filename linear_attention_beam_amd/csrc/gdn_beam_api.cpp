@@ -44,6 +44,12 @@ struct StepTimer {
     ++n;
     return true;
   }
+  // a launch that took a pair and failed gives it back (it recorded nothing)
+  void give_back(bool taken) {
+    if (!taken) return;
+    std::lock_guard<std::mutex> g(m);
+    if (n > 0) --n;
+  }
 } g_timer;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -154,9 +160,12 @@ gdn_status gdn_beam_step(gdn_beam_ctx* ctx, int32_t t, const void* q, const void
   if (t != ctx->t || ctx->mode == 2) return GDN_ERR_BAD_STATE;
   StepArgs a{c.R, c.H, key_heads(c), c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype,
              q, k, v, alpha, beta, o, ctx->ws, ctx->L, nullptr, nullptr};
-  g_timer.take(a.ev0, a.ev1);
+  const bool timed = g_timer.take(a.ev0, a.ev1);
   int err = launch_step(a, stream);
-  if (err) return hip_fail(err, "gdn_beam_step");
+  if (err) {
+    g_timer.give_back(timed);
+    return hip_fail(err, "gdn_beam_step");
+  }
   ctx->stepped = 1;
   ctx->mode = 1;
   return GDN_OK;
@@ -191,9 +200,12 @@ gdn_status gdn_fullstate_step(gdn_beam_ctx* ctx, int32_t t, const float* S_ctx, 
                  q, k, v, alpha, beta, o, states, half,
                  reinterpret_cast<const int32_t*>(static_cast<char*>(ctx->ws) + ctx->L.anc[t & 1]),
                  nullptr, nullptr};
-  g_timer.take(a.ev0, a.ev1);
+  const bool timed = g_timer.take(a.ev0, a.ev1);
   int err = launch_fullstate(a, stream);
-  if (err) return hip_fail(err, "gdn_fullstate_step");
+  if (err) {
+    g_timer.give_back(timed);
+    return hip_fail(err, "gdn_fullstate_step");
+  }
   ctx->stepped = 1;
   ctx->mode = 2;
   ctx->states = states;
