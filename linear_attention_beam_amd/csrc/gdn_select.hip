@@ -1554,10 +1554,12 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
     else hipLaunchKernelGGL(zsum_kernel<false>, dim3(unsigned(zb + tb)), dim3(256), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
-  // codes per wave: 128 .. 1024, larger while the grid keeps >= 16384 waves, so that
-  // the z operand is reloaded fewer times on large codebooks
+  // codes per wave: 128 .. 1024, larger while the grid keeps >= 8192 waves, so that
+  // the z operand is reloaded fewer times on large codebooks (at 4096 codes and
+  // 256-512 beams of d_v = 256, 8192 rather than 16384 took 30 us off a 0.44 ms
+  // selection; 32768 cost 150 us on 1024 beams of 8192 codes)
   int cpw = 128;
-  while (cpw < 1024 && cpw < a.V && int64_t(a.R) * nch * ((a.V + 2 * cpw - 1) / (2 * cpw)) >= 16384) cpw *= 2;
+  while (cpw < 1024 && cpw < a.V && int64_t(a.R) * nch * ((a.V + 2 * cpw - 1) / (2 * cpw)) >= 8192) cpw *= 2;
   const int nvg = (a.V + cpw - 1) / cpw;
   // the bounded tile selection where a request's tiles outnumber its list (and the code
   // groups' maxima number at least K); it reads the tile maxima beam-major
