@@ -98,7 +98,7 @@ def test_cpu_baseline_on_tiny():
     assert "1 of 1 requests" in res["sample"]
 
 
-@pytest.mark.parametrize("name", ["batch", "tiny"])
+@pytest.mark.parametrize("name", ["batch", "tiny", "growing"])
 def test_decode_floor_term_by_term(name):
     """The full-decode floor: init, every step launch and every selection, each at the
     larger of its bytes over 8 TB/s and its MFMA flops over the dense peak."""
