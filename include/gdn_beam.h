@@ -116,7 +116,8 @@ gdn_status gdn_beam_step(gdn_beam_ctx* ctx, int32_t t,
  * top-W is still computed into parent/token/score.  Forced entries out of range
  * are clamped and flagged in the status word (gdn_beam_export GDN_EXPORT_STATUS).
  * Then the ancestry is remapped by eq. (9) (section 2.4): only indices move,
- * never records.  Requires W_next <= W_max, V <= V_max, W_next <= W_t*V. */
+ * never records.  A NaN score ranks below every number (a NaN in o_t makes every
+ * score of that beam NaN).  Requires W_next <= W_max, V <= V_max, W_next <= W_t*V. */
 gdn_status gdn_beam_select(gdn_beam_ctx* ctx, int32_t t, const float* o,
                            const void* Wout, int32_t V, int32_t W_next,
                            const int32_t* forced_parent, const int32_t* forced_token,
@@ -154,7 +155,11 @@ typedef enum {
   GDN_EXPORT_GTR_ALPHA = 3, /* [R,H,T_max,W_max] fp32                                    */
   GDN_EXPORT_GTR_DELTA = 4, /* [R,H,T_max,W_max,d_v] fp32                                */
   GDN_EXPORT_GTR_KEY = 5,   /* [R,H_K,T_max,W_max,d_k] io_dtype                          */
-  GDN_EXPORT_STATUS = 6     /* [1] int32: bit 0 = a forced parent/token was out of range */
+  GDN_EXPORT_STATUS = 6     /* [1] int32, bits set by select since init:                 */
+                            /*   bit 0 (1): a forced parent/token was out of range       */
+                            /*   (clamped);  bit 1 (2): a selection found fewer than     */
+                            /*   W_next candidates (possible only with NaN outputs);     */
+                            /*   the missing ranks are filled with beam 0, token 0       */
 } gdn_export_what;
 gdn_status gdn_beam_export(const gdn_beam_ctx* ctx, int32_t what, void* dst,
                            size_t dst_bytes, hipStream_t stream);

@@ -36,10 +36,13 @@ __device__ __forceinline__ u32x4 pack8(const uint32_t* b) {
   return p;
 }
 
-// order-preserving key: larger float -> larger key; -0 is folded into +0 first
+// order-preserving key: larger float -> larger key; -0 is folded into +0 first.  Every
+// NaN maps to key 1, below -inf (key 0x007FFFFF) and above 0, the key of a padding code:
+// a NaN score ranks below every number, as a full sort that puts NaN last does.
 __device__ __forceinline__ uint32_t f2key(float s) {
-  uint32_t u = __float_as_uint(s + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return s != s ? 1u : k;
 }
 __device__ __forceinline__ float key2f(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);

@@ -1,7 +1,8 @@
 // Selection-side HIP kernels for large-beam Gated DeltaNet decoding on gfx950.
 //
-// Scoring follows the beam-search objective of OneLA (paper-archivist.com) section 2.1
-// and eq. (1); the exact request-level top-K with a per-row precut follows RecoGEM
+// Scoring follows the beam-search objective of OneLA (paper-archivist.com) section 1.1,
+// eq. (1) and large-beam decoding's global top-k; the exact request-level top-K with a
+// per-row precut follows RecoGEM
 // (conceptio mirror) section 4.3; the ancestry remap is OneLA eq. (9).
 //
 // No score matrix is materialised.  Codes are cut into tiles of 32 (one MFMA block of

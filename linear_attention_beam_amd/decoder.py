@@ -12,6 +12,21 @@ from . import binding as B
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
+def _need(name, x, shape, dtype, device):
+    """Refuse, on the host and before any launch, a tensor the kernels would read or
+    write out of its bounds or misread: wrong shape, dtype or device, or not dense."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(x).__name__}")
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(x.shape)}, expected {tuple(shape)}")
+    if x.dtype != dtype:
+        raise ValueError(f"{name}: dtype {x.dtype}, expected {dtype}")
+    if x.device.type != "cuda" or (device.index is not None and x.device.index != device.index):
+        raise ValueError(f"{name}: on {x.device}, expected {device}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: not contiguous")
+
+
 class BeamDecoder:
     def __init__(self, R, H, d_k, d_v, T_max, W_max, V_max, io="bf16", wout="bf16",
                  device="cuda", H_K=0):
@@ -24,19 +39,42 @@ class BeamDecoder:
         off = (-self.ws.data_ptr()) % 256            # the ABI wants a 256-byte aligned base
         self.ws_ptr = self.ws.data_ptr() + off
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.ctx = None
 
     @staticmethod
     def _stream(stream):
         return torch.cuda.current_stream() if stream is None else stream
 
+    def _step_inputs(self, q, k, v, alpha, beta, o):
+        s = self.shape
+        _, W = B.gdn_beam_query(self.ctx)
+        R, H, HK = s["R"], s["H"], s["H_K"]
+        io = _DT[self.io]
+        _need("q", q, (R, HK, W, s["d_k"]), io, self.device)
+        _need("k", k, (R, HK, W, s["d_k"]), io, self.device)
+        _need("v", v, (R, H, W, s["d_v"]), io, self.device)
+        _need("alpha", alpha, (R, H, W), torch.float32, self.device)
+        _need("beta", beta, (R, H, W), torch.float32, self.device)
+        _need("o", o, (R, H, W, s["d_v"]), torch.float32, self.device)
+
+    def _ctx(self):
+        if self.ctx is None:
+            raise RuntimeError("BeamDecoder: init() first")
+        return self.ctx
+
     def init(self, S_ctx, W0, stream=None):
+        s = self.shape
+        _need("S_ctx", S_ctx, (s["R"], s["H"], s["d_v"], s["d_k"]), torch.float32, self.device)
         self.close()
         self.ctx = B.gdn_beam_init(self.cfg, S_ctx, W0, self.ws_ptr, self.ws_bytes,
                                    self._stream(stream))
         return self
 
     def step(self, t, q, k, v, alpha, beta, o, stream=None):
+        self._ctx()
+        self._step_inputs(q, k, v, alpha, beta, o)
         B.gdn_beam_step(self.ctx, t, q, k, v, alpha, beta, o, self._stream(stream))
 
     def fullstate_step(self, t, S_ctx, q, k, v, alpha, beta, o, states, stream=None):
@@ -53,6 +91,20 @@ class BeamDecoder:
 
     def select(self, t, o, Wout, V, W_next, parent, token, score, forced_parent=None,
                forced_token=None, stream=None):
+        self._ctx()
+        s = self.shape
+        _, W = B.gdn_beam_query(self.ctx)
+        R = s["R"]
+        _need("o", o, (R, s["H"], W, s["d_v"]), torch.float32, self.device)
+        _need("Wout", Wout, (s["d_v"], V), _DT[self.wout], self.device)
+        _need("parent", parent, (R, W_next), torch.int32, self.device)
+        _need("token", token, (R, W_next), torch.int32, self.device)
+        _need("score", score, (R, W_next), torch.float32, self.device)
+        if (forced_parent is None) != (forced_token is None):
+            raise ValueError("forced_parent and forced_token go together")
+        if forced_parent is not None:
+            _need("forced_parent", forced_parent, (R, W_next), torch.int32, self.device)
+            _need("forced_token", forced_token, (R, W_next), torch.int32, self.device)
         B.gdn_beam_select(self.ctx, t, o, Wout, V, W_next, forced_parent, forced_token,
                           parent, token, score, self._stream(stream))
 
@@ -106,5 +158,13 @@ def prefill(S_out, k, v, alpha, beta, offsets, stream=None):
     k [N,H_K,d_k] may hold fewer (key) heads than v [N,H,d_v] (grouped value heads)."""
     R, H, d_v, d_k = S_out.shape
     N = k.shape[0]
+    dev = S_out.device
+    _need("S_out", S_out, (R, H, d_v, d_k), torch.float32, dev)
+    HK = k.shape[1] if k.dim() == 3 else -1
+    _need("k", k, (N, HK, d_k), torch.float32, dev)
+    _need("v", v, (N, H, d_v), torch.float32, dev)
+    _need("alpha", alpha, (N, H), torch.float32, dev)
+    _need("beta", beta, (N, H), torch.float32, dev)
+    _need("offsets", offsets, (R + 1,), torch.int32, dev)
     B.gdn_beam_prefill(R, H, k.shape[1], d_k, d_v, N, k, v, alpha, beta, offsets, S_out,
                        torch.cuda.current_stream() if stream is None else stream)

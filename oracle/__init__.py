@@ -10,9 +10,12 @@ when beams are re-parented, and scoring, selection and ancestry are done by
 brute force (full sort).  It imports nothing from the GPU package; both sides
 share only the seeded input generators in synth/.
 
-Parity status: every function here is pinned by tests/test_oracle_*.py
-(exact-arithmetic identities, closed forms, brute force, library routines);
-no function is "parity unpinned".
+Parity status: every function here is pinned by tests/test_oracle_*.py:
+exact-arithmetic identities and brute force (eqs. 3-9), closed forms, library
+routines (scipy's log-softmax, a full sort), walks of the parent pointers (SID
+prefixes, cumulative scores) and explicit per-value-head loops (grouped heads).
+tests/test_oracle_mutations.py plants plausible mistakes in a copy of this
+package and checks that a pin fails for each.  No function is "parity unpinned".
 """
 from .gdn import gdn_token, prefill, rank1_transition  # noqa: F401
 from .beam import (FullStateDecoder, ancestry_update, capacity_elements,  # noqa: F401

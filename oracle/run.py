@@ -15,13 +15,17 @@ from .gdn import prefill
 from .beam import FullStateDecoder
 
 
-def prefill_request(wl, r):
-    """S_ctx of request r: eq. (3) over its prompt in float64, then rounded to fp32."""
+def prefill_request(wl, r, heads=None):
+    """S_ctx of request r: eq. (3) over its prompt in float64, then rounded to fp32.
+    heads: the value heads to compute (all by default), in that order."""
     p = gen.prompt_tokens(wl, r)
     # grouped value heads: value head h reads the keys of key head h // group
-    S = prefill(np.repeat(p["k"].astype(np.float64), wl.group, axis=1), p["v"].astype(np.float64),
-                p["alpha"].astype(np.float64), p["beta"].astype(np.float64))
-    return S.astype(np.float32)
+    k = np.repeat(p["k"].astype(np.float64), wl.group, axis=1)
+    v, a, b = p["v"].astype(np.float64), p["alpha"].astype(np.float64), p["beta"].astype(np.float64)
+    if heads is not None:
+        hs = list(heads)
+        k, v, a, b = k[:, hs], v[:, hs], a[:, hs], b[:, hs]
+    return prefill(k, v, a, b).astype(np.float32)
 
 
 def step_arrays(wl, r, t):

@@ -19,7 +19,13 @@ from synth import gen
 from linear_attention_beam_amd import binding as B
 from linear_attention_beam_amd.decoder import BeamDecoder, prefill
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}     # max per-vector relative inf-norm error of o_t, delta_t
+# Max per-vector relative inf-norm error of o_t and delta_t.  The bf16-io bar stated for
+# the method is 2e-2 (bf16 inputs, fp32 accumulation); these tests hold the path to 1e-4
+# in both cases.  With bf16 io the inputs are exact, and the error comes from fp32
+# arithmetic and from S_ctx entering the MFMA as two bf16 terms (hi + lo, 16 significant
+# bits): about 1e-5 measured.
+TOL = {"f32": 1e-4, "bf16": 1e-4}
+TOL_STATED = {"f32": 1e-4, "bf16": 2e-2}
 NEAR_TIE = 1e-6                       # selection near-tie band, relative to max(1, |theta|)
 
 
@@ -43,7 +49,7 @@ def to_np(x: torch.Tensor) -> np.ndarray:
 
 
 class GpuDecode:
-    def __init__(self, wl, R=None, exact=(0,), short_prompt=64):
+    def __init__(self, wl, R=None, exact=(0,), short_prompt=64, exact_heads=None):
         self.wl = wl
         self.R = wl.R if R is None else R
         self.exact = tuple(r for r in exact if r < self.R)
@@ -60,10 +66,13 @@ class GpuDecode:
         say("prefill (device, short prompts)")
         prefill(self.S_ctx, p["k"], p["v"], p["alpha"], p["beta"], p["offsets"])
         self.S_exact = {}
+        # exact_heads: only those value heads of the exact requests get the oracle's state
+        # (the others keep the device prefill and are not compared)
+        hs = list(range(wl.H)) if exact_heads is None else list(exact_heads)
         for r in self.exact:
-            S = oracle.prefill_request(wl, r)
+            S = oracle.prefill_request(wl, r, heads=hs)
             self.S_exact[r] = S
-            self.S_ctx[r].copy_(torch.from_numpy(S).to(dev))
+            self.S_ctx[r, hs] = torch.from_numpy(S).to(dev)
         self.Wout = sdev.wout(wl, dev)
         self.Wout64 = gen.wout(wl).value.astype(np.float64)
         self.inputs = []
@@ -143,6 +152,25 @@ def check_selection(o_r, cum_r, Wout64, K, sel_r, where=""):
     ok = (sc[:-1] > sc[1:]) | ((sc[:-1] == sc[1:]) & (gflat[:-1] < gflat[1:]))
     assert np.all(ok), f"{where}: order is not score-descending / flat-ascending"
     return len(diff)
+
+
+def xcd_spread(R, n=8):
+    """n requests spread over R so that the step kernel's workgroups of the first
+    request of every eighth of the grid are among them: requests i R / n + i mod (R / n),
+    one in each block of R / 8 consecutive requests, which the XCD-aware block order
+    hands to one XCD."""
+    if R <= n:
+        return tuple(range(R))
+    q = R // n
+    return tuple(sorted({i * q + (i % q) for i in range(n)}))
+
+
+def score_perturbation(o_gpu, cum_gpu, o_ref, cum_ref, Wout64):
+    """Largest |s_gpu - s_ref| over every candidate of a request, both scored in float64:
+    s_gpu from the GPU's o_t and cumulative scores, s_ref from the oracle's."""
+    s_gpu = oracle.step_scores(np.asarray(o_gpu, np.float64), Wout64, np.asarray(cum_gpu, np.float64))
+    s_ref = oracle.step_scores(np.asarray(o_ref, np.float64), Wout64, np.asarray(cum_ref, np.float64))
+    return float(np.max(np.abs(s_gpu - s_ref))), s_ref
 
 
 def decode_record(name="batch", R=4, time_cap=None):

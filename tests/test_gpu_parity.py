@@ -18,7 +18,8 @@ import oracle
 import synth
 from synth import gen
 from linear_attention_beam_amd import binding as B
-from gpu_harness import GpuDecode, TOL, check_selection, decode_record, rel_err, same_bits, say, to_np
+from gpu_harness import (GpuDecode, NEAR_TIE, TOL, check_selection, decode_record, rel_err, same_bits,
+                         say, score_perturbation, to_np, xcd_spread)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +63,10 @@ DERIVED = {
     # six SID steps (five ancestor records at the last step)
     "tiny_t6": ("tiny", dict(T=6, widths=(8,) * 6)),
     "single_bf16_t6": ("single", dict(T=6, widths=(128,) * 6, io="bf16", wout="bf16")),
+    # the deepest replay the library accepts: eight SID steps (seven ancestor records)
+    "tiny_t8": ("tiny", dict(T=8, widths=(8,) * 8)),
+    "single_bf16_t8": ("single", dict(T=8, widths=(128,) * 8, io="bf16", wout="bf16")),
+    "single_t8": ("single", dict(T=8, widths=(64,) * 8)),
     # grouped value heads: two (four) value heads per key head
     "single_gqa": ("single", dict(H_K=2)),
     "batch_gqa": ("batch", dict(H_K=4)),
@@ -122,7 +127,8 @@ def test_prefill_matches_oracle(name, R):
 
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_t6", 1),
-                                    ("tiny_w1024_t6", 1),
+                                    ("tiny_w1024_t6", 1), ("tiny_t8", 1), ("single_bf16_t8", 1),
+                                    ("single_t8", 1),
                                     ("single_bf16_t6", 1), ("single_gqa", 1), ("batch_gqa", 2),
                                     ("single_dk256", 1), ("single_dv512", 1), ("single_dv512_f32io", 1),
                                     ("single_dk256_dv512", 1)])
@@ -155,7 +161,8 @@ def test_forced_parents_parity(name, R):
 
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_v37", 1),
                                     ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("tiny_shrink", 2), ("single_v300", 1),
-                                    ("single_bf16_t6", 1), ("tiny_w1024_t6", 1), ("tiny_bounded", 2),
+                                    ("single_bf16_t6", 1), ("tiny_w1024_t6", 1), ("tiny_t8", 1),
+                                    ("single_bf16_t8", 1), ("tiny_bounded", 2),
                                     ("tiny_bounded_v1000", 1), ("mixed_a", 1), ("mixed_b", 1), ("mixed_c", 1),
                                     ("multi_bounded", 3), ("multi_small", 3),
                                     ("single_gqa", 1), ("single_dk256", 1), ("single_dv512", 1),
@@ -182,19 +189,31 @@ def test_select_mode_parity(name, R):
             o_ref = _cmp_gdn(wl, decs[r], g, r, t, o, dpool, tol)
             sel_r = {k: v[r] for k, v in sel.items()}
             check_selection(o[r], cum_before[r][:wl.width(t)], g.Wout64, K, sel_r, f"r={r} t={t}")
-            s_ref = oracle.step_scores(o_ref, g.Wout64, decs[r].cum)
+            # End to end against the oracle's own top-W.  With eps the largest score
+            # difference the GPU's o_t and cumulative scores make (both scored in float64),
+            # the K-th score moves by at most eps, so a candidate in only one of the two
+            # sets scores within 2 eps + the near-tie band of the oracle's threshold.
+            eps, s_ref = score_perturbation(o[r], cum_before[r][:wl.width(t)], o_ref, decs[r].cum,
+                                            g.Wout64)
             rp, rt, rs = oracle.top_w(s_ref, K)
             V = wl.V
             d = set((rp.astype(np.int64) * V + rt).tolist()) ^ set(
                 (sel_r["parent"].astype(np.int64) * V + sel_r["token"]).tolist())
             swaps += len(d)
-            for f in d:   # end to end, only candidates at the boundary may differ
-                assert abs(s_ref.reshape(-1)[f] - rs[-1]) <= 10 * tol * max(1.0, abs(rs[-1]))
+            band = 2 * eps + NEAR_TIE * max(1.0, abs(rs[-1]))
+            for f in d:
+                assert abs(s_ref.reshape(-1)[f] - rs[-1]) <= band, (f, s_ref.reshape(-1)[f], rs[-1], eps)
             decs[r].advance(t, sel_r["parent"], sel_r["token"], s_ref[sel_r["parent"], sel_r["token"]])
             np.testing.assert_array_equal(anc[r][:K, :t + 1], decs[r].anc)
             np.testing.assert_array_equal(tok[r][:K, :t + 1], decs[r].tokens)
             assert np.all(np.abs(cum[r][:K] - decs[r].cum) <= tol * np.maximum(1, np.abs(decs[r].cum)))
     say(f"end-to-end boundary swaps vs the oracle's own top-W: {swaps}")
+
+
+def test_tolerance_is_tighter_than_stated():
+    """The bars these tests use are at or below the ones stated for the method."""
+    from gpu_harness import TOL_STATED
+    assert all(TOL[k] <= TOL_STATED[k] for k in TOL)
 
 
 @pytest.mark.parametrize("name", ["batch", "stress", "growing"])
@@ -204,12 +223,14 @@ def test_full_size_forced_sampled(name):
     sampled requests against exact float64 rescoring."""
     wl = synth.get(name)
     R = wl.R
-    exact = (0, R - 1)
-    heads = (0, wl.H - 1)
-    g = GpuDecode(wl, exact=exact)
+    # eight requests, one in each XCD's share of the step kernel's grid, and the first,
+    # middle and last head; the selection is rescored on three of them
+    exact = xcd_spread(R)
+    heads = (0, wl.H // 2, wl.H - 1)
+    rescored = (exact[0], exact[len(exact) // 2], exact[-1])
+    g = GpuDecode(wl, exact=exact, exact_heads=heads)
     tol = TOL[wl.io]
-    decs = {r: oracle.FullStateDecoder(g.S_exact[r][list(heads)].astype(np.float64), wl.width(0))
-            for r in exact}
+    decs = {r: oracle.FullStateDecoder(g.S_exact[r].astype(np.float64), wl.width(0)) for r in exact}
     anc_ref = [np.zeros((wl.width(0), 0), np.int32) for _ in range(R)]
     g.init()
     for t in range(wl.T):
@@ -223,6 +244,7 @@ def test_full_size_forced_sampled(name):
         for r in exact:
             _cmp_gdn(wl, decs[r], g, r, t, o, dpool, tol, heads=heads)
             decs[r].advance(t, fp[r], ft[r], np.zeros(K))
+        for r in rescored:
             sel_r = {k: v[r] for k, v in sel.items()}
             check_selection(o[r], cum_before[r][:wl.width(t)], g.Wout64, K, sel_r, f"r={r} t={t}")
         for r in range(R):
@@ -491,6 +513,11 @@ def test_nan_scores_terminate():
     g.o[0][0, :, 3, :] = float("nan")
     sel = g.select(0)
     K = wl.width(1)
+    # NaN ranks below every number: with 127 finite beams of 256 codes each, the NaN
+    # beam is never chosen, and no shortfall is flagged
+    assert not np.any(sel["parent"][0] == 3)
+    assert np.all(np.isfinite(sel["score"][0]))
+    assert g.export(B.GDN_EXPORT_STATUS)[0] == 0
     assert np.all((sel["parent"][0] >= 0) & (sel["parent"][0] < wl.width(0)))
     assert np.all((sel["token"][0] >= 0) & (sel["token"][0] < wl.V))
     anc = g.export(B.GDN_EXPORT_ANCESTRY)
