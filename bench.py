@@ -6,14 +6,25 @@ every SID step t: gdn_beam_step (fused projection + replay + update + record
 append) and gdn_beam_select (scoring, exact global top-W, ancestry remap).
 value = beam transitions (sum over steps of R*H*W_t) per second of wall time.
 
+The headline workload is the large-beam stress decode (R = 64, H = 16, d = 128,
+W = 1024, V = 8192, T = 4) with its heavy fan-out parent maps (forced mode: 80% of
+the children draw from the top 10% of the parents).  The growing-width decode
+(d_v = 256, W 64 -> 1024) and the batch decode (W = 256, V = 1024) run after it in
+the same process and are reported under "extra", each in its own default mode.
+
 The timed decodes run back to back with nothing else on the stream.  A second run
 of the same decodes has every step launch record its own start and end (HIP events
 stamped by the dispatch, gdn_beam_time_steps); the step kernel's achieved
 algorithmic bandwidth over those launches is reported against the 8 TB/s HBM peak.
-A third pass times the select calls between HIP events.  The CPU oracle (float64 FullState) is timed on a
-bounded sample of the same workload.
+A third pass times the select calls between HIP events.  The CPU oracle (float64
+FullState) is timed on a bounded sample of the headline workload.
 
-    python bench.py [--workload batch|stress|growing|single|tiny] [--steps K] [--warmup W]
+    python bench.py [--workload stress|growing|batch|...] [--mode forced|select]
+                    [--extra growing,batch] [--steps K] [--warmup W]
+
+Counter summaries (host side, after rocprofv3 runs of this script):
+
+    python bench.py --traffic-from FETCH_DIR WRITE_DIR --bench-json FILE --workload NAME
 """
 from __future__ import annotations
 
@@ -41,8 +52,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="batch")
-    p.add_argument("--mode", choices=["select", "forced"], default="select")
+    p.add_argument("--workload", default="stress")
+    p.add_argument("--mode", choices=["select", "forced"], default=None,
+                   help="forced: the workload's seed-fixed parent maps drive the beams (the "
+                        "top-W is still computed); select: the top-W drives them.  Default: "
+                        "forced for heavy fan-out parent maps, select otherwise")
+    p.add_argument("--extra", default="growing,batch",
+                   help="comma-separated workloads run after the headline one and reported "
+                        "under 'extra' ('' for none)")
     p.add_argument("--path", choices=["records", "fullstate"], default="records",
                    help="records: transition records and replay (gdn_beam_step); fullstate: "
                         "the per-beam state baseline (gdn_fullstate_step)")
@@ -52,6 +69,11 @@ def parse():
     p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                    help="first copy MIB MiB device-to-device 3 times (a plain copy of known size "
                         "for scaling hardware byte counters)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                   help="host only: summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
+                        "of this script into profiles/step_kernel_<workload>_traffic.json")
+    p.add_argument("--bench-json", default=None,
+                   help="with --traffic-from: the JSON line the profiled run printed")
     p.add_argument("--flush-mall", choices=["read", "write"], default=None,
                    help="cold-cache timing: read (or write) 1 GiB of scratch before every step "
                         "launch, so neither L2 nor the 256 MiB last-level cache holds its inputs; "
@@ -84,16 +106,26 @@ def step_bytes(wl, t, distinct):
     return total
 
 
-def fullstate_bytes(wl, t):
-    """Algorithmic HBM bytes of one gdn_fullstate_step launch at step t: per beam the
-    parent's state (4 d_v d_k; at t = 0 the shared S_ctx, once per (request, head)),
-    the new state (4 d_v d_k), q, k, v (e each), alpha, beta (8) and o_t (4 d_v); per
-    request the parent indices (4 W_t)."""
+def fullstate_bytes(wl, t, parents=None):
+    """Algorithmic HBM bytes of one gdn_fullstate_step launch at step t.
+
+    Per beam: the new state (4 d_v d_k), q, k, v (e each), alpha, beta (8) and o_t
+    (4 d_v).  Parent states are read once each: at t = 0 the shared S_ctx once per
+    (request, head); at t >= 1 every distinct parent state once per head, where
+    `parents[r]` = distinct parents of request r's beams (siblings share their
+    parent's state).  Per request at t >= 1: the parent indices (4 W_t).
+    """
     e = 2 if wl.io == "bf16" else 4
     W = wl.width(t)
     st = 4 * wl.d_v * wl.d_k
-    per_rh = W * (st + e * (2 * wl.d_k + wl.d_v) + 8 + 4 * wl.d_v) + (st if t == 0 else W * st)
-    return wl.R * wl.H * per_rh + (4 * W * wl.R if t > 0 else 0)
+    per_beam = st + e * (2 * wl.d_k + wl.d_v) + 8 + 4 * wl.d_v
+    total = wl.R * wl.H * W * per_beam
+    if t == 0:
+        total += wl.R * wl.H * st
+    else:
+        n_par = wl.R * W if parents is None else int(np.sum(parents))
+        total += wl.H * st * n_par + 4 * W * wl.R
+    return total
 
 
 def step_flops(wl, t):
@@ -119,19 +151,24 @@ def decode_floor_s(wl, bytes_t):
     otherwise), which the selection needs to stay exact at fp32 precision.
     """
     bw = HBM_PEAK_GBS * 1e9
-    ew = 2 if wl.wout == "bf16" else 4
     dvp = max(wl.d_v, 32)
     total = wl.R * wl.H * (4 * wl.d_v * wl.d_k + 4 * dvp * wl.d_k) / bw
     for t in range(wl.T):
-        W, Wn = wl.width(t), wl.width(t + 1)
-        total += bytes_t[t] / bw
-        sel_bytes = wl.R * (4 * wl.H * W * wl.d_v + 4 * W + 12 * Wn + 8 * (t + 1) * Wn) + wl.d_v * wl.V * ew
-        if wl.wout == "bf16":
-            sel_flops, peak = 3 * 2 * wl.R * W * wl.d_v * wl.V, MFMA_BF16_PEAK
-        else:
-            sel_flops, peak = 2 * wl.R * W * wl.d_v * wl.V, MFMA_F32_PEAK
-        total += max(sel_bytes / bw, sel_flops / peak)
+        total += bytes_t[t] / bw + select_floor_s(wl, t)
     return total
+
+
+def select_floor_s(wl, t):
+    """Floor of one select(t) call: max(bytes / 8 TB/s, MFMA flops / dense peak)."""
+    bw = HBM_PEAK_GBS * 1e9
+    ew = 2 if wl.wout == "bf16" else 4
+    W, Wn = wl.width(t), wl.width(t + 1)
+    sel_bytes = wl.R * (4 * wl.H * W * wl.d_v + 4 * W + 12 * Wn + 8 * (t + 1) * Wn) + wl.d_v * wl.V * ew
+    if wl.wout == "bf16":
+        sel_flops, peak = 3 * 2 * wl.R * W * wl.d_v * wl.V, MFMA_BF16_PEAK
+    else:
+        sel_flops, peak = 2 * wl.R * W * wl.d_v * wl.V, MFMA_F32_PEAK
+    return max(sel_bytes / bw, sel_flops / peak)
 
 
 def copy_bandwidth(torch, dev, mib=1024, reps=10):
@@ -176,7 +213,26 @@ def load_traffic(wl_name):
     return d.get("bytes_per_decode")
 
 
-def cpu_baseline(args, wl):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((int(d.get("num_threads", 0)) for d in threadpool_info()
+                    if d.get("user_api") == "blas"), default=None)
+    except Exception:
+        return None
+
+
+def cpu_baseline(args, wl, mode):
     """Time the float64 FullState oracle on the first requests of the workload."""
     import resource
     import oracle
@@ -195,9 +251,10 @@ def cpu_baseline(args, wl):
         t0 = time.perf_counter()
         for t in range(wl.T):
             o, _ = dec.step(t, *inputs[t])
-            fp, ft = forced[t] if args.mode == "forced" else (None, None)
+            fp, ft = forced[t] if mode == "forced" else (None, None)
             dec.select(t, o, Wout, wl.width(t + 1), fp, ft)
         t_tot += time.perf_counter() - t0
+        del dec, inputs
         rs += 1
         log(args, f"cpu oracle: {rs} request(s), {t_tot:.1f} s")
         if rs >= wl.R or t_tot >= args.cpu_seconds or t_tot / rs * (rs + 1) > 2 * args.cpu_seconds:
@@ -205,41 +262,28 @@ def cpu_baseline(args, wl):
     cpu1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu_s = (cpu1.ru_utime - cpu0.ru_utime) + (cpu1.ru_stime - cpu0.ru_stime)
     trans = rs * wl.H * sum(wl.width(t) for t in range(wl.T))
+    # busy cores: process CPU time over wall time (the prefill of each sampled request
+    # is outside the timed interval and inside the CPU-time window, a small excess)
     threads = max(1, round(cpu_s / max(t_tot, 1e-9)))
     return {"value": trans / t_tot, "unit": "beam-transitions/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{rs} of {wl.R} requests (all {wl.H} heads, {wl.T} steps, {args.mode} mode), "
-                      f"float64 FullState numpy, {t_tot:.1f} s; host has "
-                      f"{len(os.sched_getaffinity(0))} cores available"}
+            "kind": "oracle", "requests_sampled": rs,
+            "cpu_model": _cpu_model(), "blas_threads": _blas_threads(),
+            "cores_available": len(os.sched_getaffinity(0)),
+            "sample": f"{rs} of {wl.R} requests (all {wl.H} heads, {wl.T} steps, {mode} mode) of the "
+                      f"{wl.name} workload, float64 FullState numpy, {t_tot:.1f} s of decode steps; "
+                      f"requests are independent, so the rate scales to the whole batch"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): requests are "
-              "independent, so the one-GPU rate is one GPU's share of a sharded job.", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import synth
+def run_workload(args, wl, mode, torch, copy_gbs):
+    """Whole decodes of one workload: returns the measurement dict."""
+    import synth  # noqa: F401
     from synth import device as sdev
     from linear_attention_beam_amd import binding as B
     from linear_attention_beam_amd.decoder import BeamDecoder, prefill
 
-    wl = synth.get(args.workload)
     dev = torch.device("cuda")
     stream = torch.cuda.current_stream()
-    if args.copy_calib:
-        n = args.copy_calib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(args, f"copy calibration: 3 x {args.copy_calib} MiB device-to-device")
-        del src, dst
-    log(args, f"workload {wl.name}: {wl.summary}")
-    copy_gbs = copy_bandwidth(torch, dev)
-    log(args, f"device copy (read + write): {copy_gbs:.0f} GB/s")
+    log(args, f"workload {wl.name} ({mode} mode): {wl.summary}")
 
     # ---- inputs resident in HBM before timing
     dec = BeamDecoder(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, wl.io, wl.wout, H_K=wl.H_K)
@@ -258,7 +302,7 @@ def main():
              (("parent", torch.int32), ("token", torch.int32), ("score", torch.float32))}
             for t in range(wl.T)]
     forced = [(None, None)] * wl.T
-    if args.mode == "forced":
+    if mode == "forced":
         from synth import gen
         forced = [(torch.from_numpy(np.stack([gen.forced_parents(wl, r, t) for r in range(wl.R)])).to(dev),
                    torch.from_numpy(np.stack([gen.forced_tokens(wl, r, t) for r in range(wl.R)])).to(dev))
@@ -283,17 +327,21 @@ def main():
             dec.select(t, outs[t], Wout, wl.V, wl.width(t + 1), s["parent"], s["token"],
                        s["score"], forced[t][0], forced[t][1], stream)
 
-    # ---- distinct ancestor records per step (deterministic: same every decode)
-    distinct = []
+    # ---- distinct ancestor records and distinct parents per step (deterministic: the
+    # same every decode)
+    distinct, parents = [], []
     dec.init(S_ctx, wl.width(0), stream)
     for t in range(wl.T):
         anc = dec.export(B.GDN_EXPORT_ANCESTRY).cpu().numpy()
         W = wl.width(t)
         d = np.zeros(wl.R, dtype=np.int64)
+        pa = np.zeros(wl.R, dtype=np.int64)
         if t > 0:
             for r in range(wl.R):
                 d[r] = sum(len(np.unique(anc[r, :W, j])) for j in range(t))
+                pa[r] = len(np.unique(anc[r, :W, t - 1]))
         distinct.append(d)
+        parents.append(pa)
         x = inputs[t]
         gdn_step(t, x)
         s = sels[t]
@@ -306,13 +354,12 @@ def main():
     torch.cuda.synchronize()
 
     # ---- per-call times: an instrumented pass of the same decodes, HIP events recorded
-    # on the launch stream.  Each step(t) is issued rep times back to back between one
-    # pair of events (re-issuing step(t) rewrites the same values); select(t) runs once
-    # between its pair.  The select and init times come from here; the step times
-    # reported come from the timed decodes, except with a flush buffer.
-    # With a flush buffer, 1 GiB of it is read or written before every step launch
-    # (outside the events), so the launch finds none of its inputs in any cache.
-    def instrumented(n, rep, flush_buf=None):
+    # on the launch stream around init, every step(t) and every select(t).  The select
+    # and init times come from here; the step times reported come from the stamped
+    # launches, except with a flush buffer.  With a flush buffer, 1 GiB of it is read or
+    # written before every step launch (outside the events), so the launch finds none of
+    # its inputs in any cache.
+    def instrumented(n, flush_buf=None):
         evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(wl.T)]
                for _ in range(n)]
         evi = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
@@ -328,8 +375,7 @@ def main():
                     else:
                         flush_buf.sum()
                 evs[i][t][0].record(stream)
-                for _ in range(rep):
-                    gdn_step(t, x)
+                gdn_step(t, x)
                 evs[i][t][1].record(stream)
                 s = sels[t]
                 dec.select(t, outs[t], Wout, wl.V, wl.width(t + 1), s["parent"], s["token"],
@@ -340,7 +386,7 @@ def main():
         for i in range(n):
             it += evi[i][0].elapsed_time(evi[i][1])
             for t in range(wl.T):
-                st[t] += evs[i][t][0].elapsed_time(evs[i][t][1]) / rep
+                st[t] += evs[i][t][0].elapsed_time(evs[i][t][1])
                 se[t] += evs[i][t][1].elapsed_time(evs[i][t][2])
         return st / n, se / n, it / n
 
@@ -349,7 +395,7 @@ def main():
         # ---- timed region: K whole decodes back to back on the stream, nothing else on
         # it (a timing event between kernels costs the stream a few microseconds, and the
         # idle gap changes what the next launch finds in the caches)
-        # it)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
             decode()
@@ -366,21 +412,21 @@ def main():
         dec.time_steps(0)
         assert n_timed == n_flow * wl.T, n_timed
         step_ms = np.asarray(times, dtype=np.float64).reshape(n_flow, wl.T).mean(0)
-        alone_ms, sel_ms, _ = instrumented(n_flow, 1)
+        alone_ms, sel_ms, _ = instrumented(n_flow)
         log(args, f"step kernel ms per SID step alone between events: {np.round(alone_ms, 4).tolist()}")
     else:
         # ---- cold caches: K decodes whose every step launch follows a 1 GiB read or
         # write; the decode time is the sum of its event-timed init, step and select
         # intervals
         flush_buf = torch.zeros(256 << 20, dtype=torch.float32, device=dev)
-        step_ms, sel_ms, init_ms = instrumented(args.steps, 1, flush_buf)
+        step_ms, sel_ms, init_ms = instrumented(args.steps, flush_buf)
         elapsed = (init_ms + step_ms.sum() + sel_ms.sum()) * 1e-3 * args.steps
         del flush_buf
     value = trans * args.steps / elapsed
     if states is None:
         bytes_t = [step_bytes(wl, t, distinct[t]) for t in range(wl.T)]
     else:
-        bytes_t = [fullstate_bytes(wl, t) for t in range(wl.T)]
+        bytes_t = [fullstate_bytes(wl, t, parents[t]) for t in range(wl.T)]
     achieved = sum(bytes_t) / (step_ms.sum() * 1e-3) / 1e9
     traffic = load_traffic(wl.name) if states is None else None
     gdn_rate = trans / (step_ms.sum() * 1e-3)
@@ -393,26 +439,31 @@ def main():
               f"{np.round(sel_ms, 4).tolist()}")
     log(args, f"algorithmic bytes per step launch: {bytes_t}; distinct ancestors per request "
               f"(mean) {[float(d.mean()) for d in distinct]}")
-
+    ms_decode = elapsed / args.steps * 1e3
+    sel_floor = [select_floor_s(wl, t) * 1e3 for t in range(wl.T)]
     res = {
-        "metric": METRIC, "value": value, "unit": "beam-transitions/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "R": wl.R, "H": wl.H, "d_k": wl.d_k, "d_v": wl.d_v,
-                   "T": wl.T, "W_t": list(wl.widths), "V": wl.V, "io_dtype": wl.io,
-                   "state_dtype": "f32", "mode": args.mode, "path": args.path,
-                   "parallelism": "single GPU", "cache": f"cold ({args.flush_mall} flush)" if args.flush_mall else "pipeline"},
+        "value": value, "ms_per_decode": ms_decode, "ms_per_sid_step": ms_decode / wl.T,
+        "dtype": wl.io,
+        "config": {"workload": wl.name, "R": wl.R, "H": wl.H, "H_K": wl.hk, "d_k": wl.d_k,
+                   "d_v": wl.d_v, "T": wl.T, "W_t": list(wl.widths), "V": wl.V, "io_dtype": wl.io,
+                   "state_dtype": "f32", "mode": mode,
+                   "parents": wl.parents if mode == "forced" else "top-W", "path": args.path,
+                   "parallelism": "single GPU",
+                   "cache": f"cold ({args.flush_mall} flush)" if args.flush_mall else "pipeline"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gdn step_kernel" if states is None else "gdn fullstate_kernel",
+                     "scope": "the step kernel's launches only (select excluded; see decode_roofline)",
                      "bytes_per_decode": int(sum(bytes_t)),
+                     "bytes_per_launch": [int(b) for b in bytes_t],
                      "copy_GBs": copy_gbs,
                      "launches_per_decode": wl.T},
         "gdn_step_rate": gdn_rate,
         "gdn_step_ms": float(step_ms.sum()),
         "step_ms_per_t": [float(x) for x in step_ms],
         "select_ms": float(sel_ms.sum()),
+        "select_ms_per_t": [float(x) for x in sel_ms],
+        "select_floor_ms_per_t": sel_floor,
         "step_tflops": flops / (step_ms.sum() * 1e-3) / 1e12,
         "decode_roofline": (None if states is not None else
                             {"floor_ms": decode_floor_s(wl, bytes_t) * 1e3,
@@ -420,9 +471,163 @@ def main():
                              "basis": "sum over init, step and select launches of max(algorithmic "
                                       "bytes / 8 TB/s, MFMA flops / dense peak)"}),
     }
+    dec.close()
+    return res
+
+
+def default_mode(wl, asked):
+    if asked is not None:
+        return asked
+    return "forced" if wl.parents == "heavy" else "select"
+
+
+def main():
+    args = parse()
+    if args.traffic_from:
+        sys.exit(traffic_summary(args))
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): requests are "
+              "independent, so the one-GPU rate is one GPU's share of a sharded job.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+
+    wl = synth.get(args.workload)
+    mode = default_mode(wl, args.mode)
+    dev = torch.device("cuda")
+    if args.copy_calib:
+        n = args.copy_calib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(args, f"copy calibration: 3 x {args.copy_calib} MiB device-to-device")
+        del src, dst
+    copy_gbs = copy_bandwidth(torch, dev)
+    log(args, f"device copy (read + write): {copy_gbs:.0f} GB/s")
+
+    head = run_workload(args, wl, mode, torch, copy_gbs)
+    torch.cuda.empty_cache()
+    extra = {}
+    for name in [x for x in args.extra.split(",") if x and x != wl.name]:
+        ew = synth.get(name)
+        r = run_workload(args, ew, default_mode(ew, None), torch, copy_gbs)
+        torch.cuda.empty_cache()
+        extra[name] = {k: r[k] for k in ("value", "ms_per_decode", "ms_per_sid_step", "gdn_step_ms",
+                                         "select_ms_per_t", "select_floor_ms_per_t", "step_ms_per_t",
+                                         "gdn_step_rate")}
+        extra[name]["config"] = r["config"]
+        extra[name]["roofline"] = {k: r["roofline"][k] for k in ("achieved", "frac", "traffic",
+                                                                 "bytes_per_decode")}
+        extra[name]["decode_roofline"] = r["decode_roofline"]
+        log(args, f"extra {name}: {r['value']:.4g} beam-transitions/s, step frac "
+                  f"{r['roofline']['frac']:.3f}")
+
+    res = {
+        "metric": METRIC, "value": head["value"], "unit": "beam-transitions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        # one bench step is one whole decode (init + T SID steps of step and select)
+        "ms_per_step": head["ms_per_decode"], "ms_per_decode": head["ms_per_decode"],
+        "ms_per_sid_step": head["ms_per_sid_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"],
+        "data": "synthetic (seeded draws of the pages' input laws; no dataset or weights)",
+        "config": head["config"],
+    }
+    for k in ("roofline", "gdn_step_rate", "gdn_step_ms", "step_ms_per_t", "select_ms",
+              "select_ms_per_t", "select_floor_ms_per_t", "step_tflops", "decode_roofline"):
+        res[k] = head[k]
+    if extra:
+        res["extra"] = extra
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args, wl)
+        res["cpu_baseline"] = cpu_baseline(args, wl, mode)
     print(json.dumps(res), flush=True)
+
+
+# ---------------------------------------------------------------- counter summaries
+
+def read_counters(d):
+    """rocprofv3 --pmc csv output under directory d: per dispatch (in dispatch order)
+    [kernel name, {counter: value summed over the rows of that dispatch}]."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *counter_collection.csv under {d}")
+    rows = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                did = int(row.get("Dispatch_Id") or row["Correlation_Id"])
+                ent = rows.setdefault(did, [row["Kernel_Name"], {}])
+                name = row["Counter_Name"]
+                ent[1][name] = ent[1].get(name, 0.0) + float(row["Counter_Value"])
+    return [rows[k] for k in sorted(rows)]
+
+
+def step_t_of(kernel_name):
+    """SID step of a step_kernel<DK, DV, BF16, t> dispatch (None for other kernels)."""
+    if "step_kernel<" not in kernel_name or "fullstate" in kernel_name:
+        return None
+    inner = kernel_name.split("step_kernel<", 1)[1].split(">", 1)[0]
+    return int(inner.split(",")[-1].strip())
+
+
+def traffic_summary(args):
+    """profiles/step_kernel_<workload>_traffic.json from a FETCH_SIZE and a WRITE_SIZE run
+    of this script with --copy-calib MIB (the first three dispatches are MIB MiB device
+    copies: each reads and writes MIB MiB, which scales the counters to bytes)."""
+    fetch_dir, write_dir = args.traffic_from
+    fetch, write = read_counters(fetch_dir), read_counters(write_dir)
+    if not args.bench_json:
+        print("--traffic-from needs --bench-json (the profiled run's JSON line)", file=sys.stderr)
+        return 2
+    bj = None
+    for line in open(args.bench_json):
+        line = line.strip()
+        if line.startswith("{"):
+            bj = json.loads(line)
+    alg = bj["roofline"]["bytes_per_launch"]
+    if not args.copy_calib:
+        print("--traffic-from needs --copy-calib MIB (the size the profiled run copied)", file=sys.stderr)
+        return 2
+    kib = args.copy_calib * 1024.0
+    ff = kib / np.mean([c.get("FETCH_SIZE", np.nan) for _, c in fetch[:3]])
+    wf = kib / np.mean([c.get("WRITE_SIZE", np.nan) for _, c in write[:3]])
+    per_t = {}
+    for (name, c) in fetch:
+        t = step_t_of(name)
+        if t is not None:
+            per_t.setdefault(t, [[], []])[0].append(c["FETCH_SIZE"])
+    for (name, c) in write:
+        t = step_t_of(name)
+        if t is not None:
+            per_t.setdefault(t, [[], []])[1].append(c["WRITE_SIZE"])
+    T = len(alg)
+    hbm = []
+    rows = []
+    for t in range(T):
+        fk, wk = float(np.mean(per_t[t][0])), float(np.mean(per_t[t][1]))
+        b = (fk * ff + wk * wf) * 1024.0
+        hbm.append(int(b))
+        rows.append(f"| {t} | {fk:.0f} | {wk:.0f} | {alg[t] / 1e6:.1f} | {b / 1e6:.1f} | {b / alg[t]:.3f} |")
+    out = {"kernel_sha": kernel_hash(), "workload": args.workload, "unit": "bytes",
+           "bytes_per_launch": hbm, "bytes_per_decode": int(sum(hbm)),
+           "algorithmic_per_launch": [int(a) for a in alg],
+           "fetch_factor": float(ff), "write_factor": float(wf),
+           "dispatches_per_t": [len(per_t[t][0]) for t in range(T)],
+           "source": f"profiles/step_kernel_{args.workload}_counters.md"}
+    path = os.path.join(ROOT, "profiles", f"step_kernel_{args.workload}_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(f"wrote {path}")
+    print(f"fetch factor {ff:.4f}, write factor {wf:.4f}")
+    print("| t | FETCH_SIZE KiB | WRITE_SIZE KiB | algorithmic MB | HBM MB | ratio |")
+    print("|---|---|---|---|---|---|")
+    print("\n".join(rows))
+    tot_a, tot_b = sum(alg), sum(hbm)
+    print(f"| sum | | | {tot_a / 1e6:.1f} | {tot_b / 1e6:.1f} | {tot_b / tot_a:.3f} |")
+    return 0
 
 
 if __name__ == "__main__":

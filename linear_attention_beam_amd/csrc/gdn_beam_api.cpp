@@ -212,10 +212,15 @@ gdn_status gdn_fullstate_step(gdn_beam_ctx* ctx, int32_t t, const float* S_ctx, 
   return GDN_OK;
 }
 
-gdn_status gdn_beam_select(gdn_beam_ctx* ctx, int32_t t, const float* o, const void* Wout,
-                           int32_t V, int32_t W_next, const int32_t* forced_parent,
-                           const int32_t* forced_token, int32_t* parent, int32_t* token,
-                           float* score, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The checks of a select call, in order; GDN_OK when it may launch.
+gdn_status check_select(const gdn_beam_ctx* ctx, int32_t t, const float* o, const void* Wout,
+                        int32_t V, int32_t W_next, const int32_t* forced_parent,
+                        const int32_t* forced_token, const int32_t* parent, const int32_t* token,
+                        const float* score) {
   if (!ctx) return GDN_ERR_INVALID_ARG;
   if (!o || !Wout || !parent || !token || !score) return GDN_ERR_INVALID_ARG;
   if ((forced_parent == nullptr) != (forced_token == nullptr)) return GDN_ERR_INVALID_ARG;
@@ -230,8 +235,24 @@ gdn_status gdn_beam_select(gdn_beam_ctx* ctx, int32_t t, const float* o, const v
   if (t != ctx->t || !ctx->stepped) return GDN_ERR_BAD_STATE;
   if (V > c.V_max || W_next > c.W_max) return GDN_ERR_CAPACITY;
   if (int64_t(W_next) > int64_t(ctx->W_cur) * V) return GDN_ERR_INVALID_ARG;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_beam_select(gdn_beam_ctx* ctx, int32_t t, const float* o, const void* Wout,
+                           int32_t V, int32_t W_next, const int32_t* forced_parent,
+                           const int32_t* forced_token, int32_t* parent, int32_t* token,
+                           float* score, hipStream_t stream) {
+  const gdn_status st = check_select(ctx, t, o, Wout, V, W_next, forced_parent, forced_token,
+                                     parent, token, score);
+  if (st != GDN_OK) return st;
+  const gdn_beam_config& c = ctx->cfg;
   SelectArgs a{c.R, c.H, c.d_v, c.W_max, c.V_max, c.T_max, t, ctx->W_cur, V, W_next, c.wout_dtype,
-               o, Wout, forced_parent, forced_token, parent, token, score, ctx->ws, ctx->L};
+               o, Wout, forced_parent, forced_token, parent, token, score, ctx->ws, ctx->L,
+               static_cast<char*>(ctx->ws), ctx->L.S};
   int err = launch_select(a, stream);
   if (err) return hip_fail(err, "gdn_beam_select");
   ctx->t = t + 1;

@@ -26,17 +26,10 @@ struct SelState {
   uint32_t pad;
 };
 
-// Byte offsets of every region inside the caller's workspace (256-aligned).
-struct Layout {
-  size_t s_frag;      // [R,H] S_ctx in MFMA fragment order, 4*d_vp*d_k bytes each
-  size_t gtr_alpha;   // [R,H,T_max,W_max] f32
-  size_t gtr_delta;   // [R,H,T_max,W_max,d_v] f32
-  size_t gtr_key;     // [R,H,T_max,W_max,d_k] io dtype
-  size_t anc[2];      // [R,W_max,T_max] i32, ping-pong by step parity
-  size_t tok[2];      // [R,W_max,T_max] i32
-  size_t cum[2];      // [R,W_max] f32
-  size_t order[2];    // [R,W_max] i32 beam processing order of a step (siblings adjacent)
-  size_t opos[2];     // [R,W_max] i32 position of each beam in that order
+// Byte offsets of the per-call scratch of one selection (256-aligned): nothing in these
+// regions outlives a gdn_beam_select call.  Inside the workspace they follow the beam
+// state; a selection may also take them from another buffer laid out the same way.
+struct SelScratch {
   size_t z;           // [R,W_max,d_v] f32  head-summed outputs (fp32 codebook)
   size_t zf;          // [R,n_chunks(W_max),d_v/16,3,64] u32x4: z as bf16 hi/mid/lo MFMA operand
   size_t woutT;       // [V_max,d_v] wout dtype, codebook transposed
@@ -50,6 +43,21 @@ struct Layout {
   size_t groups;      // [R,max_groups] u32 refinement groups
   size_t gtiles;      // [R,max_groups,32] u32 the tiles of each group
   size_t rkeys;       // [R,W_max,kTile] u32 keys of the chosen tiles' candidates
+  size_t end;         // first byte past the regions (256-aligned)
+};
+
+// Byte offsets of every region inside the caller's workspace (256-aligned).
+struct Layout {
+  size_t s_frag;      // [R,H] S_ctx in MFMA fragment order, 4*d_vp*d_k bytes each
+  size_t gtr_alpha;   // [R,H,T_max,W_max] f32
+  size_t gtr_delta;   // [R,H,T_max,W_max,d_v] f32
+  size_t gtr_key;     // [R,H,T_max,W_max,d_k] io dtype
+  size_t anc[2];      // [R,W_max,T_max] i32, ping-pong by step parity
+  size_t tok[2];      // [R,W_max,T_max] i32
+  size_t cum[2];      // [R,W_max] f32
+  size_t order[2];    // [R,W_max] i32 beam processing order of a step (siblings adjacent)
+  size_t opos[2];     // [R,W_max] i32 position of each beam in that order
+  SelScratch S;       // the selection's per-call scratch
   size_t status;      // [64] i32
   size_t total;
 };
@@ -74,12 +82,35 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline int key_heads(const gdn_beam_config& c) { return c.H_K > 0 ? c.H_K : c.H; }
 
+// The selection's scratch regions of a configuration, laid out from byte `off`.
+inline SelScratch make_sel_scratch(const gdn_beam_config& c, size_t off) {
+  SelScratch S{};
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t R = c.R, W = c.W_max, V = c.V_max;
+  const size_t dv = c.d_v, ew = io_bytes(c.wout_dtype);
+  const size_t Vt = size_t(n_tiles(c.V_max));
+  S.z = take(R * W * dv * 4);
+  S.zf = take(R * size_t(n_chunks(c.W_max)) * 32 * dv * 6);
+  S.woutT = take(V * dv * ew);
+  S.tmax = take(R * Vt * W * 4);
+  S.lse_part = take(R * W * size_t(n_vgroups(c.V_max)) * 16);
+  S.lse = take(R * W * 4);
+  S.sel = take(R * sizeof(SelState));
+  S.cand = take(R * Vt * W * 4);
+  S.tiles = take(R * W * 4);
+  S.groups = take(R * size_t(max_groups(c.W_max, n_tiles(c.V_max))) * 4);
+  S.gtiles = take(R * size_t(max_groups(c.W_max, n_tiles(c.V_max))) * 32 * 4);
+  S.rkeys = take(R * W * kTile * 4);
+  S.end = off;
+  return S;
+}
+
 inline Layout make_layout(const gdn_beam_config& c) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-  const size_t R = c.R, H = c.H, T = c.T_max, W = c.W_max, V = c.V_max;
-  const size_t dk = c.d_k, dv = c.d_v, e = io_bytes(c.io_dtype), ew = io_bytes(c.wout_dtype);
+  const size_t R = c.R, H = c.H, T = c.T_max, W = c.W_max;
+  const size_t dk = c.d_k, dv = c.d_v, e = io_bytes(c.io_dtype);
   L.s_frag = take(R * H * 4 * size_t(dvp_of(c.d_v)) * dk);
   L.gtr_alpha = take(R * H * T * W * 4);
   L.gtr_delta = take(R * H * T * W * dv * 4);
@@ -89,19 +120,8 @@ inline Layout make_layout(const gdn_beam_config& c) {
   for (int i = 0; i < 2; ++i) L.cum[i] = take(R * W * 4);
   for (int i = 0; i < 2; ++i) L.order[i] = take(R * W * 4);
   for (int i = 0; i < 2; ++i) L.opos[i] = take(R * W * 4);
-  const size_t Vt = size_t(n_tiles(c.V_max));
-  L.z = take(R * W * dv * 4);
-  L.zf = take(R * size_t(n_chunks(c.W_max)) * 32 * dv * 6);
-  L.woutT = take(V * dv * ew);
-  L.tmax = take(R * Vt * W * 4);
-  L.lse_part = take(R * W * size_t(n_vgroups(c.V_max)) * 16);
-  L.lse = take(R * W * 4);
-  L.sel = take(R * sizeof(SelState));
-  L.cand = take(R * Vt * W * 4);
-  L.tiles = take(R * W * 4);
-  L.groups = take(R * size_t(max_groups(c.W_max, n_tiles(c.V_max))) * 4);
-  L.gtiles = take(R * size_t(max_groups(c.W_max, n_tiles(c.V_max))) * 32 * 4);
-  L.rkeys = take(R * W * kTile * 4);
+  L.S = make_sel_scratch(c, off);
+  off = L.S.end;
   L.status = take(64 * 4);
   L.total = off;
   return L;
@@ -135,8 +155,10 @@ struct SelectArgs {
   const int32_t *forced_parent, *forced_token;
   int32_t *parent, *token;
   float* score;
-  void* ws;
+  void* ws;               // workspace: beam state, ancestry, status
   Layout L;
+  char* scr;              // base of the selection scratch regions S (offsets from scr)
+  SelScratch S;
 };
 
 struct PrefillArgs {

@@ -1517,18 +1517,20 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   const size_t tstride = size_t(n_tiles(a.V_max)) * a.W_max;
   const int G_max = max_groups(a.W_max, n_tiles(a.V_max));
   const int split = a.wout_dtype == GDN_BF16;
-  float* z = reinterpret_cast<float*>(ws + L.z);
-  u32x4* zf = reinterpret_cast<u32x4*>(ws + L.zf);
-  void* woutT = ws + L.woutT;
-  float* tmax = reinterpret_cast<float*>(ws + L.tmax);
-  float4* lse_part = reinterpret_cast<float4*>(ws + L.lse_part);
-  float* lse = reinterpret_cast<float*>(ws + L.lse);
-  SelState* sel = reinterpret_cast<SelState*>(ws + L.sel);
-  uint32_t* cand = reinterpret_cast<uint32_t*>(ws + L.cand);
-  uint32_t* tiles = reinterpret_cast<uint32_t*>(ws + L.tiles);
-  uint32_t* groups = reinterpret_cast<uint32_t*>(ws + L.groups);
-  uint32_t* gtiles = reinterpret_cast<uint32_t*>(ws + L.gtiles);
-  uint32_t* rkeys = reinterpret_cast<uint32_t*>(ws + L.rkeys);
+  char* scr = a.scr;
+  const SelScratch& S = a.S;
+  float* z = reinterpret_cast<float*>(scr + S.z);
+  u32x4* zf = reinterpret_cast<u32x4*>(scr + S.zf);
+  void* woutT = scr + S.woutT;
+  float* tmax = reinterpret_cast<float*>(scr + S.tmax);
+  float4* lse_part = reinterpret_cast<float4*>(scr + S.lse_part);
+  float* lse = reinterpret_cast<float*>(scr + S.lse);
+  SelState* sel = reinterpret_cast<SelState*>(scr + S.sel);
+  uint32_t* cand = reinterpret_cast<uint32_t*>(scr + S.cand);
+  uint32_t* tiles = reinterpret_cast<uint32_t*>(scr + S.tiles);
+  uint32_t* groups = reinterpret_cast<uint32_t*>(scr + S.groups);
+  uint32_t* gtiles = reinterpret_cast<uint32_t*>(scr + S.gtiles);
+  uint32_t* rkeys = reinterpret_cast<uint32_t*>(scr + S.rkeys);
   float* cum = reinterpret_cast<float*>(ws + L.cum[par]);
   float* cum_next = reinterpret_cast<float*>(ws + L.cum[par ^ 1]);
   int32_t* anc = reinterpret_cast<int32_t*>(ws + L.anc[par]);

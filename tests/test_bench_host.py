@@ -60,19 +60,31 @@ def test_step_bytes_term_by_term(name, H_K):
 
 
 def test_fullstate_bytes_term_by_term():
+    """Every beam writes its state; each distinct parent state is read once per head
+    (S_ctx once per (request, head) at t = 0)."""
     b = _bench()
     wl = synth.get("batch")
     e = 2
     st = 4 * wl.d_v * wl.d_k
+    rng = np.random.default_rng(3)
     for t in range(wl.T):
         W = wl.width(t)
-        per_beam = st + st + e * (2 * wl.d_k + wl.d_v) + 8 + 4 * wl.d_v   # parent, new, q k v, gates, o
-        expect = wl.R * wl.H * W * per_beam
-        if t == 0:
-            expect += wl.R * wl.H * st - wl.R * wl.H * W * st          # parents: S_ctx once
-        else:
-            expect += 4 * W * wl.R                                      # parent indices
-        assert b.fullstate_bytes(wl, t) == expect
+        parents = rng.integers(1, W + 1, size=wl.R) if t else np.zeros(wl.R, np.int64)
+        expect = 0
+        for r in range(wl.R):
+            for _ in range(W):
+                expect += wl.H * (st                                   # the new state
+                                  + e * (2 * wl.d_k + wl.d_v)          # q, k, v
+                                  + 8                                  # alpha, beta
+                                  + 4 * wl.d_v)                        # o_t
+            if t == 0:
+                expect += wl.H * st                                    # S_ctx, once
+            else:
+                expect += wl.H * st * int(parents[r])                  # each distinct parent once
+                expect += 4 * W                                        # parent indices
+        assert b.fullstate_bytes(wl, t, parents) == expect
+    # siblings share a parent: fewer distinct parents, fewer bytes
+    assert b.fullstate_bytes(wl, 1, np.full(wl.R, 10)) < b.fullstate_bytes(wl, 1, np.full(wl.R, 200))
 
 
 def test_traffic_needs_the_current_sources(monkeypatch):
@@ -88,14 +100,70 @@ def test_traffic_needs_the_current_sources(monkeypatch):
     assert b.load_traffic("no_such_workload") is None
 
 
-def test_cpu_baseline_on_tiny():
+@pytest.mark.parametrize("mode", ["select", "forced"])
+def test_cpu_baseline_on_tiny(mode):
     b = _bench()
-    args = argparse.Namespace(mode="select", cpu_seconds=2.0, quiet=True)
+    args = argparse.Namespace(cpu_seconds=2.0, quiet=True)
     wl = synth.get("tiny")
-    res = b.cpu_baseline(args, wl)
+    res = b.cpu_baseline(args, wl, mode)
     assert res["kind"] == "oracle" and res["unit"] == "beam-transitions/s"
     assert res["value"] > 0 and res["cores"] >= 1
-    assert "1 of 1 requests" in res["sample"]
+    assert res["requests_sampled"] == 1 and "1 of 1 requests" in res["sample"]
+    assert mode in res["sample"]
+    assert res["cores_available"] >= 1 and isinstance(res["cpu_model"], str)
+
+
+def test_default_modes():
+    """The heavy fan-out workload runs on its seed-fixed parent maps by default; the
+    others let the top-W drive the beams."""
+    b = _bench()
+    assert b.default_mode(synth.get("stress"), None) == "forced"
+    assert b.default_mode(synth.get("batch"), None) == "select"
+    assert b.default_mode(synth.get("growing"), None) == "select"
+    assert b.default_mode(synth.get("stress"), "select") == "select"
+
+
+def _write_pmc(d, counter, per_dispatch):
+    """A rocprofv3-style counter csv: one row per (dispatch, dimension)."""
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "x_counter_collection.csv"), "w") as f:
+        f.write("Correlation_Id,Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (name, val) in enumerate(per_dispatch):
+            # the value split over two rows of the same dispatch, as per-XCD dimensions are
+            f.write(f'{i},{i + 1},"{name}",{counter},{val / 2}\n')
+            f.write(f'{i},{i + 1},"{name}",{counter},{val / 2}\n')
+
+
+def test_traffic_summary_from_counters(tmp_path, monkeypatch):
+    """Counter bytes per step launch: FETCH_SIZE and WRITE_SIZE averaged per SID step
+    over the step kernel's dispatches, scaled by three device copies of known size."""
+    b = _bench()
+    copy = [("copy", 0)] * 3
+    fetch = [("copy_kernel", 1000.0)] * 3 + [
+        ("void gdn::step_kernel<128, 128, true, 0>(gdn::StepK)", 100.0),
+        ("void gdn::logits_kernel<128, true>(gdn::LogitsK)", 7.0),
+        ("void gdn::step_kernel<128, 128, true, 1>(gdn::StepK)", 150.0),
+        ("void gdn::step_kernel<128, 128, true, 0>(gdn::StepK)", 120.0),
+        ("void gdn::step_kernel<128, 128, true, 1>(gdn::StepK)", 170.0)]
+    write = [("copy_kernel", 4000.0)] * 3 + [(n, 2 * v) for n, v in fetch[3:]]
+    del copy
+    _write_pmc(str(tmp_path / "f"), "FETCH_SIZE", fetch)
+    _write_pmc(str(tmp_path / "w"), "WRITE_SIZE", write)
+    bj = tmp_path / "b.json"
+    bj.write_text("noise\n" + json.dumps({"roofline": {"bytes_per_launch": [1e6, 2e6]}}) + "\n")
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    args = argparse.Namespace(traffic_from=[str(tmp_path / "f"), str(tmp_path / "w")],
+                              bench_json=str(bj), copy_calib=4, workload="wl")
+    assert b.traffic_summary(args) == 0
+    d = json.load(open(tmp_path / "profiles" / "step_kernel_wl_traffic.json"))
+    ff, wf = 4096.0 / 1000.0, 4096.0 / 4000.0
+    assert d["fetch_factor"] == pytest.approx(ff) and d["write_factor"] == pytest.approx(wf)
+    exp0 = (110.0 * ff + 220.0 * wf) * 1024
+    exp1 = (160.0 * ff + 320.0 * wf) * 1024
+    assert d["bytes_per_launch"] == [int(exp0), int(exp1)]
+    assert d["dispatches_per_t"] == [2, 2]
+    assert d["kernel_sha"] == b.kernel_hash()
 
 
 @pytest.mark.parametrize("name", ["batch", "tiny", "growing"])

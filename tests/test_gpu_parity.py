@@ -392,7 +392,14 @@ def test_step_closed_forms(name):
     d = g.export(B.GDN_EXPORT_GTR_DELTA)[0][:, 0, :wl.width(0)]
     kq = np.sum(k * q, axis=-1)
     assert rel_err(d, be[..., None] * v) <= tol
-    assert rel_err(o, be[..., None] * v * kq[..., None]) <= tol
+    # o = delta (k . q): the rounding of a dot product is bounded relative to
+    # sum |k_i q_i|, not to |k . q|, which some of the beams' random unit vectors make
+    # nearly zero (the per-vector relative error then measures cancellation, not the
+    # kernel), so the error is taken relative to |beta v|_inf sum |k_i q_i|
+    den = np.max(np.abs(be[..., None] * v), axis=-1) * np.sum(np.abs(k * q), axis=-1)
+    err = np.max(np.abs(o - be[..., None] * v * kq[..., None]), axis=-1) / den
+    say(f"closed form S_ctx = 0: error relative to the dot product's condition {err.max():.3e}")
+    assert err.max() <= tol
     g.S_ctx.copy_(torch.from_numpy(g.S_exact[0][None]).to(g.dev))
     g.inputs[0]["beta"].zero_()
     g.init()
