@@ -124,6 +124,31 @@ gdn_status gdn_beam_select(gdn_beam_ctx* ctx, int32_t t, const float* o,
                            int32_t* parent, int32_t* token, float* score,
                            hipStream_t stream);
 
+/* Size of the static selection scratch gdn_beam_select_static uses, per GPU. */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, results, errors and
+ * state machine as gdn_beam_select, and the same kernels; only the selection's per-call
+ * scratch (head sums, operand fragments, transposed codebook, tile maxima, candidate
+ * lists, refined keys) lives in a static device array of GDN_STATIC_SCRATCH_BYTES
+ * instead of the context's workspace (the beam state, ancestry and status stay there).
+ * The call allocates nothing.  Each GPU the library runs on holds its own copy of the
+ * array from this call's first use on it until the process ends; the device of
+ * `stream` must be the current device.  The scratch a configuration needs grows as
+ * R * W_max * (V_max / 8 + 6 d_v + ...) bytes (about 10 MiB for R = 32, W_max = 256,
+ * V_max = 1024, d_v = 128); a context that needs more than the array is refused with
+ * GDN_ERR_CAPACITY before any other check, and gdn_beam_last_error() states the size
+ * needed.  Every call on one GPU shares that GPU's array and leaves its contents
+ * there: calls that overlap on one GPU (other streams, other threads, other contexts)
+ * race and must be serialised by the caller.  Nothing in the array needs to start at
+ * zero: every call writes what it reads. */
+gdn_status gdn_beam_select_static(gdn_beam_ctx* ctx, int32_t t, const float* o,
+                                  const void* Wout, int32_t V, int32_t W_next,
+                                  const int32_t* forced_parent, const int32_t* forced_token,
+                                  int32_t* parent, int32_t* token, float* score,
+                                  hipStream_t stream);
+
 /* Bytes of the state buffer gdn_fullstate_step needs (host only):
  * 2 * R*H*W_max*d_v*d_k*4, two generations of one fp32 d_v x d_k state per
  * (request, head, beam). */
@@ -192,7 +217,8 @@ gdn_status gdn_beam_step_times(float* ms /* host */, int32_t cap, int32_t* n /* 
 /* Static description of a status code. */
 const char* gdn_beam_status_str(gdn_status s);
 
-/* Text of the last GDN_ERR_HIP on the calling thread ("" if none). */
+/* Text of the last GDN_ERR_HIP on the calling thread, or of a static-scratch capacity
+ * refusal of gdn_beam_select_static ("" if none). */
 const char* gdn_beam_last_error(void);
 
 /* Prefill (eq. 3, section 1.2): S_out[r,h] = the state after request r's prompt,

@@ -25,7 +25,9 @@ GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_beam_workspace_bytes", "gdn_beam_init", "gdn_beam_step", "gdn_beam_select",
            "gdn_beam_export", "gdn_beam_export_bytes", "gdn_beam_query", "gdn_beam_destroy",
            "gdn_beam_status_str", "gdn_beam_last_error", "gdn_beam_prefill",
-           "gdn_fullstate_bytes", "gdn_fullstate_step", "gdn_beam_time_steps", "gdn_beam_step_times")
+           "gdn_fullstate_bytes", "gdn_fullstate_step", "gdn_beam_time_steps", "gdn_beam_step_times",
+           "gdn_beam_select_static")
+GDN_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class gdn_beam_config(ctypes.Structure):
@@ -72,6 +74,7 @@ def _load():
         "gdn_beam_init": (st, [POINTER(gdn_beam_config), vp, i32, vp, c_size_t, vp, POINTER(vp)]),
         "gdn_beam_step": (st, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         "gdn_beam_select": (st, [vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "gdn_beam_select_static": (st, [vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]),
         "gdn_beam_export": (st, [vp, i32, vp, c_size_t, vp]),
         "gdn_beam_export_bytes": (st, [vp, i32, POINTER(c_size_t)]),
         "gdn_beam_query": (st, [vp, POINTER(i32), POINTER(i32)]),
@@ -143,6 +146,13 @@ def gdn_beam_select(ctx, t, o, Wout, V, W_next, forced_parent, forced_token, par
     _check(_lib.gdn_beam_select(ctx, t, _ptr(o), _ptr(Wout), V, W_next, _ptr(forced_parent),
                                 _ptr(forced_token), _ptr(parent), _ptr(token), _ptr(score),
                                 _stream(stream)), "gdn_beam_select")
+
+
+def gdn_beam_select_static(ctx, t, o, Wout, V, W_next, forced_parent, forced_token, parent, token,
+                           score, stream=None):
+    _check(_lib.gdn_beam_select_static(ctx, t, _ptr(o), _ptr(Wout), V, W_next, _ptr(forced_parent),
+                                       _ptr(forced_token), _ptr(parent), _ptr(token), _ptr(score),
+                                       _stream(stream)), "gdn_beam_select_static")
 
 
 def gdn_beam_export_bytes(ctx, what) -> int:

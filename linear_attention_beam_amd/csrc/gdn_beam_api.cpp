@@ -261,6 +261,38 @@ gdn_status gdn_beam_select(gdn_beam_ctx* ctx, int32_t t, const float* o, const v
   return GDN_OK;
 }
 
+gdn_status gdn_beam_select_static(gdn_beam_ctx* ctx, int32_t t, const float* o, const void* Wout,
+                                  int32_t V, int32_t W_next, const int32_t* forced_parent,
+                                  const int32_t* forced_token, int32_t* parent, int32_t* token,
+                                  float* score, hipStream_t stream) {
+  if (ctx) {
+    // the configuration's selection scratch, laid out from the start of the array
+    const SelScratch S = make_sel_scratch(ctx->cfg, 0);
+    if (S.end > kStaticScratchBytes) {
+      g_last_error = "gdn_beam_select_static: the configuration needs " + std::to_string(S.end) +
+                     " bytes of selection scratch; the static array holds " +
+                     std::to_string(kStaticScratchBytes);
+      return GDN_ERR_CAPACITY;
+    }
+  }
+  const gdn_status st = check_select(ctx, t, o, Wout, V, W_next, forced_parent, forced_token,
+                                     parent, token, score);
+  if (st != GDN_OK) return st;
+  char* base = nullptr;
+  int err = static_scratch(&base);
+  if (err) return hip_fail(err, "gdn_beam_select_static");
+  const gdn_beam_config& c = ctx->cfg;
+  SelectArgs a{c.R, c.H, c.d_v, c.W_max, c.V_max, c.T_max, t, ctx->W_cur, V, W_next, c.wout_dtype,
+               o, Wout, forced_parent, forced_token, parent, token, score, ctx->ws, ctx->L,
+               base, make_sel_scratch(c, 0)};
+  err = launch_select(a, stream);
+  if (err) return hip_fail(err, "gdn_beam_select_static");
+  ctx->t = t + 1;
+  ctx->stepped = 0;
+  ctx->W_cur = W_next;
+  return GDN_OK;
+}
+
 gdn_status gdn_beam_export_bytes(const gdn_beam_ctx* ctx, int32_t what, size_t* bytes) {
   if (!ctx || !bytes) return GDN_ERR_INVALID_ARG;
   const gdn_beam_config& c = ctx->cfg;

@@ -17,6 +17,9 @@ constexpr int kMaxT = 8;          // SID steps
 constexpr int kMaxW = 1024;       // beams per step (one sorting workgroup holds them)
 constexpr int kMaxV = 65536;      // codebook
 constexpr int kHistBins = 2048;   // radix digits per selection pass (11 bits)
+// Static selection scratch of gdn_beam_select_static, per GPU (GDN_STATIC_SCRATCH_BYTES).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kStaticScratchDevices = 64;
 
 // Per-request selection results handed from the tile choice to the refinement.
 struct SelState {
@@ -191,6 +194,9 @@ inline size_t fullstate_half_bytes(const gdn_beam_config& c) {
 int launch_init(const InitArgs& a, hipStream_t s);
 int launch_step(const StepArgs& a, hipStream_t s);
 int launch_select(const SelectArgs& a, hipStream_t s);
+// Device address of the current device's static selection scratch (kStaticScratchBytes,
+// 256-aligned); looked up once per device.  Returns a hipError_t value.
+int static_scratch(char** ptr);
 int launch_prefill(const PrefillArgs& a, hipStream_t s);
 int launch_fullstate(const FullStepArgs& a, hipStream_t s);
 int copy_d2d(void* dst, const void* src, size_t bytes, hipStream_t s);

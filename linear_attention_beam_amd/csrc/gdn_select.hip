@@ -30,6 +30,8 @@
 //   final_kernel     exact top-K over the refined keys in LDS, ties by flat index,
 //                    sort, the top-W outputs, and the remap of ancestry, SID prefixes
 //                    and cumulative scores (eq. 9).
+#include <mutex>
+
 #include "gdn_device.h"
 
 namespace gdn {
@@ -1592,6 +1594,33 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(final_kernel, dim3(a.R), dim3(1024), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
+  return 0;
+}
+
+// ---------------------------------------------------------------- static scratch
+
+// The selection scratch of gdn_beam_select_static, for callers that cannot allocate:
+// one array per GPU, which that GPU holds from the library's first use on it until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the host it
+// names a stand-in, not device memory): it uses the device address static_scratch()
+// looked up for the current device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+int static_scratch(char** ptr) {
+  static std::mutex m;
+  static char* addr[kStaticScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  if (dev < 0 || dev >= kStaticScratchDevices) return int(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> g(m);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));    // with device `dev` current
+    if (e != hipSuccess) return int(e);
+    addr[dev] = static_cast<char*>(p);
+  }
+  *ptr = addr[dev];
   return 0;
 }
 
