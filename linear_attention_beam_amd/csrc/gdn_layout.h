@@ -46,6 +46,7 @@ struct SelScratch {
   size_t groups;      // [R,max_groups] u32 refinement groups
   size_t gtiles;      // [R,max_groups,32] u32 the tiles of each group
   size_t rkeys;       // [R,W_max,kTile] u32 keys of the chosen tiles' candidates
+  size_t flog;        // [R,W_max] f32 logits of the forced candidates
   size_t end;         // first byte past the regions (256-aligned)
 };
 
@@ -104,6 +105,7 @@ inline SelScratch make_sel_scratch(const gdn_beam_config& c, size_t off) {
   S.groups = take(R * size_t(max_groups(c.W_max, n_tiles(c.V_max))) * 4);
   S.gtiles = take(R * size_t(max_groups(c.W_max, n_tiles(c.V_max))) * 32 * 4);
   S.rkeys = take(R * W * kTile * 4);
+  S.flog = take(R * W * 4);
   S.end = off;
   return S;
 }

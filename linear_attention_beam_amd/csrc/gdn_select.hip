@@ -265,6 +265,10 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   };
   // fold of a tile whose 32 codes all exist: the same arithmetic as fold below, as
   // straight-line code (selects in place of its branches)
+  // exp(x - m) as exp2(fma(x, log2 e, -m log2 e)): one rounding of the exact x log2 e -
+  // round(m log2 e), an error of about |m| 2^-24 in the exponent, below 1e-7 relative for
+  // |m| < 2 (and |m| 2^-24 absolute in the log-sum-exp, the size of the rounding of the
+  // score itself)
   auto fold_full = [&](const f32x16& acc, int c0) {
     float tm = -INFINITY;
 #pragma unroll
@@ -276,8 +280,9 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     const float sc = mrun == -INFINITY ? 0.0f : srun * __builtin_amdgcn_exp2f((mrun - tm) * kLog2e);
     srun = up ? sc : srun;
     mrun = up ? tm : mrun;
+    const float nml = -mrun * kLog2e;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) srun += __builtin_amdgcn_exp2f((acc[i] - mrun) * kLog2e);
+    for (int i = 0; i < 16; ++i) srun += __builtin_amdgcn_exp2f(fmaf(acc[i], kLog2e, nml));
   };
   auto fold = [&](const f32x16& acc, int c0) {
     const bool full = c0 + 32 <= a.V;              // block-uniform
@@ -297,14 +302,15 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
       srun = mrun == -INFINITY ? 0.0f : srun * __builtin_amdgcn_exp2f((mrun - tm) * kLog2e);
       mrun = tm;
     }
+    const float nml = -mrun * kLog2e;
     if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) srun += __builtin_amdgcn_exp2f((acc[i] - mrun) * kLog2e);
+      for (int i = 0; i < 16; ++i) srun += __builtin_amdgcn_exp2f(fmaf(acc[i], kLog2e, nml));
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (c0 + 8 * (i >> 2) + 4 * hf + (i & 3) < a.V)
-          srun += __builtin_amdgcn_exp2f((acc[i] - mrun) * kLog2e);
+          srun += __builtin_amdgcn_exp2f(fmaf(acc[i], kLog2e, nml));
     }
   };
 
@@ -866,22 +872,32 @@ __global__ void __launch_bounds__(1024) tile_select_kernel(TileSelK a) {
   const uint32_t kmin = kmin_sh, kmax = kmax_sh;
   const int shift0 = first_shift(kmin, kmax);
 
-  // ---- bounded mode: theta0 from the code groups' largest logits (hist is clear), then
-  // each beam's threshold on its tile maxima
+  // ---- bounded mode: theta0 from the code groups' largest and smallest tile maxima (hist
+  // is clear), then each beam's threshold on its tile maxima.  A group of n tiles has one
+  // tile at its largest tile maximum and n - 1 others at or above its smallest, so the
+  // multiset {max key once, min key n - 1 times} over all groups is dominated tile by tile
+  // by the true tile keys, and its K-th largest key is a lower bound on theirs (where the
+  // top-K concentrates in a few beams, counting one tile per group would be far looser)
   uint32_t theta0 = kmin;
   if constexpr (bounded) {
     if (tid < W) {
       const float c = cum_s[tid];
-      auto add = [&](float gx) {
-        const uint32_t key = f2key(cand_score(c, gx, lt));
-        if (key >= kmin && key <= kmax) atomicAdd(&hist[(key - kmin) >> shift0], 1u);
+      const int tpg = 1 << a.tg_shift;
+      auto add = [&](int u, float gx, float gn) {
+        const int n = min(tpg, a.Vt - u * tpg);
+        const uint32_t kx = f2key(cand_score(c, gx, lt)), kn = f2key(cand_score(c, gn, lt));
+        if (kx >= kmin && kx <= kmax) atomicAdd(&hist[(kx - kmin) >> shift0], 1u);
+        if (n > 1 && kn >= kmin && kn <= kmax) atomicAdd(&hist[(kn - kmin) >> shift0], uint32_t(n - 1));
       };
       if (a.nvg <= 8) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (u < a.nvg) add(q[u].x);
+          if (u < a.nvg) add(u, q[u].x, q[u].z);
       } else {
-        for (int u = 0; u < a.nvg; ++u) add(lp[u].x);
+        for (int u = 0; u < a.nvg; ++u) {
+          const float4 p = lp[u];
+          add(u, p.x, p.z);
+        }
       }
     }
     __syncthreads();
@@ -1150,15 +1166,86 @@ struct RefineK {
   const uint32_t* groups;
   const uint32_t* gtiles;
   uint32_t* rkeys;       // [R,W_max,32]: keys of the chosen tiles' candidates (0: no code)
+  int forced_blocks;     // first blocks: the forced candidates' logits (32 per block)
+  int K;                 // forced candidates per request (W_next)
+  const int32_t *forced_parent, *forced_token;   // [R,K] (or null)
+  float* flog;           // [R,W_max] logits of the forced candidates
+  int32_t* status;
 };
 
-// One wave per group: code tile j against up to 32 beams that chose it.  Columns are
+// Logit of forced candidate i of request r (forced_parent[r, i], forced_token[r, i]) into
+// flog[r, i]: an fp32 dot product of z (rebuilt exactly from its three bf16 parts for a
+// bf16 codebook) and the code's row.  Eight lanes take one candidate, each a strided set
+// of 8-element units of d_v read as 16-byte pieces, and add their partial sums; every
+// load of a wave is issued at once.  Out-of-range entries are clamped and flagged
+// (status bit 0).
+template <int DV, bool WBF16>
+__device__ __forceinline__ void forced_logit8(const RefineK& a, int r, int i) {
+  constexpr int NU = DV / 8;                               // 8-element units of d_v
+  constexpr int UPL = (NU + 7) / 8;                        // units per lane
+  constexpr int HV = DV / 2;
+  const int j = threadIdx.x & 7;
+  const bool live = i < a.K;
+  const size_t o = size_t(r) * a.K + (live ? i : 0);
+  int b = a.forced_parent[o], c = a.forced_token[o];
+  if (b < 0 || b >= a.W || c < 0 || c >= a.V) {
+    if (live && j == 0) atomicOr(a.status, 1);
+    b = b < 0 ? 0 : (b >= a.W ? a.W - 1 : b);
+    c = c < 0 ? 0 : (c >= a.V ? a.V - 1 : c);
+  }
+  float zd[UPL][8], wd[UPL][8];
+#pragma unroll
+  for (int q = 0; q < UPL; ++q) {
+    const int u = j + 8 * q;
+    const int d0 = 8 * (u < NU ? u : 0);                   // elements d0 .. d0 + 7
+    if constexpr (WBF16) {
+      const int hf = d0 / HV, kk = (d0 % HV) / 8;
+      const u32x4* p = a.zf + zf_lane_base(r, a.nch_max, DV, b, hf) + size_t(kk) * 3 * 64;
+      float zh[8], zm[8], zl[8];
+      unpack8(p[0], zh);
+      unpack8(p[64], zm);
+      unpack8(p[128], zl);
+      unpack8(static_cast<const u32x4*>(a.woutT)[(size_t(c) * DV + d0) / 8], wd[q]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zd[q][e] = u < NU ? (zh[e] + zm[e]) + zl[e] : 0.0f;
+    } else {
+      const f32x4* zp = reinterpret_cast<const f32x4*>(a.z + (size_t(r) * a.W_max + b) * DV + d0);
+      const f32x4* wp = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.woutT) + size_t(c) * DV + d0);
+      const f32x4 z0 = zp[0], z1 = zp[1], w0 = wp[0], w1 = wp[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        zd[q][e] = u < NU ? z0[e] : 0.0f;
+        zd[q][4 + e] = u < NU ? z1[e] : 0.0f;
+        wd[q][e] = w0[e];
+        wd[q][4 + e] = w1[e];
+      }
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < UPL; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(zd[q][e], wd[q][e], s);
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  if (live && j == 0) a.flog[size_t(r) * a.W_max + i] = s;
+}
+
+// Blocks [0, forced_blocks) (forced parent maps only): the forced candidates' logits, 32
+// per block, first in the grid so that they run beside the refinement.  Later blocks: one
+// wave per group: code tile j against up to 32 beams that chose it.  Columns are
 // independent in the MFMA, so every logit equals the first pass's bit for bit.
 template <int DV, bool WBF16>
 __global__ void __launch_bounds__(256, 3) refine_kernel(RefineK a) {
   constexpr int HV = DV / 2;
   const int r = blockIdx.y;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);      // < G_max by the launch
+  if (int(blockIdx.x) < a.forced_blocks) {               // block-uniform
+    forced_logit8<DV, WBF16>(a, r, int(blockIdx.x) * 32 + int(threadIdx.x >> 3));
+    return;
+  }
+  const int rb = int(blockIdx.x) - a.forced_blocks;        // block of the refinement
+  const int g = rb * 4 + (threadIdx.x >> 6);              // < G_max by the launch
   const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
   // the group count and the group's descriptor and tiles are loaded together; a wave
   // past the last group leaves once they are in (the operand loads below need them)
@@ -1235,40 +1322,12 @@ struct FinK {
   const int32_t* opos;     // [R,W_max] position of each beam in step t's processing order
   int32_t* order_next;     // [R,W_max] processing order of step t + 1
   int32_t* opos_next;
-  const float* z;
-  const u32x4* zf;
-  const void* woutT;
+  const float* flog;       // [R,W_max] logits of the forced candidates
   const int32_t *forced_parent, *forced_token;
   int32_t *parent, *token;
   float* score;
   int32_t* status;
 };
-
-// logit of one (beam, code) for a forced candidate: fp32 dot product of z (rebuilt
-// exactly from its three bf16 parts for a bf16 codebook) and the code's row.
-__device__ float forced_logit(const FinK& a, int r, int b, int c) {
-  float s = 0.0f;
-  const int HV = a.d_v / 2;
-  for (int d = 0; d < a.d_v; ++d) {
-    float zd, wd;
-    if (a.split) {
-      const int hf = d / HV, kk = (d % HV) / 8, i = d % 8;
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(a.zf + zf_lane_base(r, a.nch_max, a.d_v, b, hf) +
-                                                            size_t(kk) * 3 * 64);
-      auto part = [&](int term) {
-        const uint32_t w = p[size_t(term) * 64 * 4 + i / 2];
-        return bf2f(i & 1 ? (w >> 16) : (w & 0xFFFFu));
-      };
-      zd = (part(0) + part(1)) + part(2);
-      wd = bf2f(static_cast<const uint16_t*>(a.woutT)[size_t(c) * a.d_v + d]);
-    } else {
-      zd = a.z[(size_t(r) * a.W_max + b) * a.d_v + d];
-      wd = static_cast<const float*>(a.woutT)[size_t(c) * a.d_v + d];
-    }
-    s = fmaf(zd, wd, s);
-  }
-  return s;
-}
 
 // Refined keys kept in LDS by the final select; more than this many keys at or above
 // the tile threshold (massive ties) are read from global memory instead.
@@ -1440,14 +1499,12 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
     int fp = p, fc = c;
     float fs = sc;
     if (a.forced_parent) {
+      // the refinement flagged entries out of range; they are clamped the same way
       fp = a.forced_parent[o];
       fc = a.forced_token[o];
-      if (fp < 0 || fp >= a.W || fc < 0 || fc >= a.V) {
-        atomicOr(a.status, 1);
-        fp = fp < 0 ? 0 : (fp >= a.W ? a.W - 1 : fp);
-        fc = fc < 0 ? 0 : (fc >= a.V ? a.V - 1 : fc);
-      }
-      fs = cand_score(cum_s[fp], forced_logit(a, r, fp, fc), lse[fp]) + 0.0f;
+      fp = fp < 0 ? 0 : (fp >= a.W ? a.W - 1 : fp);
+      fc = fc < 0 ? 0 : (fc >= a.V ? a.V - 1 : fc);
+      fs = cand_score(cum_s[fp], a.flog[size_t(r) * a.W_max + i], lse[fp]) + 0.0f;
     }
     // eq. (9): the child copies its parent's ancestry and appends the parent's slot
     const bool lds = a.W * a.t <= kAncCap;                 // block-uniform
@@ -1492,7 +1549,7 @@ static int launch_dv(const SelectArgs& a, const LogitsK& lk, const RefineK& rk, 
     if (bf) hipLaunchKernelGGL((logits_kernel<DV, true>), grid, dim3(64 * kLogitsWaves), 0, s, lk);
     else hipLaunchKernelGGL((logits_kernel<DV, false>), grid, dim3(64 * kLogitsWaves), 0, s, lk);
   } else {
-    dim3 grid((groups + 3) / 4, a.R);
+    dim3 grid(groups, a.R);                       // groups: blocks, set by the caller
     if (bf) hipLaunchKernelGGL((refine_kernel<DV, true>), grid, dim3(256), 0, s, rk);
     else hipLaunchKernelGGL((refine_kernel<DV, false>), grid, dim3(256), 0, s, rk);
   }
@@ -1571,7 +1628,9 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   const bool bounded = int64_t(a.W) * Vt > kSelList && int64_t(a.W) * nvg >= Kt;
   LogitsK lk{a.R, a.W, a.W_max, a.V, nch, nvg, cpw, nch_max, bounded ? 1 : 0, z, zf, woutT, tmax, tstride,
              lse_part};
-  RefineK rk{a.W, a.W_max, a.V, Vt, G_max, nch_max, z, zf, woutT, lse, cum, sel, groups, gtiles, rkeys};
+  float* flog = reinterpret_cast<float*>(scr + S.flog);
+  RefineK rk{a.W, a.W_max, a.V, Vt, G_max, nch_max, z, zf, woutT, lse, cum, sel, groups, gtiles, rkeys,
+             0, a.W_next, a.forced_parent, a.forced_token, flog, status};
   if ((err = launch_by_dv(a, lk, rk, 0, s, false))) return err;
   {
     int tg_shift = 0;
@@ -1582,15 +1641,16 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
     else hipLaunchKernelGGL(tile_select_kernel<false>, dim3(a.R), dim3(1024), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
-  {  // groups <= ceil(Kt / 32) + min(Vt, Kt) <= G_max
+  {  // groups <= ceil(Kt / 32) + min(Vt, Kt) <= G_max; the forced candidates' logits in
+     // blocks after the refinement's (32 per block)
     const int gmax = (Kt + 31) / 32 + (Vt < Kt ? Vt : Kt);
-    if ((err = launch_by_dv(a, lk, rk, gmax, s, true))) return err;
+    rk.forced_blocks = a.forced_parent ? (a.W_next + 31) / 32 : 0;
+    if ((err = launch_by_dv(a, lk, rk, rk.forced_blocks + (gmax + 3) / 4, s, true))) return err;
   }
   {
     FinK k{a.W, a.W_max, a.V, Vt, a.W_next, Kt, a.T_max, a.t, a.d_v, nch_max, split, sel, rkeys, tiles,
-           lse, cum, cum_next, anc, anc_next, tok, tok_next, opos, order_next, opos_next, z, zf,
-           woutT, a.forced_parent,
-           a.forced_token, a.parent, a.token, a.score, status};
+           lse, cum, cum_next, anc, anc_next, tok, tok_next, opos, order_next, opos_next, flog,
+           a.forced_parent, a.forced_token, a.parent, a.token, a.score, status};
     hipLaunchKernelGGL(final_kernel, dim3(a.R), dim3(1024), 0, s, k);
     if ((err = last_launch_error())) return err;
   }
