@@ -74,6 +74,10 @@ def parse():
                         "of this script into profiles/step_kernel_<workload>_traffic.json")
     p.add_argument("--bench-json", default=None,
                    help="with --traffic-from: the JSON line the profiled run printed")
+    p.add_argument("--projection-stamps", action="store_true",
+                   help="after the timed decodes, one decode whose step launches stamp every "
+                        "projection phase (gdn_beam_stamp_projection): MFMA utilisation of the "
+                        "S_ctx projection per SIMD, reported as projection_mfma")
     p.add_argument("--flush-mall", choices=["read", "write"], default=None,
                    help="cold-cache timing: read (or write) 1 GiB of scratch before every step "
                         "launch, so neither L2 nor the 256 MiB last-level cache holds its inputs; "
@@ -471,8 +475,87 @@ def run_workload(args, wl, mode, torch, copy_gbs):
                              "basis": "sum over init, step and select launches of max(algorithmic "
                                       "bytes / 8 TB/s, MFMA flops / dense peak)"}),
     }
+    if getattr(args, "projection_stamps", False) and states is None:
+        # one more decode, every step launch stamping its projection phases
+        from linear_attention_beam_amd import binding as Bb
+        per_t = []
+        dec.init(S_ctx, wl.width(0), stream)
+        for t in range(wl.T):
+            n = stamp_records(wl, t)
+            buf = torch.zeros(n * 8, dtype=torch.int32, device=dev)
+            Bb.gdn_beam_stamp_projection(buf, n * 32)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            gdn_step(t, inputs[t])
+            ev1.record(stream)
+            s_ = sels[t]
+            dec.select(t, outs[t], Wout, wl.V, wl.width(t + 1), s_["parent"], s_["token"], s_["score"],
+                       forced[t][0], forced[t][1], stream)
+            torch.cuda.synchronize()
+            u = projection_utilisation(buf.cpu().numpy().view(np.uint32).reshape(n, 8),
+                                       MFMA_FLOPS_PER_SIMD_CYCLE[wl.io])
+            u["t"] = t
+            u["W"] = wl.width(t)
+            u["stamped_launch_ms"] = ev0.elapsed_time(ev1)
+            proj_flops = 2 * (2 if wl.io == "bf16" else 1) * 2 * wl.R * wl.H * wl.width(t) * wl.d_v * wl.d_k
+            u["projection_share_of_launch"] = (proj_flops / (MFMA_BF16_PEAK if wl.io == "bf16" else MFMA_F32_PEAK)
+                                               / (step_ms[t] * 1e-3))
+            per_t.append(u)
+            log(args, f"projection phases t={t}: MFMA utilisation {u['util']:.3f} over {u['simds']} SIMDs, "
+                      f"{u['mean_phase_cycles']:.0f} cycles per phase for {u['mfma_cycles_per_phase']:.0f} "
+                      f"MFMA cycles")
+        res["projection_mfma"] = {
+            "per_t": per_t,
+            "method": "in-kernel stamps (gdn_beam_stamp_projection): per SIMD, MFMA cycles of the "
+                      "projection phases (flops / dense flops per SIMD cycle) over the union of the "
+                      "phases' s_memtime intervals; projection_share_of_launch = executed projection "
+                      "MFMA flops / dense peak / the unstamped launch time"}
     dec.close()
     return res
+
+
+# dense MFMA flops per cycle of one SIMD (published peak / (1024 SIMDs x 2.4 GHz))
+MFMA_FLOPS_PER_SIMD_CYCLE = {"bf16": MFMA_BF16_PEAK / (1024 * 2.4e9), "f32": MFMA_F32_PEAK / (1024 * 2.4e9)}
+
+
+def stamp_records(wl, t):
+    """Projection-stamp records of one step launch: work items x waves x chunks."""
+    dvp = max(wl.d_v, 32)
+    nrb = dvp // 256 if dvp > 256 else 1
+    nw = min(dvp, 256) // 32
+    return wl.R * wl.H * nrb * nw * ((wl.width(t) + 31) // 32)
+
+
+def projection_utilisation(rec, flops_per_cycle):
+    """MFMA utilisation of the projection phases from stamp records [N, 8] uint32.
+
+    Per SIMD (XCC_ID, and HW_ID bits 4..15: SIMD, CU, shader array, engine), the union of
+    its waves' [begin, end] cycle intervals; utilisation = the phases' MFMA cycles (flops /
+    flops per SIMD cycle) over that union, summed over SIMDs.  Also the mean phase length
+    per chunk and the SIMD count."""
+    rec = np.asarray(rec, dtype=np.uint64)
+    t0 = rec[:, 0] | (rec[:, 1] << np.uint64(32))
+    t1 = rec[:, 2] | (rec[:, 3] << np.uint64(32))
+    ok = (t1 > t0) & (rec[:, 6] > 0)
+    t0, t1, rec = t0[ok].astype(np.int64), t1[ok].astype(np.int64), rec[ok]
+    key = (rec[:, 5].astype(np.int64) << 16) | ((rec[:, 4].astype(np.int64) >> 4) & 0xFFF)
+    order = np.lexsort((t0, key))
+    t0, t1, key, fl = t0[order], t1[order], key[order], rec[order, 6].astype(np.float64)
+    union = 0
+    start = np.r_[0, np.flatnonzero(np.diff(key)) + 1, len(key)]
+    for a, b in zip(start[:-1], start[1:]):
+        cur_s, cur_e = t0[a], t1[a]
+        for i in range(a + 1, b):
+            if t0[i] > cur_e:
+                union += cur_e - cur_s
+                cur_s, cur_e = t0[i], t1[i]
+            else:
+                cur_e = max(cur_e, t1[i])
+        union += cur_e - cur_s
+    mfma_cycles = float(fl.sum()) / flops_per_cycle
+    return {"util": mfma_cycles / max(union, 1), "phases": int(len(t0)), "simds": int(len(start) - 1),
+            "mean_phase_cycles": float(np.mean(t1 - t0)) if len(t0) else 0.0,
+            "mfma_cycles_per_phase": float(fl.mean() / flops_per_cycle) if len(t0) else 0.0}
 
 
 def default_mode(wl, asked):
@@ -521,6 +604,8 @@ def main():
         extra[name]["roofline"] = {k: r["roofline"][k] for k in ("achieved", "frac", "traffic",
                                                                  "bytes_per_decode")}
         extra[name]["decode_roofline"] = r["decode_roofline"]
+        if "projection_mfma" in r:
+            extra[name]["projection_mfma"] = r["projection_mfma"]
         log(args, f"extra {name}: {r['value']:.4g} beam-transitions/s, step frac "
                   f"{r['roofline']['frac']:.3f}")
 
@@ -535,8 +620,10 @@ def main():
         "config": head["config"],
     }
     for k in ("roofline", "gdn_step_rate", "gdn_step_ms", "step_ms_per_t", "select_ms",
-              "select_ms_per_t", "select_floor_ms_per_t", "step_tflops", "decode_roofline"):
-        res[k] = head[k]
+              "select_ms_per_t", "select_floor_ms_per_t", "step_tflops", "decode_roofline",
+              "projection_mfma"):
+        if k in head:
+            res[k] = head[k]
     if extra:
         res["extra"] = extra
     if not args.no_cpu_baseline:

@@ -214,6 +214,20 @@ gdn_status gdn_beam_time_steps(int32_t capacity);
  * reused for the next launches). */
 gdn_status gdn_beam_step_times(float* ms /* host */, int32_t cap, int32_t* n /* host */);
 
+/* Measurement, not an operation of the method: MFMA activity of the S_ctx projection
+ * inside the fused step (OneLA reading note, section 2.5 step 2: the accumulators start as
+ * S_ctx q_t and S_ctx k_t).  Arms the next gdn_beam_step launch of the process to write
+ * one 32-byte record per (workgroup, wave, 32-beam chunk) into buf (device, 16-byte
+ * aligned, caller-owned, `bytes` long; records past it are dropped), then disarms.  Record
+ * ((wid * NW) + wave) * ceil(W_t / 32) + chunk, wid the work item (request * H + head,
+ * times the row blocks of a head: one per 256 rows of d_v), NW = min(d_v, 256) / 32 waves;
+ * words (uint32): shader-clock cycle (s_memtime) before the chunk's first projection MFMA,
+ * lo and hi; the cycle after a VALU operation read its last results, lo and hi; HW_ID;
+ * XCC_ID; MFMA flops of the phase; the bits of the value read.  With stamps on, that
+ * launch waits for the projection before the chunk's dot products; its outputs are
+ * unchanged.  buf = NULL disarms.  Errors: misaligned buf or bytes < 32 (INVALID_ARG). */
+gdn_status gdn_beam_stamp_projection(void* buf, size_t bytes);
+
 /* Static description of a status code. */
 const char* gdn_beam_status_str(gdn_status s);
 

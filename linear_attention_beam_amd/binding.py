@@ -26,7 +26,7 @@ EXPORTS = ("gdn_beam_workspace_bytes", "gdn_beam_init", "gdn_beam_step", "gdn_be
            "gdn_beam_export", "gdn_beam_export_bytes", "gdn_beam_query", "gdn_beam_destroy",
            "gdn_beam_status_str", "gdn_beam_last_error", "gdn_beam_prefill",
            "gdn_fullstate_bytes", "gdn_fullstate_step", "gdn_beam_time_steps", "gdn_beam_step_times",
-           "gdn_beam_select_static")
+           "gdn_beam_select_static", "gdn_beam_stamp_projection")
 GDN_STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -80,6 +80,7 @@ def _load():
         "gdn_beam_query": (st, [vp, POINTER(i32), POINTER(i32)]),
         "gdn_beam_destroy": (None, [vp]),
         "gdn_beam_time_steps": (st, [i32]),
+        "gdn_beam_stamp_projection": (st, [vp, c_size_t]),
         "gdn_beam_step_times": (st, [POINTER(ctypes.c_float), i32, POINTER(i32)]),
         "gdn_beam_status_str": (c_char_p, [st]),
         "gdn_beam_last_error": (c_char_p, []),
@@ -177,6 +178,10 @@ def gdn_beam_destroy(ctx):
 
 def gdn_beam_time_steps(capacity):
     _check(_lib.gdn_beam_time_steps(capacity), "gdn_beam_time_steps")
+
+
+def gdn_beam_stamp_projection(buf, nbytes):
+    _check(_lib.gdn_beam_stamp_projection(_ptr(buf), nbytes), "gdn_beam_stamp_projection")
 
 
 def gdn_beam_step_times(cap):

@@ -52,6 +52,22 @@ struct StepTimer {
   }
 } g_timer;
 
+// Projection-phase stamps: the next step launch of the process writes them, once armed.
+struct StampArm {
+  std::mutex m;
+  uint32_t* buf = nullptr;
+  size_t records = 0;
+  bool take(uint32_t*& b, size_t& n) {
+    std::lock_guard<std::mutex> g(m);
+    if (!buf) return false;
+    b = buf;
+    n = records;
+    buf = nullptr;
+    records = 0;
+    return true;
+  }
+} g_stamp;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 gdn_status hip_fail(int err, const char* where) {
@@ -159,7 +175,8 @@ gdn_status gdn_beam_step(gdn_beam_ctx* ctx, int32_t t, const void* q, const void
   if (t >= c.T_max) return GDN_ERR_CAPACITY;
   if (t != ctx->t || ctx->mode == 2) return GDN_ERR_BAD_STATE;
   StepArgs a{c.R, c.H, key_heads(c), c.d_k, c.d_v, c.W_max, c.T_max, t, ctx->W_cur, c.io_dtype,
-             q, k, v, alpha, beta, o, ctx->ws, ctx->L, nullptr, nullptr};
+             q, k, v, alpha, beta, o, ctx->ws, ctx->L, nullptr, nullptr, nullptr, 0};
+  g_stamp.take(a.stamps, a.stamp_records);
   const bool timed = g_timer.take(a.ev0, a.ev1);
   int err = launch_step(a, stream);
   if (err) {
@@ -359,6 +376,14 @@ gdn_status gdn_beam_time_steps(int32_t capacity) {
   }
   g_timer.ev.swap(ev);
   g_timer.cap = capacity;
+  return GDN_OK;
+}
+
+gdn_status gdn_beam_stamp_projection(void* buf, size_t bytes) {
+  if (buf && (!aligned16(buf) || bytes < size_t(kStampWords) * 4)) return GDN_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_stamp.m);
+  g_stamp.buf = static_cast<uint32_t*>(buf);
+  g_stamp.records = buf ? bytes / (size_t(kStampWords) * 4) : 0;
   return GDN_OK;
 }
 

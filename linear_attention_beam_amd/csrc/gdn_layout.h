@@ -150,7 +150,16 @@ struct StepArgs {
   void* ws;
   Layout L;
   hipEvent_t ev0, ev1;    // non-null: the launch records its own start and end on them
+  uint32_t* stamps;       // non-null: projection-phase stamps (kStampWords per record)
+  size_t stamp_records;   // records the buffer holds
 };
+
+// Projection-phase stamp of one (workgroup, wave, chunk) of a step launch, as uint32
+// words: shader-clock cycle before the first projection MFMA (lo, hi), after the last
+// result is read (lo, hi), HW_ID, XCC_ID, MFMA flops of the phase, and the bits of the
+// value that read the results.  Record ((wid * NW) + wave) * chunks + chunk, wid the
+// launch's work item (request-head, then row block), NW waves per workgroup.
+constexpr int kStampWords = 8;
 
 struct SelectArgs {
   int R, H, d_v, W_max, V_max, T_max, t, W, V, W_next;

@@ -8,7 +8,6 @@
 //   init_kernel      S_ctx -> MFMA fragment order in the workspace; clear beam state.
 //   step_kernel      fused step: S_ctx [q|k] on MFMA (eqs. 6-7 initial terms), replay
 //                    along the ancestor records (eqs. 6-7), eq. (8), record append.
-//   prefill_kernel   eq. (3) over each request's prompt (the state S_ctx).
 #include <hip/hip_ext.h>
 
 #include "gdn_device.h"
@@ -87,6 +86,8 @@ struct StepK {
   void* gtr_key;
   const int32_t* anc;
   const int32_t* order;    // [R,W_max] processing order of the beams (steps t >= 1)
+  uint32_t* stamps;        // projection-phase stamps (measurement), or null
+  uint32_t stamp_records;
 };
 
 // Sizes of the fused step for head dims (DK, DV) and io dtype.
@@ -404,15 +405,50 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
         }
       }
     };
+    // projection-phase stamps (a measurement; the launch's results are the same): the
+    // shader clock before the first projection MFMA and after a VALU operation has read
+    // the last results, which waits for them.  With stamps on, the dot products of the
+    // chunk start only after that wait.
+    const bool stamping = a.stamps != nullptr;             // launch-uniform
+    uint64_t ts0 = 0;
+    auto stamp_begin = [&]() {
+      if (stamping) {
+        __builtin_amdgcn_sched_barrier(0);
+        ts0 = __builtin_amdgcn_s_memtime();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto stamp_end = [&]() {
+      if (stamping) {
+        __builtin_amdgcn_sched_barrier(0);
+        const float probe = accq[15] + acck[15];          // waits for both accumulators
+        __builtin_amdgcn_sched_barrier(0);
+        const uint64_t ts1 = __builtin_amdgcn_s_memtime();
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t rec = uint32_t((wid * C::NW + w) * nch + c);
+        if (lane == 0 && rec < a.stamp_records) {
+          constexpr uint32_t flops = BF16 ? uint32_t(DK / 16) * 4u * 32768u : uint32_t(DK / 8) * 8u * 4096u;
+          const uint32_t hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));   // HW_ID
+          const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)); // XCC_ID
+          u32x4* dst = reinterpret_cast<u32x4*>(a.stamps + size_t(rec) * kStampWords);
+          dst[0] = u32x4{uint32_t(ts0), uint32_t(ts0 >> 32), uint32_t(ts1), uint32_t(ts1 >> 32)};
+          dst[1] = u32x4{hw, xcc, flops, __float_as_uint(probe)};
+        }
+      }
+    };
     // with at most two records to replay (d_k <= 128) the projection goes first, on the
     // matrix cores while the records' keys are still on their way; deeper replays and
     // wider keys keep the order that fits their registers
     if constexpr (NJ <= 2 && DK <= 128) {
+      stamp_begin();
       project();
+      stamp_end();
       dots();
     } else {
       dots();
+      stamp_begin();
       project();
+      stamp_end();
     }
 
     {
@@ -533,63 +569,6 @@ __global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(St
   }
 }
 
-// ---------------------------------------------------------------- prefill (eq. 3)
-
-// One workgroup per (request, head, block of up to 128 rows): rows of S evolve
-// independently given the token.  Thread (row, part) holds S[row][part*COLS ..] in
-// registers.  Each token: u = S k (row dot, reduced over the row's lanes),
-// S <- alpha S + beta (v - alpha u) k^T.
-template <int DK, int DV>
-struct PrefillCfg {
-  static constexpr int RB = DV < 128 ? DV : 128;                         // rows per block
-  static constexpr int TPR = DV < 32 ? 256 / DV : (DK > 128 ? 4 : 2);    // lanes per row
-  static constexpr int NT = RB * TPR;
-};
-
-template <int DK, int DV>
-__global__ void __launch_bounds__((PrefillCfg<DK, DV>::NT)) prefill_kernel(PrefillArgs a) {
-  constexpr int TPR = PrefillCfg<DK, DV>::TPR;
-  constexpr int COLS = DK / TPR;
-  const int rh = blockIdx.x, r = rh / a.H, h = rh % a.H;
-  const int hk = h / (a.H / a.HK);                        // key head of value head h
-  const int row = blockIdx.y * PrefillCfg<DK, DV>::RB + threadIdx.x / TPR, cp = threadIdx.x % TPR;
-  int beg = a.offsets[r], end = a.offsets[r + 1];
-  beg = beg < 0 ? 0 : (beg > a.N ? int(a.N) : beg);
-  end = end < beg ? beg : (end > a.N ? int(a.N) : end);
-  float S[COLS];
-#pragma unroll
-  for (int c = 0; c < COLS; ++c) S[c] = 0.0f;
-  float kc[COLS];
-  float vn = 0.0f, an = 0.0f, bn = 0.0f;
-  auto load = [&](int i, float* kk, float& vv, float& aa, float& bb) {
-    const float* kp = a.k + (size_t(i) * a.HK + hk) * DK + cp * COLS;
-#pragma unroll
-    for (int c = 0; c < COLS; ++c) kk[c] = kp[c];
-    vv = a.v[(size_t(i) * a.H + h) * DV + row];
-    aa = a.alpha[size_t(i) * a.H + h];
-    bb = a.beta[size_t(i) * a.H + h];
-  };
-  if (beg < end) load(beg, kc, vn, an, bn);
-  for (int i = beg; i < end; ++i) {
-    float kcur[COLS];
-#pragma unroll
-    for (int c = 0; c < COLS; ++c) kcur[c] = kc[c];
-    const float vv = vn, aa = an, bb = bn;
-    if (i + 1 < end) load(i + 1, kc, vn, an, bn);
-    float u = 0.0f;
-#pragma unroll
-    for (int c = 0; c < COLS; ++c) u = fmaf(S[c], kcur[c], u);
-#pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) u += __shfl_xor(u, off);
-    const float d = bb * (vv - aa * u);
-#pragma unroll
-    for (int c = 0; c < COLS; ++c) S[c] = fmaf(d, kcur[c], aa * S[c]);
-  }
-  float* out = a.S_out + ((size_t(rh) * DV + row) * DK) + cp * COLS;
-#pragma unroll
-  for (int c = 0; c < COLS; ++c) out[c] = S[c];
-}
-
 // ---------------------------------------------------------------- launchers
 
 int launch_init(const InitArgs& a, hipStream_t s) {
@@ -614,7 +593,8 @@ static int launch_step_t(const StepArgs& a, hipStream_t s) {
           ws + a.L.s_frag, reinterpret_cast<float*>(ws + a.L.gtr_alpha),
           reinterpret_cast<float*>(ws + a.L.gtr_delta), ws + a.L.gtr_key,
           reinterpret_cast<const int32_t*>(ws + a.L.anc[a.t & 1]),
-          reinterpret_cast<const int32_t*>(ws + a.L.order[a.t & 1])};
+          reinterpret_cast<const int32_t*>(ws + a.L.order[a.t & 1]),
+          a.stamps, uint32_t(a.stamp_records < 0xFFFFFFFFu ? a.stamp_records : 0xFFFFFFFFu)};
   // with timing events, the dispatch itself stamps its start and end (nothing more is
   // put on the stream)
   auto go = [&](auto kern) {
@@ -643,24 +623,6 @@ int launch_step(const StepArgs& a, hipStream_t s) {
   if (a.d_k == 256 && a.d_v == 256 && bf) return launch_step_t<256, 256, true>(a, s);
   if (a.d_k == 128 && a.d_v == 512) return bf ? launch_step_t<128, 512, true>(a, s) : launch_step_t<128, 512, false>(a, s);
   if (a.d_k == 256 && a.d_v == 512 && bf) return launch_step_t<256, 512, true>(a, s);
-  return int(hipErrorInvalidValue);
-}
-
-template <int DK, int DV>
-static int launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
-  using C = PrefillCfg<DK, DV>;
-  hipLaunchKernelGGL((prefill_kernel<DK, DV>), dim3(a.R * a.H, DV / C::RB), dim3(C::NT), 0, s, a);
-  return last_launch_error();
-}
-
-int launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  (void)hipGetLastError();
-  if (a.d_k == 16 && a.d_v == 16) return launch_prefill_t<16, 16>(a, s);
-  if (a.d_k == 128 && a.d_v == 128) return launch_prefill_t<128, 128>(a, s);
-  if (a.d_k == 128 && a.d_v == 256) return launch_prefill_t<128, 256>(a, s);
-  if (a.d_k == 256 && a.d_v == 256) return launch_prefill_t<256, 256>(a, s);
-  if (a.d_k == 128 && a.d_v == 512) return launch_prefill_t<128, 512>(a, s);
-  if (a.d_k == 256 && a.d_v == 512) return launch_prefill_t<256, 512>(a, s);
   return int(hipErrorInvalidValue);
 }
 

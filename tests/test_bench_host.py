@@ -191,3 +191,31 @@ def test_decode_floor_term_by_term(name):
             flops *= 3
         sel += max(moved / bw, flops / peak)
     assert b.decode_floor_s(wl, bytes_t) == pytest.approx(init + steps + sel, rel=1e-12)
+
+
+def test_projection_utilisation_on_synthetic_stamps():
+    """Per SIMD, MFMA cycles over the union of the phase intervals: two SIMDs, one with two
+    overlapping phases, one with two disjoint ones; records never written are ignored."""
+    b = _bench()
+    def rec(t0, t1, hw, xcc, flops):
+        return [t0 & 0xFFFFFFFF, t0 >> 32, t1 & 0xFFFFFFFF, t1 >> 32, hw, xcc, flops, 0]
+    f = 1024.0
+    r = np.array([
+        rec(1000, 1400, 0x10, 0, 200 * 1024),      # SIMD (0, 1): [1000, 1600] after merging
+        rec(1200, 1600, 0x13, 0, 300 * 1024),      # same SIMD (wave id in the low bits)
+        rec(5000, 5100, 0x20, 1, 50 * 1024),       # SIMD (1, 2): two disjoint phases, 100 + 100
+        rec(6000, 6100, 0x20, 1, 50 * 1024),
+        [0] * 8,                                   # not written
+    ], dtype=np.uint64)
+    u = b.projection_utilisation(r, f)
+    assert u["simds"] == 2 and u["phases"] == 4
+    assert u["util"] == pytest.approx((200 + 300 + 50 + 50) / (600 + 200))
+    assert u["mean_phase_cycles"] == pytest.approx((400 + 400 + 100 + 100) / 4)
+
+
+def test_stamp_records_count():
+    b = _bench()
+    wl = synth.get("batch")
+    assert b.stamp_records(wl, 0) == wl.R * wl.H * 4 * 8          # 4 waves, 8 chunks of 32
+    wv = synth.get("wide_v")                                      # d_v = 512: two row blocks of 8 waves
+    assert b.stamp_records(wv, 0) == wv.R * wv.H * 2 * 8 * 8

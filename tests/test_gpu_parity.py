@@ -531,3 +531,32 @@ def test_nan_scores_terminate():
     assert np.all((anc[0][:K, 0] >= 0) & (anc[0][:K, 0] < wl.width(0)))
     g.step(1)                     # the next step gathers through that ancestry
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["single", "batch"])
+def test_projection_stamps_keep_results(name):
+    """A step launch that stamps its projection phases (gdn_beam_stamp_projection) gives
+    the same bits as one that does not; every record of that launch is written, ends after
+    it begins and carries the phase's MFMA flops; the next launch is not stamped."""
+    wl = synth.get(name)
+    g = GpuDecode(wl, R=1, exact=())
+    g.init()
+    plain = to_np(g.step(0)).copy()
+    dv, nch = max(wl.d_v, 32), (wl.width(0) + 31) // 32
+    n = wl.H * (dv // 32) * nch
+    buf = torch.zeros(n * 8 + 8, dtype=torch.int32, device=g.dev)
+    B.gdn_beam_stamp_projection(buf, buf.numel() * 4)
+    stamped = to_np(g.step(0)).copy()                       # re-issued step(0): same values
+    assert same_bits(plain, stamped)
+    rec = buf.cpu().numpy().view(np.uint32).reshape(-1, 8).astype(np.uint64)
+    t0 = rec[:n, 0] | (rec[:n, 1] << np.uint64(32))
+    t1 = rec[:n, 2] | (rec[:n, 3] << np.uint64(32))
+    assert np.all(t1 > t0), "every record written, end after begin"
+    flops = (wl.d_k // 16) * 4 * 32768 if wl.io == "bf16" else (wl.d_k // 8) * 8 * 4096
+    assert np.all(rec[:n, 6] == flops)
+    assert np.all(rec[n:] == 0), "nothing past the launch's records"
+    say(f"{name}: projection phases {np.mean(t1 - t0):.0f} cycles on average")
+    buf.zero_()
+    g.step(0)
+    torch.cuda.synchronize()
+    assert int(buf.abs().sum()) == 0, "only the armed launch stamps"
