@@ -662,8 +662,8 @@ def step_t_of(kernel_name):
 
 def traffic_summary(args):
     """profiles/step_kernel_<workload>_traffic.json from a FETCH_SIZE and a WRITE_SIZE run
-    of this script with --copy-calib MIB (the first three dispatches are MIB MiB device
-    copies: each reads and writes MIB MiB, which scales the counters to bytes)."""
+    of this script with --copy-calib MIB (its first three copy dispatches are MIB MiB
+    device copies: each reads and writes MIB MiB, which scales the counters to bytes)."""
     fetch_dir, write_dir = args.traffic_from
     fetch, write = read_counters(fetch_dir), read_counters(write_dir)
     if not args.bench_json:
@@ -679,8 +679,14 @@ def traffic_summary(args):
         print("--traffic-from needs --copy-calib MIB (the size the profiled run copied)", file=sys.stderr)
         return 2
     kib = args.copy_calib * 1024.0
-    ff = kib / np.mean([c.get("FETCH_SIZE", np.nan) for _, c in fetch[:3]])
-    wf = kib / np.mean([c.get("WRITE_SIZE", np.nan) for _, c in write[:3]])
+    # the calibration copies: the first three copy dispatches (a fill that allocates the
+    # copy's source comes before them)
+    fcal = [c["FETCH_SIZE"] for n, c in fetch if "copy" in n.lower()][:3]
+    wcal = [c["WRITE_SIZE"] for n, c in write if "copy" in n.lower()][:3]
+    if len(fcal) < 3 or len(wcal) < 3:
+        print("fewer than three copy dispatches in the counter runs", file=sys.stderr)
+        return 2
+    ff, wf = kib / np.mean(fcal), kib / np.mean(wcal)
     per_t = {}
     for (name, c) in fetch:
         t = step_t_of(name)

@@ -139,13 +139,13 @@ def test_traffic_summary_from_counters(tmp_path, monkeypatch):
     over the step kernel's dispatches, scaled by three device copies of known size."""
     b = _bench()
     copy = [("copy", 0)] * 3
-    fetch = [("copy_kernel", 1000.0)] * 3 + [
+    fetch = [("fill_kernel", 5.0)] + [("copy_kernel", 1000.0)] * 3 + [
         ("void gdn::step_kernel<128, 128, true, 0>(gdn::StepK)", 100.0),
         ("void gdn::logits_kernel<128, true>(gdn::LogitsK)", 7.0),
         ("void gdn::step_kernel<128, 128, true, 1>(gdn::StepK)", 150.0),
         ("void gdn::step_kernel<128, 128, true, 0>(gdn::StepK)", 120.0),
         ("void gdn::step_kernel<128, 128, true, 1>(gdn::StepK)", 170.0)]
-    write = [("copy_kernel", 4000.0)] * 3 + [(n, 2 * v) for n, v in fetch[3:]]
+    write = [("fill_kernel", 4000.0)] + [("copy_kernel", 4000.0)] * 3 + [(n, 2 * v) for n, v in fetch[4:]]
     del copy
     _write_pmc(str(tmp_path / "f"), "FETCH_SIZE", fetch)
     _write_pmc(str(tmp_path / "w"), "WRITE_SIZE", write)
