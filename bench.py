@@ -29,7 +29,6 @@ Counter summaries (host side, after rocprofv3 runs of this script):
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,9 +41,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GDN beam-transitions/sec (R×H×W per SID step) at 1 MI355X; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
-# the step kernel and everything it includes: counter runs taken on other sources are stale
-STEP_SOURCES = [os.path.join(ROOT, "linear_attention_beam_amd", "csrc", f)
-                for f in ("gdn_step.hip", "gdn_device.h", "gdn_layout.h")]
+# the step kernel's compiled machine code (written by the build): counter runs taken on
+# other code are stale
+STEP_HASH_FILE = os.path.join(ROOT, "linear_attention_beam_amd", "step_kernel_code.sha")
 
 
 def parse():
@@ -195,10 +194,11 @@ def copy_bandwidth(torch, dev, mib=1024, reps=10):
 
 
 def kernel_hash():
-    h = hashlib.sha256()
-    for f in STEP_SOURCES:
-        h.update(open(f, "rb").read())
-    return h.hexdigest()[:16]
+    """sha256[:16] of the built step kernel's machine code (None before a build)."""
+    try:
+        return open(STEP_HASH_FILE).read().strip() or None
+    except OSError:
+        return None
 
 
 def load_traffic(wl_name):
@@ -212,7 +212,7 @@ def load_traffic(wl_name):
         d = json.load(open(f))
     except Exception:
         return None
-    if d.get("kernel_sha") != kernel_hash():
+    if kernel_hash() is None or d.get("kernel_sha") != kernel_hash():
         return None
     return d.get("bytes_per_decode")
 

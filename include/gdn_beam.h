@@ -108,6 +108,11 @@ gdn_status gdn_beam_step(gdn_beam_ctx* ctx, int32_t t,
  * the codebook projection shared by all heads.  Per request: z_b = sum_h o_b,
  * logit_bc = z_b . Wout[:,c], and candidate (b, c) scores
  * cum_b + (logit_bc - logsumexp_c logit_b)  (log form of eq. 1).
+ * Logits are computed with fp32 precision: z (fp32) enters the matrix cores as three bf16
+ * terms against a bf16 codebook, or, for selections of at least 2^33 multiply-adds
+ * (R*W_t*V*d_v; the environment variable GDN_BEAM_F16_MIN_MACS, read per call, changes
+ * the threshold), as two fp16 terms against the codebook rescaled exactly into fp16 tile
+ * by tile, where every 32-code tile's nonzero entries span at most 32 binades.
  * The exact top-W_next over the request's W_t*V candidates, ordered by score
  * descending then flat index b*V + c ascending, is written to parent, token
  * [R,W_next] int32 and score [R,W_next] fp32 (RecoGEM section 4.3).
@@ -184,7 +189,10 @@ typedef enum {
                             /*   bit 0 (1): a forced parent/token was out of range       */
                             /*   (clamped);  bit 1 (2): a selection found fewer than     */
                             /*   W_next candidates (possible only with NaN outputs);     */
-                            /*   the missing ranks are filled with beam 0, token 0       */
+                            /*   the missing ranks are filled with beam 0, token 0;      */
+                            /*   bit 2 (4): a selection in the two-term fp16 form fell   */
+                            /*   back to three bf16 terms, a code tile's exponents       */
+                            /*   spanning more than fp16 can hold                        */
 } gdn_export_what;
 gdn_status gdn_beam_export(const gdn_beam_ctx* ctx, int32_t what, void* dst,
                            size_t dst_bytes, hipStream_t stream);

@@ -26,6 +26,52 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build the HIP library)")
 
 
+STEP_HASH = os.path.join(PKG, "step_kernel_code.sha")
+
+
+def _elf_symbols(data: bytes):
+    """(name, section index, value, size) of every symbol of a 64-bit little-endian ELF,
+    and its section headers (addr, offset)."""
+    import struct
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    secs = [struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize) for i in range(shnum)]
+    out = []
+    for sh in secs:
+        if sh[1] != 2:                                   # SHT_SYMTAB
+            continue
+        strtab = secs[sh[6]]
+        for k in range(sh[5] // 24):
+            st_name, st_info, st_other, st_shndx, st_value, st_size = struct.unpack_from(
+                "<IBBHQQ", data, sh[4] + 24 * k)
+            end = data.index(b"\0", strtab[4] + st_name)
+            out.append((data[strtab[4] + st_name:end].decode(), st_shndx, st_value, st_size))
+    return out, secs
+
+
+def step_kernel_code_hash(device_obj: str) -> str:
+    """sha256[:16] of the step kernel's machine code: every step_kernel instantiation's
+    instructions and kernel descriptor, by name, from the gfx950 device object of
+    gdn_step.hip.  The descriptor's bytes 16..23 (the offset from the descriptor to the
+    code, which moves when other kernels of the file change size) are left out; the rest
+    of it holds the LDS, scratch and register counts.  It changes only when the compiled
+    kernel does."""
+    import hashlib
+    data = open(device_obj, "rb").read()
+    syms, secs = _elf_symbols(data)
+    h = hashlib.sha256()
+    chosen = sorted(x for x in syms if "step_kernel" in x[0] and x[3] > 0)
+    for name, shndx, value, size in chosen:
+        sec = secs[shndx]
+        off = sec[4] + (value - sec[3])
+        blob = data[off:off + size]
+        if name.endswith(".kd"):
+            blob = blob[:16] + blob[24:]
+        h.update(name.encode())
+        h.update(blob)
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     cc = hipcc()
@@ -49,6 +95,17 @@ def build(verbose: bool = False) -> str:
         if verbose and err.strip():
             print(err, file=sys.stderr)
         objs.append(obj)
+    # the step kernel's device code on its own, for the hash that tells whether hardware
+    # counters taken earlier still describe it
+    dev = os.path.join(objdir, "gdn_step.gfx950.o")
+    cmd = [cc, *common, f"--offload-arch={ARCH}", "--offload-device-only", "--no-gpu-bundle-output",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-c",
+           os.path.join(CSRC, "gdn_step.hip"), "-o", dev]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"device compile failed: gdn_step.hip\n{r.stdout}\n{r.stderr}")
+    with open(STEP_HASH, "w") as fh:
+        fh.write(step_kernel_code_hash(dev) + "\n")
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

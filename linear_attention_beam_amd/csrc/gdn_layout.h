@@ -47,6 +47,11 @@ struct SelScratch {
   size_t gtiles;      // [R,max_groups,32] u32 the tiles of each group
   size_t rkeys;       // [R,W_max,kTile] u32 keys of the chosen tiles' candidates
   size_t flog;        // [R,W_max] f32 logits of the forced candidates
+  size_t f16flag;     // u32: a code tile of the bf16 codebook does not fit fp16 (zero
+                      // between selections)
+  size_t tscale;      // [n_tiles(V_max)] i32: exponent s_j of code tile j's fp16 scale 2^s_j
+  size_t woutT16;     // [V_max,d_v] fp16: the bf16 codebook transposed, tile j scaled by 2^s_j
+  size_t zscale;      // [R,W_max] f32: 2^-t_b, undoes beam b's scale of z
   size_t end;         // first byte past the regions (256-aligned)
 };
 
@@ -106,6 +111,10 @@ inline SelScratch make_sel_scratch(const gdn_beam_config& c, size_t off) {
   S.gtiles = take(R * size_t(max_groups(c.W_max, n_tiles(c.V_max))) * 32 * 4);
   S.rkeys = take(R * W * kTile * 4);
   S.flog = take(R * W * 4);
+  S.f16flag = take(128);
+  S.tscale = take(Vt * 4);
+  S.woutT16 = take(V * dv * 2);
+  S.zscale = take(R * W * 4);
   S.end = off;
   return S;
 }

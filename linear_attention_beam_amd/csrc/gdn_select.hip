@@ -30,11 +30,15 @@
 //   final_kernel     exact top-K over the refined keys in LDS, ties by flat index,
 //                    sort, the top-W outputs, and the remap of ancestry, SID prefixes
 //                    and cumulative scores (eq. 9).
+#include <cstdlib>
 #include <mutex>
+#include <type_traits>
 
 #include "gdn_device.h"
 
 namespace gdn {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -47,14 +51,132 @@ __device__ __forceinline__ size_t zf_lane_base(int r, int nch_max, int d_v, int 
   return (size_t(r) * nch_max + (b >> 5)) * size_t(d_v / 16) * 3 * 64 + (b & 31) + 32 * hf;
 }
 
+__device__ __forceinline__ uint32_t f2h_bits(float x) {
+  return uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
+}
+__device__ __forceinline__ float h2f(uint32_t b) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(b)));
+}
+
+// ---- two-term fp16 operands (bf16 codebook)
+//
+// The logits take z in two fp16 terms, h = fp16(z 2^t) and l = fp16(z 2^t - h), against
+// the bf16 codebook rescaled into fp16 tile by tile (code tile j times 2^s_j): fp16 holds
+// 11 significant bits, so |z 2^t - h - l| <= 2^-24 |z 2^t|, the precision of fp32 itself,
+// and the products are exact in the fp32 accumulator.  A tile fits when its entries' 8
+// significant bits stay on fp16's grid after its scale, which holds when its nonzero
+// entries' exponents span at most 32 binades (and none is subnormal, infinite or NaN).
+// If any tile does not fit, z goes in three bf16 terms (hi, mid, lo) against the
+// codebook as it is: 24 significant bits, one more MFMA per k-step.  t is chosen per
+// beam so that its largest |z| lands in [2^14, 2^15); s_j so that the tile's largest
+// entry stays below 2^15.
+
+struct WprepK {
+  int d_v, V, split;
+  const void* wout;     // [d_v,V]
+  void* woutT;          // [V,d_v]
+  uint16_t* woutT16;    // [V,d_v] fp16, tile j scaled by 2^s_j
+  int32_t* tscale;      // [n_tiles(V)] s_j
+  uint32_t* f16flag;    // set if a tile does not fit fp16
+};
+
+// Codebook transpose Wout[d_v,V] -> Wout^T[V,d_v], the first launch of a selection; for a
+// bf16 codebook also each code tile's fp16 form.  Block j: the 32 codes of tile j, one per
+// lane of each half-wave, and d_v / 8 rows per half-wave: every load of a thread is issued
+// at once (a half-wave reads 32 consecutive codes of a row), the tile's exponent range is
+// reduced over the block, and each thread writes its rows of the tile's 32 transposed
+// rows in both forms.  The flag is touched only by a tile that does not fit.
+template <int DV>
+__global__ void __launch_bounds__(256) wprep_kernel(WprepK a) {
+  constexpr int RPT = DV / 8;                       // rows per thread
+  const int j = blockIdx.x;
+  const int ci = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  const int c = 32 * j + ci, r0 = rg * RPT;
+  const bool live = c < a.V;
+  if (!a.split) {                                   // launch-uniform
+    const float* w = static_cast<const float*>(a.wout);
+    float x[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) x[i] = live ? w[size_t(r0 + i) * a.V + c] : 0.0f;
+    if (live) {
+      float* dst = static_cast<float*>(a.woutT) + size_t(c) * DV + r0;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) dst[i] = x[i];
+    }
+    return;
+  }
+  const uint16_t* w = static_cast<const uint16_t*>(a.wout);
+  uint32_t x[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) x[i] = live ? uint32_t(w[size_t(r0 + i) * a.V + c]) : 0u;
+  uint32_t emax = 0u, nemin = 0u, bad = 0u;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const uint32_t e = (x[i] >> 7) & 0xFFu;
+    if (x[i] & 0x7FFFu) {
+      emax = max(emax, e);
+      nemin = max(nemin, 255u - e);
+      bad |= (e == 0u || e == 255u) ? 1u : 0u;
+    }
+  }
+  __shared__ uint32_t part[3][4];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    emax = max(emax, uint32_t(__shfl_xor(int(emax), off)));
+    nemin = max(nemin, uint32_t(__shfl_xor(int(nemin), off)));
+    bad |= uint32_t(__shfl_xor(int(bad), off));
+  }
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    part[0][wv] = emax;
+    part[1][wv] = nemin;
+    part[2][wv] = bad;
+  }
+  __syncthreads();
+  emax = max(max(part[0][0], part[0][1]), max(part[0][2], part[0][3]));
+  nemin = max(max(part[1][0], part[1][1]), max(part[1][2], part[1][3]));
+  bad = part[2][0] | part[2][1] | part[2][2] | part[2][3];
+  const uint32_t emin = 255u - nemin;
+  const bool fits = bad == 0u && (emax == 0u || emax - emin <= 31u);
+  // |W| < 2^(emax - 126): scaled by 2^(141 - emax) the tile's largest entry is below 2^15
+  const int sj = emax ? 141 - int(emax) : 0;
+  if (threadIdx.x == 0) {
+    a.tscale[j] = sj;
+    if (!fits) atomicOr(a.f16flag, 1u);
+  }
+  if (live) {
+    uint16_t* d16 = static_cast<uint16_t*>(a.woutT) + size_t(c) * DV + r0;
+    uint16_t* h16 = a.woutT16 + size_t(c) * DV + r0;
+    if constexpr (RPT >= 8) {
+#pragma unroll
+      for (int q = 0; q < RPT / 8; ++q) {
+        uint32_t hb[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) hb[k] = f2h_bits(ldexpf(bf2f(x[8 * q + k]), sj));
+        reinterpret_cast<u32x4*>(d16)[q] = pack8(x + 8 * q);
+        reinterpret_cast<u32x4*>(h16)[q] = pack8(hb);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        d16[i] = uint16_t(x[i]);
+        h16[i] = uint16_t(f2h_bits(ldexpf(bf2f(x[i]), sj)));
+      }
+    }
+  }
+}
+
 struct ZsumK {
   int R, H, W, W_max, d_v, V, nch_max;
-  int zblocks;          // blocks of the head sum; the blocks after them transpose
+  int zblocks;          // blocks of the head sum; blocks after them transpose the codebook
   int split;            // bf16 codebook: write zf; fp32 codebook: write z
+  int f16_on;           // the two-term fp16 form may be used (its codebook prepared)
   const float* o;       // [R,H,W,d_v]
   float* z;             // [R,W_max,d_v]
   u32x4* zf;
-  const void* wout;     // [d_v,V]
+  float* zscale;        // [R,W_max] 2^-t_b (two-term fp16 form)
+  const uint32_t* f16flag;
+  const void* wout;     // [d_v,V] (transpose blocks)
   void* woutT;          // [V,d_v]
 };
 
@@ -80,11 +202,15 @@ __device__ void transpose_codebook(const WT* __restrict__ w, WT* __restrict__ wt
   }
 }
 
-// Blocks [0, zblocks): one thread per 8 consecutive elements of one beam of one
-// request (beams padded to a multiple of 32 with zeros); all heads' loads are in
-// flight at once (up to 16), the sum runs in head order.  Later blocks: codebook
-// transpose.  STREAM: o is far larger than the last-level cache, and its loads are
-// non-temporal (streamed past that cache rather than evicting the step's records).
+
+// Blocks [0, zblocks): one thread per 8 consecutive elements of one beam of one request
+// (beams padded to a multiple of 32 with zeros); all heads' loads are in flight at once
+// (up to 16), the sum runs in head order.  For a bf16 codebook z is written as the MFMA
+// operand: two fp16 terms and the beam's scale where that form is on and every code tile
+// fits fp16, else three bf16 terms.  Later blocks (when the codebook was not prepared by
+// wprep_kernel): the codebook transpose.  STREAM: o is far larger than the last-level
+// cache, and its loads are non-temporal (streamed past that cache rather than evicting
+// the step's records).
 template <bool STREAM>
 __global__ void __launch_bounds__(256) zsum_kernel(ZsumK a) {
   if (int(blockIdx.x) >= a.zblocks) {
@@ -95,9 +221,12 @@ __global__ void __launch_bounds__(256) zsum_kernel(ZsumK a) {
       transpose_codebook(static_cast<const float*>(a.wout), static_cast<float*>(a.woutT), a.d_v, a.V, t0, nb);
     return;
   }
+  const bool f16 = a.split && a.f16_on && *a.f16flag == 0u;   // launch-uniform
   const int g8 = a.d_v / 8, HV = a.d_v / 2;
   const int per_req = ((a.W + 31) & ~31) * g8;
   const int n = a.R * per_req;
+  // a beam's g8 threads are consecutive lanes of one wave (per_req is a multiple of
+  // 32 g8 and the stride of 64): the loop runs the same count on every lane
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += a.zblocks * blockDim.x) {
     const int r = i / per_req, e = i % per_req;
     const int b = e / g8, d0 = 8 * (e % g8);
@@ -124,20 +253,43 @@ __global__ void __launch_bounds__(256) zsum_kernel(ZsumK a) {
       }
     }
     if (a.split) {
-      uint32_t bh[8], bm[8], bl[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float x = k < 4 ? s0[k] : s1[k - 4];
-        bh[k] = f2bf(x);
-        const float r1 = x - bf2f(bh[k]);
-        bm[k] = f2bf(r1);
-        bl[k] = f2bf(r1 - bf2f(bm[k]));
-      }
       const int hf = d0 / HV, kk = (d0 % HV) / 8;
       u32x4* dst = a.zf + zf_lane_base(r, a.nch_max, a.d_v, b, hf) + size_t(kk) * 3 * 64;
-      dst[0] = pack8(bh);
-      dst[64] = pack8(bm);
-      dst[128] = pack8(bl);
+      if (f16) {
+        // the beam's largest |z| over its g8 threads, then the scale 2^t that puts it in
+        // [2^14, 2^15)
+        float mx = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mx = fmaxf(mx, fmaxf(fabsf(s0[k]), fabsf(s1[k])));
+        for (int off = 1; off < g8; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        int ex = 0;
+        (void)frexpf(mx, &ex);                                // mx < 2^ex
+        int tb = (mx > 0.0f && __builtin_isfinite(mx)) ? 15 - ex : 0;
+        tb = tb < -100 ? -100 : (tb > 100 ? 100 : tb);
+        uint32_t hh[8], hl[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float x = ldexpf(k < 4 ? s0[k] : s1[k - 4], tb);
+          hh[k] = f2h_bits(x);
+          hl[k] = f2h_bits(x - h2f(hh[k]));
+        }
+        dst[0] = pack8(hh);
+        dst[64] = pack8(hl);
+        if (d0 == 0 && b < a.W) a.zscale[size_t(r) * a.W_max + b] = ldexpf(1.0f, -tb);
+      } else {
+        uint32_t bh[8], bm[8], bl[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float x = k < 4 ? s0[k] : s1[k - 4];
+          bh[k] = f2bf(x);
+          const float r1 = x - bf2f(bh[k]);
+          bm[k] = f2bf(r1);
+          bl[k] = f2bf(r1 - bf2f(bm[k]));
+        }
+        dst[0] = pack8(bh);
+        dst[64] = pack8(bm);
+        dst[128] = pack8(bl);
+      }
     } else if (b < a.W) {
       float* dst = a.z + (size_t(r) * a.W_max + b) * a.d_v + d0;
       *reinterpret_cast<f32x4*>(dst) = s0;
@@ -175,6 +327,27 @@ __device__ __forceinline__ f32x16 block_mfma_bf16(const u32x4* w, const u32x4* z
   return acc;
 }
 
+// The same block with z in two fp16 terms (h, l) against the rescaled fp16 codebook.
+template <int KS>
+__device__ __forceinline__ f32x16 block_mfma_f16(const u32x4* w, const u32x4* zh, const u32x4* zl,
+                                                 f32x16 acc = {}) {
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const f16x8 x = __builtin_bit_cast(f16x8, w[kk]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(x, __builtin_bit_cast(f16x8, zl[kk]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(x, __builtin_bit_cast(f16x8, zh[kk]), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Either form of the bf16-codebook block: two fp16 terms (F16) or three bf16 terms.
+template <bool F16, int KS>
+__device__ __forceinline__ f32x16 block_mfma_split(const u32x4* w, const u32x4* zh, const u32x4* zm,
+                                                   const u32x4* zl, f32x16 acc = {}) {
+  if constexpr (F16) return block_mfma_f16<KS>(w, zh, zm, acc);
+  else return block_mfma_bf16<KS>(w, zh, zm, zl, acc);
+}
+
 template <int DV>
 __device__ __forceinline__ f32x16 block_mfma_f32(const float* wt, int code, int V, int hf,
                                                  const float* zv) {
@@ -195,6 +368,11 @@ struct LogitsK {
   const float* z;        // [R,W_max,DV]      fp32 codebook
   const u32x4* zf;       // operand fragments bf16 codebook
   const void* woutT;     // [V,DV]
+  const void* woutT16;   // [V,DV] fp16, tile j scaled by 2^s_j (two-term form)
+  const float* zscale;   // [R,W_max] 2^-t_b (two-term form)
+  const int32_t* tscale; // [n_tiles(V)] s_j
+  const uint32_t* f16flag; // set: the three-term form
+  int f16_on;            // the two-term form may be used
   float* tmax;           // per request: largest logit of each (beam, tile)
   size_t tmax_stride;    // elements per request
   float4* lse_part;      // [R,W_max,nvg]: max, sum of exp(x - max), min tile max
@@ -269,11 +447,13 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   // round(m log2 e), an error of about |m| 2^-24 in the exponent, below 1e-7 relative for
   // |m| < 2 (and |m| 2^-24 absolute in the log-sum-exp, the size of the rounding of the
   // score itself)
-  auto fold_full = [&](const f32x16& acc, int c0) {
+  // fb: the logits are acc x fb (1 but for the two-term fp16 form, whose accumulators
+  // carry the scale 2^(s + t_b)); lb = log2 e x fb
+  auto fold_full = [&](const f32x16& acc, int c0, float fb, float lb) {
     float tm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) tm = fmaxf(tm, acc[i]);
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    tm = fmaxf(tm, __shfl_xor(tm, 32)) * fb;
     put_tm(tm, c0);
     nrun = fminf(nrun, tm);
     const bool up = tm > mrun;
@@ -282,9 +462,9 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     mrun = up ? tm : mrun;
     const float nml = -mrun * kLog2e;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) srun += __builtin_amdgcn_exp2f(fmaf(acc[i], kLog2e, nml));
+    for (int i = 0; i < 16; ++i) srun += __builtin_amdgcn_exp2f(fmaf(acc[i], lb, nml));
   };
-  auto fold = [&](const f32x16& acc, int c0) {
+  auto fold = [&](const f32x16& acc, int c0, float fb, float lb) {
     const bool full = c0 + 32 <= a.V;              // block-uniform
     float tm = -INFINITY;
     if (full) {
@@ -295,7 +475,7 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
       for (int i = 0; i < 16; ++i)
         if (c0 + 8 * (i >> 2) + 4 * hf + (i & 3) < a.V) tm = fmaxf(tm, acc[i]);
     }
-    tm = fmaxf(tm, __shfl_xor(tm, 32));            // code c0 is valid: tm is finite
+    tm = fmaxf(tm, __shfl_xor(tm, 32)) * fb;       // code c0 is valid: tm is finite
     put_tm(tm, c0);
     nrun = fminf(nrun, tm);
     if (tm > mrun) {
@@ -305,24 +485,37 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     const float nml = -mrun * kLog2e;
     if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) srun += __builtin_amdgcn_exp2f(fmaf(acc[i], kLog2e, nml));
+      for (int i = 0; i < 16; ++i) srun += __builtin_amdgcn_exp2f(fmaf(acc[i], lb, nml));
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (c0 + 8 * (i >> 2) + 4 * hf + (i & 3) < a.V)
-          srun += __builtin_amdgcn_exp2f(fmaf(acc[i], kLog2e, nml));
+          srun += __builtin_amdgcn_exp2f(fmaf(acc[i], lb, nml));
     }
   };
 
-  if constexpr (WBF16) {
+  // the bf16 codebook's two forms: z in two fp16 terms against the rescaled codebook
+  // (F16), or in three bf16 terms; one instantiation runs, chosen per launch
+  auto bf16_body = [&](auto f16c) {
+    constexpr bool F16 = decltype(f16c)::value;
     constexpr int KS = DV / 16;
+    constexpr int NTERM = F16 ? 2 : 3;             // MFMAs per k-step
     constexpr int RS = DV / 8 + 1;                 // LDS row stride in u32x4 (16 B pad)
+    // the logits of tile j are acc x 2^-(t_b + s_j): the beam's factor, the tile's
+    // exponents (staged in LDS with the first codebook tile)
+    const float zsb = F16 ? (bvalid ? a.zscale[size_t(r) * a.W_max + b] : 1.0f) : 1.0f;
+    __shared__ float tsf[F16 ? kMaxGroupTiles : 1];        // 2^-s_j of the group's tiles
+    if constexpr (F16) {
+      if (threadIdx.x < kMaxGroupTiles && code_lo + 32 * int(threadIdx.x) < code_hi)
+        tsf[threadIdx.x] = ldexpf(1.0f, -a.tscale[(code_lo >> 5) + threadIdx.x]);
+    }
+    auto tfac = [&](int c0) { return F16 ? zsb * tsf[(c0 - code_lo) >> 5] : 1.0f; };
     // codebook tiles staged per barrier: two where the z operand leaves the registers
     constexpr int TPS = KS <= 8 ? 2 : 1;
     constexpr int NE = TPS * 32 * DV / 8;          // u32x4 per stage
     constexpr int PT = (NE + 64 * kLogitsWaves - 1) / (64 * kLogitsWaves);
     __shared__ u32x4 tile[2][TPS * 32 * RS];
-    const u32x4* wt = static_cast<const u32x4*>(a.woutT);
+    const u32x4* wt = static_cast<const u32x4*>(F16 ? a.woutT16 : a.woutT);
     // thread e-th entry of a tile: row e / (DV / 8), column e % (DV / 8); rows past the
     // codebook load code 0 (never used)
     u32x4 stg[PT];
@@ -348,24 +541,25 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
       // the first tile's loads go out before the z operand's (loads complete in order,
       // so staging the tile then waits for those alone)
       fetch(code_lo);
-      u32x4 zh[KS], zm[KS], zl[KS];
+      u32x4 zh[KS], zm[KS], zl[F16 ? 1 : KS];
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         zh[kk] = zb[(3 * kk) * 64];
         zm[kk] = zb[(3 * kk + 1) * 64];
-        zl[kk] = zb[(3 * kk + 2) * 64];
+        if constexpr (!F16) zl[kk] = zb[(3 * kk + 2) * 64];
       }
       put(0);
       // wait for the whole z operand here, so that inside the loop only the prefetched
       // tile is waited for
-      asm volatile("" ::"v"(zl[KS - 1][0]));
+      if constexpr (F16) asm volatile("" ::"v"(zm[KS - 1][0]));
+      else asm volatile("" ::"v"(zl[KS - 1][0]));
       __syncthreads();
       if (code_lo + 32 * TPS < code_hi) fetch(code_lo + 32 * TPS);
       auto mfma_tile = [&](int buf, int sub) {
         u32x4 w[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) w[kk] = tile[buf][(32 * sub + m) * RS + (HV / 8) * hf + kk];
-        return block_mfma_bf16<KS>(w, zh, zm, zl);
+        return block_mfma_split<F16, KS>(w, zh, zm, zl);
       };
       // software pipeline over stages of two tiles (64 codes, one barrier): the MFMAs of
       // stage i + 1 are issued before the epilogue of stage i, so the matrix cores and
@@ -385,10 +579,11 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
           __syncthreads();
           fetch(c0 + 128);
           const f32x16 n0 = mfma_tile(buf ^ 1, 0), n1 = mfma_tile(buf ^ 1, 1);
-          fold_full(a0, c0);
-          fold_full(a1, c0 + 32);
+          const float f0 = tfac(c0), f1 = tfac(c0 + 32);
+          fold_full(a0, c0, f0, kLog2e * f0);
+          fold_full(a1, c0 + 32, f1, kLog2e * f1);
 #pragma unroll
-          for (int i = 0; i < 6 * KS; ++i) {
+          for (int i = 0; i < 2 * NTERM * KS; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
           }
@@ -396,13 +591,18 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
           a1 = n1;
           buf ^= 1;
         }
-        fold(a0, c0);
-        if (c0 + 32 < code_hi) fold(a1, c0 + 32);
+        const float f0 = tfac(c0);
+        fold(a0, c0, f0, kLog2e * f0);
+        if (c0 + 32 < code_hi) {
+          const float f1 = tfac(c0 + 32);
+          fold(a1, c0 + 32, f1, kLog2e * f1);
+        }
       } else {
         int buf = 0;
         for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
           const bool more = c0 + 32 < code_hi;       // block-uniform
-          fold(mfma_tile(buf, 0), c0);
+          const float f0 = tfac(c0);
+          fold(mfma_tile(buf, 0), c0, f0, kLog2e * f0);
           if (more) {
             put(buf ^ 1);
             __syncthreads();
@@ -430,17 +630,22 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
           for (int kk = 0; kk < KZ; ++kk) {
             zh[kk] = zb[(3 * (k0 + kk)) * 64];
             zm[kk] = zb[(3 * (k0 + kk) + 1) * 64];
-            zl[kk] = zb[(3 * (k0 + kk) + 2) * 64];
+            zl[kk] = F16 ? zm[kk] : zb[(3 * (k0 + kk) + 2) * 64];
             w[kk] = tile[buf][m * RS + (HV / 8) * hf + k0 + kk];
           }
-          acc = block_mfma_bf16<KZ>(w, zh, zm, zl, acc);
+          acc = block_mfma_split<F16, KZ>(w, zh, zm, zl, acc);
         }
-        fold(acc, c0);
+        const float f0 = tfac(c0);
+        fold(acc, c0, f0, kLog2e * f0);
         if (more) put(buf ^ 1);
         __syncthreads();
         buf ^= 1;
       }
     }
+  };
+  if constexpr (WBF16) {
+    if (a.f16_on && *a.f16flag == 0u) bf16_body(std::true_type{});   // launch-uniform
+    else bf16_body(std::false_type{});
   } else {
     const float* zr = a.z + (size_t(r) * a.W_max + (bvalid ? b : 0)) * DV + HV * hf;
     float zv[HV];
@@ -448,7 +653,7 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     for (int i = 0; i < HV; ++i) zv[i] = bvalid ? zr[i] : 0.0f;
     const float* wt = static_cast<const float*>(a.woutT);
     for (int c0 = code_lo; c0 < code_hi; c0 += 32)
-      fold(block_mfma_f32<DV>(wt, c0 + m, a.V, hf, zv), c0);
+      fold(block_mfma_f32<DV>(wt, c0 + m, a.V, hf, zv), c0, 1.0f, kLog2e);
   }
   if constexpr (STAGE_TM) {
     __syncthreads();
@@ -1166,6 +1371,11 @@ struct RefineK {
   const uint32_t* groups;
   const uint32_t* gtiles;
   uint32_t* rkeys;       // [R,W_max,32]: keys of the chosen tiles' candidates (0: no code)
+  const void* woutT16;   // [V,DV] fp16, tile j scaled by 2^s_j (two-term form)
+  const float* zscale;   // [R,W_max] 2^-t_b (two-term form)
+  const int32_t* tscale; // [n_tiles(V)] s_j
+  const uint32_t* f16flag; // set: the three-term form
+  int f16_on;            // the two-term form may be used
   int forced_blocks;     // first blocks: the forced candidates' logits (32 per block)
   int K;                 // forced candidates per request (W_next)
   const int32_t *forced_parent, *forced_token;   // [R,K] (or null)
@@ -1194,6 +1404,10 @@ __device__ __forceinline__ void forced_logit8(const RefineK& a, int r, int i) {
     c = c < 0 ? 0 : (c >= a.V ? a.V - 1 : c);
   }
   float zd[UPL][8], wd[UPL][8];
+  // z from its operand terms: (h + l) 2^-t (exact: h + l has 22 significant bits) for the
+  // two-term fp16 form, (hi + mid) + lo for the three bf16 terms
+  const bool f16 = WBF16 && a.f16_on && *a.f16flag == 0u;
+  const float zs = f16 ? a.zscale[size_t(r) * a.W_max + b] : 1.0f;
 #pragma unroll
   for (int q = 0; q < UPL; ++q) {
     const int u = j + 8 * q;
@@ -1201,13 +1415,23 @@ __device__ __forceinline__ void forced_logit8(const RefineK& a, int r, int i) {
     if constexpr (WBF16) {
       const int hf = d0 / HV, kk = (d0 % HV) / 8;
       const u32x4* p = a.zf + zf_lane_base(r, a.nch_max, DV, b, hf) + size_t(kk) * 3 * 64;
-      float zh[8], zm[8], zl[8];
-      unpack8(p[0], zh);
-      unpack8(p[64], zm);
-      unpack8(p[128], zl);
+      const u32x4 p0 = p[0], p1 = p[64], p2 = f16 ? p1 : p[128];
       unpack8(static_cast<const u32x4*>(a.woutT)[(size_t(c) * DV + d0) / 8], wd[q]);
+      if (f16) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) zd[q][e] = u < NU ? (zh[e] + zm[e]) + zl[e] : 0.0f;
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t hb = (e & 1) ? (p0[e / 2] >> 16) : (p0[e / 2] & 0xFFFFu);
+          const uint32_t lb = (e & 1) ? (p1[e / 2] >> 16) : (p1[e / 2] & 0xFFFFu);
+          zd[q][e] = u < NU ? (h2f(hb) + h2f(lb)) * zs : 0.0f;
+        }
+      } else {
+        float zh[8], zm[8], zl[8];
+        unpack8(p0, zh);
+        unpack8(p1, zm);
+        unpack8(p2, zl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zd[q][e] = u < NU ? (zh[e] + zm[e]) + zl[e] : 0.0f;
+      }
     } else {
       const f32x4* zp = reinterpret_cast<const f32x4*>(a.z + (size_t(r) * a.W_max + b) * DV + d0);
       const f32x4* wp = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.woutT) + size_t(c) * DV + d0);
@@ -1260,27 +1484,37 @@ __global__ void __launch_bounds__(256, 3) refine_kernel(RefineK a) {
   // the beam's cumulative score and log-sum-exp go out with the operands
   const float cb = a.cum[size_t(r) * a.W_max + b], lb = a.lse[size_t(r) * a.W_max + b];
   f32x16 acc;
+  float fb = 1.0f;                                          // logits = acc x fb
   if constexpr (WBF16) {
-    // the same MFMA sequence as the first pass (kk ascending), operands held for at
-    // most eight kk at a time
+    // the same MFMA sequence as the first pass (kk ascending), in the same form, with
+    // operands held for at most eight kk at a time
     constexpr int KS = DV / 16, KP = KS > 8 ? 8 : KS;
     const u32x4* zb = a.zf + zf_lane_base(r, a.nch_max, DV, b, hf);
-    const u32x4* wt = static_cast<const u32x4*>(a.woutT);
     const int code = c0 + m;
     const size_t row = size_t(code < a.V ? code : 0) * DV + HV * hf;
-    acc = f32x16{};
+    auto run = [&](auto f16c) {
+      constexpr bool F16 = decltype(f16c)::value;
+      const u32x4* wt = static_cast<const u32x4*>(F16 ? a.woutT16 : a.woutT);
+      acc = f32x16{};
 #pragma unroll 1
-    for (int k0 = 0; k0 < KS; k0 += KP) {
-      u32x4 zh[KP], zm[KP], zl[KP], w[KP];
+      for (int k0 = 0; k0 < KS; k0 += KP) {
+        u32x4 zh[KP], zm[KP], zl[KP], w[KP];
 #pragma unroll
-      for (int kk = 0; kk < KP; ++kk) {
-        zh[kk] = zb[(3 * (k0 + kk)) * 64];
-        zm[kk] = zb[(3 * (k0 + kk) + 1) * 64];
-        zl[kk] = zb[(3 * (k0 + kk) + 2) * 64];
-        w[kk] = wt[row / 8 + k0 + kk];
+        for (int kk = 0; kk < KP; ++kk) {
+          zh[kk] = zb[(3 * (k0 + kk)) * 64];
+          zm[kk] = zb[(3 * (k0 + kk) + 1) * 64];
+          zl[kk] = F16 ? zm[kk] : zb[(3 * (k0 + kk) + 2) * 64];
+          w[kk] = wt[row / 8 + k0 + kk];
+        }
+        __builtin_amdgcn_sched_barrier(0);        // every operand load issued before the MFMAs
+        acc = block_mfma_split<F16, KP>(w, zh, zm, zl, acc);
       }
-      __builtin_amdgcn_sched_barrier(0);          // every operand load issued before the MFMAs
-      acc = block_mfma_bf16<KP>(w, zh, zm, zl, acc);
+    };
+    if (a.f16_on && *a.f16flag == 0u) {                     // launch-uniform
+      fb = ldexpf(a.zscale[size_t(r) * a.W_max + b], -a.tscale[j]);
+      run(std::true_type{});
+    } else {
+      run(std::false_type{});
     }
   } else {
     const float* zr = a.z + (size_t(r) * a.W_max + b) * DV + HV * hf;
@@ -1297,7 +1531,7 @@ __global__ void __launch_bounds__(256, 3) refine_kernel(RefineK a) {
       u32x4 kq;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t key = f2key(cand_score(cb, acc[4 * q + e], lb));
+        const uint32_t key = f2key(cand_score(cb, acc[4 * q + e] * fb, lb));
         kq[e] = c0 + 8 * q + 4 * hf + e < a.V ? key : 0u;
       }
       out[2 * q + hf] = kq;
@@ -1327,6 +1561,8 @@ struct FinK {
   int32_t *parent, *token;
   float* score;
   int32_t* status;
+  uint32_t* f16flag;
+  int f16_on;
 };
 
 // Refined keys kept in LDS by the final select; more than this many keys at or above
@@ -1536,6 +1772,12 @@ __global__ void __launch_bounds__(1024) final_kernel(FinK a) {
     a.order_next[size_t(r) * a.W_max + p] = tid;
     a.opos_next[size_t(r) * a.W_max + tid] = int32_t(p);
   }
+  // every kernel that reads the fp16 flag has run: report the three-term form (status
+  // bit 2), then clear the flag for the next selection
+  if (r == 0 && tid == 0) {
+    if (a.split && a.f16_on && *a.f16flag != 0u) atomicOr(a.status, 4);
+    *a.f16flag = 0u;
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1602,13 +1844,39 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   int32_t* opos_next = reinterpret_cast<int32_t*>(ws + L.opos[par ^ 1]);
   int err;
 
-  {  // head sum into the MFMA operand; codebook transpose in the last grid row
+  float* flog = reinterpret_cast<float*>(scr + S.flog);
+  uint32_t* f16flag = reinterpret_cast<uint32_t*>(scr + S.f16flag);
+  int32_t* tscale = reinterpret_cast<int32_t*>(scr + S.tscale);
+  void* woutT16 = scr + S.woutT16;
+  float* zscale = reinterpret_cast<float*>(scr + S.zscale);
+  // The two-term fp16 form saves a third of the logits' MFMA work but needs the codebook
+  // prepared by a launch of its own (~11 us); it pays where the selection's MFMA work is
+  // large (R W V d_v >= 2^33 multiply-adds: the stress and growing decodes), and small
+  // selections keep three bf16 terms with the transpose inside the head-sum launch.
+  // GDN_BEAM_F16_MIN_MACS overrides the threshold (0: wherever the codebook fits)
+  double min_macs = 8589934592.0;
+  if (const char* e = getenv("GDN_BEAM_F16_MIN_MACS")) {
+    if (*e) min_macs = atof(e);
+  }
+  const int f16_on = split && double(a.R) * a.W * a.V * a.d_v >= min_macs;
+  if (f16_on) {  // codebook transpose and each code tile's fp16 form
+    WprepK k{a.d_v, a.V, split, a.Wout, woutT, static_cast<uint16_t*>(woutT16), tscale, f16flag};
+    const dim3 g = dim3(unsigned(Vt)), b = dim3(256);
+    if (a.d_v == 16) hipLaunchKernelGGL(wprep_kernel<16>, g, b, 0, s, k);
+    else if (a.d_v == 128) hipLaunchKernelGGL(wprep_kernel<128>, g, b, 0, s, k);
+    else if (a.d_v == 256) hipLaunchKernelGGL(wprep_kernel<256>, g, b, 0, s, k);
+    else hipLaunchKernelGGL(wprep_kernel<512>, g, b, 0, s, k);
+    if ((err = last_launch_error())) return err;
+  }
+  {  // head sum into the MFMA operand; the codebook transpose in the last blocks unless
+     // wprep_kernel did it
     const long n = long(a.R) * nch * 32 * (a.d_v / 8);
-    const int ntr = ((a.V + 31) / 32) * ((a.d_v + 31) / 32);   // transpose tiles
     long zb = (n + 255) / 256;
     zb = zb < 1 ? 1 : (zb > 65536 ? 65536 : zb);
-    const int tb = ntr < 256 ? ntr : 256;
-    ZsumK k{a.R, a.H, a.W, a.W_max, a.d_v, a.V, nch_max, int(zb), split, a.o, z, zf, a.Wout, woutT};
+    const int ntr = ((a.V + 31) / 32) * ((a.d_v + 31) / 32);
+    const int tb = f16_on ? 0 : (ntr < 256 ? ntr : 256);
+    ZsumK k{a.R, a.H, a.W, a.W_max, a.d_v, a.V, nch_max, int(zb), split, f16_on, a.o, z, zf, zscale,
+            f16flag, a.Wout, woutT};
     // o above half of the 256 MiB last-level cache: streamed (512 MiB of o: 144 -> 120
     // us per launch; 64 MiB of o is still in that cache, and plain loads hit it)
     const bool stream = size_t(a.R) * a.H * a.W * a.d_v * 4 > (size_t(128) << 20);
@@ -1626,11 +1894,11 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   // the bounded tile selection where a request's tiles outnumber its list (and the code
   // groups' maxima number at least K); it reads the tile maxima beam-major
   const bool bounded = int64_t(a.W) * Vt > kSelList && int64_t(a.W) * nvg >= Kt;
-  LogitsK lk{a.R, a.W, a.W_max, a.V, nch, nvg, cpw, nch_max, bounded ? 1 : 0, z, zf, woutT, tmax, tstride,
-             lse_part};
-  float* flog = reinterpret_cast<float*>(scr + S.flog);
+  LogitsK lk{a.R, a.W, a.W_max, a.V, nch, nvg, cpw, nch_max, bounded ? 1 : 0, z, zf, woutT, woutT16,
+             zscale, tscale, f16flag, f16_on, tmax, tstride, lse_part};
   RefineK rk{a.W, a.W_max, a.V, Vt, G_max, nch_max, z, zf, woutT, lse, cum, sel, groups, gtiles, rkeys,
-             0, a.W_next, a.forced_parent, a.forced_token, flog, status};
+             woutT16, zscale, tscale, f16flag, f16_on, 0, a.W_next, a.forced_parent, a.forced_token, flog,
+             status};
   if ((err = launch_by_dv(a, lk, rk, 0, s, false))) return err;
   {
     int tg_shift = 0;
@@ -1650,7 +1918,7 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   {
     FinK k{a.W, a.W_max, a.V, Vt, a.W_next, Kt, a.T_max, a.t, a.d_v, nch_max, split, sel, rkeys, tiles,
            lse, cum, cum_next, anc, anc_next, tok, tok_next, opos, order_next, opos_next, flog,
-           a.forced_parent, a.forced_token, a.parent, a.token, a.score, status};
+           a.forced_parent, a.forced_token, a.parent, a.token, a.score, status, f16flag, f16_on};
     hipLaunchKernelGGL(final_kernel, dim3(a.R), dim3(1024), 0, s, k);
     if ((err = last_launch_error())) return err;
   }

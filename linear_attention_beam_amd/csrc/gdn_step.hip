@@ -71,6 +71,9 @@ __global__ void __launch_bounds__(256) init_kernel(InitArgs a) {
   }
   if (blockIdx.x == 0 && threadIdx.x < 64)
     reinterpret_cast<int32_t*>(ws + a.L.status)[threadIdx.x] = 0;
+  // the selection's flag for code tiles that do not fit fp16 starts clear (each selection
+  // clears it after use)
+  if (blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<uint32_t*>(ws + a.L.S.f16flag) = 0u;
 }
 
 // ---------------------------------------------------------------- step

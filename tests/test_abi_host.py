@@ -58,7 +58,8 @@ def expected_bytes(R, H, d_k, d_v, T, W, V, e, ew, HK=None):
                R * HK * T * W * d_k * e, R * W * T * 4, R * W * T * 4, R * W * T * 4, R * W * T * 4,
                R * W * 4, R * W * 4, R * W * 4, R * W * 4, R * W * 4, R * W * 4, R * W * d_v * 4, R * nch * 32 * d_v * 6, V * d_v * ew,
                R * Vt * W * 4, R * W * nvg * 16, R * W * 4, R * 16, R * Vt * W * 4, R * W * 4,
-               R * groups * 4, R * groups * 32 * 4, R * W * 32 * 4, R * W * 4, 64 * 4]
+               R * groups * 4, R * groups * 32 * 4, R * W * 32 * 4, R * W * 4, 128, Vt * 4, V * d_v * 2, R * W * 4,
+               64 * 4]
     return sum(_a(x) for x in regions)
 
 

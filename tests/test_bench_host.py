@@ -219,3 +219,21 @@ def test_stamp_records_count():
     assert b.stamp_records(wl, 0) == wl.R * wl.H * 4 * 8          # 4 waves, 8 chunks of 32
     wv = synth.get("wide_v")                                      # d_v = 512: two row blocks of 8 waves
     assert b.stamp_records(wv, 0) == wv.R * wv.H * 2 * 8 * 8
+
+
+def test_step_kernel_code_hash_matches_the_build():
+    """The hash the build writes is the machine code of every step_kernel instantiation
+    in the gfx950 device object, and bench.py reads that file."""
+    import importlib.util as iu
+    spec = iu.spec_from_file_location("gdn_build", os.path.join(ROOT, "linear_attention_beam_amd", "build.py"))
+    m = iu.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    dev = os.path.join(ROOT, "linear_attention_beam_amd", "_build", "gdn_step.gfx950.o")
+    if not os.path.exists(dev) or not os.path.exists(m.STEP_HASH):
+        pytest.skip("the library is not built")
+    h = m.step_kernel_code_hash(dev)
+    assert len(h) == 16 and open(m.STEP_HASH).read().strip() == h
+    assert _bench().kernel_hash() == h
+    syms, _ = m._elf_symbols(open(dev, "rb").read())
+    names = [x[0] for x in syms if "step_kernel" in x[0] and x[3] > 0]
+    assert any("step_kernelILi128ELi128ELb1ELi3E" in n for n in names)

@@ -560,3 +560,60 @@ def test_projection_stamps_keep_results(name):
     g.step(0)
     torch.cuda.synchronize()
     assert int(buf.abs().sum()) == 0, "only the armed launch stamps"
+
+
+@pytest.fixture
+def f16_everywhere(monkeypatch):
+    """Selections of any size take the two-term fp16 form where the codebook fits."""
+    monkeypatch.setenv("GDN_BEAM_F16_MIN_MACS", "0")
+
+
+@pytest.mark.parametrize("name,R", [("batch", 2), ("single_bf16_t6", 1), ("mixed_c", 1), ("multi_bounded", 3),
+                                    ("single_dk256", 1), ("single_dv512", 1), ("batch_gqa", 2)])
+def test_select_mode_parity_fp16_form(name, R, f16_everywhere):
+    """The select-mode parity of the small cases with the two-term fp16 logits (the
+    default takes it only for selections of 2^33 multiply-adds or more)."""
+    test_select_mode_parity(name, R)
+
+
+@pytest.mark.parametrize("name,R", [("batch", 2), ("single_bf16_t8", 1), ("single_dv512", 1)])
+def test_forced_parents_parity_fp16_form(name, R, f16_everywhere):
+    test_forced_parents_parity(name, R)
+
+
+@pytest.mark.parametrize("name", ["mixed_c", "single_dv512", "tiny_bounded"])
+def test_codebook_outside_fp16_range(name, f16_everywhere):
+    """A bf16 codebook whose exponents span more than fp16 holds (row 0 scaled by 2^-40,
+    exact in bf16 and float64) takes z in three bf16 terms (status bit 2); the selection
+    is still exact against float64 rescoring, and the ancestry follows eq. (9)."""
+    wl = _wl(name)
+    if wl.wout != "bf16":
+        wl = wl.scaled(name=name + "_bf16", io="bf16", wout="bf16")
+    g = GpuDecode(wl, R=1, exact=())
+    g.Wout[0, :] = g.Wout[0, :] * 2.0 ** -40
+    g.Wout64[0, :] = g.Wout64[0, :] * 2.0 ** -40
+    torch.cuda.synchronize()
+    anc_ref = np.zeros((wl.width(0), 0), np.int32)
+    g.init()
+    for t in range(wl.T):
+        o = to_np(g.step(t))
+        cum_before = g.export(B.GDN_EXPORT_CUM)
+        sel = g.select(t)
+        K = wl.width(t + 1)
+        check_selection(o[0], cum_before[0][:wl.width(t)], g.Wout64, K, {k: v[0] for k, v in sel.items()},
+                        f"t={t}")
+        anc_ref = _eq9(anc_ref, sel["parent"][0], t)
+        np.testing.assert_array_equal(g.export(B.GDN_EXPORT_ANCESTRY)[0][:K, :t + 1], anc_ref)
+    assert g.export(B.GDN_EXPORT_STATUS)[0] == 4
+
+
+def test_fp16_form_for_ordinary_codebooks(f16_everywhere):
+    """A codebook within fp16's range (the workloads' N(0, 1/d_v) draws) takes the two-term
+    fp16 form: status bit 2 stays clear."""
+    wl = _wl("mixed_c")
+    g = GpuDecode(wl, R=1, exact=())
+    g.init()
+    for t in range(wl.T):
+        g.step(t)
+        g.select(t)
+    assert g.export(B.GDN_EXPORT_STATUS)[0] == 0
