@@ -150,8 +150,8 @@ def decode_floor_s(wl, bytes_t):
     below the MFMA ridge).  select(t): o_t read (4 H W_t d_v per request), cumulative
     scores, the codebook (once), the top-W outputs (12 W_next) and the new ancestry and
     SID prefixes (8 (t + 1) W_next); flops: the logits W_t x d_v x V, 2 per element,
-    three times with z split into three bf16 terms for a bf16 codebook (fp32 MFMA
-    otherwise), which the selection needs to stay exact at fp32 precision.
+    twice for a bf16 codebook (z in two fp16 terms against the codebook rescaled into
+    fp16, which keeps fp32 precision; fp32 MFMA for an fp32 codebook).
     """
     bw = HBM_PEAK_GBS * 1e9
     dvp = max(wl.d_v, 32)
@@ -168,7 +168,7 @@ def select_floor_s(wl, t):
     W, Wn = wl.width(t), wl.width(t + 1)
     sel_bytes = wl.R * (4 * wl.H * W * wl.d_v + 4 * W + 12 * Wn + 8 * (t + 1) * Wn) + wl.d_v * wl.V * ew
     if wl.wout == "bf16":
-        sel_flops, peak = 3 * 2 * wl.R * W * wl.d_v * wl.V, MFMA_BF16_PEAK
+        sel_flops, peak = 2 * 2 * wl.R * W * wl.d_v * wl.V, MFMA_BF16_PEAK
     else:
         sel_flops, peak = 2 * wl.R * W * wl.d_v * wl.V, MFMA_F32_PEAK
     return max(sel_bytes / bw, sel_flops / peak)
