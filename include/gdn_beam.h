@@ -247,12 +247,25 @@ const char* gdn_beam_last_error(void);
  * starting from zero.  Prompt tokens of all requests are stacked:
  * k [N,H_K,d_k] (H_K = 0: H), v [N,H,d_v], alpha, beta [N,H] fp32, request r owning rows
  * offsets[r] .. offsets[r+1]-1, with offsets [R+1] int32 (device), nondecreasing,
- * offsets[R] = N.  Offsets are clamped to [0, N] on the device.
- * S_out [R,H,d_v,d_k] fp32.  Same head dims as the decode. */
+ * offsets[R] = N.  Offsets are clamped to [0, N] on the device (decreasing offsets give
+ * unspecified states, never an access outside the arrays).  S_out [R,H,d_v,d_k] fp32.
+ * Same head dims as the decode.
+ *
+ * workspace = NULL: eq. (3) token by token in fp32 (no scratch memory).
+ * workspace != NULL (256-byte aligned, workspace_bytes >= gdn_beam_prefill_workspace_bytes):
+ * the chunked form of eq. (3) (32-token chunks; within a chunk the update vectors solve a
+ * unit lower-triangular system, whose inverse a first kernel forms for every chunk in
+ * parallel; a second kernel applies the chunks of each (request, head) in order as matrix
+ * products on MFMA, operands split into bf16 hi + lo parts, fp32 accumulation).  Chunks are
+ * 32-token blocks of the stacked array; a block shared by two prompts is split between
+ * them.  The caller owns the workspace; its contents are scratch.  d_k = 16 has only the
+ * token-sequential form and ignores the workspace.  A short workspace is GDN_ERR_WORKSPACE. */
+size_t gdn_beam_prefill_workspace_bytes(int32_t H, int32_t d_k, int32_t d_v, int64_t N);
 gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t H_K, int32_t d_k, int32_t d_v, int64_t N,
                             const float* k, const float* v, const float* alpha,
                             const float* beta, const int32_t* offsets,
-                            float* S_out, hipStream_t stream);
+                            float* S_out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,7 @@ GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_beam_workspace_bytes", "gdn_beam_init", "gdn_beam_step", "gdn_beam_select",
            "gdn_beam_export", "gdn_beam_export_bytes", "gdn_beam_query", "gdn_beam_destroy",
            "gdn_beam_status_str", "gdn_beam_last_error", "gdn_beam_prefill",
+           "gdn_beam_prefill_workspace_bytes",
            "gdn_fullstate_bytes", "gdn_fullstate_step", "gdn_beam_time_steps", "gdn_beam_step_times",
            "gdn_beam_select_static", "gdn_beam_stamp_projection")
 GDN_STATIC_SCRATCH_BYTES = 64 << 20
@@ -84,7 +85,9 @@ def _load():
         "gdn_beam_step_times": (st, [POINTER(ctypes.c_float), i32, POINTER(i32)]),
         "gdn_beam_status_str": (c_char_p, [st]),
         "gdn_beam_last_error": (c_char_p, []),
-        "gdn_beam_prefill": (st, [i32, i32, i32, i32, i32, c_int64, vp, vp, vp, vp, vp, vp, vp]),
+        "gdn_beam_prefill": (st, [i32, i32, i32, i32, i32, c_int64, vp, vp, vp, vp, vp, vp,
+                                  vp, c_size_t, vp]),
+        "gdn_beam_prefill_workspace_bytes": (c_size_t, [i32, i32, i32, c_int64]),
         "gdn_fullstate_bytes": (st, [POINTER(gdn_beam_config), POINTER(c_size_t)]),
         "gdn_fullstate_step": (st, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp]),
     }
@@ -201,9 +204,15 @@ def gdn_beam_last_error() -> str:
     return _lib.gdn_beam_last_error().decode()
 
 
-def gdn_beam_prefill(R, H, H_K, d_k, d_v, N, k, v, alpha, beta, offsets, S_out, stream=None):
+def gdn_beam_prefill_workspace_bytes(H, d_k, d_v, N):
+    return int(_lib.gdn_beam_prefill_workspace_bytes(H, d_k, d_v, N))
+
+
+def gdn_beam_prefill(R, H, H_K, d_k, d_v, N, k, v, alpha, beta, offsets, S_out,
+                     workspace=None, workspace_bytes=0, stream=None):
     _check(_lib.gdn_beam_prefill(R, H, H_K, d_k, d_v, N, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                 _ptr(offsets), _ptr(S_out), _stream(stream)), "gdn_beam_prefill")
+                                 _ptr(offsets), _ptr(S_out), _ptr(workspace), workspace_bytes,
+                                 _stream(stream)), "gdn_beam_prefill")
 
 
 def gdn_fullstate_bytes(cfg: gdn_beam_config) -> int:

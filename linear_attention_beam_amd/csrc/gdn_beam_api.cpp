@@ -401,10 +401,15 @@ gdn_status gdn_beam_step_times(float* ms, int32_t cap, int32_t* n) {
   return GDN_OK;
 }
 
+size_t gdn_beam_prefill_workspace_bytes(int32_t H, int32_t d_k, int32_t d_v, int64_t N) {
+  if (H < 1 || N < 0 || !dims_supported(d_k, d_v)) return 0;
+  return prefill_workspace_bytes(H, d_k, N);
+}
+
 gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t H_K, int32_t d_k, int32_t d_v, int64_t N,
                             const float* k, const float* v, const float* alpha,
                             const float* beta, const int32_t* offsets, float* S_out,
-                            hipStream_t stream) {
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (R < 1 || H < 1 || N < 0 || H_K < 0) return GDN_ERR_INVALID_ARG;
   if (H_K == 0) H_K = H;
   if (H % H_K != 0) return GDN_ERR_INVALID_ARG;
@@ -415,7 +420,13 @@ gdn_status gdn_beam_prefill(int32_t R, int32_t H, int32_t H_K, int32_t d_k, int3
   if (N > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned16(beta)))
     return GDN_ERR_INVALID_ARG;
   if (N >= (int64_t(1) << 31)) return GDN_ERR_CAPACITY;
-  PrefillArgs a{R, H, H_K, d_k, d_v, N, k, v, alpha, beta, offsets, S_out};
+  float* ws = nullptr;
+  if (workspace && prefill_chunked(d_k)) {
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return GDN_ERR_INVALID_ARG;
+    if (workspace_bytes < prefill_workspace_bytes(H, d_k, N)) return GDN_ERR_WORKSPACE;
+    ws = static_cast<float*>(workspace);
+  }
+  PrefillArgs a{R, H, H_K, d_k, d_v, N, k, v, alpha, beta, offsets, S_out, ws};
   int err = launch_prefill(a, stream);
   if (err) return hip_fail(err, "gdn_beam_prefill");
   return GDN_OK;

@@ -184,12 +184,18 @@ struct SelectArgs {
   SelScratch S;
 };
 
+// Chunked prefill: 32-token chunks; per (chunk, head) the preparation kernel stores the
+// 32 x 32 chunk matrix and two 32-entry decay products.
+constexpr int kChunk = 32;
+constexpr int kPrepFloats = kChunk * kChunk + 2 * kChunk;
+
 struct PrefillArgs {
   int R, H, HK, d_k, d_v;
   int64_t N;
   const float *k, *v, *alpha, *beta;
   const int32_t* offsets;
   float* S_out;
+  float* ws;            // chunked form's workspace, or null for the token-sequential form
 };
 
 struct FullStepArgs {
@@ -218,6 +224,8 @@ int launch_select(const SelectArgs& a, hipStream_t s);
 // 256-aligned); looked up once per device.  Returns a hipError_t value.
 int static_scratch(char** ptr);
 int launch_prefill(const PrefillArgs& a, hipStream_t s);
+bool prefill_chunked(int d_k);
+size_t prefill_workspace_bytes(int H, int d_k, int64_t N);
 int launch_fullstate(const FullStepArgs& a, hipStream_t s);
 int copy_d2d(void* dst, const void* src, size_t bytes, hipStream_t s);
 const char* hip_error_string(int err);

@@ -153,9 +153,11 @@ class BeamDecoder:
             pass
 
 
-def prefill(S_out, k, v, alpha, beta, offsets, stream=None):
+def prefill(S_out, k, v, alpha, beta, offsets, stream=None, chunked=True, workspace=None):
     """S_out [R,H,d_v,d_k] <- eq. (3) over stacked prompt tokens (see gdn_beam_prefill);
-    k [N,H_K,d_k] may hold fewer (key) heads than v [N,H,d_v] (grouped value heads)."""
+    k [N,H_K,d_k] may hold fewer (key) heads than v [N,H,d_v] (grouped value heads).
+    chunked: the chunked form, with `workspace` (a uint8 device tensor of at least
+    gdn_beam_prefill_workspace_bytes) or a fresh one; otherwise token by token."""
     R, H, d_v, d_k = S_out.shape
     N = k.shape[0]
     dev = S_out.device
@@ -166,5 +168,16 @@ def prefill(S_out, k, v, alpha, beta, offsets, stream=None):
     _need("alpha", alpha, (N, H), torch.float32, dev)
     _need("beta", beta, (N, H), torch.float32, dev)
     _need("offsets", offsets, (R + 1,), torch.int32, dev)
+    nbytes = 0
+    if chunked:
+        nbytes = B.gdn_beam_prefill_workspace_bytes(H, d_k, d_v, N)
+        if workspace is None and nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            _need("workspace", workspace, (workspace.numel(),), torch.uint8, dev)
+            nbytes = workspace.numel()
+    else:
+        workspace = None
     B.gdn_beam_prefill(R, H, k.shape[1], d_k, d_v, N, k, v, alpha, beta, offsets, S_out,
+                       workspace, nbytes,
                        torch.cuda.current_stream() if stream is None else stream)

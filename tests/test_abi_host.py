@@ -21,7 +21,7 @@ FAKE = 0x7F0000000000            # 256-aligned, never dereferenced
 
 def header_functions():
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:gdn_status|void|const char\*)\s+(gdn_\w+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:gdn_status|void|size_t|const char\*)\s+(gdn_\w+)\s*\(", txt, re.M)))
 
 
 def test_header_symbols_exported():
@@ -186,15 +186,35 @@ def test_step_timing_argument_errors():
 
 def test_prefill_argument_errors():
     f = lambda *a: B.raw_status("gdn_beam_prefill", *a)
-    assert f(2, 3, 0, 64, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_UNSUPPORTED
-    assert f(0, 3, 0, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
-    assert f(2, 3, 0, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == B.GDN_ERR_INVALID_ARG
-    assert f(2, 3, 0, 128, 128, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
-    assert f(2, 3, 0, 128, 128, 10, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
-    assert f(2, 3, 0, 128, 128, 1 << 31, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_CAPACITY
+    F6 = (FAKE,) * 6
+    assert f(2, 3, 0, 64, 64, 10, *F6, None, 0, None) == B.GDN_ERR_UNSUPPORTED
+    assert f(0, 3, 0, 128, 128, 10, *F6, None, 0, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 0, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 0, 128, 128, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 0, 128, 128, 10, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 0, 128, 128, 1 << 31, *F6, None, 0, None) == B.GDN_ERR_CAPACITY
     # grouped value heads: H a multiple of H_K
-    assert f(2, 4, 3, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
-    assert f(2, 4, -1, 128, 128, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 4, 3, 128, 128, 10, *F6, None, 0, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 4, -1, 128, 128, 10, *F6, None, 0, None) == B.GDN_ERR_INVALID_ARG
+    # chunked form: workspace 256-byte aligned and at least the stated size
+    need = B.gdn_beam_prefill_workspace_bytes(3, 128, 128, 10)
+    assert f(2, 3, 0, 128, 128, 10, *F6, FAKE + 16, need, None) == B.GDN_ERR_INVALID_ARG
+    assert f(2, 3, 0, 128, 128, 10, *F6, FAKE, need - 1, None) == B.GDN_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("H,d_k,d_v,N", [(3, 128, 128, 10), (16, 128, 256, 559622),
+                                         (4, 256, 512, 64), (1, 128, 128, 0)])
+def test_prefill_workspace_bytes(H, d_k, d_v, N):
+    """One 32 x 32 chunk matrix and two 32-entry decay products (fp32) per 32-token
+    block of the stacked prompts and value head."""
+    blocks = -(-N // 32)
+    assert B.gdn_beam_prefill_workspace_bytes(H, d_k, d_v, N) == blocks * H * (32 * 32 + 64) * 4
+
+
+def test_prefill_workspace_bytes_token_form():
+    """d_k = 16 has only the token-sequential form; unsupported dims need nothing."""
+    assert B.gdn_beam_prefill_workspace_bytes(1, 16, 16, 64) == 0
+    assert B.gdn_beam_prefill_workspace_bytes(1, 64, 64, 64) == 0
 
 
 def test_status_strings():
