@@ -21,6 +21,8 @@
 // a block holding the end of one prompt and the start of the next has two segments, and
 // every in-chunk product (decays, A, X) stays inside one segment, so block b serves each
 // request it overlaps with that request's tokens only.
+#include <type_traits>
+
 #include "gdn_device.h"
 
 namespace gdn {
@@ -268,11 +270,22 @@ struct ChunkCfg {
   static constexpr int XA = KD + 2 * KD_HALF;
   static constexpr int XA_HALF = 32 * 64;
   static constexpr int GC = XA + 2 * XA_HALF;
-  static constexpr int BUF = GC + 16;
-  static constexpr int KITEMS = 8 * (DK / 4);     // 4 tokens x 4 columns of K each
-  static constexpr int XITEMS = 32 * 8;           // 4 columns of one X row each
-  static constexpr int KPT = (KITEMS + NT - 1) / NT;
-  static constexpr int XPT = (XITEMS + NT - 1) / NT;
+  // With d_k = 128 and 8 waves, V of the chunk also goes through LDS (16-byte loads
+  // instead of one 4-byte load per token and lane): rows of 32 tokens as token pairs,
+  // [pair][row][2], pair rows padded so that tokens t and t + 4 (the two lane halves of an
+  // accumulator) fall on different LDS banks.
+  static constexpr bool VL = DK == 128 && NW == 8;
+  static constexpr int VPS = 2 * RB + 16;         // floats per token pair
+  static constexpr int VS = GC + 16;
+  static constexpr int BUF = VS + (VL ? 16 * VPS * 4 : 0);
+  static constexpr int KITEMS = 16 * (DK / 4);    // 2 tokens x 4 columns of K each
+  static constexpr int XITEMS = 32 * 16;          // 2 columns of one X row each
+  static constexpr int VITEMS = 16 * (RB / 4);    // 2 tokens x 4 rows of V each
+  static constexpr int KPT = KITEMS / NT;
+  static constexpr int XPT = XITEMS / NT;
+  static constexpr int VPT = VL ? VITEMS / NT : 1;
+  static_assert(KITEMS % NT == 0 && XITEMS % NT == 0 && VITEMS % NT == 0,
+                "items split evenly over threads");
 };
 
 // byte offset of 16-byte unit q of row t of KA (swizzled over 16 rows)
@@ -281,11 +294,27 @@ __device__ __forceinline__ int ka_off(int t, int q) { return t * (DK * 2) + ((q 
 // byte offset of 16-byte unit q (0..3) of row m of a 32-column fragment array (KD, XA)
 __device__ __forceinline__ int k32_off(int m, int q) { return (m << 6) + ((q ^ ((m >> 2) & 3)) << 4); }
 
-__device__ __forceinline__ uint2 pack4(const __bf16* v) {
-  uint2 r;
-  r.x = uint32_t(__builtin_bit_cast(uint16_t, v[0])) | (uint32_t(__builtin_bit_cast(uint16_t, v[1])) << 16);
-  r.y = uint32_t(__builtin_bit_cast(uint16_t, v[2])) | (uint32_t(__builtin_bit_cast(uint16_t, v[3])) << 16);
-  return r;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 hi + lo parts of a pair, packed: hi = bf16(x) (nearest even), lo = bf16(x - hi).
+// The hi values are read back from the packed word, one rounding per pair.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hp, uint32_t& lp) {
+  hp = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x0, x1}), bf16x2));
+  const f32x2 r = {x0 - __uint_as_float(hp << 16), x1 - __uint_as_float(hp & 0xFFFF0000u)};
+  lp = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+}
+__device__ __forceinline__ void split8p(const float* x, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t hq, lq;
+    split2(x[2 * q], x[2 * q + 1], hq, lq);
+    h[q] = hq;
+    l[q] = lq;
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
 }
 
 template <int DK, int DV>
@@ -300,114 +329,170 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
   int beg, end;
   request_span(a, r, beg, end);
   const int b0 = beg / kChunk, b1 = end > beg ? (end - 1) / kChunk + 1 : b0;
+  const size_t kstride = size_t(a.HK) * DK, vstride = size_t(a.H) * DV;   // floats per token
 
-  // ---- registers in flight for one chunk: K tiles, X quads, g/sfx of the K rows, V
-  f32x4 kreg[C::KPT][4];
-  float kg[C::KPT][4], ks[C::KPT][4];
-  f32x4 xreg[C::XPT];
+  // Loads use a per-chunk base (uniform) plus offsets fixed per thread; only the array's
+  // last block, which may reach past N, clamps its rows (to row 0 of the block).  Rows of
+  // other requests are loaded and then replaced by zeros where a block is shared.
+  f32x4 kreg[C::KPT][2], vreg[C::VPT][2];
+  f32x2 kgs[C::KPT][2];                  // g and sfx of the item's two tokens
+  f32x2 xreg[C::XPT];
   float gcl = 1.0f;
-  auto valid = [&](int b, int t) { const int p = b * kChunk + t; return p >= beg && p < end; };
-  auto fetch = [&](int b) {
+  // byte offsets (fixed per thread) of the K rows, X pairs and V rows this thread loads
+  uint32_t koff[C::KPT][2], voff[16], vloff[C::VPT][2];
+#pragma unroll
+  for (int m = 0; m < C::KPT; ++m) {
+    const int it = tid + m * C::NT, t2 = it / (DK / 4), d4 = it % (DK / 4);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) koff[m][e] = uint32_t(((2 * t2 + e) * kstride + 4 * d4) * 4);
+  }
+#pragma unroll
+  for (int m = 0; m < C::VPT; ++m) {
+    const int it = tid + m * C::NT, tp = it / (C::RB / 4), g = it % (C::RB / 4);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) vloff[m][e] = uint32_t(((2 * tp + e) * vstride + 4 * g) * 4);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    voff[i] = uint32_t(((8 * (i >> 2) + 4 * hf + (i & 3)) * vstride + row) * 4);
+  // clamp: the array's last block, which may reach past N (rows past N read row 0)
+  auto fetch = [&](int b, auto clamp) {
+    const char* kb = reinterpret_cast<const char*>(a.k + size_t(b) * kChunk * kstride + size_t(hk) * DK);
     const float* pw = a.ws + (size_t(b) * a.H + h) * kPrepFloats;
+    const int nrow = int(a.N - int64_t(b) * kChunk);
 #pragma unroll
     for (int m = 0; m < C::KPT; ++m) {
-      const int it = tid + m * C::NT;
-      if (C::KITEMS % C::NT == 0 || it < C::KITEMS) {
-        const int t4 = it / (DK / 4), d4 = it % (DK / 4);
+      const int it = tid + m * C::NT, t2 = it / (DK / 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 4 * t4 + e;
-          const bool ok = valid(b, t);
-          const size_t p = ok ? size_t(b) * kChunk + t : 0;
-          kreg[m][e] = ok ? *reinterpret_cast<const f32x4*>(a.k + (p * a.HK + hk) * DK + 4 * d4)
-                          : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-          kg[m][e] = ok ? pw[kChunk * kChunk + t] : 0.0f;
-          ks[m][e] = ok ? pw[kChunk * kChunk + kChunk + t] : 0.0f;
+      for (int e = 0; e < 2; ++e) {
+        uint32_t o = koff[m][e];
+        if constexpr (decltype(clamp)::value)
+          o = 2 * t2 + e < nrow ? o : o - uint32_t((2 * t2 + e) * kstride * 4);
+        kreg[m][e] = *reinterpret_cast<const f32x4*>(kb + o);
+      }
+      kgs[m][0] = *reinterpret_cast<const f32x2*>(pw + kChunk * kChunk + 2 * t2);
+      kgs[m][1] = *reinterpret_cast<const f32x2*>(pw + kChunk * kChunk + kChunk + 2 * t2);
+    }
+    if constexpr (C::VL) {
+      const char* vb = reinterpret_cast<const char*>(a.v + size_t(b) * kChunk * vstride +
+                                                     size_t(h) * DV + size_t(rb) * C::RB);
+#pragma unroll
+      for (int m = 0; m < C::VPT; ++m) {
+        const int it = tid + m * C::NT, tp = it / (C::RB / 4);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          uint32_t o = vloff[m][e];
+          if constexpr (decltype(clamp)::value)
+            o = 2 * tp + e < nrow ? o : o - uint32_t((2 * tp + e) * vstride * 4);
+          vreg[m][e] = *reinterpret_cast<const f32x4*>(vb + o);
         }
       }
     }
 #pragma unroll
     for (int m = 0; m < C::XPT; ++m) {
-      const int it = (C::NT - 1 - tid) + m * C::NT;
-      if (C::XITEMS % C::NT == 0 || it < C::XITEMS) {
-        const int tr = it >> 3, q4 = it & 7;
-        xreg[m] = valid(b, tr) ? *reinterpret_cast<const f32x4*>(pw + tr * kChunk + 4 * q4)
-                               : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
+      const int it = tid + m * C::NT, tr = it >> 4, q2 = it & 15;
+      xreg[m] = *reinterpret_cast<const f32x2*>(pw + tr * kChunk + 2 * q2);
     }
-    if (tid == 0) {
-      int tlast = end - b * kChunk;
-      tlast = (tlast > kChunk ? kChunk : tlast) - 1;
-      gcl = pw[kChunk * kChunk + tlast];
-    }
+    // g of the request's last token in the block; only thread 0 keeps it (a per-thread
+    // address keeps this a vector load, off the scalar path that LDS waits share)
+    int tlast = end - b * kChunk;
+    tlast = (tlast > kChunk ? kChunk : tlast) - 1;
+    gcl = pw[kChunk * kChunk + (tid == 0 ? tlast : 0)];
   };
-  // registers -> LDS buffer (bf16 hi/lo fragments)
-  auto stage = [&](unsigned char* buf) {
+  auto shared_block = [&](int b) { return b * kChunk < beg || (b + 1) * kChunk > end; };
+  auto valid = [&](int b, int t) { const int p = b * kChunk + t; return p >= beg && p < end; };
+  // registers of block b -> LDS buffer (bf16 hi/lo fragments)
+  auto stage = [&](int b, unsigned char* buf) {
+    const bool part = shared_block(b);
 #pragma unroll
     for (int m = 0; m < C::KPT; ++m) {
-      const int it = tid + m * C::NT;
-      if (C::KITEMS % C::NT == 0 || it < C::KITEMS) {
-        const int t4 = it / (DK / 4), d4 = it % (DK / 4);
-        // KA rows t = 4 t4 + e: -g_t k_t[4 d4 .. +4], one 8-byte piece each (hi, lo)
+      const int it = tid + m * C::NT, t2 = it / (DK / 4), d4 = it % (DK / 4);
+      f32x4 kv[2];
+      float gv[2], sv[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 4 * t4 + e;
-          const int d = 4 * d4;
-          const int q = ((d >> 5) << 2) | (k32_unit(d & 31));
-          const int off = ka_off<DK>(t, q) + (k32_slot(d & 31) << 1);
-          __bf16 hv[4], lv[4];
+      for (int e = 0; e < 2; ++e) {
+        kv[e] = kreg[m][e];
+        gv[e] = kgs[m][0][e];
+        sv[e] = kgs[m][1][e];
+      }
+      if (part) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const float x = -kg[m][e] * kreg[m][e][s];
-            hv[s] = static_cast<__bf16>(x);
-            lv[s] = static_cast<__bf16>(x - static_cast<float>(hv[s]));
-          }
-          *reinterpret_cast<uint2*>(buf + C::KA + off) = pack4(hv);
-          *reinterpret_cast<uint2*>(buf + C::KA + C::KA_HALF + off) = pack4(lv);
+        for (int e = 0; e < 2; ++e) {
+          const bool ok = valid(b, 2 * t2 + e);
+          kv[e] = ok ? kv[e] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          gv[e] = ok ? gv[e] : 0.0f;
+          sv[e] = ok ? sv[e] : 0.0f;
         }
-        // KD rows d = 4 d4 + s: sfx_t k_t[d] for t = 4 t4 .. +4
+      }
+      const int d = 4 * d4;
+      // KA rows t: -g_t k_t[d .. d+4], one 8-byte piece each (hi, lo)
+      const int q = ((d >> 5) << 2) | k32_unit(d & 31);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int d = 4 * d4 + s, t = 4 * t4;
-          const int off = k32_off(d, k32_unit(t)) + (k32_slot(t) << 1);
-          __bf16 hv[4], lv[4];
+      for (int e = 0; e < 2; ++e) {
+        const int off = ka_off<DK>(2 * t2 + e, q) + (k32_slot(d & 31) << 1);
+        uint2 hv, lv;
+        split2(-gv[e] * kv[e][0], -gv[e] * kv[e][1], hv.x, lv.x);
+        split2(-gv[e] * kv[e][2], -gv[e] * kv[e][3], hv.y, lv.y);
+        *reinterpret_cast<uint2*>(buf + C::KA + off) = hv;
+        *reinterpret_cast<uint2*>(buf + C::KA + C::KA_HALF + off) = lv;
+      }
+      // KD rows d + s: sfx_t k_t[d + s] for the token pair, one 4-byte piece each
+      const int t = 2 * t2;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = ks[m][e] * kreg[m][e][s];
-            hv[e] = static_cast<__bf16>(x);
-            lv[e] = static_cast<__bf16>(x - static_cast<float>(hv[e]));
-          }
-          *reinterpret_cast<uint2*>(buf + C::KD + off) = pack4(hv);
-          *reinterpret_cast<uint2*>(buf + C::KD + C::KD_HALF + off) = pack4(lv);
-        }
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int off = k32_off(d + s2, k32_unit(t)) + (k32_slot(t) << 1);
+        uint32_t hv, lv;
+        split2(sv[0] * kv[0][s2], sv[1] * kv[1][s2], hv, lv);
+        *reinterpret_cast<uint32_t*>(buf + C::KD + off) = hv;
+        *reinterpret_cast<uint32_t*>(buf + C::KD + C::KD_HALF + off) = lv;
       }
     }
 #pragma unroll
     for (int m = 0; m < C::XPT; ++m) {
-      const int it = (C::NT - 1 - tid) + m * C::NT;
-      if (C::XITEMS % C::NT == 0 || it < C::XITEMS) {
-        const int tr = it >> 3, t = 4 * (it & 7);
-        const int off = k32_off(tr, k32_unit(t)) + (k32_slot(t) << 1);
-        __bf16 hv[4], lv[4];
+      const int it = tid + m * C::NT, tr = it >> 4, t = 2 * (it & 15);
+      f32x2 xv = xreg[m];
+      if (part && !valid(b, tr)) xv = f32x2{0.0f, 0.0f};
+      const int off = k32_off(tr, k32_unit(t)) + (k32_slot(t) << 1);
+      uint32_t hv, lv;
+      split2(xv[0], xv[1], hv, lv);
+      *reinterpret_cast<uint32_t*>(buf + C::XA + off) = hv;
+      *reinterpret_cast<uint32_t*>(buf + C::XA + C::XA_HALF + off) = lv;
+    }
+    if constexpr (C::VL) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hv[e] = static_cast<__bf16>(xreg[m][e]);
-          lv[e] = static_cast<__bf16>(xreg[m][e] - static_cast<float>(hv[e]));
+      for (int m = 0; m < C::VPT; ++m) {
+        const int it = tid + m * C::NT, tp = it / (C::RB / 4), g = it % (C::RB / 4);
+        f32x4 v0 = vreg[m][0], v1 = vreg[m][1];
+        if (part) {
+          v0 = valid(b, 2 * tp) ? v0 : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          v1 = valid(b, 2 * tp + 1) ? v1 : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
-        *reinterpret_cast<uint2*>(buf + C::XA + off) = pack4(hv);
-        *reinterpret_cast<uint2*>(buf + C::XA + C::XA_HALF + off) = pack4(lv);
+        float* vp = reinterpret_cast<float*>(buf + C::VS) + tp * C::VPS + 8 * g;
+        *reinterpret_cast<f32x4*>(vp) = f32x4{v0[0], v1[0], v0[1], v1[1]};
+        *reinterpret_cast<f32x4*>(vp + 4) = f32x4{v0[2], v1[2], v0[3], v1[3]};
       }
     }
     if (tid == 0) *reinterpret_cast<float*>(buf + C::GC) = gcl;
   };
   // V rows of the chunk in accumulator order: register i holds token 8 (i/4) + 4 hf + i%4
-  auto fetch_v = [&](int b, f32x16& vv) {
+  auto fetch_v = [&](int b, f32x16& vv, auto clamp) {
+    const char* vb = reinterpret_cast<const char*>(a.v + size_t(b) * kChunk * vstride + size_t(h) * DV);
+    const int nrow = int(a.N - int64_t(b) * kChunk);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int t = 8 * (i >> 2) + 4 * hf + (i & 3);
-      const bool ok = valid(b, t);
-      const size_t p = ok ? size_t(b) * kChunk + t : 0;
-      vv[i] = ok ? a.v[(p * a.H + h) * DV + row] : 0.0f;
+      uint32_t o = voff[i];
+      if constexpr (decltype(clamp)::value)
+        o = 8 * (i >> 2) + 4 * hf + (i & 3) < nrow ? o : uint32_t(row * 4);
+      vv[i] = *reinterpret_cast<const float*>(vb + o);
+    }
+  };
+  auto mask_v = [&](int b, f32x16& vv) {
+    if (shared_block(b)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = 8 * (i >> 2) + 4 * hf + (i & 3);
+        vv[i] = valid(b, t) ? vv[i] : 0.0f;
+      }
     }
   };
 
@@ -417,35 +502,31 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
 #pragma unroll
     for (int i = 0; i < 16; ++i) S[nt][i] = 0.0f;
 
-  f32x16 vcur, vnext;
-  if (b0 < b1) {
-    fetch(b0);
-    fetch_v(b0, vcur);
-    stage(lds);
-    if (b0 + 1 < b1) fetch(b0 + 1);
-  }
-  __syncthreads();
-
-  for (int b = b0; b < b1; ++b) {
-    unsigned char* cur = lds + ((b - b0) & 1) * C::BUF;
-    unsigned char* nxt = lds + (((b - b0) & 1) ^ 1) * C::BUF;
-    if (b + 1 < b1) {
-      stage(nxt);
-      fetch_v(b + 1, vnext);
+  // one chunk from LDS buffer cur: E = V - diag(g) K S^T, D = X E,
+  // S^T <- g_{n-1} S^T + (diag(sfx) K)^T D
+  auto compute = [&](int b, const unsigned char* cur, f32x16 E) {
+    if constexpr (C::VL) {        // V rows of tokens 8 (i/4) + 4 hf + i%4, i = 2q, 2q + 1
+      const float* vp = reinterpret_cast<const float*>(cur + C::VS) + 2 * (32 * wave + ln);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int t = 8 * (q >> 1) + 4 * hf + 2 * (q & 1);
+        const f32x2 x = *reinterpret_cast<const f32x2*>(vp + (t >> 1) * C::VPS);
+        E[2 * q] = x[0];
+        E[2 * q + 1] = x[1];
+      }
+    } else {
+      mask_v(b, E);
     }
-    if (b + 2 < b1) fetch(b + 2);
-
-    // E = V - diag(g) K S^T   (KA holds -g_t k_t)
-    f32x16 E = vcur;
+    // KA holds -g_t k_t
 #pragma unroll
     for (int nt = 0; nt < C::NTD; ++nt) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         float sv[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) sv[s] = S[nt][8 * u + s];
+        for (int s2 = 0; s2 < 8; ++s2) sv[s2] = S[nt][8 * u + s2];
         bf16x8 bh, bl;
-        split8(sv, bh, bl);
+        split8p(sv, bh, bl);
         const int off = ka_off<DK>(ln, (nt << 2) | (u << 1) | hf);
         const bf16x8 ah = *reinterpret_cast<const bf16x8*>(cur + C::KA + off);
         const bf16x8 al = *reinterpret_cast<const bf16x8*>(cur + C::KA + C::KA_HALF + off);
@@ -454,7 +535,6 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
         E = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, E, 0, 0, 0);
       }
     }
-    // D = X E
     f32x16 D;
 #pragma unroll
     for (int i = 0; i < 16; ++i) D[i] = 0.0f;
@@ -462,9 +542,9 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
     for (int u = 0; u < 2; ++u) {
       float ev[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) ev[s] = E[8 * u + s];
+      for (int s2 = 0; s2 < 8; ++s2) ev[s2] = E[8 * u + s2];
       bf16x8 bh, bl;
-      split8(ev, bh, bl);
+      split8p(ev, bh, bl);
       const int off = k32_off(ln, (u << 1) | hf);
       const bf16x8 ah = *reinterpret_cast<const bf16x8*>(cur + C::XA + off);
       const bf16x8 al = *reinterpret_cast<const bf16x8*>(cur + C::XA + C::XA_HALF + off);
@@ -472,14 +552,13 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
       D = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, D, 0, 0, 0);
       D = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, D, 0, 0, 0);
     }
-    // S^T <- g_{n-1} S^T + (diag(sfx) K)^T D
     bf16x8 dh[2], dl[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float dv[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) dv[s] = D[8 * u + s];
-      split8(dv, dh[u], dl[u]);
+      for (int s2 = 0; s2 < 8; ++s2) dv[s2] = D[8 * u + s2];
+      split8p(dv, dh[u], dl[u]);
     }
     const float gc = *reinterpret_cast<const float*>(cur + C::GC);
 #pragma unroll
@@ -496,8 +575,38 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
         S[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, dh[u], S[nt], 0, 0, 0);
       }
     }
+  };
+
+  // Blocks [b0, bin) lie inside the array and run pipelined with straight-line loads; a
+  // request that holds the array's last, partial block finishes with it unpipelined.
+  const int bin = b1 < int(a.N / kChunk) ? b1 : int(a.N / kChunk);
+  const std::false_type inside;
+  f32x16 vcur, vnext;
+  if (b0 < bin) {
+    fetch(b0, inside);
+    if constexpr (!C::VL) fetch_v(b0, vcur, inside);
+    stage(b0, lds);
+    fetch(b0 + 1 < bin ? b0 + 1 : b0, inside);
+  }
+  __syncthreads();
+  for (int b = b0; b < bin; ++b) {
+    unsigned char* cur = lds + ((b - b0) & 1) * C::BUF;
+    unsigned char* nxt = lds + (((b - b0) & 1) ^ 1) * C::BUF;
+    if (b + 1 < bin) stage(b + 1, nxt);
+    // the last chunks load the final block again (unused) rather than branch around loads
+    if constexpr (!C::VL) fetch_v(b + 1 < bin ? b + 1 : b, vnext, inside);
+    fetch(b + 2 < bin ? b + 2 : bin - 1, inside);
+    compute(b, cur, vcur);
     vcur = vnext;
     __syncthreads();
+  }
+  if (bin < b1) {
+    const int b = b1 - 1;
+    fetch(b, std::true_type{});
+    if constexpr (!C::VL) fetch_v(b, vcur, std::true_type{});
+    stage(b, lds);
+    __syncthreads();
+    compute(b, lds, vcur);
   }
 
   // S_out[r][h][row][d]: register i of tile nt holds d = 32 nt + 8 (i/4) + 4 hf + i%4
