@@ -278,6 +278,45 @@ def cpu_baseline(args, wl, mode):
                       f"requests are independent, so the rate scales to the whole batch"}
 
 
+def prefill_bytes(wl, N):
+    """Algorithmic HBM bytes of one prefill: the stacked prompts read once (k per key
+    head, v, alpha, beta in fp32, the offsets) and S_ctx written once."""
+    return (N * (wl.hk * wl.d_k + wl.H * wl.d_v + 2 * wl.H) * 4 + (wl.R + 1) * 4
+            + wl.R * wl.H * wl.d_v * wl.d_k * 4)
+
+
+def measure_prefill(args, wl, p, S_ctx, prefill, B, torch, stream, n=5):
+    """Prefill of the workload's stacked prompts (eq. 3 over every prompt token) in both
+    forms, each timed between HIP events on the launch stream (mean of n calls after one
+    untimed call); S_ctx keeps the chunked form's result."""
+    N = p["N"]
+    ws = torch.empty(B.gdn_beam_prefill_workspace_bytes(wl.H, wl.d_k, wl.d_v, N), dtype=torch.uint8,
+                     device=S_ctx.device)
+    args_p = (p["k"], p["v"], p["alpha"], p["beta"], p["offsets"])
+
+    def timed(chunked, reps):
+        prefill(S_ctx, *args_p, stream=stream, chunked=chunked, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            prefill(S_ctx, *args_p, stream=stream, chunked=chunked, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    token_ms = timed(False, 1)
+    ms = timed(True, n)                   # last: S_ctx holds the chunked result
+    nbytes = prefill_bytes(wl, N)
+    flops = 4.0 * N * wl.H * wl.d_k * wl.d_v          # eq. (3): S k and the rank-1 update
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(args, f"prefill of {N} prompt tokens x {wl.H} heads: chunked {ms:.3f} ms, "
+              f"token-sequential {token_ms:.3f} ms; {gbs:.0f} GB/s of algorithmic bytes")
+    return {"ms": ms, "ms_token_sequential": token_ms, "tokens": int(N),
+            "tokens_per_s": N / (ms * 1e-3), "bytes": int(nbytes), "achieved_GBs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS, "eq3_TFLOPs": flops / (ms * 1e-3) / 1e12,
+            "timing": f"mean of {n} calls between HIP events, workspace allocated beforehand"}
+
+
 def run_workload(args, wl, mode, torch, copy_gbs):
     """Whole decodes of one workload: returns the measurement dict."""
     import synth  # noqa: F401
@@ -293,10 +332,7 @@ def run_workload(args, wl, mode, torch, copy_gbs):
     dec = BeamDecoder(wl.R, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, wl.io, wl.wout, H_K=wl.H_K)
     p = sdev.prompts(wl, dev)
     S_ctx = torch.empty((wl.R, wl.H, wl.d_v, wl.d_k), dtype=torch.float32, device=dev)
-    t0 = time.perf_counter()
-    prefill(S_ctx, p["k"], p["v"], p["alpha"], p["beta"], p["offsets"])
-    torch.cuda.synchronize()
-    log(args, f"prefill of {p['N']} prompt tokens x {wl.H} heads: {time.perf_counter() - t0:.3f} s")
+    pre = measure_prefill(args, wl, p, S_ctx, prefill, B, torch, stream)
     del p
     Wout = sdev.wout(wl, dev)
     inputs = [sdev.step_inputs(wl, t, dev) for t in range(wl.T)]
@@ -468,6 +504,7 @@ def run_workload(args, wl, mode, torch, copy_gbs):
         "select_ms": float(sel_ms.sum()),
         "select_ms_per_t": [float(x) for x in sel_ms],
         "select_floor_ms_per_t": sel_floor,
+        "prefill": pre,
         "step_tflops": flops / (step_ms.sum() * 1e-3) / 1e12,
         "decode_roofline": (None if states is not None else
                             {"floor_ms": decode_floor_s(wl, bytes_t) * 1e3,
@@ -604,6 +641,7 @@ def main():
         extra[name]["roofline"] = {k: r["roofline"][k] for k in ("achieved", "frac", "traffic",
                                                                  "bytes_per_decode")}
         extra[name]["decode_roofline"] = r["decode_roofline"]
+        extra[name]["prefill"] = r["prefill"]
         if "projection_mfma" in r:
             extra[name]["projection_mfma"] = r["projection_mfma"]
         log(args, f"extra {name}: {r['value']:.4g} beam-transitions/s, step frac "
@@ -621,7 +659,7 @@ def main():
     }
     for k in ("roofline", "gdn_step_rate", "gdn_step_ms", "step_ms_per_t", "select_ms",
               "select_ms_per_t", "select_floor_ms_per_t", "step_tflops", "decode_roofline",
-              "projection_mfma"):
+              "projection_mfma", "prefill"):
         if k in head:
             res[k] = head[k]
     if extra:

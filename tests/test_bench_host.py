@@ -237,3 +237,14 @@ def test_step_kernel_code_hash_matches_the_build():
     syms, _ = m._elf_symbols(open(dev, "rb").read())
     names = [x[0] for x in syms if "step_kernel" in x[0] and x[3] > 0]
     assert any("step_kernelILi128ELi128ELb1ELi3E" in n for n in names)
+
+
+def test_prefill_bytes_counts_keys_per_key_head():
+    """A prefill reads every prompt token's k once per key head (not per value head), its
+    v, alpha and beta per value head, and writes one fp32 state per (request, head)."""
+    bench = _bench()
+    wl = synth.get("grouped")                  # 32 value heads on 16 key heads
+    N = 1000
+    per_token = (wl.hk * wl.d_k + wl.H * wl.d_v + 2 * wl.H) * 4
+    assert bench.prefill_bytes(wl, N) == N * per_token + (wl.R + 1) * 4 + wl.R * wl.H * wl.d_v * wl.d_k * 4
+    assert bench.prefill_bytes(wl, 2 * N) - bench.prefill_bytes(wl, N) == N * per_token
