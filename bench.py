@@ -193,12 +193,23 @@ def copy_bandwidth(torch, dev, mib=1024, reps=10):
     return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
-def kernel_hash():
-    """sha256[:16] of the built step kernel's machine code (None before a build)."""
+def kernel_hash(dims=None):
+    """sha256[:16] of the built step kernel's machine code: of the instantiations of head
+    dims (d_k, d_v) when given, else of all of them (None before a build)."""
     try:
-        return open(STEP_HASH_FILE).read().strip() or None
-    except OSError:
+        d = json.load(open(STEP_HASH_FILE))
+    except (OSError, ValueError):
         return None
+    return d.get("all" if dims is None else f"{dims[0]}x{dims[1]}")
+
+
+def _dims(wl_name):
+    import synth
+    try:
+        wl = synth.get(wl_name)
+    except KeyError:
+        return None
+    return (wl.d_k, wl.d_v)
 
 
 def load_traffic(wl_name):
@@ -212,7 +223,8 @@ def load_traffic(wl_name):
         d = json.load(open(f))
     except Exception:
         return None
-    if kernel_hash() is None or d.get("kernel_sha") != kernel_hash():
+    h = kernel_hash(_dims(wl_name))
+    if h is None or d.get("kernel_sha") != h:
         return None
     return d.get("bytes_per_decode")
 
@@ -742,7 +754,9 @@ def traffic_summary(args):
         b = (fk * ff + wk * wf) * 1024.0
         hbm.append(int(b))
         rows.append(f"| {t} | {fk:.0f} | {wk:.0f} | {alg[t] / 1e6:.1f} | {b / 1e6:.1f} | {b / alg[t]:.3f} |")
-    out = {"kernel_sha": kernel_hash(), "workload": args.workload, "unit": "bytes",
+    cfg = bj.get("config", {})
+    dims = (cfg["d_k"], cfg["d_v"]) if "d_k" in cfg and "d_v" in cfg else _dims(args.workload)
+    out = {"kernel_sha": kernel_hash(dims), "workload": args.workload, "unit": "bytes",
            "bytes_per_launch": hbm, "bytes_per_decode": int(sum(hbm)),
            "algorithmic_per_launch": [int(a) for a in alg],
            "fetch_factor": float(ff), "write_factor": float(wf),

@@ -6,7 +6,9 @@ Packed fp32 VALU forms are switched off for all device code.
 """
 from __future__ import annotations
 
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -49,18 +51,19 @@ def _elf_symbols(data: bytes):
     return out, secs
 
 
-def step_kernel_code_hash(device_obj: str) -> str:
-    """sha256[:16] of the step kernel's machine code: every step_kernel instantiation's
-    instructions and kernel descriptor, by name, from the gfx950 device object of
-    gdn_step.hip.  The descriptor's bytes 16..23 (the offset from the descriptor to the
-    code, which moves when other kernels of the file change size) are left out; the rest
-    of it holds the LDS, scratch and register counts.  It changes only when the compiled
-    kernel does."""
+def step_kernel_code_hash(device_obj: str, d_k=None, d_v=None) -> str:
+    """sha256[:16] of the step kernel's machine code: the instructions and kernel
+    descriptor of every step_kernel instantiation (of head dims d_k x d_v when given), by
+    name, from the gfx950 device object of gdn_step.hip.  The descriptor's bytes 16..23
+    (the offset from the descriptor to the code, which moves when other kernels of the
+    file change size) are left out; the rest of it holds the LDS, scratch and register
+    counts.  It changes only when the compiled kernel does."""
     import hashlib
     data = open(device_obj, "rb").read()
     syms, secs = _elf_symbols(data)
     h = hashlib.sha256()
-    chosen = sorted(x for x in syms if "step_kernel" in x[0] and x[3] > 0)
+    tag = None if d_k is None else f"ILi{d_k}ELi{d_v}E"
+    chosen = sorted(x for x in syms if "step_kernel" in x[0] and x[3] > 0 and (tag is None or tag in x[0]))
     for name, shndx, value, size in chosen:
         sec = secs[shndx]
         off = sec[4] + (value - sec[3])
@@ -70,6 +73,17 @@ def step_kernel_code_hash(device_obj: str) -> str:
         h.update(name.encode())
         h.update(blob)
     return h.hexdigest()[:16]
+
+
+def step_kernel_hashes(device_obj: str) -> dict:
+    """{"all": hash of every instantiation, "<d_k>x<d_v>": hash of that head geometry's}"""
+    syms, _ = _elf_symbols(open(device_obj, "rb").read())
+    dims = sorted({(int(m.group(1)), int(m.group(2))) for x in syms if "step_kernel" in x[0]
+                   for m in [re.search(r"step_kernelILi(\d+)ELi(\d+)E", x[0])] if m})
+    out = {"all": step_kernel_code_hash(device_obj)}
+    for dk, dv in dims:
+        out[f"{dk}x{dv}"] = step_kernel_code_hash(device_obj, dk, dv)
+    return out
 
 
 def build(verbose: bool = False) -> str:
@@ -105,7 +119,8 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"device compile failed: gdn_step.hip\n{r.stdout}\n{r.stderr}")
     with open(STEP_HASH, "w") as fh:
-        fh.write(step_kernel_code_hash(dev) + "\n")
+        json.dump(step_kernel_hashes(dev), fh, indent=1)
+        fh.write("\n")
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -93,9 +93,9 @@ def test_traffic_needs_the_current_sources(monkeypatch):
     b = _bench()
     f = os.path.join(ROOT, "profiles", "step_kernel_batch_traffic.json")
     d = json.load(open(f))
-    monkeypatch.setattr(b, "kernel_hash", lambda: d["kernel_sha"])
+    monkeypatch.setattr(b, "kernel_hash", lambda dims=None: d["kernel_sha"] if dims == (128, 128) else None)
     assert b.load_traffic("batch") == d["bytes_per_decode"]
-    monkeypatch.setattr(b, "kernel_hash", lambda: "0" * 16)
+    monkeypatch.setattr(b, "kernel_hash", lambda dims=None: "0" * 16)
     assert b.load_traffic("batch") is None
     assert b.load_traffic("no_such_workload") is None
 
@@ -222,8 +222,9 @@ def test_stamp_records_count():
 
 
 def test_step_kernel_code_hash_matches_the_build():
-    """The hash the build writes is the machine code of every step_kernel instantiation
-    in the gfx950 device object, and bench.py reads that file."""
+    """The hashes the build writes are the machine code of the step_kernel instantiations
+    in the gfx950 device object, all of them and per head geometry, and bench.py reads
+    that file; a workload's traffic file is keyed to its own geometry's hash."""
     import importlib.util as iu
     spec = iu.spec_from_file_location("gdn_build", os.path.join(ROOT, "linear_attention_beam_amd", "build.py"))
     m = iu.module_from_spec(spec)
@@ -231,9 +232,13 @@ def test_step_kernel_code_hash_matches_the_build():
     dev = os.path.join(ROOT, "linear_attention_beam_amd", "_build", "gdn_step.gfx950.o")
     if not os.path.exists(dev) or not os.path.exists(m.STEP_HASH):
         pytest.skip("the library is not built")
-    h = m.step_kernel_code_hash(dev)
-    assert len(h) == 16 and open(m.STEP_HASH).read().strip() == h
-    assert _bench().kernel_hash() == h
+    hs = json.load(open(m.STEP_HASH))
+    assert hs == m.step_kernel_hashes(dev)
+    assert hs["all"] == m.step_kernel_code_hash(dev) and len(hs["all"]) == 16
+    assert {"128x128", "128x256", "256x256", "128x512", "256x512", "16x16"} <= set(hs)
+    assert len(set(hs.values())) == len(hs)
+    b = _bench()
+    assert b.kernel_hash() == hs["all"] and b.kernel_hash((128, 256)) == hs["128x256"]
     syms, _ = m._elf_symbols(open(dev, "rb").read())
     names = [x[0] for x in syms if "step_kernel" in x[0] and x[3] > 0]
     assert any("step_kernelILi128ELi128ELb1ELi3E" in n for n in names)
