@@ -10,6 +10,8 @@
 //                    along the ancestor records (eqs. 6-7), eq. (8), record append.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "gdn_device.h"
 
 namespace gdn {
@@ -94,10 +96,17 @@ struct StepK {
 };
 
 // Sizes of the fused step for head dims (DK, DV) and io dtype.
-template <int DK, int DV, bool BF16>
+template <int DK, int DV, bool BF16, int TT = 0>
 struct StepCfg {
   static constexpr int DVP = DV < 32 ? 32 : DV;
-  static constexpr int DVB = DVP > 256 ? 256 : DVP;   // rows of d_v per workgroup
+  // rows of d_v per workgroup.  d_k = 256 from t = 1 on: 128 rows (four waves, each with
+  // the full register file: its S_ctx fragments alone take 128 registers), so that the
+  // ancestor records' keys and delta rows stay in registers too; t = 0 replays nothing
+  // and keeps 256 rows with two waves per SIMD
+  static constexpr bool WIDE = DK > 128 && TT > 0;
+  static constexpr int DVMAX = WIDE ? 128 : 256;
+  static constexpr int DVB = DVP > DVMAX ? DVMAX : DVP;
+  static constexpr int MINB = WIDE ? 1 : 2;            // workgroups per CU the registers allow
   static constexpr int NRB = DVP / DVB;          // workgroups per (request, head)
   static constexpr int NW = DVB / 32;            // one wave per 32-row block of d_v
   static constexpr int NT = NW * 64;
@@ -151,8 +160,8 @@ __device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float s) 
 // one parent adjacent, subtrees contiguous), so the records that siblings and cousins
 // share are gathered back to back, from cache.
 template <int DK, int DV, bool BF16, int TT>
-__global__ void __launch_bounds__((StepCfg<DK, DV, BF16>::NT), 2) step_kernel(StepK a) {
-  using C = StepCfg<DK, DV, BF16>;
+__global__ void __launch_bounds__((StepCfg<DK, DV, BF16, TT>::NT), (StepCfg<DK, DV, BF16, TT>::MINB)) step_kernel(StepK a) {
+  using C = StepCfg<DK, DV, BF16, TT>;
   constexpr int NT = C::NT, QROW = C::QROW, VROW = C::VROW, TPB = C::TPB;
   constexpr int UPQ = C::QB / 16, UPV = C::VB / 16;      // 16-byte units per row
   constexpr int NJ = TT;                                 // ancestor records replayed
@@ -586,11 +595,7 @@ int launch_init(const InitArgs& a, hipStream_t s) {
 
 template <int DK, int DV, bool BF16>
 static int launch_step_t(const StepArgs& a, hipStream_t s) {
-  constexpr int NT = StepCfg<DK, DV, BF16>::NT;
   const int nrh = a.R * a.H;
-  // one workgroup per (request, head, 256 rows of d_v): S_ctx is read once and kept in
-  // registers
-  const long grid = (long(nrh) * StepCfg<DK, DV, BF16>::NRB + 7) / 8 * 8;
   char* ws = static_cast<char*>(a.ws);
   StepK k{a.H, a.HK, a.W, a.W_max, a.T_max, a.t, nrh, a.q, a.k, a.v, a.alpha, a.beta, a.o,
           ws + a.L.s_frag, reinterpret_cast<float*>(ws + a.L.gtr_alpha),
@@ -598,21 +603,26 @@ static int launch_step_t(const StepArgs& a, hipStream_t s) {
           reinterpret_cast<const int32_t*>(ws + a.L.anc[a.t & 1]),
           reinterpret_cast<const int32_t*>(ws + a.L.order[a.t & 1]),
           a.stamps, uint32_t(a.stamp_records < 0xFFFFFFFFu ? a.stamp_records : 0xFFFFFFFFu)};
-  // with timing events, the dispatch itself stamps its start and end (nothing more is
-  // put on the stream)
-  auto go = [&](auto kern) {
-    if (a.ev0) hipExtLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, s, a.ev0, a.ev1, 0, k);
-    else hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, s, k);
+  // one workgroup per (request, head, block of d_v rows): S_ctx is read once and kept
+  // in registers.  With timing events, the dispatch itself stamps its start and end
+  // (nothing more is put on the stream)
+  auto go = [&](auto tt) {
+    constexpr int TT = decltype(tt)::value;
+    using C = StepCfg<DK, DV, BF16, TT>;
+    const long grid = (long(nrh) * C::NRB + 7) / 8 * 8;
+    auto kern = step_kernel<DK, DV, BF16, TT>;
+    if (a.ev0) hipExtLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, s, a.ev0, a.ev1, 0, k);
+    else hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, s, k);
   };
   switch (a.t) {
-    case 0: go(step_kernel<DK, DV, BF16, 0>); break;
-    case 1: go(step_kernel<DK, DV, BF16, 1>); break;
-    case 2: go(step_kernel<DK, DV, BF16, 2>); break;
-    case 3: go(step_kernel<DK, DV, BF16, 3>); break;
-    case 4: go(step_kernel<DK, DV, BF16, 4>); break;
-    case 5: go(step_kernel<DK, DV, BF16, 5>); break;
-    case 6: go(step_kernel<DK, DV, BF16, 6>); break;
-    default: go(step_kernel<DK, DV, BF16, 7>); break;
+    case 0: go(std::integral_constant<int, 0>{}); break;
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    default: go(std::integral_constant<int, 7>{}); break;
   }
   return last_launch_error();
 }
