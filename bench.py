@@ -62,6 +62,10 @@ def parse():
     p.add_argument("--path", choices=["records", "fullstate"], default="records",
                    help="records: transition records and replay (gdn_beam_step); fullstate: "
                         "the per-beam state baseline (gdn_fullstate_step)")
+    p.add_argument("--groups", type=int, default=2,
+                   help="timed decodes: the requests split into this many equal groups, one "
+                        "decoder and one stream each (requests are independent; one group's "
+                        "selection overlaps another's step); 1: one decoder on one stream")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU oracle time")
     p.add_argument("--quiet", action="store_true")
@@ -362,6 +366,18 @@ def run_workload(args, wl, mode, torch, copy_gbs):
     torch.cuda.synchronize()
 
     states = dec.alloc_states() if args.path == "fullstate" else None
+    # request groups for the timed decodes (records path): G decoders of R / G requests,
+    # each on its own stream (default priority), fed slices of the same input tensors
+    G = args.groups if (args.groups > 1 and wl.R % args.groups == 0 and states is None) else 1
+    if G != args.groups:
+        log(args, f"request groups: 1 ({wl.R} requests, path {args.path})")
+    gdecs, gstreams, gsl = [], [], []
+    if G > 1:
+        Rg = wl.R // G
+        gdecs = [BeamDecoder(Rg, wl.H, wl.d_k, wl.d_v, wl.T, wl.W_max, wl.V, wl.io, wl.wout, H_K=wl.H_K)
+                 for _ in range(G)]
+        gstreams = [stream] + [torch.cuda.Stream(device=dev) for _ in range(G - 1)]
+        gsl = [slice(g * Rg, (g + 1) * Rg) for g in range(G)]
 
     def gdn_step(t, x):
         if states is None:
@@ -378,6 +394,24 @@ def run_workload(args, wl, mode, torch, copy_gbs):
             s = sels[t]
             dec.select(t, outs[t], Wout, wl.V, wl.width(t + 1), s["parent"], s["token"],
                        s["score"], forced[t][0], forced[t][1], stream)
+
+    def decode_grouped():
+        """One decode of every request: the groups' launches interleaved per SID step,
+        each group on its own stream (no group waits for another)."""
+        for g in range(G):
+            gdecs[g].init(S_ctx[gsl[g]], wl.width(0), gstreams[g])
+        for t in range(wl.T):
+            x, s = inputs[t], sels[t]
+            for g in range(G):
+                q, st = gsl[g], gstreams[g]
+                gdecs[g].step(t, x["q"][q], x["k"][q], x["v"][q], x["alpha"][q], x["beta"][q],
+                              outs[t][q], st)
+                fp = forced[t][0][q] if forced[t][0] is not None else None
+                ft = forced[t][1][q] if forced[t][1] is not None else None
+                gdecs[g].select(t, outs[t][q], Wout, wl.V, wl.width(t + 1), s["parent"][q],
+                                s["token"][q], s["score"][q], fp, ft, st)
+
+    timed_decode = decode_grouped if G > 1 else decode
 
     # ---- distinct ancestor records and distinct parents per step (deterministic: the
     # same every decode)
@@ -403,6 +437,8 @@ def run_workload(args, wl, mode, torch, copy_gbs):
 
     for _ in range(args.warmup):
         decode()
+        if G > 1:
+            decode_grouped()
     torch.cuda.synchronize()
 
     # ---- per-call times: an instrumented pass of the same decodes, HIP events recorded
@@ -444,13 +480,14 @@ def run_workload(args, wl, mode, torch, copy_gbs):
 
     trans = wl.transitions()
     if not args.flush_mall:
-        # ---- timed region: K whole decodes back to back on the stream, nothing else on
-        # it (a timing event between kernels costs the stream a few microseconds, and the
-        # idle gap changes what the next launch finds in the caches)
+        # ---- timed region: K whole decodes back to back, nothing else on the streams
+        # (a timing event between kernels costs a stream a few microseconds, and the idle
+        # gap changes what the next launch finds in the caches); with request groups,
+        # each group's decodes follow each other on its own stream
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            decode()
+            timed_decode()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         # ---- step kernel times: the same decodes back to back again, every step launch
@@ -501,6 +538,7 @@ def run_workload(args, wl, mode, torch, copy_gbs):
                    "state_dtype": "f32", "mode": mode,
                    "parents": wl.parents if mode == "forced" else "top-W", "path": args.path,
                    "parallelism": "single GPU",
+                   "request_groups": G if not args.flush_mall else 1,
                    "cache": f"cold ({args.flush_mall} flush)" if args.flush_mall else "pipeline"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
