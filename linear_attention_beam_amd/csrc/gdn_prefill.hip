@@ -393,17 +393,17 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
       const int it = tid + m * C::NT, tr = it >> 4, q2 = it & 15;
       xreg[m] = *reinterpret_cast<const f32x2*>(pw + tr * kChunk + 2 * q2);
     }
-    // g of the request's last token in the block; only thread 0 keeps it (a per-thread
-    // address keeps this a vector load, off the scalar path that LDS waits share)
+    // g of the request's last token in the block (the chunk's decay of the state)
     int tlast = end - b * kChunk;
     tlast = (tlast > kChunk ? kChunk : tlast) - 1;
-    gcl = pw[kChunk * kChunk + (tid == 0 ? tlast : 0)];
+    gcl = pw[kChunk * kChunk + tlast];
   };
   auto shared_block = [&](int b) { return b * kChunk < beg || (b + 1) * kChunk > end; };
   auto valid = [&](int b, int t) { const int p = b * kChunk + t; return p >= beg && p < end; };
   // registers of block b -> LDS buffer (bf16 hi/lo fragments)
-  auto stage = [&](int b, unsigned char* buf) {
-    const bool part = shared_block(b);
+  // MASK: a block shared with another request (its rows are replaced by zeros)
+  auto stage = [&](int b, unsigned char* buf, auto mask) {
+    constexpr bool part = decltype(mask)::value;
 #pragma unroll
     for (int m = 0; m < C::KPT; ++m) {
       const int it = tid + m * C::NT, t2 = it / (DK / 4), d4 = it % (DK / 4);
@@ -415,7 +415,7 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
         gv[e] = kgs[m][0][e];
         sv[e] = kgs[m][1][e];
       }
-      if (part) {
+      if constexpr (part) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const bool ok = valid(b, 2 * t2 + e);
@@ -451,7 +451,7 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
     for (int m = 0; m < C::XPT; ++m) {
       const int it = tid + m * C::NT, tr = it >> 4, t = 2 * (it & 15);
       f32x2 xv = xreg[m];
-      if (part && !valid(b, tr)) xv = f32x2{0.0f, 0.0f};
+      if constexpr (part) xv = valid(b, tr) ? xv : f32x2{0.0f, 0.0f};
       const int off = k32_off(tr, k32_unit(t)) + (k32_slot(t) << 1);
       uint32_t hv, lv;
       split2(xv[0], xv[1], hv, lv);
@@ -463,7 +463,7 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
       for (int m = 0; m < C::VPT; ++m) {
         const int it = tid + m * C::NT, tp = it / (C::RB / 4), g = it % (C::RB / 4);
         f32x4 v0 = vreg[m][0], v1 = vreg[m][1];
-        if (part) {
+        if constexpr (part) {
           v0 = valid(b, 2 * tp) ? v0 : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
           v1 = valid(b, 2 * tp + 1) ? v1 : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
@@ -472,7 +472,10 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
         *reinterpret_cast<f32x4*>(vp + 4) = f32x4{v0[2], v1[2], v0[3], v1[3]};
       }
     }
-    if (tid == 0) *reinterpret_cast<float*>(buf + C::GC) = gcl;
+  };
+  auto stage_any = [&](int b, unsigned char* buf) {
+    if (shared_block(b)) stage(b, buf, std::true_type{});
+    else stage(b, buf, std::false_type{});
   };
   // V rows of the chunk in accumulator order: register i holds token 8 (i/4) + 4 hf + i%4
   auto fetch_v = [&](int b, f32x16& vv, auto clamp) {
@@ -504,7 +507,7 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
 
   // one chunk from LDS buffer cur: E = V - diag(g) K S^T, D = X E,
   // S^T <- g_{n-1} S^T + (diag(sfx) K)^T D
-  auto compute = [&](int b, const unsigned char* cur, f32x16 E) {
+  auto compute = [&](int b, const unsigned char* cur, f32x16 E, float gc, auto mask) {
     if constexpr (C::VL) {        // V rows of tokens 8 (i/4) + 4 hf + i%4, i = 2q, 2q + 1
       const float* vp = reinterpret_cast<const float*>(cur + C::VS) + 2 * (32 * wave + ln);
 #pragma unroll
@@ -514,7 +517,7 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
         E[2 * q] = x[0];
         E[2 * q + 1] = x[1];
       }
-    } else {
+    } else if constexpr (decltype(mask)::value) {
       mask_v(b, E);
     }
     // KA holds -g_t k_t
@@ -560,7 +563,6 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
       for (int s2 = 0; s2 < 8; ++s2) dv[s2] = D[8 * u + s2];
       split8p(dv, dh[u], dl[u]);
     }
-    const float gc = *reinterpret_cast<const float*>(cur + C::GC);
 #pragma unroll
     for (int nt = 0; nt < C::NTD; ++nt) {
 #pragma unroll
@@ -579,34 +581,63 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
 
   // Blocks [b0, bin) lie inside the array and run pipelined with straight-line loads; a
   // request that holds the array's last, partial block finishes with it unpipelined.
+  // Only a request's first and last blocks can be shared with another request: the first
+  // is staged before the loop, the last in the loop's last-but-one pass, so the body of
+  // the main loop is one straight run of code (no masks, no branches) in which the
+  // compiler can place the next chunk's staging among the current chunk's MFMAs.
   const int bin = b1 < int(a.N / kChunk) ? b1 : int(a.N / kChunk);
-  const std::false_type inside;
+  const std::false_type inside, whole;
+  const std::true_type masked;
   f32x16 vcur, vnext;
+  float g0 = 1.0f, g1 = 1.0f;                       // chunk decays of blocks b, b + 1
   if (b0 < bin) {
     fetch(b0, inside);
-    if constexpr (!C::VL) fetch_v(b0, vcur, inside);
-    stage(b0, lds);
+    g0 = gcl;
+    if constexpr (!C::VL) {
+      fetch_v(b0, vcur, inside);
+      mask_v(b0, vcur);
+    }
+    stage_any(b0, lds);
     fetch(b0 + 1 < bin ? b0 + 1 : b0, inside);
+    g1 = gcl;
   }
   __syncthreads();
-  for (int b = b0; b < bin; ++b) {
+  int b = b0;
+  for (; b + 2 < bin; ++b) {                        // stages b + 1 <= bin - 2: whole blocks
     unsigned char* cur = lds + ((b - b0) & 1) * C::BUF;
     unsigned char* nxt = lds + (((b - b0) & 1) ^ 1) * C::BUF;
-    if (b + 1 < bin) stage(b + 1, nxt);
-    // the last chunks load the final block again (unused) rather than branch around loads
-    if constexpr (!C::VL) fetch_v(b + 1 < bin ? b + 1 : b, vnext, inside);
-    fetch(b + 2 < bin ? b + 2 : bin - 1, inside);
-    compute(b, cur, vcur);
+    if constexpr (!C::VL) fetch_v(b + 1, vnext, inside);
+    // the products read cur first; the staging of block b + 1 (register arithmetic, then
+    // LDS writes to nxt) follows them in program order, so that its arithmetic can move
+    // in among the MFMAs; block b + 2's loads go out last and land during the next pass
+    compute(b, cur, vcur, g0, whole);
+    stage(b + 1, nxt, whole);
+    fetch(b + 2, inside);
+    g0 = g1;
+    g1 = gcl;
     vcur = vnext;
     __syncthreads();
   }
-  if (bin < b1) {
-    const int b = b1 - 1;
-    fetch(b, std::true_type{});
-    if constexpr (!C::VL) fetch_v(b, vcur, std::true_type{});
-    stage(b, lds);
+  if (b + 1 < bin) {                                // stages the last block of the array part
+    unsigned char* cur = lds + ((b - b0) & 1) * C::BUF;
+    unsigned char* nxt = lds + (((b - b0) & 1) ^ 1) * C::BUF;
+    stage_any(b + 1, nxt);
+    if constexpr (!C::VL) fetch_v(b + 1, vnext, inside);
+    compute(b, cur, vcur, g0, masked);
+    g0 = g1;
+    vcur = vnext;
     __syncthreads();
-    compute(b, lds, vcur);
+    ++b;
+  }
+  if (b < bin) compute(b, lds + ((b - b0) & 1) * C::BUF, vcur, g0, masked);
+  if (bin < b1) {
+    const int bt = b1 - 1;
+    __syncthreads();
+    fetch(bt, std::true_type{});
+    if constexpr (!C::VL) fetch_v(bt, vcur, std::true_type{});
+    stage(bt, lds, masked);
+    __syncthreads();
+    compute(bt, lds, vcur, gcl, masked);
   }
 
   // S_out[r][h][row][d]: register i of tile nt holds d = 32 nt + 8 (i/4) + 4 hf + i%4
