@@ -262,21 +262,21 @@ struct ChunkCfg {
   static constexpr int NB = DV / RB;              // workgroups per (request, head)
   static constexpr int NTD = DK / 32;
   // LDS buffer: KA (32 rows t x DK, A of E), KD (DK rows d x 32, A of the state update),
-  // XA (32 x 32, A of D), each as bf16 hi then lo; then g_{n-1} of the chunk.
+  // XA (32 x 32, A of D), each as bf16 hi then lo.  The chunk decays g_{n-1} stay in
+  // registers.
   static constexpr int KA = 0;
   static constexpr int KA_HALF = 32 * DK * 2;
   static constexpr int KD = KA + 2 * KA_HALF;
   static constexpr int KD_HALF = DK * 64;
   static constexpr int XA = KD + 2 * KD_HALF;
   static constexpr int XA_HALF = 32 * 64;
-  static constexpr int GC = XA + 2 * XA_HALF;
   // With d_k = 128 and 8 waves, V of the chunk also goes through LDS (16-byte loads
   // instead of one 4-byte load per token and lane): rows of 32 tokens as token pairs,
   // [pair][row][2], pair rows padded so that tokens t and t + 4 (the two lane halves of an
   // accumulator) fall on different LDS banks.
   static constexpr bool VL = DK == 128 && NW == 8;
   static constexpr int VPS = 2 * RB + 16;         // floats per token pair
-  static constexpr int VS = GC + 16;
+  static constexpr int VS = XA + 2 * XA_HALF;
   static constexpr int BUF = VS + (VL ? 16 * VPS * 4 : 0);
   static constexpr int KITEMS = 16 * (DK / 4);    // 2 tokens x 4 columns of K each
   static constexpr int XITEMS = 32 * 16;          // 2 columns of one X row each
@@ -333,7 +333,9 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
 
   // Loads use a per-chunk base (uniform) plus offsets fixed per thread; only the array's
   // last block, which may reach past N, clamps its rows (to row 0 of the block).  Rows of
-  // other requests are loaded and then replaced by zeros where a block is shared.
+  // other requests are loaded and then replaced by zeros where a block is shared.  The
+  // lambdas that touch these arrays are forced inline: one call left out of line (past the
+  // inliner's cost limit) passes them by address and puts them in scratch memory.
   f32x4 kreg[C::KPT][2], vreg[C::VPT][2];
   f32x2 kgs[C::KPT][2];                  // g and sfx of the item's two tokens
   f32x2 xreg[C::XPT];
@@ -356,7 +358,7 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
   for (int i = 0; i < 16; ++i)
     voff[i] = uint32_t(((8 * (i >> 2) + 4 * hf + (i & 3)) * vstride + row) * 4);
   // clamp: the array's last block, which may reach past N (rows past N read row 0)
-  auto fetch = [&](int b, auto clamp) {
+  auto fetch = [&](int b, auto clamp) __attribute__((always_inline)) {
     const char* kb = reinterpret_cast<const char*>(a.k + size_t(b) * kChunk * kstride + size_t(hk) * DK);
     const float* pw = a.ws + (size_t(b) * a.H + h) * kPrepFloats;
     const int nrow = int(a.N - int64_t(b) * kChunk);
@@ -402,7 +404,7 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
   auto valid = [&](int b, int t) { const int p = b * kChunk + t; return p >= beg && p < end; };
   // registers of block b -> LDS buffer (bf16 hi/lo fragments)
   // MASK: a block shared with another request (its rows are replaced by zeros)
-  auto stage = [&](int b, unsigned char* buf, auto mask) {
+  auto stage = [&](int b, unsigned char* buf, auto mask) __attribute__((always_inline)) {
     constexpr bool part = decltype(mask)::value;
 #pragma unroll
     for (int m = 0; m < C::KPT; ++m) {
@@ -473,12 +475,12 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
       }
     }
   };
-  auto stage_any = [&](int b, unsigned char* buf) {
+  auto stage_any = [&](int b, unsigned char* buf) __attribute__((always_inline)) {
     if (shared_block(b)) stage(b, buf, std::true_type{});
     else stage(b, buf, std::false_type{});
   };
   // V rows of the chunk in accumulator order: register i holds token 8 (i/4) + 4 hf + i%4
-  auto fetch_v = [&](int b, f32x16& vv, auto clamp) {
+  auto fetch_v = [&](int b, f32x16& vv, auto clamp) __attribute__((always_inline)) {
     const char* vb = reinterpret_cast<const char*>(a.v + size_t(b) * kChunk * vstride + size_t(h) * DV);
     const int nrow = int(a.N - int64_t(b) * kChunk);
 #pragma unroll
@@ -489,7 +491,7 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
       vv[i] = *reinterpret_cast<const float*>(vb + o);
     }
   };
-  auto mask_v = [&](int b, f32x16& vv) {
+  auto mask_v = [&](int b, f32x16& vv) __attribute__((always_inline)) {
     if (shared_block(b)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -507,7 +509,8 @@ __global__ void __launch_bounds__((ChunkCfg<DK, DV>::NT)) __attribute__((amdgpu_
 
   // one chunk from LDS buffer cur: E = V - diag(g) K S^T, D = X E,
   // S^T <- g_{n-1} S^T + (diag(sfx) K)^T D
-  auto compute = [&](int b, const unsigned char* cur, f32x16 E, float gc, auto mask) {
+  auto compute = [&](int b, const unsigned char* cur, f32x16 E, float gc, auto mask)
+      __attribute__((always_inline)) {
     if constexpr (C::VL) {        // V rows of tokens 8 (i/4) + 4 hf + i%4, i = 2q, 2q + 1
       const float* vp = reinterpret_cast<const float*>(cur + C::VS) + 2 * (32 * wave + ln);
 #pragma unroll
