@@ -555,10 +555,14 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
       else asm volatile("" ::"v"(zl[KS - 1][0]));
       __syncthreads();
       if (code_lo + 32 * TPS < code_hi) fetch(code_lo + 32 * TPS);
-      auto mfma_tile = [&](int buf, int sub) {
-        u32x4 w[KS];
+      // A fragments of tile `sub` of LDS buffer `buf`
+      auto frags = [&](u32x4* w, int buf, int sub) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) w[kk] = tile[buf][(32 * sub + m) * RS + (HV / 8) * hf + kk];
+      };
+      auto mfma_tile = [&](int buf, int sub) {
+        u32x4 w[KS];
+        frags(w, buf, sub);
         return block_mfma_split<F16, KS>(w, zh, zm, zl);
       };
       // software pipeline over stages of two tiles (64 codes, one barrier): the MFMAs of
@@ -578,14 +582,46 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
           put(buf ^ 1);
           __syncthreads();
           fetch(c0 + 128);
-          const f32x16 n0 = mfma_tile(buf ^ 1, 0), n1 = mfma_tile(buf ^ 1, 1);
           const float f0 = tfac(c0), f1 = tfac(c0 + 32);
-          fold_full(a0, c0, f0, kLog2e * f0);
-          fold_full(a1, c0 + 32, f1, kLog2e * f1);
+          f32x16 n0, n1;
+          if constexpr (F16) {
+            // two fp16 terms: two MFMAs per A fragment.  Left to itself the compiler
+            // reads each fragment into one register set and waits for it before its two
+            // MFMAs, and the folds follow all of them.  So each tile's eight fragments
+            // are read first, behind a scheduling barrier (the MFMAs then wait for them
+            // in order), and its 16 MFMAs go out among the fold of one tile of the
+            // stage before.
+            u32x4 w[KS];
+            frags(w, buf ^ 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            n0 = block_mfma_split<F16, KS>(w, zh, zm, zl);
+            fold_full(a0, c0, f0, kLog2e * f0);
 #pragma unroll
-          for (int i = 0; i < 2 * NTERM * KS; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+            for (int i = 0; i < NTERM * KS; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            frags(w, buf ^ 1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            n1 = block_mfma_split<F16, KS>(w, zh, zm, zl);
+            fold_full(a1, c0 + 32, f1, kLog2e * f1);
+#pragma unroll
+            for (int i = 0; i < NTERM * KS; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          } else {
+            n0 = mfma_tile(buf ^ 1, 0);
+            n1 = mfma_tile(buf ^ 1, 1);
+            fold_full(a0, c0, f0, kLog2e * f0);
+            fold_full(a1, c0 + 32, f1, kLog2e * f1);
+#pragma unroll
+            for (int i = 0; i < 2 * NTERM * KS; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+            }
           }
           a0 = n0;
           a1 = n1;
@@ -659,12 +695,13 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     __syncthreads();
     const int nt = (code_hi - code_lo + 31) >> 5;
     if (a.beam_major) {
-      // 32 lanes per beam: one contiguous row of the group's tiles
-      const int ti = threadIdx.x & 31;
+      // 32 lanes per beam: one contiguous row of the group's tiles, 32 at a time
+      const int t0 = threadIdx.x & 31;
       for (int bb = threadIdx.x >> 5; bb < kLogitsWaves * 32; bb += 2 * kLogitsWaves) {
         const int rs = slot_r[bb >> 5], bs = slot_b[bb >> 5] + (bb & 31);
-        if (ti < nt && rs >= 0 && bs < a.W)
-          a.tmax[size_t(rs) * a.tmax_stride + size_t(bs) * vt + (code_lo >> 5) + ti] = tms[ti * kTmRow + bb];
+        if (rs >= 0 && bs < a.W)
+          for (int ti = t0; ti < nt; ti += 32)
+            a.tmax[size_t(rs) * a.tmax_stride + size_t(bs) * vt + (code_lo >> 5) + ti] = tms[ti * kTmRow + bb];
       }
     } else {
       for (int e = threadIdx.x; e < nt * kLogitsWaves * 32; e += 64 * kLogitsWaves) {
