@@ -86,6 +86,22 @@ def step_kernel_hashes(device_obj: str) -> dict:
     return out
 
 
+def kernel_resources(device_obj: str) -> dict:
+    """{kernel symbol: (LDS bytes, scratch bytes per lane)} from the kernel descriptors
+    (the `.kd` symbols: group and private segment sizes, their first two words) of a
+    gfx950 device object."""
+    import struct
+    data = open(device_obj, "rb").read()
+    syms, secs = _elf_symbols(data)
+    out = {}
+    for name, shndx, value, size in syms:
+        if name.endswith(".kd") and size >= 64:
+            sec = secs[shndx]
+            lds, scratch = struct.unpack_from("<II", data, sec[4] + (value - sec[3]))
+            out[name[:-3]] = (lds, scratch)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     cc = hipcc()
@@ -121,6 +137,14 @@ def build(verbose: bool = False) -> str:
     with open(STEP_HASH, "w") as fh:
         json.dump(step_kernel_hashes(dev), fh, indent=1)
         fh.write("\n")
+    # the prefill kernels' device code with the library's own flags, whose kernel
+    # descriptors the host tests read (scratch memory of the chunk kernel)
+    cmd = [cc, *common, f"--offload-arch={ARCH}", "--offload-device-only", "--no-gpu-bundle-output",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics", "-c",
+           os.path.join(CSRC, "gdn_prefill.hip"), "-o", os.path.join(objdir, "gdn_prefill.gfx950.o")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"device compile failed: gdn_prefill.hip\n{r.stdout}\n{r.stderr}")
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
