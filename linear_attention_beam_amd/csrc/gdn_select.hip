@@ -376,12 +376,18 @@ struct LogitsK {
   float* tmax;           // per request: largest logit of each (beam, tile)
   size_t tmax_stride;    // elements per request
   float4* lse_part;      // [R,W_max,nvg]: max, sum of exp(x - max), min tile max
+  int gpb = 1;           // code groups per block (consecutive; one z operand load)
+  int cpw_shift = 0;     // log2 cpw
 };
 
 // Beam chunks (waves) per first-pass block; the block shares one code group.
 constexpr int kLogitsWaves = 8;
 // Codes per group are at most 1024 (the launcher's choice): 32 tiles.
 constexpr int kMaxGroupTiles = 32;
+// Code groups one block may take in turn (the launcher's choice, d_v <= 128 with a bf16
+// codebook), and the blocks below which it stops merging them: one per CU.
+constexpr int kMaxGroupsPerBlock = 8;
+constexpr int kLogitsMinBlocks = 256;
 // LDS row of the staged tile maxima: one tile for the block's 256 beams, padded so
 // that a beam-major read of 32 tiles of one beam spreads over the banks.
 constexpr int kTmRow = kLogitsWaves * 32 + 1;
@@ -405,10 +411,11 @@ template <int DV, bool WBF16>
 __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   constexpr int HV = DV / 2;
   const int wave = threadIdx.x >> 6;
-  // 1-D grid over (chunk group, code group), code group fastest; the blocks of one
-  // chunk group (which read the same z operand) share an XCD
+  // 1-D grid over (chunk group, run of gpb code groups), code groups fastest; the blocks
+  // of one chunk group (which read the same z operand) share an XCD
+  const int nbg = (a.nvg + a.gpb - 1) / a.gpb;
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
-  const int vg = wid % a.nvg, cg = wid / a.nvg;
+  const int vg0 = (wid % nbg) * a.gpb, cg = wid / nbg;
   const int gc = cg * kLogitsWaves + wave;          // chunk over all requests
   const bool wvalid = gc < a.R * a.nchunk;
   const int r = wvalid ? gc / a.nchunk : 0, chunk = wvalid ? gc % a.nchunk : 0;
@@ -416,16 +423,17 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   const int b = chunk * 32 + m;
   const bool bvalid = wvalid && b < a.W;
   float* tm_r = a.tmax + size_t(r) * a.tmax_stride;
-  const int code_lo = vg * a.cpw;
-  const int code_hi = min(a.V, code_lo + a.cpw);
+  const int code_lo = vg0 * a.cpw;
+  const int code_hi = min(a.V, code_lo + a.gpb * a.cpw);
 
   float mrun = -INFINITY, srun = 0.0f, nrun = INFINITY;
   // tile maxima of the block, staged in LDS on the bf16 paths with z in registers (the
   // folds of the pair loop below then hold no branch) and written out, coalesced in
-  // either layout, at the end
+  // either layout, once their code group is done; two buffers, for code groups of even
+  // and odd index
   constexpr bool STAGE_TM = WBF16 && DV <= 256;
   const int vt = (a.V + 31) >> 5;
-  __shared__ float tms[STAGE_TM ? kMaxGroupTiles * kTmRow : 1];
+  __shared__ float tms[STAGE_TM ? 2 * kMaxGroupTiles * kTmRow : 1];
   // request and first beam of each wave's chunk (request -1: no chunk), for the flush
   __shared__ int slot_r[STAGE_TM ? kLogitsWaves : 1], slot_b[STAGE_TM ? kLogitsWaves : 1];
   if constexpr (STAGE_TM) {
@@ -436,7 +444,8 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   }
   auto put_tm = [&](float tm, int c0) {
     if constexpr (STAGE_TM) {
-      tms[((c0 - code_lo) >> 5) * kTmRow + wave * 32 + m] = tm;
+      const int rel = c0 - code_lo;
+      tms[((((rel >> a.cpw_shift) & 1) * kMaxGroupTiles) + ((rel & (a.cpw - 1)) >> 5)) * kTmRow + wave * 32 + m] = tm;
     } else if (hf == 0 && bvalid) {
       tm_r[a.beam_major ? size_t(b) * vt + (c0 >> 5) : size_t(c0 >> 5) * a.W + b] = tm;
     }
@@ -494,6 +503,46 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     }
   };
 
+  // Code group g done: its tile maxima from LDS to tmax (all threads, after a barrier
+  // that follows the group's last fold) ...
+  auto flush_tm = [&](int g) {
+    if constexpr (STAGE_TM) {
+      const int glo = g * a.cpw, nt = (min(a.V, glo + a.cpw) - glo + 31) >> 5;
+      const float* tb = tms + ((g - vg0) & 1) * kMaxGroupTiles * kTmRow;
+      if (a.beam_major) {
+        // 32 lanes per beam: one contiguous row of the group's tiles, 32 at a time
+        const int t0 = threadIdx.x & 31;
+        for (int bb = threadIdx.x >> 5; bb < kLogitsWaves * 32; bb += 2 * kLogitsWaves) {
+          const int rs = slot_r[bb >> 5], bs = slot_b[bb >> 5] + (bb & 31);
+          if (rs >= 0 && bs < a.W)
+            for (int ti = t0; ti < nt; ti += 32)
+              a.tmax[size_t(rs) * a.tmax_stride + size_t(bs) * vt + (glo >> 5) + ti] = tb[ti * kTmRow + bb];
+        }
+      } else {
+        for (int e = threadIdx.x; e < nt * kLogitsWaves * 32; e += 64 * kLogitsWaves) {
+          const int bb = e % (kLogitsWaves * 32), ti = e / (kLogitsWaves * 32);
+          const int rs = slot_r[bb >> 5], bs = slot_b[bb >> 5] + (bb & 31);
+          if (rs >= 0 && bs < a.W)
+            a.tmax[size_t(rs) * a.tmax_stride + size_t((glo >> 5) + ti) * a.W + bs] = tb[ti * kTmRow + bb];
+        }
+      }
+    }
+  };
+  // ... and its log-sum-exp part (the two lane halves of beam b merged), after which the
+  // running state starts again for the next group
+  auto flush_lse = [&](int g) {
+    const float mo = __shfl_xor(mrun, 32), so = __shfl_xor(srun, 32);
+    const float mm = fmaxf(mrun, mo);
+    float ss = 0.0f;
+    if (mrun != -INFINITY) ss += srun * __builtin_amdgcn_exp2f((mrun - mm) * kLog2e);
+    if (mo != -INFINITY) ss += so * __builtin_amdgcn_exp2f((mo - mm) * kLog2e);
+    if (hf == 0 && bvalid) a.lse_part[(size_t(r) * a.W_max + b) * a.nvg + g] = make_float4(mm, ss, nrun, 0.0f);
+    mrun = -INFINITY;
+    srun = 0.0f;
+    nrun = INFINITY;
+  };
+  int tm_next = vg0;                                 // first group whose maxima are still in LDS
+
   // the bf16 codebook's two forms: z in two fp16 terms against the rescaled codebook
   // (F16), or in three bf16 terms; one instantiation runs, chosen per launch
   auto bf16_body = [&](auto f16c) {
@@ -504,9 +553,9 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     // the logits of tile j are acc x 2^-(t_b + s_j): the beam's factor, the tile's
     // exponents (staged in LDS with the first codebook tile)
     const float zsb = F16 ? (bvalid ? a.zscale[size_t(r) * a.W_max + b] : 1.0f) : 1.0f;
-    __shared__ float tsf[F16 ? kMaxGroupTiles : 1];        // 2^-s_j of the group's tiles
+    __shared__ float tsf[F16 ? kMaxGroupTiles * kMaxGroupsPerBlock : 1];   // 2^-s_j of the block's tiles
     if constexpr (F16) {
-      if (threadIdx.x < kMaxGroupTiles && code_lo + 32 * int(threadIdx.x) < code_hi)
+      if (threadIdx.x < kMaxGroupTiles * kMaxGroupsPerBlock && code_lo + 32 * int(threadIdx.x) < code_hi)
         tsf[threadIdx.x] = ldexpf(1.0f, -a.tscale[(code_lo >> 5) + threadIdx.x]);
     }
     auto tfac = [&](int c0) { return F16 ? zsb * tsf[(c0 - code_lo) >> 5] : 1.0f; };
@@ -581,6 +630,11 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
         for (; c0 + 64 < code_hi; c0 += 64) {
           put(buf ^ 1);
           __syncthreads();
+          if (c0 != code_lo && (c0 & (a.cpw - 1)) == 0) {    // block-uniform: c0 opens a group
+            flush_lse((c0 >> a.cpw_shift) - 1);
+            flush_tm((c0 >> a.cpw_shift) - 1);
+            tm_next = c0 >> a.cpw_shift;
+          }
           fetch(c0 + 128);
           const float f0 = tfac(c0), f1 = tfac(c0 + 32);
           f32x16 n0, n1;
@@ -627,6 +681,8 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
           a1 = n1;
           buf ^= 1;
         }
+        // the last stage may open a group: the previous group's maxima go out at the end
+        if (c0 != code_lo && (c0 & (a.cpw - 1)) == 0) flush_lse((c0 >> a.cpw_shift) - 1);
         const float f0 = tfac(c0);
         fold(a0, c0, f0, kLog2e * f0);
         if (c0 + 32 < code_hi) {
@@ -691,34 +747,13 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     for (int c0 = code_lo; c0 < code_hi; c0 += 32)
       fold(block_mfma_f32<DV>(wt, c0 + m, a.V, hf, zv), c0, 1.0f, kLog2e);
   }
+  // the block's last group (and a group the last stage closed)
+  const int g_last = (code_hi - 1) >> a.cpw_shift;
   if constexpr (STAGE_TM) {
     __syncthreads();
-    const int nt = (code_hi - code_lo + 31) >> 5;
-    if (a.beam_major) {
-      // 32 lanes per beam: one contiguous row of the group's tiles, 32 at a time
-      const int t0 = threadIdx.x & 31;
-      for (int bb = threadIdx.x >> 5; bb < kLogitsWaves * 32; bb += 2 * kLogitsWaves) {
-        const int rs = slot_r[bb >> 5], bs = slot_b[bb >> 5] + (bb & 31);
-        if (rs >= 0 && bs < a.W)
-          for (int ti = t0; ti < nt; ti += 32)
-            a.tmax[size_t(rs) * a.tmax_stride + size_t(bs) * vt + (code_lo >> 5) + ti] = tms[ti * kTmRow + bb];
-      }
-    } else {
-      for (int e = threadIdx.x; e < nt * kLogitsWaves * 32; e += 64 * kLogitsWaves) {
-        const int bb = e % (kLogitsWaves * 32), ti = e / (kLogitsWaves * 32);
-        const int rs = slot_r[bb >> 5], bs = slot_b[bb >> 5] + (bb & 31);
-        if (rs >= 0 && bs < a.W)
-          a.tmax[size_t(rs) * a.tmax_stride + size_t((code_lo >> 5) + ti) * a.W + bs] = tms[ti * kTmRow + bb];
-      }
-    }
+    for (int g = tm_next; g <= g_last; ++g) flush_tm(g);
   }
-  // merge the two lane halves of beam b
-  const float mo = __shfl_xor(mrun, 32), so = __shfl_xor(srun, 32);
-  const float mm = fmaxf(mrun, mo);
-  float ss = 0.0f;
-  if (mrun != -INFINITY) ss += srun * __builtin_amdgcn_exp2f((mrun - mm) * kLog2e);
-  if (mo != -INFINITY) ss += so * __builtin_amdgcn_exp2f((mo - mm) * kLog2e);
-  if (hf == 0 && bvalid) a.lse_part[(size_t(r) * a.W_max + b) * a.nvg + vg] = make_float4(mm, ss, nrun, 0.0f);
+  flush_lse(g_last);
 }
 
 // ---------------------------------------------------------------- block-wide radix and sort helpers
@@ -1824,7 +1859,7 @@ static int launch_dv(const SelectArgs& a, const LogitsK& lk, const RefineK& rk, 
                      hipStream_t s, bool refine) {
   const bool bf = a.wout_dtype == GDN_BF16;
   if (!refine) {
-    dim3 grid(((a.R * lk.nchunk + kLogitsWaves - 1) / kLogitsWaves) * lk.nvg);
+    dim3 grid(((a.R * lk.nchunk + kLogitsWaves - 1) / kLogitsWaves) * ((lk.nvg + lk.gpb - 1) / lk.gpb));
     if (bf) hipLaunchKernelGGL((logits_kernel<DV, true>), grid, dim3(64 * kLogitsWaves), 0, s, lk);
     else hipLaunchKernelGGL((logits_kernel<DV, false>), grid, dim3(64 * kLogitsWaves), 0, s, lk);
   } else {
@@ -1933,6 +1968,23 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   const bool bounded = int64_t(a.W) * Vt > kSelList && int64_t(a.W) * nvg >= Kt;
   LogitsK lk{a.R, a.W, a.W_max, a.V, nch, nvg, cpw, nch_max, bounded ? 1 : 0, z, zf, woutT, woutT16,
              zscale, tscale, f16flag, f16_on, tmax, tstride, lse_part};
+  while ((1 << lk.cpw_shift) < cpw) ++lk.cpw_shift;         // cpw is a power of two
+  // d_v <= 128 with a bf16 codebook (the two-tile pipeline): a block takes up to eight
+  // code groups in turn while the grid keeps a block per CU, so that fewer blocks start
+  // and end one after the other on a CU (each group's tile maxima and log-sum-exp part
+  // are those of a block of its own).  GDN_BEAM_LOGITS_GPB sets it (tests).
+  if (a.d_v <= 128 && split) {
+    const int64_t nchg = (int64_t(a.R) * nch + kLogitsWaves - 1) / kLogitsWaves;
+    int cap = kMaxGroupsPerBlock;
+    bool forced_gpb = false;
+    if (const char* e = getenv("GDN_BEAM_LOGITS_GPB")) {
+      const int v = atoi(e);
+      if (v >= 1) { cap = v < kMaxGroupsPerBlock ? v : kMaxGroupsPerBlock; forced_gpb = true; }
+    }
+    while (lk.gpb * 2 <= cap && lk.gpb * 2 <= nvg &&
+           (forced_gpb || nchg * ((nvg + 2 * lk.gpb - 1) / (2 * lk.gpb)) >= kLogitsMinBlocks))
+      lk.gpb *= 2;
+  }
   RefineK rk{a.W, a.W_max, a.V, Vt, G_max, nch_max, z, zf, woutT, lse, cum, sel, groups, gtiles, rkeys,
              woutT16, zscale, tscale, f16flag, f16_on, 0, a.W_next, a.forced_parent, a.forced_token, flog,
              status};
