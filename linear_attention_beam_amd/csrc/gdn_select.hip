@@ -567,29 +567,33 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
     const u32x4* wt = static_cast<const u32x4*>(F16 ? a.woutT16 : a.woutT);
     // thread e-th entry of a tile: row e / (DV / 8), column e % (DV / 8); rows past the
     // codebook load code 0 (never used)
-    u32x4 stg[PT];
-    auto fetch = [&](int c0) {
+    // two register sets for tiles in flight (the pipelined path fetches two stages ahead)
+    u32x4 stg[PT], stg2[PT];
+    // (every thread has PT entries where NE is a multiple of the block: the loads are
+    // then unconditional, and the compiler counts them exactly)
+    constexpr bool ALL_E = NE % (64 * kLogitsWaves) == 0;
+    auto fetch = [&](int c0, u32x4* dst) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < PT; ++u) {
         const int e = threadIdx.x + u * 64 * kLogitsWaves;
-        if (e < NE) {
+        if (ALL_E || e < NE) {
           const int row = c0 + e / (DV / 8);
-          stg[u] = wt[size_t(row < a.V ? row : 0) * (DV / 8) + e % (DV / 8)];
+          dst[u] = wt[size_t(row < a.V ? row : 0) * (DV / 8) + e % (DV / 8)];
         }
       }
     };
-    auto put = [&](int buf) {
+    auto put = [&](int buf, const u32x4* src) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < PT; ++u) {
         const int e = threadIdx.x + u * 64 * kLogitsWaves;
-        if (e < NE) tile[buf][(e / (DV / 8)) * RS + e % (DV / 8)] = stg[u];
+        if (ALL_E || e < NE) tile[buf][(e / (DV / 8)) * RS + e % (DV / 8)] = src[u];
       }
     };
     const u32x4* zb = a.zf + zf_lane_base(r, a.nch_max, DV, chunk * 32, hf) + m;
     if constexpr (KS <= 16) {
       // the first tile's loads go out before the z operand's (loads complete in order,
       // so staging the tile then waits for those alone)
-      fetch(code_lo);
+      fetch(code_lo, stg);
       u32x4 zh[KS], zm[KS], zl[F16 ? 1 : KS];
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
@@ -597,13 +601,13 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
         zm[kk] = zb[(3 * kk + 1) * 64];
         if constexpr (!F16) zl[kk] = zb[(3 * kk + 2) * 64];
       }
-      put(0);
+      put(0, stg);
       // wait for the whole z operand here, so that inside the loop only the prefetched
       // tile is waited for
       if constexpr (F16) asm volatile("" ::"v"(zm[KS - 1][0]));
       else asm volatile("" ::"v"(zl[KS - 1][0]));
       __syncthreads();
-      if (code_lo + 32 * TPS < code_hi) fetch(code_lo + 32 * TPS);
+      if (code_lo + 32 * TPS < code_hi) fetch(code_lo + 32 * TPS, stg);
       // A fragments of tile `sub` of LDS buffer `buf`
       auto frags = [&](u32x4* w, int buf, int sub) {
 #pragma unroll
@@ -623,19 +627,28 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
       if constexpr (KS <= 8) {
         f32x16 a0 = mfma_tile(0, 0), a1 = mfma_tile(0, 1);
         int buf = 0, c0 = code_lo;
+        // the tiles of stage 1 are in flight in stg; those of stage 2 go into stg2: a
+        // stage's tiles are fetched two passes before they are staged
+        fetch(code_lo + 128, stg2);
         // stages with a successor: both of their tiles are whole, and the body is one
-        // basic block in which the 48 MFMAs of the next stage interleave with the folds
-        // of this one (the next fetch is issued unconditionally on clamped rows; past
-        // the group it is never staged)
-        for (; c0 + 64 < code_hi; c0 += 64) {
-          put(buf ^ 1);
+        // basic block in which the MFMAs of the next stage interleave with the folds of
+        // this one (fetches are issued unconditionally on clamped rows; past the block's
+        // codes they are never staged).  `slot` holds the next stage's tiles and then
+        // takes those of the stage after the following one; the loop alternates stg and
+        // stg2.
+        auto stage = [&](u32x4* slot) __attribute__((always_inline)) {
+          put(buf ^ 1, slot);
           __syncthreads();
           if (c0 != code_lo && (c0 & (a.cpw - 1)) == 0) {    // block-uniform: c0 opens a group
             flush_lse((c0 >> a.cpw_shift) - 1);
             flush_tm((c0 >> a.cpw_shift) - 1);
             tm_next = c0 >> a.cpw_shift;
+            // the flush's stores complete here (vmcnt 0): with stores in flight the
+            // compiler waits for every load before staging a tile, and the tiles of two
+            // stages ahead are in flight here
+            __builtin_amdgcn_s_waitcnt(0x0F70);
           }
-          fetch(c0 + 128);
+          fetch(c0 + 192, slot);
           const float f0 = tfac(c0), f1 = tfac(c0 + 32);
           f32x16 n0, n1;
           if constexpr (F16) {
@@ -680,7 +693,16 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
           a0 = n0;
           a1 = n1;
           buf ^= 1;
+          c0 += 64;
+        };
+        // n stages with a successor, in pairs (one back edge: every load the loop
+        // leaves in flight is then one the compiler can count), an odd one last
+        const int n = (code_hi - code_lo + 63) / 64 - 1;
+        for (int k = 0; k < (n >> 1); ++k) {
+          stage(stg);
+          stage(stg2);
         }
+        if (n & 1) stage(stg);
         // the last stage may open a group: the previous group's maxima go out at the end
         if (c0 != code_lo && (c0 & (a.cpw - 1)) == 0) flush_lse((c0 >> a.cpw_shift) - 1);
         const float f0 = tfac(c0);
@@ -696,9 +718,9 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
           const float f0 = tfac(c0);
           fold(mfma_tile(buf, 0), c0, f0, kLog2e * f0);
           if (more) {
-            put(buf ^ 1);
+            put(buf ^ 1, stg);
             __syncthreads();
-            if (c0 + 64 < code_hi) fetch(c0 + 64);
+            if (c0 + 64 < code_hi) fetch(c0 + 64, stg);
           }
           buf ^= 1;
         }
@@ -707,13 +729,13 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
       // d_v > 256: the z operand does not fit in registers; each tile re-reads it in
       // chunks of eight k-steps (same MFMA order, kk ascending)
       constexpr int KZ = 8;
-      fetch(code_lo);
-      put(0);
+      fetch(code_lo, stg);
+      put(0, stg);
       __syncthreads();
       int buf = 0;
       for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
         const bool more = c0 + 32 < code_hi;         // block-uniform
-        if (more) fetch(c0 + 32);
+        if (more) fetch(c0 + 32, stg);
         f32x16 acc = {};
 #pragma unroll 1
         for (int k0 = 0; k0 < KS; k0 += KZ) {
@@ -729,7 +751,7 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
         }
         const float f0 = tfac(c0);
         fold(acc, c0, f0, kLog2e * f0);
-        if (more) put(buf ^ 1);
+        if (more) put(buf ^ 1, stg);
         __syncthreads();
         buf ^= 1;
       }
