@@ -384,7 +384,7 @@ struct LogitsK {
 constexpr int kLogitsWaves = 8;
 // Codes per group are at most 1024 (the launcher's choice): 32 tiles.
 constexpr int kMaxGroupTiles = 32;
-// Code groups one block may take in turn (the launcher's choice, d_v <= 128 with a bf16
+// Code groups one block may take in turn (the launcher's choice, d_v <= 256 with a bf16
 // codebook), and the blocks below which it stops merging them: one per CU.
 constexpr int kMaxGroupsPerBlock = 8;
 constexpr int kLogitsMinBlocks = 256;
@@ -711,10 +711,67 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
           const float f1 = tfac(c0 + 32);
           fold(a1, c0 + 32, f1, kLog2e * f1);
         }
+      } else if constexpr (F16) {
+        // d_v = 256, two fp16 terms (z takes 128 registers): one tile per stage,
+        // pipelined as above.  A tile's 16 fragments are read in two halves of eight
+        // (the MFMAs keep their order, kk ascending); the first half's 16 MFMAs go out
+        // among the fold of the tile before.  Tiles are fetched two stages ahead.
+        static_assert(KS == 16, "d_v = 256");
+        f32x16 a0 = mfma_tile(0, 0);
+        int buf = 0, c0 = code_lo;
+        fetch(code_lo + 64, stg2);
+        auto stage = [&](u32x4* slot) __attribute__((always_inline)) {
+          put(buf ^ 1, slot);
+          __syncthreads();
+          if (c0 != code_lo && (c0 & (a.cpw - 1)) == 0) {    // block-uniform: c0 opens a group
+            flush_lse((c0 >> a.cpw_shift) - 1);
+            flush_tm((c0 >> a.cpw_shift) - 1);
+            tm_next = c0 >> a.cpw_shift;
+            __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): the flush's stores
+          }
+          fetch(c0 + 96, slot);
+          const float f0 = tfac(c0);
+          u32x4 w[8];
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) w[kk] = tile[buf ^ 1][m * RS + (HV / 8) * hf + kk];
+          __builtin_amdgcn_sched_barrier(0);
+          f32x16 n0 = block_mfma_split<F16, 8>(w, zh, zm, zl);
+          fold_full(a0, c0, f0, kLog2e * f0);
+#pragma unroll
+          for (int i = 0; i < NTERM * 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) w[kk] = tile[buf ^ 1][m * RS + (HV / 8) * hf + 8 + kk];
+          __builtin_amdgcn_sched_barrier(0);
+          n0 = block_mfma_split<F16, 8>(w, zh + 8, zm + 8, zl, n0);
+          __builtin_amdgcn_sched_barrier(0);
+          a0 = n0;
+          buf ^= 1;
+          c0 += 32;
+        };
+        const int n = (code_hi - code_lo + 31) / 32 - 1;       // tiles with a successor
+        for (int k = 0; k < (n >> 1); ++k) {
+          stage(stg);
+          stage(stg2);
+        }
+        if (n & 1) stage(stg);
+        // the last tile may open a group: the previous group's maxima go out at the end
+        if (c0 != code_lo && (c0 & (a.cpw - 1)) == 0) flush_lse((c0 >> a.cpw_shift) - 1);
+        const float f0 = tfac(c0);
+        fold(a0, c0, f0, kLog2e * f0);
       } else {
         int buf = 0;
         for (int c0 = code_lo; c0 < code_hi; c0 += 32) {
           const bool more = c0 + 32 < code_hi;       // block-uniform
+          if (c0 != code_lo && (c0 & (a.cpw - 1)) == 0) {    // block-uniform: c0 opens a group
+            flush_lse((c0 >> a.cpw_shift) - 1);
+            flush_tm((c0 >> a.cpw_shift) - 1);
+            tm_next = c0 >> a.cpw_shift;
+            __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): the flush's stores
+          }
           const float f0 = tfac(c0);
           fold(mfma_tile(buf, 0), c0, f0, kLog2e * f0);
           if (more) {
@@ -1991,11 +2048,12 @@ int launch_select(const SelectArgs& a, hipStream_t s) {
   LogitsK lk{a.R, a.W, a.W_max, a.V, nch, nvg, cpw, nch_max, bounded ? 1 : 0, z, zf, woutT, woutT16,
              zscale, tscale, f16flag, f16_on, tmax, tstride, lse_part};
   while ((1 << lk.cpw_shift) < cpw) ++lk.cpw_shift;         // cpw is a power of two
-  // d_v <= 128 with a bf16 codebook (the two-tile pipeline): a block takes up to eight
-  // code groups in turn while the grid keeps a block per CU, so that fewer blocks start
-  // and end one after the other on a CU (each group's tile maxima and log-sum-exp part
-  // are those of a block of its own).  GDN_BEAM_LOGITS_GPB sets it (tests).
-  if (a.d_v <= 128 && split) {
+  // d_v <= 256 with a bf16 codebook (z in registers, tile maxima staged): a block takes
+  // up to eight code groups in turn while the grid keeps a block per CU, so that fewer
+  // blocks start and end one after the other on a CU (each group's tile maxima and
+  // log-sum-exp part are those of a block of its own).  GDN_BEAM_LOGITS_GPB sets it
+  // (tests).
+  if (a.d_v <= 256 && split) {
     const int64_t nchg = (int64_t(a.R) * nch + kLogitsWaves - 1) / kLogitsWaves;
     int cap = kMaxGroupsPerBlock;
     bool forced_gpb = false;

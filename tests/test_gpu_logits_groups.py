@@ -21,6 +21,8 @@ CASES = {
     "mixed_c": ("single", dict(widths=(64, 700, 700), V=777, io="bf16", wout="bf16")),
     # 512 beams x 1000 codes: the bounded pass over a partial last group
     "bounded_v1000": ("tiny", dict(widths=(512, 512, 512), V=1000, io="bf16", wout="bf16")),
+    # d_v = 256 (one tile per stage), 777 codes
+    "dv256_v777": ("single", dict(d_k=256, d_v=256, widths=(64, 300, 300), V=777, io="bf16", wout="bf16")),
 }
 
 
