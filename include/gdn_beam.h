@@ -113,6 +113,8 @@ gdn_status gdn_beam_step(gdn_beam_ctx* ctx, int32_t t,
  * (R*W_t*V*d_v; the environment variable GDN_BEAM_F16_MIN_MACS, read per call, changes
  * the threshold), as two fp16 terms against the codebook rescaled exactly into fp16 tile
  * by tile, where every 32-code tile's nonzero entries span at most 32 binades.
+ * The environment variable GDN_BEAM_LOGITS_GPB (1..8, read per call) sets how many code
+ * groups one logits block takes in turn; results do not depend on it (for tests).
  * The exact top-W_next over the request's W_t*V candidates, ordered by score
  * descending then flat index b*V + c ascending, is written to parent, token
  * [R,W_next] int32 and score [R,W_next] fp32 (RecoGEM section 4.3).
