@@ -15,9 +15,13 @@
 // is taken over their 32 K candidates.
 //
 // Kernels
-//   zsum_kernel      z_b = sum_h o_b, stored as the bf16 hi/mid/lo MFMA operand (bf16
-//                    codebook) or fp32 (fp32 codebook); its last grid row transposes
-//                    the codebook Wout[d_v,V] -> [V,d_v] (MFMA operand order).
+//   wprep_kernel     large selections: the codebook transposed to [V,d_v] and rescaled
+//                    into fp16 tile by tile (exponent per 32-code tile).
+//   zsum_kernel      z_b = sum_h o_b, stored as the MFMA operand: two fp16 terms and the
+//                    beam's scale where wprep_kernel ran and every tile fits fp16, else
+//                    bf16 hi/mid/lo (bf16 codebook), or fp32 (fp32 codebook); its last
+//                    grid row transposes the codebook Wout[d_v,V] -> [V,d_v] where
+//                    wprep_kernel did not run.
 //   logits_kernel    first pass on MFMA: per (beam, tile) largest logit, online
 //                    log-sum-exp parts per code group.
 //   tile_select_kernel  one block per request: log-sum-exp per beam, then the exact
@@ -398,15 +402,15 @@ constexpr int kSelList = 8192;
 constexpr int kSelPairs = 4096;
 constexpr int kMaxGroupsMask = 128;
 
-// Block: kLogitsWaves chunks of 32 beams x one group of cpw codes.  Chunks are numbered
-// over all requests, request-major, so that every wave has one wherever a request has
-// fewer chunks than a block has waves (the codebook is the same for all requests).
-// Each 32-code tile of
-// the codebook is staged once per block in LDS (double-buffered; one barrier per stage
-// of two tiles for d_v <= 128, of one tile above) and read by every wave as its A
-// operand.  Lane l keeps beam l % 32 and folds its 16
-// codes of every tile into the tile maximum (with its partner half) and a running
-// log-sum-exp.  Waves past the last chunk follow the barriers and store nothing.
+// Block: kLogitsWaves chunks of 32 beams x gpb consecutive groups of cpw codes, taken
+// in turn.  Chunks are numbered over all requests, request-major, so that every wave
+// has one wherever a request has fewer chunks than a block has waves (the codebook is
+// the same for all requests).  Each 32-code tile of the codebook is staged once per
+// block in LDS (double-buffered; one barrier per stage of two tiles for d_v <= 128, of
+// one tile above) and read by every wave as its A operand.  Lane l keeps beam l % 32
+// and folds its 16 codes of every tile into the tile maximum (with its partner half)
+// and a running log-sum-exp; at the end of each code group both go out and the running
+// state starts again.  Waves past the last chunk follow the barriers and store nothing.
 template <int DV, bool WBF16>
 __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
   constexpr int HV = DV / 2;
