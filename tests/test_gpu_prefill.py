@@ -142,3 +142,28 @@ def test_prefill_workspace_reuse_and_short_workspace():
     with pytest.raises(B.GdnBeamError) as ei:
         prefill(S, p["k"], p["v"], p["alpha"], p["beta"], p["offsets"], workspace=ws)
     assert ei.value.status == B.GDN_ERR_WORKSPACE
+
+
+def test_prefill_zero_and_tiny_decay():
+    """Decay gates of 0 (the state restarts from that token) and of 1e-20 (whose products
+    underflow in fp32), inside a chunk, at a chunk's last and first tokens and over a
+    run: both forms agree with the oracle and stay finite.  The chunked form takes its
+    in-chunk decay ratios as direct products over the tokens between, never as quotients,
+    so no 0/0 or inf can arise."""
+    wl = _wl("single")
+    lengths = [100, 70]                          # request 1 starts inside block 3
+    p = sdev.prompts(wl, torch.device("cuda"), R=2, lengths=lengths)
+    a = p["alpha"]
+    a[5, :] = 0.0
+    a[31, :] = 0.0                               # last token of block 0
+    a[32, :] = 1e-20                             # first token of block 1
+    a[77, :] = 0.0
+    a[120, :2] = 1e-20                           # two heads only
+    a[150:153, :] = 0.0                          # a run, in request 1
+    for form in FORMS:
+        S = _run(p, wl, 2, form)
+        for r in range(2):
+            assert np.isfinite(S[r]).all(), (form, r)
+            e = rel_err(S[r], _oracle_from_device(p, wl, r))
+            say(f"{form} r={r} rel err {e:.3e}")
+            assert e <= TOL
