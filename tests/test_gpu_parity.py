@@ -137,6 +137,74 @@ def test_forced_parents_parity(name, R):
     assert g.export(B.GDN_EXPORT_STATUS)[0] == 0
 
 
+def _gate_edges(t, alpha, beta):
+    """Gate values at the ends of their ranges for step t, from float32 alpha, beta [H, W]:
+    step 1 forgets every parent (alpha = 0), step 2 keeps every parent unchanged
+    (alpha = 1, beta = 0); the other steps mix, per (head, beam), alpha = 0, alpha = 1,
+    beta = 0, beta = 1, alpha = beta = 0 (a zero state and output) and the drawn values."""
+    a, b = alpha.copy(), beta.copy()
+    if t == 1:
+        a[:] = 0.0
+    elif t == 2:
+        a[:] = 1.0
+        b[:] = 0.0
+    else:
+        code = np.random.default_rng(1000 + t).integers(0, 6, a.shape)
+        code.flat[:6] = np.arange(6)                  # every case at least once
+        a[code == 0] = 0.0
+        a[code == 1] = 1.0
+        b[code == 2] = 0.0
+        b[code == 3] = 1.0
+        a[code == 4] = 0.0
+        b[code == 4] = 0.0
+    return a, b
+
+
+@pytest.mark.parametrize("name", ["tiny_t6", "single", "single_t8", "single_bf16_t8", "single_gqa",
+                                  "single_dk256", "single_dv512"])
+def test_gate_edges_parity(name):
+    """Eq. (4) with decay gates of 0 and 1 and write strengths of 0 and 1, set alike in the
+    device inputs and the oracle's: a parent forgotten, kept unchanged, overwritten along
+    k, or a state of zeros, also as ancestor records that later steps replay (eqs. 6-7)."""
+    wl = _wl(name)
+    g = GpuDecode(wl, R=1, exact=(0,))
+    tol = TOL[wl.io]
+    gates = {}
+    for t in range(wl.T):
+        x = gen.step_inputs(wl, 0, t)
+        a, b = _gate_edges(t, x["alpha"], x["beta"])
+        gates[t] = (a, b)
+        g.inputs[t]["alpha"][0].copy_(torch.from_numpy(a))
+        g.inputs[t]["beta"][0].copy_(torch.from_numpy(b))
+    torch.cuda.synchronize()
+    plain = g.step_inputs64
+
+    def step_inputs64(r, t):
+        q, k, v, _, _ = plain(r, t)
+        a, b = gates[t]
+        return q, k, v, a.astype(np.float64), b.astype(np.float64)
+
+    g.step_inputs64 = step_inputs64
+    dec = oracle.FullStateDecoder(g.S_exact[0].astype(np.float64), wl.width(0))
+    g.init()
+    for t in range(wl.T):
+        o = to_np(g.step(t))
+        cum_before = g.export(B.GDN_EXPORT_CUM)
+        fp, ft = g.forced_maps(t)
+        sel = g.select(t, forced=(fp, ft))
+        dpool = g.export(B.GDN_EXPORT_GTR_DELTA)
+        o_ref = _cmp_gdn(wl, dec, g, 0, t, o, dpool, tol)
+        if t != 2:
+            # alpha = beta = 0 (present at the mixed steps) gives an output of zeros, which the
+            # relative bound above holds the device's output to exactly
+            assert np.any(np.all(o_ref == 0.0, axis=-1)) == (t != 1)
+        check_selection(o[0], cum_before[0][:wl.width(t)], g.Wout64, wl.width(t + 1),
+                        {k: v[0] for k, v in sel.items()}, f"t={t}")
+        dec.select(t, o_ref, g.Wout64, wl.width(t + 1), fp[0], ft[0])
+        np.testing.assert_array_equal(g.export(B.GDN_EXPORT_ANCESTRY)[0][:wl.width(t + 1), :t + 1], dec.anc)
+    assert g.export(B.GDN_EXPORT_STATUS)[0] == 0
+
+
 @pytest.mark.parametrize("name,R", [("tiny", 1), ("single", 1), ("batch", 2), ("tiny_v37", 1),
                                     ("tiny_odd_w", 2), ("tiny_few_tiles", 1), ("tiny_shrink", 2), ("single_v300", 1),
                                     ("single_bf16_t6", 1), ("tiny_w1024_t6", 1), ("tiny_t8", 1),
