@@ -76,6 +76,13 @@ DERIVED = {
     "single_dv512": ("single", dict(d_v=512, io="bf16", wout="bf16")),
     "single_dv512_f32io": ("single", dict(d_v=512, wout="bf16")),
     "single_dk256_dv512": ("single", dict(d_k=256, d_v=512, io="bf16", wout="bf16")),
+    # degenerate beams and codebooks: one beam (greedy decoding, K = 1 in every
+    # selection), one code (every beam has a single candidate whose log-softmax is 0, so
+    # the selection orders the beams by their cumulative scores), and both
+    "tiny_w1": ("tiny", dict(widths=(1, 1, 1), V=37)),
+    "tiny_v1": ("tiny", dict(V=1)),
+    "tiny_w1_v1": ("tiny", dict(widths=(1, 1, 1), V=1)),
+    "single_bf16_v1": ("single", dict(V=1, io="bf16", wout="bf16")),
 }
 
 
@@ -109,7 +116,8 @@ def _cmp_gdn(wl, dec, g, r, t, o, dpool, tol, heads=None):
                                     ("single_t8", 1),
                                     ("single_bf16_t6", 1), ("single_gqa", 1), ("batch_gqa", 2),
                                     ("single_dk256", 1), ("single_dv512", 1), ("single_dv512_f32io", 1),
-                                    ("single_dk256_dv512", 1)])
+                                    ("single_dk256_dv512", 1), ("tiny_w1", 1), ("tiny_v1", 1),
+                                    ("tiny_w1_v1", 1), ("single_bf16_v1", 1)])
 def test_forced_parents_parity(name, R):
     wl = _wl(name)
     g = GpuDecode(wl, R=R, exact=range(R))
@@ -212,7 +220,8 @@ def test_gate_edges_parity(name):
                                     ("tiny_bounded_v1000", 1), ("mixed_a", 1), ("mixed_b", 1), ("mixed_c", 1),
                                     ("multi_bounded", 3), ("multi_small", 3),
                                     ("single_gqa", 1), ("single_dk256", 1), ("single_dv512", 1),
-                                    ("single_dk256_dv512", 1)])
+                                    ("single_dk256_dv512", 1), ("tiny_w1", 1), ("tiny_v1", 1),
+                                    ("tiny_w1_v1", 1), ("single_bf16_v1", 1)])
 def test_select_mode_parity(name, R):
     """Top-W drives the beams.  The oracle follows the GPU's choice (teacher forcing)
     after the selection itself has been checked against the exact top-W."""
