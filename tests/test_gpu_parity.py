@@ -83,6 +83,9 @@ DERIVED = {
     "tiny_v1": ("tiny", dict(V=1)),
     "tiny_w1_v1": ("tiny", dict(widths=(1, 1, 1), V=1)),
     "single_bf16_v1": ("single", dict(V=1, io="bf16", wout="bf16")),
+    # a single SID step (T_max = 1: ancestry of one column, no record replayed)
+    "tiny_t1": ("tiny", dict(T=1, widths=(8,))),
+    "single_bf16_t1": ("single", dict(T=1, widths=(64,), io="bf16", wout="bf16")),
 }
 
 
@@ -117,7 +120,8 @@ def _cmp_gdn(wl, dec, g, r, t, o, dpool, tol, heads=None):
                                     ("single_bf16_t6", 1), ("single_gqa", 1), ("batch_gqa", 2),
                                     ("single_dk256", 1), ("single_dv512", 1), ("single_dv512_f32io", 1),
                                     ("single_dk256_dv512", 1), ("tiny_w1", 1), ("tiny_v1", 1),
-                                    ("tiny_w1_v1", 1), ("single_bf16_v1", 1)])
+                                    ("tiny_w1_v1", 1), ("single_bf16_v1", 1), ("tiny_t1", 1),
+                                    ("single_bf16_t1", 1)])
 def test_forced_parents_parity(name, R):
     wl = _wl(name)
     g = GpuDecode(wl, R=R, exact=range(R))
@@ -221,7 +225,8 @@ def test_gate_edges_parity(name):
                                     ("multi_bounded", 3), ("multi_small", 3),
                                     ("single_gqa", 1), ("single_dk256", 1), ("single_dv512", 1),
                                     ("single_dk256_dv512", 1), ("tiny_w1", 1), ("tiny_v1", 1),
-                                    ("tiny_w1_v1", 1), ("single_bf16_v1", 1)])
+                                    ("tiny_w1_v1", 1), ("single_bf16_v1", 1), ("tiny_t1", 1),
+                                    ("single_bf16_t1", 1)])
 def test_select_mode_parity(name, R):
     """Top-W drives the beams.  The oracle follows the GPU's choice (teacher forcing)
     after the selection itself has been checked against the exact top-W."""
