@@ -661,7 +661,8 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
             // MFMAs, and the folds follow all of them.  So each tile's eight fragments
             // are read first, behind a scheduling barrier (the MFMAs then wait for them
             // in order), and its 16 MFMAs go out among the fold of one tile of the
-            // stage before.
+            // stage before, four vector instructions after each (five or six: 2-5%
+            // slower on stress; three: 1% slower).
             u32x4 w[KS];
             frags(w, buf ^ 1, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -670,7 +671,7 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
 #pragma unroll
             for (int i = 0; i < NTERM * KS; ++i) {
               __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-              __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
+              __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
             }
             __builtin_amdgcn_sched_barrier(0);
             frags(w, buf ^ 1, 1);
@@ -680,7 +681,7 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
 #pragma unroll
             for (int i = 0; i < NTERM * KS; ++i) {
               __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
           } else {
@@ -744,7 +745,7 @@ __global__ void __launch_bounds__(64 * kLogitsWaves) logits_kernel(LogitsK a) {
 #pragma unroll
           for (int i = 0; i < NTERM * 8; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
