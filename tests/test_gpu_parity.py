@@ -76,6 +76,9 @@ DERIVED = {
     "single_dv512": ("single", dict(d_v=512, io="bf16", wout="bf16")),
     "single_dv512_f32io": ("single", dict(d_v=512, wout="bf16")),
     "single_dk256_dv512": ("single", dict(d_k=256, d_v=512, io="bf16", wout="bf16")),
+    # d_k = 256 over six SID steps: the records of the next beam chunk gathered during the
+    # current one (t = 1..3), then gathered per chunk (t = 4, 5)
+    "single_dk256_t6": ("single", dict(d_k=256, d_v=256, T=6, widths=(128,) * 6, io="bf16", wout="bf16")),
     # degenerate beams and codebooks: one beam (greedy decoding, K = 1 in every
     # selection), one code (every beam has a single candidate whose log-softmax is 0, so
     # the selection orders the beams by their cumulative scores), and both
@@ -121,7 +124,7 @@ def _cmp_gdn(wl, dec, g, r, t, o, dpool, tol, heads=None):
                                     ("single_dk256", 1), ("single_dv512", 1), ("single_dv512_f32io", 1),
                                     ("single_dk256_dv512", 1), ("tiny_w1", 1), ("tiny_v1", 1),
                                     ("tiny_w1_v1", 1), ("single_bf16_v1", 1), ("tiny_t1", 1),
-                                    ("single_bf16_t1", 1)])
+                                    ("single_bf16_t1", 1), ("single_dk256_t6", 1)])
 def test_forced_parents_parity(name, R):
     wl = _wl(name)
     g = GpuDecode(wl, R=R, exact=range(R))
@@ -173,7 +176,7 @@ def _gate_edges(t, alpha, beta):
 
 
 @pytest.mark.parametrize("name", ["tiny_t6", "single", "single_t8", "single_bf16_t8", "single_gqa",
-                                  "single_dk256", "single_dv512"])
+                                  "single_dk256", "single_dv512", "single_dk256_t6"])
 def test_gate_edges_parity(name):
     """Eq. (4) with decay gates of 0 and 1 and write strengths of 0 and 1, set alike in the
     device inputs and the oracle's: a parent forgotten, kept unchanged, overwritten along
@@ -226,7 +229,7 @@ def test_gate_edges_parity(name):
                                     ("single_gqa", 1), ("single_dk256", 1), ("single_dv512", 1),
                                     ("single_dk256_dv512", 1), ("tiny_w1", 1), ("tiny_v1", 1),
                                     ("tiny_w1_v1", 1), ("single_bf16_v1", 1), ("tiny_t1", 1),
-                                    ("single_bf16_t1", 1)])
+                                    ("single_bf16_t1", 1), ("single_dk256_t6", 1)])
 def test_select_mode_parity(name, R):
     """Top-W drives the beams.  The oracle follows the GPU's choice (teacher forcing)
     after the selection itself has been checked against the exact top-W."""
