@@ -145,6 +145,13 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"device compile failed: gdn_prefill.hip\n{r.stdout}\n{r.stderr}")
+    # the selection kernels' device code, for the same checks (scratch memory)
+    cmd = [cc, *common, f"--offload-arch={ARCH}", "--offload-device-only", "--no-gpu-bundle-output",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics", "-c",
+           os.path.join(CSRC, "gdn_select.hip"), "-o", os.path.join(objdir, "gdn_select.gfx950.o")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"device compile failed: gdn_select.hip\n{r.stdout}\n{r.stderr}")
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
