@@ -80,6 +80,16 @@ class BeamDecoder:
     def fullstate_step(self, t, S_ctx, q, k, v, alpha, beta, o, states, stream=None):
         """The FullState baseline in place of step(t); `states` is a device buffer of
         fullstate_bytes() bytes (see alloc_states)."""
+        self._ctx()
+        s = self.shape
+        if S_ctx is not None:                          # read at t = 0 only
+            _need("S_ctx", S_ctx, (s["R"], s["H"], s["d_v"], s["d_k"]), torch.float32, self.device)
+        self._step_inputs(q, k, v, alpha, beta, o)
+        if not isinstance(states, torch.Tensor) or not states.is_cuda or not states.is_contiguous():
+            raise ValueError("states: expected a dense device tensor (see alloc_states)")
+        if states.numel() * states.element_size() < self.fullstate_bytes():
+            raise ValueError(f"states: {states.numel() * states.element_size()} bytes, "
+                             f"expected at least {self.fullstate_bytes()}")
         B.gdn_fullstate_step(self.ctx, t, S_ctx, q, k, v, alpha, beta, o, states,
                              states.numel() * states.element_size(), self._stream(stream))
 
