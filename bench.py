@@ -197,6 +197,32 @@ def copy_bandwidth(torch, dev, mib=1024, reps=10):
     return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
+def stream_bandwidth(torch, dev, mib=1024, reps=6):
+    """GB/s of the library's streaming probe (gdn_beam_stream_probe): a copy (every byte
+    read and written) and a read of `mib` MiB with 16-byte non-temporal accesses, four
+    workgroups per compute unit; the fastest of `reps` launches after the first."""
+    from linear_attention_beam_amd import binding as Bb
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for mode, name, moved in ((0, "copy", 2 * n), (1, "read", n)):
+        Bb.gdn_beam_stream_probe(dst, src, n, mode, stream)
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            Bb.gdn_beam_stream_probe(dst, src, n, mode, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        out[name] = moved / (best * 1e-3) / 1e9
+    del src, dst
+    return out
+
+
 def kernel_hash(dims=None):
     """sha256[:16] of the built step kernel's machine code: of the instantiations of head
     dims (d_k, d_v) when given, else of all of them (None before a build)."""
@@ -676,8 +702,19 @@ def main():
         del src, dst
     copy_gbs = copy_bandwidth(torch, dev)
     log(args, f"device copy (read + write): {copy_gbs:.0f} GB/s")
+    stream_gbs = stream_bandwidth(torch, dev)
+    log(args, f"streaming probe: copy {stream_gbs['copy']:.0f} GB/s, read {stream_gbs['read']:.0f} GB/s")
 
     head = run_workload(args, wl, mode, torch, copy_gbs)
+
+    def with_stream(rf):
+        # the step kernel's achieved rate against the streaming probe (not the peak)
+        rf["stream_copy_GBs"] = stream_gbs["copy"]
+        rf["stream_read_GBs"] = stream_gbs["read"]
+        rf["frac_of_stream_copy"] = rf["achieved"] / stream_gbs["copy"]
+        return rf
+
+    with_stream(head["roofline"])
     torch.cuda.empty_cache()
     extra = {}
     for name in [x for x in args.extra.split(",") if x and x != wl.name]:
@@ -688,8 +725,8 @@ def main():
                                          "select_ms_per_t", "select_floor_ms_per_t", "step_ms_per_t",
                                          "gdn_step_rate")}
         extra[name]["config"] = r["config"]
-        extra[name]["roofline"] = {k: r["roofline"][k] for k in ("achieved", "frac", "traffic",
-                                                                 "bytes_per_decode")}
+        extra[name]["roofline"] = with_stream({k: r["roofline"][k] for k in ("achieved", "frac", "traffic",
+                                                                             "bytes_per_decode")})
         extra[name]["decode_roofline"] = r["decode_roofline"]
         extra[name]["prefill"] = r["prefill"]
         if "projection_mfma" in r:

@@ -238,6 +238,16 @@ gdn_status gdn_beam_step_times(float* ms /* host */, int32_t cap, int32_t* n /* 
  * unchanged.  buf = NULL disarms.  Errors: misaligned buf or bytes < 32 (INVALID_ARG). */
 gdn_status gdn_beam_stamp_projection(void* buf, size_t bytes);
 
+/* Measurement, not an operation of the method: the device's streaming rate, the
+ * reference against which HBM-bound launches are read.  mode 0 copies `bytes` from src
+ * to dst; mode 1 reads src and writes at most one 4-byte word at dst.  Both device,
+ * caller-owned, 16-byte aligned, bytes a multiple of 16 (not overlapping for mode 0);
+ * 16-byte non-temporal loads and stores, four 256-thread workgroups per compute unit,
+ * grid-strided, on `stream`.  Errors: null or misaligned pointers, bytes not a multiple
+ * of 16, mode outside 0..1 (INVALID_ARG); a launch failure (HIP). */
+gdn_status gdn_beam_stream_probe(void* dst, const void* src, size_t bytes, int32_t mode,
+                                 hipStream_t stream);
+
 /* Static description of a status code. */
 const char* gdn_beam_status_str(gdn_status s);
 

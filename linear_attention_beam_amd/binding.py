@@ -27,7 +27,7 @@ EXPORTS = ("gdn_beam_workspace_bytes", "gdn_beam_init", "gdn_beam_step", "gdn_be
            "gdn_beam_status_str", "gdn_beam_last_error", "gdn_beam_prefill",
            "gdn_beam_prefill_workspace_bytes",
            "gdn_fullstate_bytes", "gdn_fullstate_step", "gdn_beam_time_steps", "gdn_beam_step_times",
-           "gdn_beam_select_static", "gdn_beam_stamp_projection")
+           "gdn_beam_select_static", "gdn_beam_stamp_projection", "gdn_beam_stream_probe")
 GDN_STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -82,6 +82,7 @@ def _load():
         "gdn_beam_destroy": (None, [vp]),
         "gdn_beam_time_steps": (st, [i32]),
         "gdn_beam_stamp_projection": (st, [vp, c_size_t]),
+        "gdn_beam_stream_probe": (st, [vp, vp, c_size_t, i32, vp]),
         "gdn_beam_step_times": (st, [POINTER(ctypes.c_float), i32, POINTER(i32)]),
         "gdn_beam_status_str": (c_char_p, [st]),
         "gdn_beam_last_error": (c_char_p, []),
@@ -185,6 +186,11 @@ def gdn_beam_time_steps(capacity):
 
 def gdn_beam_stamp_projection(buf, nbytes):
     _check(_lib.gdn_beam_stamp_projection(_ptr(buf), nbytes), "gdn_beam_stamp_projection")
+
+
+def gdn_beam_stream_probe(dst, src, nbytes, mode, stream=None):
+    _check(_lib.gdn_beam_stream_probe(_ptr(dst), _ptr(src), nbytes, mode, _stream(stream)),
+           "gdn_beam_stream_probe")
 
 
 def gdn_beam_step_times(cap):

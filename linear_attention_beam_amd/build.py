@@ -17,7 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdnbeam.so")
-SOURCES = ["gdn_beam_api.cpp", "gdn_step.hip", "gdn_select.hip", "gdn_fullstate.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_beam_api.cpp", "gdn_step.hip", "gdn_select.hip", "gdn_fullstate.hip", "gdn_prefill.hip",
+           "gdn_probe.hip"]
 ARCH = "gfx950"
 
 

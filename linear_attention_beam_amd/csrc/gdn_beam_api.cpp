@@ -387,6 +387,15 @@ gdn_status gdn_beam_stamp_projection(void* buf, size_t bytes) {
   return GDN_OK;
 }
 
+gdn_status gdn_beam_stream_probe(void* dst, const void* src, size_t bytes, int32_t mode,
+                                 hipStream_t stream) {
+  if (!dst || !src || !aligned16(dst) || !aligned16(src) || bytes % 16 != 0 || mode < 0 || mode > 1)
+    return GDN_ERR_INVALID_ARG;
+  if (bytes == 0) return GDN_OK;
+  const int err = launch_stream_probe(dst, src, bytes, mode, stream);
+  return err ? hip_fail(err, "gdn_beam_stream_probe") : GDN_OK;
+}
+
 gdn_status gdn_beam_step_times(float* ms, int32_t cap, int32_t* n) {
   if (!n || cap < 0 || (cap > 0 && !ms)) return GDN_ERR_INVALID_ARG;
   std::lock_guard<std::mutex> g(g_timer.m);

@@ -227,6 +227,8 @@ int launch_prefill(const PrefillArgs& a, hipStream_t s);
 bool prefill_chunked(int d_k);
 size_t prefill_workspace_bytes(int H, int d_k, int64_t N);
 int launch_fullstate(const FullStepArgs& a, hipStream_t s);
+// Streaming probe (gdn_probe.hip): mode 0 copies bytes / 16 16-byte units, mode 1 reads them.
+int launch_stream_probe(void* dst, const void* src, size_t bytes, int mode, hipStream_t s);
 int copy_d2d(void* dst, const void* src, size_t bytes, hipStream_t s);
 const char* hip_error_string(int err);
 
