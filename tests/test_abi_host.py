@@ -184,6 +184,21 @@ def test_step_timing_argument_errors():
     assert f("gdn_beam_step_times", None, 0, ctypes.byref(n)) == B.GDN_OK and n.value == 0
 
 
+def test_stream_probe_argument_errors():
+    """The streaming probe refuses null or misaligned pointers, sizes that are not whole
+    16-byte units and unknown modes before any HIP call; nothing to move is a no-op."""
+    f = lambda *a: B.raw_status("gdn_beam_stream_probe", *a)
+    A = 1 << 20                                    # aligned host-side stand-ins, never used
+    assert f(None, A, 64, 0, None) == B.GDN_ERR_INVALID_ARG
+    assert f(A, None, 64, 1, None) == B.GDN_ERR_INVALID_ARG
+    assert f(A + 4, A, 64, 0, None) == B.GDN_ERR_INVALID_ARG
+    assert f(A, A + 8, 64, 0, None) == B.GDN_ERR_INVALID_ARG
+    assert f(A, A, 60, 0, None) == B.GDN_ERR_INVALID_ARG
+    assert f(A, A, 64, 2, None) == B.GDN_ERR_INVALID_ARG
+    assert f(A, A, 64, -1, None) == B.GDN_ERR_INVALID_ARG
+    assert f(A, A, 0, 0, None) == B.GDN_OK
+
+
 def test_prefill_argument_errors():
     f = lambda *a: B.raw_status("gdn_beam_prefill", *a)
     F6 = (FAKE,) * 6
