@@ -199,15 +199,16 @@ def copy_bandwidth(torch, dev, mib=1024, reps=10):
 
 def stream_bandwidth(torch, dev, mib=1024, reps=6):
     """GB/s of the library's streaming probe (gdn_beam_stream_probe): a copy (every byte
-    read and written) and a read of `mib` MiB with 16-byte non-temporal accesses, four
-    workgroups per compute unit; the fastest of `reps` launches after the first."""
+    read and written) and a read of `mib` MiB with 16-byte non-temporal accesses, and a
+    write of `mib` MiB in the fused step's store pattern, four workgroups per compute
+    unit; the fastest of `reps` launches after the first."""
     from linear_attention_beam_amd import binding as Bb
     n = mib * (1 << 20)
     src = torch.ones(n // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     stream = torch.cuda.current_stream()
     out = {}
-    for mode, name, moved in ((0, "copy", 2 * n), (1, "read", n)):
+    for mode, name, moved in ((0, "copy", 2 * n), (1, "read", n), (2, "write", n)):
         Bb.gdn_beam_stream_probe(dst, src, n, mode, stream)
         best = None
         for _ in range(reps):
@@ -703,7 +704,8 @@ def main():
     copy_gbs = copy_bandwidth(torch, dev)
     log(args, f"device copy (read + write): {copy_gbs:.0f} GB/s")
     stream_gbs = stream_bandwidth(torch, dev)
-    log(args, f"streaming probe: copy {stream_gbs['copy']:.0f} GB/s, read {stream_gbs['read']:.0f} GB/s")
+    log(args, f"streaming probe: copy {stream_gbs['copy']:.0f} GB/s, read {stream_gbs['read']:.0f} GB/s, "
+              f"write {stream_gbs['write']:.0f} GB/s")
 
     head = run_workload(args, wl, mode, torch, copy_gbs)
 
@@ -711,6 +713,7 @@ def main():
         # the step kernel's achieved rate against the streaming probe (not the peak)
         rf["stream_copy_GBs"] = stream_gbs["copy"]
         rf["stream_read_GBs"] = stream_gbs["read"]
+        rf["stream_write_GBs"] = stream_gbs["write"]
         rf["frac_of_stream_copy"] = rf["achieved"] / stream_gbs["copy"]
         return rf
 

@@ -240,11 +240,14 @@ gdn_status gdn_beam_stamp_projection(void* buf, size_t bytes);
 
 /* Measurement, not an operation of the method: the device's streaming rate, the
  * reference against which HBM-bound launches are read.  mode 0 copies `bytes` from src
- * to dst; mode 1 reads src and writes at most one 4-byte word at dst.  Both device,
- * caller-owned, 16-byte aligned, bytes a multiple of 16 (not overlapping for mode 0);
- * 16-byte non-temporal loads and stores, four 256-thread workgroups per compute unit,
+ * to dst; mode 1 reads src and writes at most one 4-byte word at dst; mode 2 only
+ * writes dst (src unused, may be NULL), as 512-byte rows in the fused step's store
+ * pattern (each row in four 128-byte pieces from four waves, eight rows per store;
+ * floor(bytes / 16384) groups of 32 rows).  Pointers are device, caller-owned, 16-byte
+ * aligned, bytes a multiple of 16 (not overlapping for mode 0); 16-byte accesses
+ * (non-temporal for modes 0 and 1), four 256-thread workgroups per compute unit,
  * grid-strided, on `stream`.  Errors: null or misaligned pointers, bytes not a multiple
- * of 16, mode outside 0..1 (INVALID_ARG); a launch failure (HIP). */
+ * of 16, mode outside 0..2 (INVALID_ARG); a launch failure (HIP). */
 gdn_status gdn_beam_stream_probe(void* dst, const void* src, size_t bytes, int32_t mode,
                                  hipStream_t stream);
 

@@ -389,8 +389,8 @@ gdn_status gdn_beam_stamp_projection(void* buf, size_t bytes) {
 
 gdn_status gdn_beam_stream_probe(void* dst, const void* src, size_t bytes, int32_t mode,
                                  hipStream_t stream) {
-  if (!dst || !src || !aligned16(dst) || !aligned16(src) || bytes % 16 != 0 || mode < 0 || mode > 1)
-    return GDN_ERR_INVALID_ARG;
+  if (!dst || !aligned16(dst) || bytes % 16 != 0 || mode < 0 || mode > 2) return GDN_ERR_INVALID_ARG;
+  if (mode != 2 && (!src || !aligned16(src))) return GDN_ERR_INVALID_ARG;
   if (bytes == 0) return GDN_OK;
   const int err = launch_stream_probe(dst, src, bytes, mode, stream);
   return err ? hip_fail(err, "gdn_beam_stream_probe") : GDN_OK;

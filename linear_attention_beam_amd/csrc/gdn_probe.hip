@@ -1,8 +1,9 @@
 // Measurement kernels, not part of the method: the device's streaming rate, as a
 // reference for the library's HBM-bound launches.  A grid-strided copy (every 16 bytes
 // read once and written once) and a grid-strided read, with 16-byte non-temporal
-// accesses and four 256-thread workgroups per compute unit (the shape that streamed
-// fastest among 4, 16 and 64 per unit on MI355X).
+// accesses, and a write in the fused step's store pattern; four 256-thread workgroups
+// per compute unit (the shape that streamed fastest among 4, 16 and 64 per unit on
+// MI355X).
 #include "gdn_device.h"
 
 namespace gdn {
@@ -28,6 +29,21 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restric
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Writes only, in the fused step's store pattern: 512-byte rows (a d_v = 128 fp32 row),
+// a 4-wave workgroup per 32 rows, wave w writing bytes [128 w, 128 w + 128) of each row,
+// eight lanes per row (eight rows per store); rows past the last whole group of 32 are
+// not written.
+__global__ void __launch_bounds__(256) stream_write_kernel(u32x4* __restrict__ dst, size_t rows) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const u32x4 v = {0x3F800000u, 0x3F800000u, 0x3F800000u, 0x3F800000u};
+  for (size_t g = blockIdx.x; g < rows / 32; g += gridDim.x)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const size_t row = 32 * g + 8 * q + (lane >> 3);
+      dst[row * 32 + 8 * w + (lane & 7)] = v;
+    }
+}
+
 int launch_stream_probe(void* dst, const void* src, size_t bytes, int mode, hipStream_t s) {
   (void)hipGetLastError();
   int dev = 0, cus = 0;
@@ -39,6 +55,9 @@ int launch_stream_probe(void* dst, const void* src, size_t bytes, int mode, hipS
   if (mode == 0)
     hipLaunchKernelGGL(stream_copy_kernel, dim3(grid), dim3(256), 0, s, static_cast<const u32x4*>(src),
                        static_cast<u32x4*>(dst), n);
+  else if (mode == 2)
+    hipLaunchKernelGGL(stream_write_kernel, dim3(grid), dim3(256), 0, s, static_cast<u32x4*>(dst),
+                       bytes / 512);
   else
     hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, s, static_cast<const u32x4*>(src),
                        static_cast<uint32_t*>(dst), n);

@@ -194,8 +194,10 @@ def test_stream_probe_argument_errors():
     assert f(A + 4, A, 64, 0, None) == B.GDN_ERR_INVALID_ARG
     assert f(A, A + 8, 64, 0, None) == B.GDN_ERR_INVALID_ARG
     assert f(A, A, 60, 0, None) == B.GDN_ERR_INVALID_ARG
-    assert f(A, A, 64, 2, None) == B.GDN_ERR_INVALID_ARG
+    assert f(A, A, 64, 3, None) == B.GDN_ERR_INVALID_ARG
     assert f(A, A, 64, -1, None) == B.GDN_ERR_INVALID_ARG
+    assert f(None, None, 64, 2, None) == B.GDN_ERR_INVALID_ARG      # the write needs dst
+    assert f(A + 4, None, 64, 2, None) == B.GDN_ERR_INVALID_ARG
     assert f(A, A, 0, 0, None) == B.GDN_OK
 
 

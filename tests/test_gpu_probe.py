@@ -28,11 +28,20 @@ def test_stream_probe_copy_and_read():
     assert bool((sink[1:] == 5).all())
 
 
+def test_stream_probe_write_pattern():
+    """The write covers whole groups of 32 rows of 512 bytes and nothing past them."""
+    rows = 3 * 32 + 5                               # a partial group at the end
+    dst = torch.zeros(rows * 128, device="cuda", dtype=torch.float32)
+    B.gdn_beam_stream_probe(dst, None, rows * 512, 2)
+    torch.cuda.synchronize()
+    assert bool((dst[:96 * 128] == 1.0).all()) and bool((dst[96 * 128:] == 0.0).all())
+
+
 def test_stream_probe_refuses_bad_arguments():
     x = torch.zeros(1024, device="cuda", dtype=torch.int32)
     for args in ((x, x[1:], 64, 0),               # misaligned source
                  (x, x, 60, 0),                   # not a multiple of 16 bytes
-                 (x, x, 64, 2),                   # no such mode
+                 (x, x, 64, 3),                   # no such mode
                  (None, x, 64, 1)):
         with pytest.raises(B.GdnBeamError) as e:
             B.gdn_beam_stream_probe(*args)
